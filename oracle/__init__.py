@@ -1,0 +1,227 @@
+"""fp64 CPU oracle of the Gated DeltaNet token mixer (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import this package.  It shares no code with the GPU library
+(``linear_attention_sequence_causal_amd``) and neither imports the other.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, token by token); this
+module builds it with gcc when needed and marshals numpy arrays to it.  See the
+header of ``gdn_oracle.c`` for the passages of the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_gdn.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gdn_oracle.c into liboracle_gdn.so with gcc (plain -O2)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            d = ctypes.c_double
+            pd = ctypes.POINTER(ctypes.c_double)
+            p64 = ctypes.POINTER(ctypes.c_int64)
+            i32 = ctypes.c_int
+            i64 = ctypes.c_int64
+            lib.oracle_sigmoid.restype = d
+            lib.oracle_sigmoid.argtypes = [d]
+            lib.oracle_silu.restype = d
+            lib.oracle_silu.argtypes = [d]
+            lib.oracle_softplus.restype = d
+            lib.oracle_softplus.argtypes = [d]
+            lib.oracle_gates.restype = None
+            lib.oracle_gates.argtypes = [i64, pd, pd, d, d, pd, pd]
+            lib.oracle_prologue.restype = None
+            lib.oracle_prologue.argtypes = [i64, i32, i32, i32, i32, pd, pd, pd, pd, pd,
+                                            d, d, pd, pd, pd]
+            lib.oracle_recurrence.restype = None
+            lib.oracle_recurrence.argtypes = [i64, i32, pd, pd, pd, pd, pd, pd, pd]
+            lib.oracle_epilogue.restype = None
+            lib.oracle_epilogue.argtypes = [i64, i32, pd, pd, i64, pd, d, pd, i64]
+            lib.oracle_prefill.restype = i32
+            lib.oracle_prefill.argtypes = [i32, p64, i32, i32, i32, pd, pd, pd, pd, pd, pd,
+                                           pd, pd, pd, pd, d, d, d, pd, pd, pd, pd, pd, i32]
+            lib.oracle_decode_step.restype = i32
+            lib.oracle_decode_step.argtypes = [i32, i32, i32, i32, pd, pd, pd, pd, pd, pd,
+                                               pd, pd, pd, pd, d, d, d, pd, pd, pd, i32]
+            _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """C-contiguous float64 copy (or view) of x; None stays None."""
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+# ----------------------------------------------------------------- scalars
+
+def sigmoid(u: float) -> float:
+    return _load().oracle_sigmoid(float(u))
+
+
+def silu(u: float) -> float:
+    return _load().oracle_silu(float(u))
+
+
+def softplus(u: float) -> float:
+    return _load().oracle_softplus(float(u))
+
+
+def gates(a, b, A_log: float, dt_bias: float):
+    """alpha, beta of one head for token arrays a, b (model-card decay gate)."""
+    a = _f64(a).ravel()
+    b = _f64(b).ravel()
+    al = np.empty_like(a)
+    be = np.empty_like(a)
+    _load().oracle_gates(a.size, _ptr(a), _ptr(b), float(A_log), float(dt_bias),
+                         _ptr(al), _ptr(be))
+    return al, be
+
+
+# ------------------------------------------------------------------ stages
+
+def prologue(q, k, v, conv_w, h: int, hist=None, q_scale=1.0, l2_eps=1e-6):
+    """Post-conv/SiLU/L2 q, k (q/k head h // r) and v (v head h) of one sequence.
+
+    q, k: [T, Hk, D]; v: [T, Hv, D]; conv_w: [Cc, 4]; hist: [3, Cc] or None.
+    Returns three [T, D] float64 arrays.
+    """
+    q, k, v, conv_w, hist = map(_f64, (q, k, v, conv_w, hist))
+    T, Hk, D = q.shape
+    Hv = v.shape[1]
+    qo = np.empty((T, D))
+    ko = np.empty((T, D))
+    vo = np.empty((T, D))
+    _load().oracle_prologue(T, Hk, Hv, D, h, _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w),
+                            _ptr(hist), float(q_scale), float(l2_eps),
+                            _ptr(qo), _ptr(ko), _ptr(vo))
+    return qo, ko, vo
+
+
+def recurrence(alpha, beta, q, k, v, S0=None):
+    """Bare gated delta recurrence of one head (column convention, S: key->value).
+
+    q, k, v: [T, D]; alpha, beta: [T]; S0: [D, D] (S[value][key]) or None.
+    Returns (y [T, D], S_T [D, D]).
+    """
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    T, D = q.shape
+    S = np.zeros((D, D)) if S0 is None else _f64(S0).copy()
+    y = np.empty((T, D))
+    _load().oracle_recurrence(T, D, _ptr(alpha), _ptr(beta), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(S), _ptr(y))
+    return y, S
+
+
+def epilogue(y, z, norm_w=None, rms_eps=1e-6):
+    """RMS-normalise y per token over D, scale by norm_w, gate with SiLU(z)."""
+    y, z, norm_w = map(_f64, (y, z, norm_w))
+    T, D = y.shape
+    o = np.empty((T, D))
+    _load().oracle_epilogue(T, D, _ptr(y), _ptr(z), D, _ptr(norm_w), float(rms_eps),
+                            _ptr(o), D)
+    return o
+
+
+# ------------------------------------------------------------------- mixer
+
+def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *,
+            cu_seqlens=None, init_state=None, conv_in=None,
+            q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+    """Whole mixer over packed sequences, fp64.
+
+    Returns (o [T, Hv, D], final_state [N, Hv, D, D] as H = S^T, conv_out [N, 3, Cc]).
+    """
+    q, k, v, a, b, z = map(_f64, (q, k, v, a, b, z))
+    conv_w, A_log, dt_bias, norm_w = map(_f64, (conv_w, A_log, dt_bias, norm_w))
+    init_state, conv_in = _f64(init_state), _f64(conv_in)
+    T, Hk, D = q.shape
+    Hv = v.shape[1]
+    if cu_seqlens is None:
+        cu_seqlens = [0, T]
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.size - 1
+    Cc = 2 * Hk * D + Hv * D
+    o = np.empty((T, Hv, D))
+    fs = np.empty((N, Hv, D, D))
+    co = np.empty((N, 3, Cc))
+    rc = _load().oracle_prefill(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), Hk, Hv, D,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z), _ptr(conv_w), _ptr(A_log),
+        _ptr(dt_bias), _ptr(norm_w), float(q_scale), float(l2_eps), float(rms_eps),
+        _ptr(init_state), _ptr(conv_in), _ptr(o), _ptr(fs), _ptr(co),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_prefill: invalid arguments")
+    return o, fs, co
+
+
+def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
+                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+    """One decode step for B sequences.  Returns (o, new_state, new_conv_cache)."""
+    q, k, v, a, b, z = map(_f64, (q, k, v, a, b, z))
+    conv_w, A_log, dt_bias, norm_w = map(_f64, (conv_w, A_log, dt_bias, norm_w))
+    state = _f64(state).copy()
+    cache = _f64(conv_cache).copy()
+    B, Hk, D = q.shape
+    Hv = v.shape[1]
+    o = np.empty((B, Hv, D))
+    rc = _load().oracle_decode_step(
+        B, Hk, Hv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z), _ptr(conv_w),
+        _ptr(A_log), _ptr(dt_bias), _ptr(norm_w), float(q_scale), float(l2_eps),
+        float(rms_eps), _ptr(state), _ptr(cache), _ptr(o), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_decode_step: invalid arguments")
+    return o, state, cache
+
+
+def select_heads(qk_heads, Hk: int, Hv: int, D: int):
+    """Index helpers to run the oracle on a subset of q/k heads (and their v heads).
+
+    Returns (qk_idx, v_idx, conv_channel_idx) for slicing q/k [.., Hk, D],
+    v/z/a/b [.., Hv(, D)] and conv weights / history [.., Cc].
+    """
+    r = Hv // Hk
+    qk_idx = np.asarray(sorted(qk_heads), dtype=np.int64)
+    v_idx = np.asarray([g * r + j for g in qk_idx for j in range(r)], dtype=np.int64)
+    ch = [g * D + i for g in qk_idx for i in range(D)]
+    ch += [Hk * D + g * D + i for g in qk_idx for i in range(D)]
+    ch += [2 * Hk * D + h * D + i for h in v_idx for i in range(D)]
+    return qk_idx, v_idx, np.asarray(ch, dtype=np.int64)

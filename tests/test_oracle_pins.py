@@ -1,0 +1,457 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: the worked
+two-token example (tests/golden), closed forms, invariants, special cases that
+reduce to textbook formulas, and brute force on tiny inputs.  The passages:
+field guide "Qwen3-Next 80B-A3B", cutaway 02 (six update steps, counts, RMSNorm
+and SiLU(z) gate); Qwen3.8-Flash-Next model card (decay gate g, chunk state
+update); tech report Fig. 2 caption (short causal convs, L2-normalised q/k,
+decay and write gates).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "two_token_example.json")
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def _l2(x, eps=1e-6):
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + eps)
+
+
+# --------------------------------------------------------------- scalars
+
+def test_scalar_closed_forms():
+    assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), abs=1e-15)
+    assert oracle.softplus(math.log(math.e - 1.0)) == pytest.approx(1.0, abs=1e-15)
+    assert oracle.softplus(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert oracle.softplus(-40.0) == pytest.approx(math.exp(-40.0), rel=1e-12)
+    assert oracle.softplus(float("inf")) == float("inf")
+    assert oracle.softplus(float("-inf")) == 0.0
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.sigmoid(math.log(3.0)) == pytest.approx(0.75, abs=1e-15)
+    assert oracle.sigmoid(float("inf")) == 1.0
+    assert oracle.sigmoid(float("-inf")) == 0.0
+    assert oracle.silu(2.0) == pytest.approx(2.0 / (1.0 + math.exp(-2.0)), abs=1e-15)
+    assert oracle.silu(0.0) == 0.0
+
+
+def test_gate_closed_forms():
+    # A_log = 0, a + dt_bias = 0  ->  g = -ln 2  ->  alpha = 1/2;  b = 0 -> beta = 1/2
+    al, be = oracle.gates([0.0], [0.0], 0.0, 0.0)
+    assert al[0] == pytest.approx(0.5, abs=1e-15) and be[0] == 0.5
+    # A_log = ln 3, a + dt_bias = ln(e - 1)  ->  g = -3
+    al, _ = oracle.gates([math.log(math.e - 1.0) - 0.25], [0.0], math.log(3.0), 0.25)
+    assert al[0] == pytest.approx(math.exp(-3.0), rel=1e-14)
+    # the bias enters inside softplus, not outside
+    al1, _ = oracle.gates([1.0], [0.0], 0.0, -1.0)
+    assert al1[0] == pytest.approx(0.5, abs=1e-15)
+    # extremes: A_log = -inf -> alpha = 1; A_log = 100 -> alpha underflows to 0
+    al, be = oracle.gates([0.3, -2.0], [float("inf"), float("-inf")], float("-inf"), 0.0)
+    assert np.all(al == 1.0) and be[0] == 1.0 and be[1] == 0.0
+    al, _ = oracle.gates([0.3, -2.0], [0.0, 0.0], 100.0, 0.0)
+    assert np.all(al == 0.0) and not np.any(np.isnan(al))
+
+
+# ------------------------------------------------------- worked example (P4)
+
+def test_two_token_worked_example():
+    ex = json.load(open(GOLDEN))
+    y, S = oracle.recurrence(ex["alpha"], ex["beta"], ex["q"], ex["k"], ex["v"])
+    np.testing.assert_allclose(y, ex["y"], atol=1e-15)
+    np.testing.assert_allclose(S, ex["S2"], atol=1e-15)
+    y1, S1 = oracle.recurrence(ex["alpha"][:1], ex["beta"][:1], ex["q"][:1], ex["k"][:1],
+                               ex["v"][:1])
+    np.testing.assert_allclose(S1, ex["S1"], atol=1e-15)
+    # beta_2 = 1: the write makes S2 k2 = v2 exactly
+    _, Sb = oracle.recurrence(ex["alpha"], [0.5, 1.0], ex["q"], ex["k"], ex["v"])
+    np.testing.assert_allclose(Sb, ex["S2_beta2_one"], atol=1e-15)
+    np.testing.assert_allclose(Sb @ np.array(ex["k"][1]), ex["v"][1], atol=1e-15)
+    # epilogue of y2 (w = 1, eps = 0, z large so SiLU(z) = z; divide it out)
+    z = np.full((1, 2), 60.0)
+    o = oracle.epilogue(np.array([ex["y"][1]]), z, None, rms_eps=0.0)
+    np.testing.assert_allclose(o[0] / 60.0, ex["y2_rmsnorm_eps0"], atol=1e-15)
+    # the carried state is read with S0 q (beta = 0, alpha = 1)
+    yc, Sc = oracle.recurrence([1.0, 1.0], [0.0, 0.0], ex["q"], ex["k"], ex["v"],
+                               S0=ex["carry_S0"])
+    np.testing.assert_allclose(yc, ex["carry_y"], atol=1e-15)
+    assert np.array_equal(Sc, np.array(ex["carry_S0"]))
+
+
+def test_two_token_example_through_the_mixer():
+    """The worked example's gates and keys through the whole mixer; the stored
+    state must be H = S^T.
+
+    One-hot conv taps on the current token and raw q, k = 40 * (golden unit
+    vectors) make the post-prologue q, k equal the golden ones to 1e-15
+    (SiLU(40) = 40 (1 - 4e-18), SiLU(0) = 0, then L2 normalisation).  v passes
+    through SiLU, so the expected state is rebuilt from SiLU(v) with the
+    cutaway's six steps.
+    """
+    ex = json.load(open(GOLDEN))
+    D, Hk, Hv = 2, 1, 1
+    kk = np.array(ex["k"]) * 40.0
+    qq = np.array(ex["q"]) * 40.0
+    vv = np.array(ex["v"])
+    conv_w = np.zeros((2 * Hk * D + Hv * D, 4))
+    conv_w[:, 3] = 1.0
+    z = np.full((2, Hv, D), 60.0)
+    o, fs, _ = oracle.prefill(qq.reshape(2, Hk, D), kk.reshape(2, Hk, D), vv.reshape(2, Hv, D),
+                              np.zeros((2, Hv)), np.zeros((2, Hv)), z, conv_w, [0.0], [0.0],
+                              None, l2_eps=0.0, rms_eps=0.0)
+    qpost = _silu(qq) / np.linalg.norm(_silu(qq), axis=1, keepdims=True)
+    kpost = _silu(kk) / np.linalg.norm(_silu(kk), axis=1, keepdims=True)
+    np.testing.assert_allclose(kpost, ex["k"], atol=1e-15)
+    np.testing.assert_allclose(qpost, ex["q"], atol=1e-15)
+    vpost = _silu(vv)
+    S = np.zeros((2, 2))
+    ys = []
+    for t in range(2):  # alpha = beta = 1/2 from A_log = a = dt_bias = b = 0
+        S = 0.5 * S
+        e = vpost[t] - S @ kpost[t]
+        S = S + 0.5 * np.outer(e, kpost[t])
+        ys.append(S @ qpost[t])
+    np.testing.assert_allclose(fs[0, 0], S.T, atol=1e-14)
+    assert abs(fs[0, 0][0, 1] - fs[0, 0][1, 0]) > 1e-3  # not symmetric: orientation matters
+    yt = np.array(ys)
+    oref = yt / np.sqrt((yt ** 2).mean(1, keepdims=True)) * _silu(60.0)
+    np.testing.assert_allclose(o[:, 0, :], oref, atol=1e-13)
+
+
+# ------------------------------------------------------ recurrence invariants
+
+def _rand_unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=1, keepdims=True)
+
+
+def test_p1_identity_gates_keep_state():
+    rng = np.random.default_rng(1)
+    D, T = 8, 13
+    S0 = rng.standard_normal((D, D))
+    q, k, v = rng.standard_normal((T, D)), _rand_unit(rng, T, D), rng.standard_normal((T, D))
+    y, S = oracle.recurrence(np.ones(T), np.zeros(T), q, k, v, S0=S0)
+    assert np.array_equal(S, S0)
+    np.testing.assert_allclose(y, q @ S0.T, atol=1e-13)
+
+
+def test_p2_full_write_reproduces_value():
+    rng = np.random.default_rng(2)
+    D, T = 16, 20
+    k = _rand_unit(rng, T, D)
+    v = rng.standard_normal((T, D))
+    q = rng.standard_normal((T, D))
+    S = rng.standard_normal((D, D))
+    for t in range(T):
+        _, S = oracle.recurrence([1.0], [1.0], q[t:t + 1], k[t:t + 1], v[t:t + 1], S0=S)
+        np.testing.assert_allclose(S @ k[t], v[t], atol=1e-13)
+
+
+def test_p3_state_size_fixed():
+    rng = np.random.default_rng(3)
+    D = 4
+    for T in (1, 17, 512):
+        _, S = oracle.recurrence(rng.uniform(0.5, 1, T), rng.uniform(0, 1, T),
+                                 rng.standard_normal((T, D)), _rand_unit(rng, T, D),
+                                 rng.standard_normal((T, D)))
+        assert S.shape == (D, D)
+
+
+def test_p5_orthogonal_keys_is_decayed_linear_attention():
+    """With orthonormal keys the read-back is zero, so the recurrence reduces to
+    decay-masked causal linear attention: y = ((Q K^T) * Dmask) diag(beta) V."""
+    rng = np.random.default_rng(5)
+    D = T = 12
+    K = np.linalg.qr(rng.standard_normal((D, D)))[0].T  # rows orthonormal
+    Q = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    alpha = rng.uniform(0.3, 1.0, T)
+    beta = rng.uniform(0.0, 1.0, T)
+    y, _ = oracle.recurrence(alpha, beta, Q, K, V)
+    Dm = np.zeros((T, T))
+    for t in range(T):
+        for s in range(t + 1):
+            Dm[t, s] = np.prod(alpha[s + 1:t + 1])  # decay applied after the write at s
+    yref = ((Q @ K.T) * Dm) @ (beta[:, None] * V)
+    np.testing.assert_allclose(y, yref, atol=1e-13)
+
+
+def test_p6_projection_property():
+    rng = np.random.default_rng(6)
+    D, T = 10, 15
+    k = _rand_unit(rng, T, D)
+    q, v = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    S = rng.standard_normal((D, D))
+    for t in range(T):
+        P = np.eye(D) - np.outer(k[t], k[t])
+        _, Sn = oracle.recurrence([1.0], [1.0], q[t:t + 1], k[t:t + 1], v[t:t + 1], S0=S)
+        np.testing.assert_allclose(Sn @ P, S @ P, atol=1e-13)
+        S = Sn
+
+
+def test_p12_forgetting_limit():
+    rng = np.random.default_rng(12)
+    D, T = 8, 9
+    q, k, v = rng.standard_normal((T, D)), _rand_unit(rng, T, D), rng.standard_normal((T, D))
+    beta = rng.uniform(0, 1, T)
+    al, _ = oracle.gates(rng.standard_normal(T), np.zeros(T), 100.0, 0.0)
+    assert np.all(al == 0.0)
+    y, S = oracle.recurrence(al, beta, q, k, v, S0=rng.standard_normal((D, D)))
+    np.testing.assert_allclose(S, beta[-1] * np.outer(v[-1], k[-1]), atol=1e-15)
+    np.testing.assert_allclose(y, (beta * (k * q).sum(1))[:, None] * v, atol=1e-14)
+    assert not np.any(np.isnan(y))
+
+
+def test_decay_precedes_read_and_write():
+    """Order of the cutaway: decay, then read S'k, then write.  A single token
+    with S0 = I, k = e0, v = 0: S1 = alpha I - beta alpha e0 e0^T."""
+    D = 3
+    alpha, beta = 0.25, 0.5
+    k = np.array([[1.0, 0, 0]])
+    y, S = oracle.recurrence([alpha], [beta], np.array([[0, 1.0, 0]]), k, np.zeros((1, D)),
+                             S0=np.eye(D))
+    ref = alpha * np.eye(D) - beta * alpha * np.outer(k[0], k[0])
+    np.testing.assert_allclose(S, ref, atol=1e-16)
+    np.testing.assert_allclose(y[0], ref @ np.array([0, 1.0, 0]), atol=1e-16)
+
+
+def test_p11_scale_invariance_in_v():
+    rng = np.random.default_rng(11)
+    D, T = 8, 10
+    q, k, v = rng.standard_normal((T, D)), _rand_unit(rng, T, D), rng.standard_normal((T, D))
+    al, be = rng.uniform(0.2, 1, T), rng.uniform(0, 1, T)
+    y1, _ = oracle.recurrence(al, be, q, k, v)
+    y3, _ = oracle.recurrence(al, be, q, k, 3.0 * v)
+    np.testing.assert_allclose(y3, 3.0 * y1, rtol=1e-12, atol=1e-14)
+    z = rng.standard_normal((T, D))
+    np.testing.assert_allclose(oracle.epilogue(y3, z, rms_eps=0.0),
+                               oracle.epilogue(y1, z, rms_eps=0.0), rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------ prologue pins
+
+def _mixer_inputs(rng, T, Hk, Hv, D, scale=1.0):
+    q = rng.standard_normal((T, Hk, D)) * scale
+    k = rng.standard_normal((T, Hk, D)) * scale
+    v = rng.standard_normal((T, Hv, D)) * scale
+    return q, k, v
+
+
+def test_p10_conv_taps_and_channel_sections():
+    rng = np.random.default_rng(10)
+    T, Hk, Hv, D = 9, 2, 4, 8
+    Cc = 2 * Hk * D + Hv * D
+    q, k, v = _mixer_inputs(rng, T, Hk, Hv, D)
+    hist = rng.standard_normal((3, Cc))
+    w = np.zeros((Cc, 4))
+    w[: Hk * D, 3] = 1.0            # q: current token
+    w[Hk * D: 2 * Hk * D, 2] = 1.0  # k: one step back
+    w[2 * Hk * D:, 0] = 1.0         # v: three steps back
+    for h in range(Hv):
+        g = h // (Hv // Hk)
+        qo, ko, vo = oracle.prologue(q, k, v, w, h, hist=hist, l2_eps=1e-6)
+        np.testing.assert_allclose(qo, _l2(_silu(q[:, g])), atol=1e-15)
+        kprev = np.concatenate([hist[2:3, Hk * D + g * D: Hk * D + (g + 1) * D], k[:-1, g]])
+        np.testing.assert_allclose(ko, _l2(_silu(kprev)), atol=1e-15)
+        c0 = 2 * Hk * D + h * D
+        vprev = np.concatenate([hist[:, c0:c0 + D], v[:-3, h]])
+        np.testing.assert_allclose(vo, _silu(vprev), atol=1e-15)
+    # zero history by default: v three steps back is SiLU(0) = 0 for t < 3
+    _, _, vo = oracle.prologue(q, k, v, w, 1)
+    assert np.all(vo[:3] == 0.0)
+
+
+def test_conv_is_a_weighted_sum_of_four_taps():
+    rng = np.random.default_rng(13)
+    T, Hk, Hv, D = 7, 1, 2, 4
+    Cc = 2 * Hk * D + Hv * D
+    q, k, v = _mixer_inputs(rng, T, Hk, Hv, D)
+    w = rng.standard_normal((Cc, 4))
+    _, _, vo = oracle.prologue(q, k, v, w, 1, l2_eps=0.0)
+    c0 = 2 * Hk * D + 1 * D
+    xpad = np.concatenate([np.zeros((3, D)), v[:, 1]])
+    pre = sum(w[c0:c0 + D, j][None, :] * xpad[j:j + T] for j in range(4))
+    np.testing.assert_allclose(vo, _silu(pre), atol=1e-14)
+
+
+def test_l2_normalisation_and_query_scale():
+    rng = np.random.default_rng(14)
+    T, Hk, Hv, D = 5, 1, 1, 16
+    q, k, v = _mixer_inputs(rng, T, Hk, Hv, D, scale=3.0)
+    w = np.zeros((2 * D + D, 4))
+    w[:, 3] = 1.0
+    qo, ko, _ = oracle.prologue(q, k, v, w, 0, q_scale=0.5, l2_eps=0.0)
+    np.testing.assert_allclose(np.linalg.norm(ko, axis=1), 1.0, atol=1e-15)
+    np.testing.assert_allclose(np.linalg.norm(qo, axis=1), 0.5, atol=1e-15)
+    # eps keeps an all-zero vector at zero instead of NaN
+    qz = np.zeros_like(q)
+    w0 = np.zeros_like(w)
+    qo, ko, _ = oracle.prologue(qz, qz, v, w0, 0, l2_eps=1e-6)
+    assert np.all(qo == 0.0) and np.all(ko == 0.0)
+
+
+# ------------------------------------------------------------ epilogue pins
+
+def test_epilogue_closed_forms():
+    D = 8
+    c = -0.3
+    y = np.full((1, D), c)
+    wn = np.linspace(0.5, 2.0, D)
+    z = np.full((1, D), 2.0)
+    o = oracle.epilogue(y, z, wn, rms_eps=1e-6)
+    np.testing.assert_allclose(o[0], c / math.sqrt(c * c + 1e-6) * wn * _silu(2.0), atol=1e-15)
+    o0 = oracle.epilogue(np.random.default_rng(0).standard_normal((3, D)), np.zeros((3, D)))
+    assert np.all(o0 == 0.0)
+
+
+# --------------------------------------------------------------- mixer pins
+
+def _mixer_case(rng, lengths, Hk=2, Hv=4, D=16, init=True, hist=True):
+    T = int(sum(lengths))
+    N = len(lengths)
+    Cc = 2 * Hk * D + Hv * D
+    q, k, v = _mixer_inputs(rng, T, Hk, Hv, D)
+    return dict(
+        q=q, k=k, v=v, a=rng.standard_normal((T, Hv)), b=rng.standard_normal((T, Hv)),
+        z=rng.standard_normal((T, Hv, D)), conv_w=rng.standard_normal((Cc, 4)) * 0.5,
+        A_log=rng.uniform(0, math.log(16), Hv), dt_bias=rng.uniform(-1, 1, Hv),
+        norm_w=rng.uniform(0.5, 1.5, D),
+        cu=np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64),
+        init=rng.standard_normal((N, Hv, D, D)) * 0.1 if init else None,
+        hist=rng.standard_normal((N, 3, Cc)) if hist else None)
+
+
+def _run(c, sl=None, cu=None, init="keep", hist="keep"):
+    sl = slice(None) if sl is None else sl
+    return oracle.prefill(c["q"][sl], c["k"][sl], c["v"][sl], c["a"][sl], c["b"][sl],
+                          c["z"][sl], c["conv_w"], c["A_log"], c["dt_bias"], c["norm_w"],
+                          cu_seqlens=c["cu"] if cu is None else cu,
+                          init_state=c["init"] if isinstance(init, str) else init,
+                          conv_in=c["hist"] if isinstance(hist, str) else hist)
+
+
+def test_p1_mixer_level_state_unchanged():
+    rng = np.random.default_rng(21)
+    c = _mixer_case(rng, [11])
+    c["b"][:] = -np.inf
+    c["A_log"][:] = -np.inf
+    o, fs, _ = _run(c)
+    assert np.array_equal(fs, c["init"])
+    # y = S0 q = H0^T q  with q from the prologue
+    for h in range(4):
+        qo, _, _ = oracle.prologue(c["q"], c["k"], c["v"], c["conv_w"], h, hist=c["hist"][0])
+        y = qo @ c["init"][0, h]
+        yn = y / np.sqrt((y * y).mean(1, keepdims=True) + 1e-6)
+        np.testing.assert_allclose(o[:, h], yn * c["norm_w"] * _silu(c["z"][:, h]), atol=1e-13)
+
+
+def test_p2_mixer_level_full_write():
+    rng = np.random.default_rng(22)
+    c = _mixer_case(rng, [6])
+    c["b"][:] = np.inf
+    c["A_log"][:] = -np.inf
+    _, fs, _ = _run(c)
+    for h in range(4):
+        _, ko, vo = oracle.prologue(c["q"], c["k"], c["v"], c["conv_w"], h, hist=c["hist"][0])
+        S = fs[0, h].T
+        np.testing.assert_allclose(S @ ko[-1], vo[-1], atol=1e-5 * np.abs(vo[-1]).max())
+
+
+def test_gqa_head_mapping():
+    """v heads 2g and 2g+1 read q/k head g: make q.k positive on q/k head 0 and
+    negative on head 1; in the forgetting limit o flips sign exactly there."""
+    T, Hk, Hv, D = 3, 2, 4, 4
+    Cc = 2 * Hk * D + Hv * D
+    q = np.zeros((T, Hk, D))
+    k = np.zeros((T, Hk, D))
+    k[:, :, 0] = 30.0
+    q[:, 0, 0] = 30.0
+    q[:, 1, 0], q[:, 1, 1] = -30.0, 30.0  # SiLU -> (-~0, 30): q.k slightly negative
+    rng = np.random.default_rng(23)
+    v = np.abs(rng.standard_normal((T, Hv, D))) + 5.0
+    w = np.zeros((Cc, 4))
+    w[:, 3] = 1.0
+    z = np.full((T, Hv, D), 40.0)
+    o, _, _ = oracle.prefill(q, k, v, np.zeros((T, Hv)), np.zeros((T, Hv)), z, w,
+                             np.full(Hv, 100.0), np.zeros(Hv), None)
+    assert np.all(o[:, 0:2] > 0) and np.all(o[:, 2:4] < 0)
+
+
+def test_p7_split_sequence_bitwise():
+    rng = np.random.default_rng(7)
+    T = 23
+    c = _mixer_case(rng, [T])
+    o_full, fs_full, co_full = _run(c)
+    for t0 in (1, 2, 3, 10, 22):
+        oa, fa, ca = _run(c, sl=slice(0, t0), cu=[0, t0])
+        ob, fb, cb = _run(c, sl=slice(t0, T), cu=[0, T - t0], init=fa, hist=ca)
+        assert np.array_equal(np.concatenate([oa, ob]), o_full)
+        assert np.array_equal(fb, fs_full)
+        assert np.array_equal(cb, co_full)
+
+
+def test_p8_decode_after_prefill_bitwise():
+    rng = np.random.default_rng(8)
+    T, n = 9, 4
+    c = _mixer_case(rng, [T + n])
+    o_full, fs_full, co_full = _run(c)
+    o_pre, st, cache = _run(c, sl=slice(0, T), cu=[0, T])
+    for i in range(n):
+        t = T + i
+        sl = slice(t, t + 1)
+        o_t, st, cache = oracle.decode_step(c["q"][sl], c["k"][sl], c["v"][sl], c["a"][sl],
+                                            c["b"][sl], c["z"][sl], c["conv_w"], c["A_log"],
+                                            c["dt_bias"], c["norm_w"], st, cache)
+        assert np.array_equal(o_t, o_full[sl])
+    assert np.array_equal(st, fs_full)
+    assert np.array_equal(cache, co_full)
+
+
+def test_varlen_packing_equals_separate_runs():
+    rng = np.random.default_rng(30)
+    lengths = [5, 0, 1, 2, 17, 3]
+    c = _mixer_case(rng, lengths)
+    o, fs, co = _run(c)
+    cu = c["cu"]
+    for n, L in enumerate(lengths):
+        sl = slice(cu[n], cu[n + 1])
+        on, fn, cn = _run(c, sl=sl, cu=[0, L], init=c["init"][n:n + 1], hist=c["hist"][n:n + 1])
+        assert np.array_equal(on, o[sl])
+        assert np.array_equal(fn[0], fs[n])
+        assert np.array_equal(cn[0], co[n])
+    # an empty sequence returns its initial state and its history unchanged
+    assert np.array_equal(fs[1], c["init"][1])
+    assert np.array_equal(co[1], c["hist"][1])
+
+
+def test_conv_out_holds_last_three_raw_rows():
+    rng = np.random.default_rng(31)
+    Hk, Hv, D = 1, 2, 4
+    c = _mixer_case(rng, [5, 2], Hk=Hk, Hv=Hv, D=D)
+    _, _, co = _run(c)
+    raw = np.concatenate([c["q"].reshape(-1, Hk * D), c["k"].reshape(-1, Hk * D),
+                          c["v"].reshape(-1, Hv * D)], axis=1)
+    assert np.array_equal(co[0], raw[2:5])
+    # length 2: one row of inherited history, then the two tokens
+    assert np.array_equal(co[1], np.concatenate([c["hist"][1][2:3], raw[5:7]]))
+
+
+def test_no_nan_at_extreme_gates():
+    rng = np.random.default_rng(32)
+    c = _mixer_case(rng, [12])
+    c["a"][::2] = 30.0
+    c["b"][1::3] = np.inf
+    c["b"][2::3] = -np.inf
+    c["A_log"][0] = 100.0
+    c["A_log"][1] = -np.inf
+    o, fs, _ = _run(c)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(fs))
