@@ -1,0 +1,177 @@
+"""Gated DeltaNet token mixer on MI355X (gfx950): thin Python binding.
+
+Every step of the mixer runs in the HIP kernels of ``libgdn.so`` (built from
+``csrc/`` by ``build.py``); this module only marshals torch tensors (device
+memory and the current stream) into the C ABI declared in ``include/gdn.h``.
+There is no CPU fallback: if the library is missing, loading fails loudly.
+
+Mixer definition: "Qwen3-Next 80B-A3B" field guide, cutaway 02 (gated delta
+update, counts, RMSNorm + SiLU(z) gate); "Qwen3.8-Flash-Next" model card
+(decay gate, chunk state update); tech report Fig. 2 caption (short convs,
+L2-normalised q/k).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_BF16, GDN_F32 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
+          3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
+EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
+            "gdn_status_string", "gdn_last_error", "gdn_version")
+
+
+class GdnParams(ctypes.Structure):
+    _fields_ = [("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m linear_attention_sequence_causal_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            pp = ctypes.POINTER(GdnParams)
+            L.gdn_prefill_workspace_bytes.restype = sz
+            L.gdn_prefill_workspace_bytes.argtypes = [pp, i32, i64]
+            L.gdn_prefill.restype = ctypes.c_int
+            L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, i32, i64, vp, vp, vp,
+                                      vp, vp, sz, vp]
+            L.gdn_decode_step.restype = ctypes.c_int
+            L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32, vp]
+            L.gdn_status_string.restype = ctypes.c_char_p
+            L.gdn_status_string.argtypes = [ctypes.c_int]
+            L.gdn_last_error.restype = ctypes.c_char_p
+            L.gdn_last_error.argtypes = []
+            L.gdn_version.restype = ctypes.c_char_p
+            L.gdn_version.argtypes = []
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_params(num_qk_heads, num_v_heads, head_dim, act_dtype, conv_w, A_log, dt_bias,
+                norm_w=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6) -> GdnParams:
+    dt = GDN_BF16 if act_dtype == torch.bfloat16 else GDN_F32 if act_dtype == torch.float32 else -1
+    return GdnParams(int(num_qk_heads), int(num_v_heads), int(head_dim), dt, float(q_scale),
+                     float(l2_eps), float(rms_eps), _ptr(conv_w), _ptr(A_log), _ptr(dt_bias),
+                     _ptr(norm_w))
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to the mixer must be contiguous")
+
+
+def workspace_bytes(params: GdnParams, num_seqs: int, total_tokens: int) -> int:
+    n = lib().gdn_prefill_workspace_bytes(ctypes.byref(params), int(num_seqs), int(total_tokens))
+    if n == ctypes.c_size_t(-1).value:
+        raise GdnError(1, lib().gdn_last_error().decode())
+    return n
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *, init_state=None,
+            cu_seqlens=None, conv_state=None, return_conv_state=False, q_scale=1.0,
+            l2_eps=1e-6, rms_eps=1e-6, out=None, final_state=None):
+    """Chunked prefill over packed sequences -> (o, final_state[, conv_state_out]).
+
+    q, k [T, Hk, D]; v, z [T, Hv, D] (bf16 or fp32); a, b [T, Hv] fp32;
+    conv_w [Cc, 4]; A_log, dt_bias [Hv]; norm_w [D] or None; init_state
+    [N, Hv, D, D] fp32 or None; cu_seqlens [N+1] int32 or None (one sequence);
+    conv_state [N, 3, Cc] or None.  Outputs are allocated on q's device unless
+    given; the work is enqueued on torch's current stream.
+    """
+    T, Hk, D = q.shape
+    Hv = v.shape[1]
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, init_state, cu_seqlens, conv_state)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    o = torch.empty_like(v) if out is None else out
+    fs = (torch.empty((N, Hv, D, D), dtype=torch.float32, device=q.device)
+          if final_state is None else final_state)
+    Cc = 2 * Hk * D + Hv * D
+    cso = torch.empty((N, 3, Cc), dtype=q.dtype, device=q.device) if return_conv_state else None
+    nbytes = workspace_bytes(p, N, T)
+    ws = _workspace(nbytes, q.device)
+    _check(lib().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
+                             ctypes.byref(p), _ptr(init_state), _ptr(cu_seqlens), N, T,
+                             _ptr(conv_state), _ptr(o), _ptr(fs), _ptr(cso), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream()))
+    if return_conv_state:
+        return o, fs, cso
+    return o, fs
+
+
+def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, *,
+                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None):
+    """One decode step; updates `state` and `conv_state` in place, returns o.
+
+    q, k [B, Hk, D]; v, z [B, Hv, D]; a, b [B, Hv]; state [B, Hv, D, D] fp32;
+    conv_state [B, 3, Cc] in the activation dtype.
+    """
+    B, Hk, D = q.shape
+    Hv = v.shape[1]
+    _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    o = torch.empty_like(v) if out is None else out
+    _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
+                                 ctypes.byref(p), _ptr(state), _ptr(conv_state), _ptr(o), B,
+                                 _stream()))
+    return o
+
+
+def version() -> str:
+    return lib().gdn_version().decode()

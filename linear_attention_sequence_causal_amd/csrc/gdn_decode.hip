@@ -1,0 +1,231 @@
+// gdn_decode.hip -- single-token decode step of the Gated DeltaNet mixer, gfx950.
+//
+// One workgroup per (sequence b, q/k head g) handles all r = Hv/Hk v heads that
+// read g (the field guide's 16 q/k : 32 v head sharing), so it exclusively owns
+// the conv-state channels of q/k head g and of those v heads and shifts them in
+// place.  Work per workgroup:
+//   1. conv (width 4: the 3 cached raw rows + the new row) + SiLU on the
+//      channels of q, k and the r v heads; L2-normalise q and k; k.q.
+//   2. per v head: gates alpha = exp(-exp(A_log) softplus(a + dt_bias)),
+//      beta = sigmoid(b) (model card gated-DeltaNet entry; Fig. 2 caption).
+//   3. stream the fp32 state H = S^T ([dk][dv]) once: the field guide's six
+//      update steps fused into one read and one write,
+//        vhat_j = alpha sum_i H_ij k_i                 (S' k)
+//        e_j    = v_j - vhat_j
+//        H_ij  <- alpha H_ij + beta k_i e_j             (S'' = S' + beta e k^T)
+//        y_j    = alpha sum_i H_ij q_i + beta (k.q) e_j  (S'' q)
+//   4. gated RMSNorm epilogue o = y rsqrt(mean y^2 + eps) w SiLU(z).
+// The state is ~97% of the bytes moved, so the kernel is HBM-bound.  Each
+// thread holds 64 floats of one head's state and already has the next head's
+// 64 floats in flight while it works on the current one.
+#include "gdn_device.h"
+
+namespace gdn {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecMaxRatio = 8;  // largest Hv / Hk the decode kernel accepts
+
+template <typename T>
+__global__ void __launch_bounds__(kDecThreads)
+decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+                   const float *__restrict__ a, const float *__restrict__ b,
+                   const T *__restrict__ z, const float *__restrict__ conv_w,
+                   const float *__restrict__ A_log, const float *__restrict__ dt_bias,
+                   const float *__restrict__ norm_w, float q_scale, float l2_eps, float rms_eps,
+                   float *__restrict__ state, T *__restrict__ conv_state, T *__restrict__ o,
+                   int Hk, int Hv) {
+  const int g = blockIdx.x % Hk;
+  const int bseq = blockIdx.x / Hk;
+  const int r = Hv / Hk;
+  const int tid = threadIdx.x;
+  const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
+
+  __shared__ float s_x[2 + kDecMaxRatio][kD];  // post-prologue q, k, then v of each v head
+  __shared__ float s_red[8][2][kD];            // partial column sums per row group
+  __shared__ float s_e[kD];
+  __shared__ float s_y[kD];
+  __shared__ float s_misc[4];
+
+  // thread t of the state stream: columns 4*(t%32)..+3, rows 16*(t/32)..+15
+  const int col = (tid & 31) * 4;
+  const int rg = tid >> 5;
+  const int row0 = rg * 16;
+  auto head_ptr = [&](int j) {
+    return state + (((int64_t)bseq * Hv + r * g + j) * kD + row0) * kD + col;
+  };
+  // Start streaming the first head's state before the prologue.
+  f32x4 Hcur[16];
+  {
+    const float *Hp = head_ptr(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Hcur[i] = ld_nt4(Hp + i * kD);
+  }
+
+  // ---- 1. prologue --------------------------------------------------------------
+  // Pass 0: sections (64 threads each) = q, k, v of heads 0 and 1 of the group;
+  // pass p >= 1: v heads 2 + 4(p-1) + section.  Each thread takes 2 channels.
+  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+  const int c0 = (tid & 63) * 2;
+  const int sec = tid >> 6;
+  for (int pass = 0; pass == 0 || 2 + 4 * (pass - 1) < r; ++pass) {
+    int slot, jv = -1;
+    if (pass == 0) {
+      slot = sec;
+      if (sec >= 2) jv = sec - 2;
+    } else {
+      jv = 2 + 4 * (pass - 1) + sec;
+      slot = 2 + jv;
+    }
+    const bool active = jv < r;  // jv = -1 for q and k
+    int64_t cbase;
+    const T *src;
+    int64_t sidx;
+    if (slot == 0) {
+      cbase = (int64_t)g * kD;
+      src = q;
+      sidx = ((int64_t)bseq * Hk + g) * kD;
+    } else if (slot == 1) {
+      cbase = (int64_t)Hk * kD + (int64_t)g * kD;
+      src = k;
+      sidx = ((int64_t)bseq * Hk + g) * kD;
+    } else {
+      cbase = 2LL * Hk * kD + (int64_t)(r * g + jv) * kD;
+      src = v;
+      sidx = ((int64_t)bseq * Hv + r * g + jv) * kD;
+    }
+    float xv[2] = {0.f, 0.f};
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t ch = cbase + c0 + u;
+        const float raw = Act<T>::load(src, sidx + c0 + u);
+        const float h0 = Act<T>::load(cs, ch), h1 = Act<T>::load(cs, Cc + ch),
+                    h2 = Act<T>::load(cs, 2 * Cc + ch);
+        const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
+        xv[u] = siluf_(w.x * h0 + w.y * h1 + w.z * h2 + w.w * raw);
+        // shift the cache in place (reads above precede these writes)
+        Act<T>::store(cs, ch, h1);
+        Act<T>::store(cs, Cc + ch, h2);
+        Act<T>::store(cs, 2 * Cc + ch, raw);
+      }
+    }
+    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) over 128 channels
+      const float ss = wave_sum(xv[0] * xv[0] + xv[1] * xv[1]);
+      const float f = (slot == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
+      xv[0] *= f;
+      xv[1] *= f;
+    }
+    if (active) {
+      s_x[slot][c0] = xv[0];
+      s_x[slot][c0 + 1] = xv[1];
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const float kq = wave_sum(s_x[0][2 * tid] * s_x[1][2 * tid] +
+                              s_x[0][2 * tid + 1] * s_x[1][2 * tid + 1]);
+    if (tid == 0) s_misc[0] = kq;
+  }
+  __syncthreads();
+  const float kq = s_misc[0];
+
+  float kr[16], qr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    kr[i] = s_x[1][row0 + i];
+    qr[i] = s_x[0][row0 + i];
+  }
+
+  // ---- 3./4. per v head: state stream and epilogue ---------------------------------
+  for (int j = 0; j < r; ++j) {
+    const int h = r * g + j;
+    f32x4 Hnext[16];
+    if (j + 1 < r) {
+      const float *Hn = head_ptr(j + 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Hnext[i] = ld_nt4(Hn + i * kD);
+    }
+    const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
+    const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
+    float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sk[0] += Hcur[i].x * kr[i]; sk[1] += Hcur[i].y * kr[i];
+      sk[2] += Hcur[i].z * kr[i]; sk[3] += Hcur[i].w * kr[i];
+      sq[0] += Hcur[i].x * qr[i]; sq[1] += Hcur[i].y * qr[i];
+      sq[2] += Hcur[i].z * qr[i]; sq[3] += Hcur[i].w * qr[i];
+    }
+    *reinterpret_cast<f32x4 *>(&s_red[rg][0][col]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
+    *reinterpret_cast<f32x4 *>(&s_red[rg][1][col]) = f32x4{sq[0], sq[1], sq[2], sq[3]};
+    __syncthreads();
+    if (tid < kD) {
+      float vk = 0.f, vq = 0.f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        vk += s_red[p][0][tid];
+        vq += s_red[p][1][tid];
+      }
+      const float e = s_x[2 + j][tid] - alpha * vk;  // e = v - S'k
+      const float y = alpha * vq + beta * kq * e;    // S'' q
+      s_e[tid] = e;
+      s_y[tid] = y;
+      const float ssum = wave_sum(y * y);
+      if ((tid & 63) == 0) s_misc[1 + (tid >> 6)] = ssum;
+    }
+    __syncthreads();
+    float ec[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ec[c] = beta * s_e[col + c];
+    float *Hp = head_ptr(j);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f32x4 hn;
+      hn.x = alpha * Hcur[i].x + kr[i] * ec[0];
+      hn.y = alpha * Hcur[i].y + kr[i] * ec[1];
+      hn.z = alpha * Hcur[i].z + kr[i] * ec[2];
+      hn.w = alpha * Hcur[i].w + kr[i] * ec[3];
+      st_nt4(Hp + i * kD, hn);
+    }
+    if (tid < kD) {
+      const float inv = rsqrtf((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
+      const float w = norm_w ? norm_w[tid] : 1.0f;
+      const int64_t oi = ((int64_t)bseq * Hv + h) * kD + tid;
+      Act<T>::store(o, oi, s_y[tid] * inv * w * siluf_(Act<T>::load(z, oi)));
+    }
+    __syncthreads();  // s_red, s_e, s_y, s_misc are reused by the next head
+    if (j + 1 < r) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Hcur[i] = Hnext[i];
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *a,
+                         const float *b, const void *z, const float *conv_w, const float *A_log,
+                         const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
+                         float rms_eps, float *state, void *conv_state, void *o, int batch,
+                         int Hk, int Hv, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  dim3 grid((unsigned)batch * (unsigned)Hk);
+  hipLaunchKernelGGL((decode_step_kernel<T>), grid, dim3(kDecThreads), 0, stream,
+                     (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
+                     dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state, (T *)o,
+                     Hk, Hv);
+  return hipGetLastError();
+}
+
+int decode_max_ratio() { return kDecMaxRatio; }
+
+template hipError_t launch_decode<float>(const void *, const void *, const void *, const float *,
+                                         const float *, const void *, const float *,
+                                         const float *, const float *, const float *, float,
+                                         float, float, float *, void *, void *, int, int, int,
+                                         hipStream_t);
+template hipError_t launch_decode<bf16_t>(const void *, const void *, const void *,
+                                          const float *, const float *, const void *,
+                                          const float *, const float *, const float *,
+                                          const float *, float, float, float, float *, void *,
+                                          void *, int, int, int, hipStream_t);
+
+}  // namespace gdn

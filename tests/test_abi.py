@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: exports, status strings, argument validation.
+
+All validation happens on the host before any HIP call, so invalid arguments
+are reported here without a device, and valid calls report GDN_ERR_NO_DEVICE
+in a container without a GPU.  Output buffers are host memory in these tests
+(the library never dereferences them on the host); they must be untouched
+after an error.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_sequence_causal_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = gdn.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(gdn.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    L = gdn.lib()
+    for code, name in gdn.STATUS.items():
+        assert L.gdn_status_string(code).decode() == name
+    assert gdn.version().startswith("gdn-gfx950")
+
+
+def _host(n, dtype=np.float32, fill=7.0):
+    return np.full(n, fill, dtype=dtype)
+
+
+def _params(Hk=2, Hv=4, D=128, dtype=gdn.GDN_BF16, host=None):
+    host = host or {}
+    Cc = 2 * Hk * D + Hv * D
+    host.setdefault("conv", _host(max(Cc, 1) * 4))
+    host.setdefault("alog", _host(max(Hv, 1)))
+    host.setdefault("dt", _host(max(Hv, 1)))
+    p = gdn.GdnParams(Hk, Hv, D, dtype, 1.0, 1e-6, 1e-6, host["conv"].ctypes.data,
+                      host["alog"].ctypes.data, host["dt"].ctypes.data, None)
+    return p, host
+
+
+def _decode(p, B=2, out=None, **over):
+    bufs = {n: _host(1 << 16) for n in ("q", "k", "v", "a", "b", "z", "state", "cache")}
+    o = out if out is not None else _host(1 << 16)
+    ptr = {n: ctypes.c_void_p(x.ctypes.data) for n, x in bufs.items()}
+    ptr.update(over)
+    return gdn.lib().gdn_decode_step(ptr["q"], ptr["k"], ptr["v"], ptr["a"], ptr["b"], ptr["z"],
+                                     ctypes.byref(p) if p is not None else None, ptr["state"],
+                                     ptr["cache"], ctypes.c_void_p(o.ctypes.data), B, None)
+
+
+def _prefill(p, N=1, T=64, out=None, ws=None, ws_bytes=0, cu=True, **over):
+    bufs = {n: _host(1 << 16) for n in ("q", "k", "v", "a", "b", "z", "fs")}
+    o = out if out is not None else _host(1 << 16)
+    cu_arr = np.zeros(N + 1, dtype=np.int32)
+    ptr = {n: ctypes.c_void_p(x.ctypes.data) for n, x in bufs.items()}
+    ptr.update(over)
+    return gdn.lib().gdn_prefill(ptr["q"], ptr["k"], ptr["v"], ptr["a"], ptr["b"], ptr["z"],
+                                 ctypes.byref(p) if p is not None else None, None,
+                                 ctypes.c_void_p(cu_arr.ctypes.data) if cu else None, N, T, None,
+                                 ctypes.c_void_p(o.ctypes.data), ptr["fs"], None,
+                                 ws, ws_bytes, None)
+
+
+INVALID, UNSUPPORTED, WORKSPACE, NO_DEVICE = 1, 2, 3, 4
+
+
+def test_decode_argument_errors_leave_outputs_untouched():
+    o = _host(1 << 16, fill=3.0)
+    p, h = _params()
+    assert _decode(None, out=o) == INVALID
+    p, h = _params(Hk=3, Hv=4)
+    assert _decode(p, out=o) == INVALID
+    assert "multiple" in gdn.lib().gdn_last_error().decode()
+    p, h = _params(D=64)
+    assert _decode(p, out=o) == UNSUPPORTED
+    p, h = _params(dtype=7)
+    assert _decode(p, out=o) == INVALID
+    p, h = _params()
+    assert _decode(p, B=-1, out=o) == INVALID
+    assert _decode(p, out=o, q=None) == INVALID
+    p, h = _params(Hk=1, Hv=16)
+    assert _decode(p, out=o) == UNSUPPORTED  # ratio above the decode kernel's limit
+    p, h = _params()
+    p.conv_weight = None
+    assert _decode(p, out=o) == INVALID
+    assert np.all(o == 3.0)
+
+
+def test_prefill_argument_errors():
+    o = _host(1 << 16, fill=5.0)
+    p, h = _params()
+    assert _prefill(None, out=o) == INVALID
+    assert _prefill(p, N=-1, out=o) == INVALID
+    assert _prefill(p, T=-3, out=o) == INVALID
+    assert _prefill(p, N=2, cu=False, out=o) == INVALID
+    assert _prefill(p, out=o, z=None) == INVALID
+    assert _prefill(p, out=o, fs=None) == INVALID
+    p64, _ = _params(D=64)
+    assert _prefill(p64, out=o) == UNSUPPORTED
+    assert np.all(o == 5.0)
+
+
+def test_prefill_workspace_rules():
+    p, h = _params(Hk=16, Hv=32)
+    L = gdn.lib()
+    n_short = L.gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 0)
+    assert 0 < n_short < 4096  # the device-built segment table only
+    n_long = L.gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 65536)
+    assert n_long > 1 << 20  # long sequences are split into segments that need maps
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(p), 0, 0) == 0
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(p), -1, 10) == ctypes.c_size_t(-1).value
+    o = _host(1 << 16, fill=1.0)
+    assert _prefill(p, T=65536, out=o, ws=None, ws_bytes=0) == WORKSPACE
+    ws = _host(16)
+    assert _prefill(p, T=65536, out=o, ws=ctypes.c_void_p(ws.ctypes.data),
+                    ws_bytes=n_long - 1) == WORKSPACE
+    assert np.all(o == 1.0)
+
+
+def test_valid_calls_report_missing_device(monkeypatch):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    p, h = _params()
+    assert _decode(p) == NO_DEVICE
+    n = gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 64)
+    raw = np.zeros(n + 512, dtype=np.uint8)
+    addr = (raw.ctypes.data + 255) // 256 * 256
+    assert _prefill(p, ws=ctypes.c_void_p(addr), ws_bytes=n) == NO_DEVICE
+    assert np.all(raw == 0)
