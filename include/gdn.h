@@ -124,6 +124,15 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            const gdn_params *p, float *state, void *conv_state,
                            void *o, int32_t batch, void *stream);
 
+/* Diagnostics: per-kernel device time of the last gdn_prefill call made on
+ * this thread while the environment had GDN_KERNEL_TIMING=1.  The library then
+ * records HIP events on the caller's stream between its kernels (segment table,
+ * map pass A, map pass B, combine, full pass, conv-state copy).  Writes up to
+ * `max_kernels` milliseconds (0 for a kernel that did not run) and returns the
+ * number of slots written, or -1 when there is no timed call.  Waits for the
+ * timed call's last event (host synchronisation). */
+int gdn_prefill_last_kernel_times(float *ms, int max_kernels);
+
 /* Static text for a status code. */
 const char *gdn_status_string(gdn_status s);
 

@@ -25,7 +25,9 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
-            "gdn_status_string", "gdn_last_error", "gdn_version")
+            "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
+            "gdn_version")
+PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
 
 
 class GdnParams(ctypes.Structure):
@@ -71,6 +73,9 @@ def lib() -> ctypes.CDLL:
             L.gdn_last_error.argtypes = []
             L.gdn_version.restype = ctypes.c_char_p
             L.gdn_version.argtypes = []
+            L.gdn_prefill_last_kernel_times.restype = ctypes.c_int
+            L.gdn_prefill_last_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                        ctypes.c_int]
             _lib = L
     return _lib
 
@@ -171,6 +176,15 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
                                  ctypes.byref(p), _ptr(state), _ptr(conv_state), _ptr(o), B,
                                  _stream()))
     return o
+
+
+def last_kernel_times():
+    """{kernel name: ms} of the last prefill call made with GDN_KERNEL_TIMING=1."""
+    buf = (ctypes.c_float * len(PREFILL_KERNELS))()
+    n = lib().gdn_prefill_last_kernel_times(buf, len(PREFILL_KERNELS))
+    if n < 0:
+        return None
+    return {PREFILL_KERNELS[i]: float(buf[i]) for i in range(n)}
 
 
 def version() -> str:

@@ -28,6 +28,7 @@ int decode_max_ratio();
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local gdn::PrefillTiming g_timing;
 
 gdn_status fail(gdn_status s, const char *fmt, ...) {
   va_list ap;
@@ -109,6 +110,19 @@ const char *gdn_status_string(gdn_status s) {
 
 const char *gdn_last_error(void) { return g_err; }
 
+int gdn_prefill_last_kernel_times(float *ms, int max_kernels) {
+  if (!g_timing.created || !g_timing.valid || !ms || max_kernels <= 0) return -1;
+  if (hipEventSynchronize(g_timing.ev[gdn::kTimedKernels]) != hipSuccess) return -1;
+  const int n = max_kernels < gdn::kTimedKernels ? max_kernels : gdn::kTimedKernels;
+  for (int i = 0; i < n; ++i) {
+    float t = 0.f;
+    if (g_timing.ran[i] && hipEventElapsedTime(&t, g_timing.ev[i], g_timing.ev[i + 1]) != hipSuccess)
+      t = 0.f;
+    ms[i] = g_timing.ran[i] ? t : 0.f;
+  }
+  return n;
+}
+
 const char *gdn_version(void) { return "gdn-gfx950 0.1"; }
 
 size_t gdn_prefill_workspace_bytes(const gdn_params *p, int32_t num_seqs, int64_t total_tokens) {
@@ -162,9 +176,21 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
       return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d, expected total_tokens %lld",
                   cu[num_seqs], (long long)total_tokens);
   }
+  gdn::PrefillTiming *tm = nullptr;
+  if (const char *tv = getenv("GDN_KERNEL_TIMING"); tv && tv[0] == '1') {
+    if (!g_timing.created) {
+      for (int i = 0; i <= gdn::kTimedKernels; ++i) {
+        hipError_t ce = hipEventCreate(&g_timing.ev[i]);
+        if (ce != hipSuccess) return hip_fail(ce, "hipEventCreate");
+      }
+      g_timing.created = true;
+    }
+    tm = &g_timing;
+  }
   hipError_t e = gdn::launch_prefill(plan, q, k, v, a, b, z, *p, init_state, cu_seqlens,
                                      num_seqs, total_tokens, conv_state_in, o, final_state,
-                                     conv_state_out, workspace, (hipStream_t)stream);
+                                     conv_state_out, workspace, (hipStream_t)stream, tm);
+  if (tm) tm->valid = (e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return GDN_OK;
 }

@@ -64,10 +64,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 // Sum over lanes that differ only in bits below `width` (width a power of 2).
+// (W <= 32; uses the LDS swizzle unit in bit-mask mode, lane ^ o within 32 lanes)
+template <int PATTERN>
+__device__ __forceinline__ float swizzle(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), PATTERN));
+}
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32, "group width");
+  if (W >= 32) x += swizzle<0x1F | (16 << 10)>(x);
+  if (W >= 16) x += swizzle<0x1F | (8 << 10)>(x);
+  if (W >= 8) x += swizzle<0x1F | (4 << 10)>(x);
+  if (W >= 4) x += swizzle<0x1F | (2 << 10)>(x);
+  x += swizzle<0x1F | (1 << 10)>(x);
+  return x;
+}
+
+// Value the optimiser cannot see through (keeps derived addresses local).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
   return x;
 }
 

@@ -46,11 +46,19 @@ struct PrefillPlan {
 
 PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_heads);
 
+// Optional events between the prefill kernels (GDN_KERNEL_TIMING=1).
+constexpr int kTimedKernels = 6;
+struct PrefillTiming {
+  hipEvent_t ev[kTimedKernels + 1];
+  bool created = false, valid = false;
+  bool ran[kTimedKernels];
+};
+
 hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k, const void *v,
                           const float *a, const float *b, const void *z, const gdn_params &p,
                           const float *init_state, const int32_t *cu_seqlens, int32_t num_seqs,
                           int64_t total_tokens, const void *conv_state_in, void *o,
                           float *final_state, void *conv_state_out, void *workspace,
-                          hipStream_t stream);
+                          hipStream_t stream, PrefillTiming *timing);
 
 }  // namespace gdn

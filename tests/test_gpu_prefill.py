@@ -1,0 +1,279 @@
+"""GPU parity of the chunked prefill against the fp64 oracle.
+
+Bars (relative L2 over the whole tensor): o <= 3e-3, final state <= 1e-3.
+Indexing is bit-exact: a packed sequence's rows and final state equal its
+standalone run bit for bit.  Full-size workloads run in the launch
+configuration the benchmark uses; the oracle recomputes sampled heads (a v
+head's chain is independent of the others, so a sampled head is checked over
+every token).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as S
+import oracle
+
+gpu = pytest.mark.gpu
+O_TOL, STATE_TOL = 3e-3, 1e-3
+
+
+def rel_l2(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+
+
+def _gdn():
+    import linear_attention_sequence_causal_amd as gdn
+    return gdn
+
+
+def run_gpu(d, cu=True, **kw):
+    gdn = _gdn()
+    args = dict(init_state=d["init_state"], conv_state=d["conv_in"])
+    args.update(kw)
+    out = gdn.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["z"], d["conv_w"], d["A_log"],
+                      d["dt_bias"], d["norm_w"], cu_seqlens=d["cu_seqlens"] if cu else None,
+                      return_conv_state=True, **args)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle(d, qk_heads=None):
+    """Oracle on the given q/k heads (and their v heads); returns (o, fs, v_idx)."""
+    f = S.to_f64
+    Hk = d["q"].shape[1]
+    Hv = d["v"].shape[1]
+    D = d["q"].shape[2]
+    if qk_heads is None:
+        qk_heads = range(Hk)
+    qi, vi, ch = oracle.select_heads(qk_heads, Hk, Hv, D)
+    qi_t = torch.as_tensor(qi, device=d["q"].device)
+    vi_t = torch.as_tensor(vi, device=d["q"].device)
+    ch_t = torch.as_tensor(ch, device=d["q"].device)
+    sel = lambda t, idx, dim=1: f(t.index_select(dim, idx))
+    init = d["init_state"]
+    conv_in = d["conv_in"]
+    o, fs, co = oracle.prefill(
+        sel(d["q"], qi_t), sel(d["k"], qi_t), sel(d["v"], vi_t), sel(d["a"], vi_t),
+        sel(d["b"], vi_t), sel(d["z"], vi_t), sel(d["conv_w"], ch_t, 0), sel(d["A_log"], vi_t, 0),
+        sel(d["dt_bias"], vi_t, 0), f(d["norm_w"]), cu_seqlens=d["cu_seqlens"].cpu().numpy(),
+        init_state=None if init is None else sel(init, vi_t),
+        conv_in=None if conv_in is None else sel(conv_in, ch_t, 2))
+    return o, fs, co, vi
+
+
+def check_parity(d, qk_heads=None, tag=""):
+    o, fs, co = run_gpu(d)
+    o_ref, fs_ref, co_ref, vi = run_oracle(d, qk_heads)
+    o_g = S.to_f64(o)[:, vi]
+    fs_g = S.to_f64(fs)[:, vi]
+    eo, es = rel_l2(o_g, o_ref), rel_l2(fs_g, fs_ref)
+    print(f"{tag}: o rel-L2 {eo:.3e}  final-state rel-L2 {es:.3e}", flush=True)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(fs_g))
+    assert eo <= O_TOL, eo
+    assert es <= STATE_TOL, es
+    return o, fs, co
+
+
+@gpu
+def test_tiny_fp32_full_parity():
+    d = S.prefill_inputs(S.TINY, "cuda")
+    _, _, co = check_parity(d, tag="T=512 Hk=1 Hv=2 fp32")
+
+
+@gpu
+def test_prefill_4k_full_parity():
+    d = S.prefill_inputs(S.PREFILL_4K, "cuda")
+    check_parity(d, tag="T=4096 Hk=16 Hv=32 bf16")
+
+
+@gpu
+def test_prefill_64k_sampled_heads():
+    d = S.prefill_inputs(S.PREFILL_64K, "cuda")
+    check_parity(d, qk_heads=[0, 15], tag="T=65536 bf16, v heads 0,1,30,31")
+
+
+@gpu
+def test_varlen_64_sampled_heads():
+    d = S.prefill_inputs(S.VARLEN_64, "cuda")
+    check_parity(d, qk_heads=[7], tag=f"varlen N=64 T={d['q'].shape[0]}, v heads 14,15")
+
+
+@gpu
+@pytest.mark.parametrize("T", [1, 2, 3, 63, 64, 65, 130, 700])
+def test_ragged_lengths_small_heads(T):
+    w = S.scaled(S.PREFILL_4K, lengths=(T,), num_qk_heads=2, num_v_heads=4, seed=100 + T,
+                 init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, co = check_parity(d, tag=f"T={T}")
+    _, _, co_ref, _ = run_oracle(d)
+    assert np.array_equal(S.to_f64(co), co_ref)  # conv state: raw rows, bit-exact
+
+
+@gpu
+def test_varlen_with_empty_and_short_sequences():
+    w = S.scaled(S.PREFILL_4K, lengths=(5, 0, 1, 64, 2, 0, 129, 3, 600), num_qk_heads=2,
+                 num_v_heads=4, seed=7, init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, co = check_parity(d, tag="varlen with empty/short sequences")
+    # empty sequences return their initial state bit for bit
+    for n in (1, 5):
+        assert torch.equal(fs[n], d["init_state"][n])
+        assert torch.equal(co[n], d["conv_in"][n])
+
+
+@gpu
+def test_packing_is_bit_exact():
+    """Each packed sequence's o rows and final state equal its standalone run."""
+    w = S.scaled(S.PREFILL_4K, lengths=(300, 77, 1024, 5, 2000), seed=9, init_state_std=0.01,
+                 conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, co = run_gpu(d)
+    cu = d["cu_seqlens"].cpu().tolist()
+    gdn = _gdn()
+    for n in range(len(cu) - 1):
+        sl = slice(cu[n], cu[n + 1])
+        on, fn, cn = gdn.prefill(d["q"][sl].contiguous(), d["k"][sl].contiguous(),
+                                 d["v"][sl].contiguous(), d["a"][sl].contiguous(),
+                                 d["b"][sl].contiguous(), d["z"][sl].contiguous(), d["conv_w"],
+                                 d["A_log"], d["dt_bias"], d["norm_w"],
+                                 init_state=d["init_state"][n:n + 1].contiguous(),
+                                 conv_state=d["conv_in"][n:n + 1].contiguous(),
+                                 return_conv_state=True)
+        torch.cuda.synchronize()
+        # segments start at each sequence's first token and the segment length
+        # is the same for the packed (T = 3406) and standalone runs (512 tokens)
+        assert torch.equal(on, o[sl])
+        assert torch.equal(fn, fs[n:n + 1])
+        assert torch.equal(cn, co[n:n + 1])
+
+
+@gpu
+def test_packing_bit_exact_single_segment():
+    """With every sequence inside one segment the packed and standalone runs
+    execute the same chunk sequence: bitwise equal."""
+    w = S.scaled(S.PREFILL_4K, lengths=(200, 64, 1, 511, 90), num_qk_heads=2, num_v_heads=4,
+                 seed=11, init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, co = run_gpu(d)
+    cu = d["cu_seqlens"].cpu().tolist()
+    gdn = _gdn()
+    for n in range(len(cu) - 1):
+        sl = slice(cu[n], cu[n + 1])
+        on, fn = gdn.prefill(d["q"][sl].contiguous(), d["k"][sl].contiguous(),
+                             d["v"][sl].contiguous(), d["a"][sl].contiguous(),
+                             d["b"][sl].contiguous(), d["z"][sl].contiguous(), d["conv_w"],
+                             d["A_log"], d["dt_bias"], d["norm_w"],
+                             init_state=d["init_state"][n:n + 1].contiguous(),
+                             conv_state=d["conv_in"][n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(on, o[sl])
+        assert torch.equal(fn, fs[n:n + 1])
+
+
+@gpu
+def test_identity_gates_keep_state_and_zero_gate_zeroes_output():
+    w = S.scaled(S.PREFILL_4K, lengths=(1000,), num_qk_heads=2, num_v_heads=4, seed=12,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    d["b"] = torch.full_like(d["b"], -float("inf"))       # beta = 0
+    d["A_log"] = torch.full_like(d["A_log"], -float("inf"))  # alpha = 1
+    d["z"] = torch.zeros_like(d["z"])
+    o, fs, _ = run_gpu(d)
+    assert torch.equal(fs, d["init_state"])
+    assert torch.count_nonzero(o) == 0
+
+
+@gpu
+def test_final_state_may_alias_init_state():
+    w = S.scaled(S.PREFILL_4K, lengths=(3000, 700), num_qk_heads=2, num_v_heads=4, seed=13,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    o_ref, fs_ref, _ = run_gpu(d)
+    st = d["init_state"].clone()
+    gdn = _gdn()
+    o, fs = gdn.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["z"], d["conv_w"], d["A_log"],
+                        d["dt_bias"], d["norm_w"], cu_seqlens=d["cu_seqlens"], init_state=st,
+                        final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    assert torch.equal(st, fs_ref)
+
+
+@gpu
+def test_deterministic():
+    d = S.prefill_inputs(S.scaled(S.PREFILL_4K, seed=14), "cuda")
+    o1, f1, _ = run_gpu(d)
+    o2, f2, _ = run_gpu(d)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def _split_run(d, t0):
+    gdn = _gdn()
+    ca = lambda t, a, b: t[a:b].contiguous()
+    T = d["q"].shape[0]
+    oa, fa, cva = gdn.prefill(ca(d["q"], 0, t0), ca(d["k"], 0, t0), ca(d["v"], 0, t0),
+                              ca(d["a"], 0, t0), ca(d["b"], 0, t0), ca(d["z"], 0, t0),
+                              d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"],
+                              init_state=d["init_state"], return_conv_state=True)
+    ob, fb = gdn.prefill(ca(d["q"], t0, T), ca(d["k"], t0, T), ca(d["v"], t0, T),
+                         ca(d["a"], t0, T), ca(d["b"], t0, T), ca(d["z"], t0, T),
+                         d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"],
+                         init_state=fa, conv_state=cva)
+    torch.cuda.synchronize()
+    return torch.cat([oa, ob]), fb
+
+
+@gpu
+def test_split_sequence_carries_state():
+    """prefill(x) equals prefill(x[t0:], init = final(x[:t0]), conv = conv(x[:t0]))
+    within the bars (the split changes chunk boundaries, segments and which
+    chunks take the split-precision state update)."""
+    w = S.scaled(S.PREFILL_4K, lengths=(1280,), num_qk_heads=2, num_v_heads=4, seed=15,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, _ = run_gpu(d)
+    for t0 in (256, 100, 1):
+        o2, fb = _split_run(d, t0)
+        assert rel_l2(S.to_f64(o2), S.to_f64(o)) < O_TOL
+        assert rel_l2(S.to_f64(fb), S.to_f64(fs)) < STATE_TOL
+
+
+@gpu
+def test_split_at_chunk_boundary_is_bitwise(monkeypatch):
+    """With one segment and the split-precision update on every chunk, a split
+    at a multiple of 64 runs exactly the same chunk sequence: bitwise equal."""
+    monkeypatch.setenv("GDN_PRECISE_ALL", "1")
+    w = S.scaled(S.PREFILL_4K, lengths=(448,), num_qk_heads=2, num_v_heads=4, seed=17,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, _ = run_gpu(d)
+    for t0 in (64, 256):
+        o2, fb = _split_run(d, t0)
+        assert torch.equal(o2, o) and torch.equal(fb, fs)
+
+
+@gpu
+def test_decode_after_prefill_matches_longer_prefill():
+    gdn = _gdn()
+    w = S.scaled(S.PREFILL_4K, lengths=(777,), num_qk_heads=16, num_v_heads=32, seed=16,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    T, n = 770, 7
+    o_all, fs_all, _ = run_gpu(d)
+    c = lambda t, a, b: t[a:b].contiguous()
+    o_p, st, cs = gdn.prefill(c(d["q"], 0, T), c(d["k"], 0, T), c(d["v"], 0, T),
+                              c(d["a"], 0, T), c(d["b"], 0, T), c(d["z"], 0, T), d["conv_w"],
+                              d["A_log"], d["dt_bias"], d["norm_w"], init_state=d["init_state"],
+                              return_conv_state=True)
+    outs = [o_p]
+    for t in range(T, T + n):
+        outs.append(gdn.decode_step(c(d["q"], t, t + 1), c(d["k"], t, t + 1), c(d["v"], t, t + 1),
+                                    c(d["a"], t, t + 1), c(d["b"], t, t + 1), c(d["z"], t, t + 1),
+                                    d["conv_w"], d["A_log"], d["dt_bias"], d["norm_w"], st, cs))
+    torch.cuda.synchronize()
+    o2 = torch.cat(outs)
+    assert rel_l2(S.to_f64(o2), S.to_f64(o_all)) < O_TOL
+    assert rel_l2(S.to_f64(st), S.to_f64(fs_all)) < STATE_TOL
