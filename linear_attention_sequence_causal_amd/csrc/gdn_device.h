@@ -22,9 +22,7 @@ __device__ __forceinline__ void st_nt4(float *p, f32x4 x) {
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN, Inf stays Inf).
 __device__ __forceinline__ bf16_t f2bf(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
 }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -37,14 +35,38 @@ __device__ __forceinline__ void split_bf(float x, bf16_t &hi, bf16_t &lo) {
 template <typename T> struct Act;
 template <> struct Act<float> {
   static __device__ __forceinline__ float load(const float *p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ uint32_t bits(const float *p, int64_t i) {
+    return __float_as_uint(p[i]);
+  }
+  static __device__ __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b); }
   static __device__ __forceinline__ void store(float *p, int64_t i, float x) { p[i] = x; }
 };
 template <> struct Act<bf16_t> {
   static __device__ __forceinline__ float load(const bf16_t *p, int64_t i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ uint32_t bits(const bf16_t *p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
   static __device__ __forceinline__ void store(bf16_t *p, int64_t i, float x) { p[i] = f2bf(x); }
 };
 
 __device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
+// sigmoid / SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float sigmoid_fast(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
+__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (round to nearest even, one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+// hi/lo split of a pair: a = bf16(hi.x) + bf16(lo.x) to ~2^-16, same for b
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pk_bf16(a, b);
+  const float ah = __uint_as_float(hi << 16), bh = __uint_as_float(hi & 0xFFFF0000u);
+  lo = pk_bf16(a - ah, b - bh);
+}
 __device__ __forceinline__ float siluf_(float u) { return u * sigmoidf_(u); }
 // log(1 + e^u) without overflow: max(u, 0) + log1p(e^-|u|).
 __device__ __forceinline__ float softplusf_(float u) {
@@ -65,18 +87,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 // Sum over lanes that differ only in bits below `width` (width a power of 2).
 // (W <= 32; uses the LDS swizzle unit in bit-mask mode, lane ^ o within 32 lanes)
-template <int PATTERN>
-__device__ __forceinline__ float swizzle(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), PATTERN));
-}
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32, "group width");
-  if (W >= 32) x += swizzle<0x1F | (16 << 10)>(x);
-  if (W >= 16) x += swizzle<0x1F | (8 << 10)>(x);
-  if (W >= 8) x += swizzle<0x1F | (4 << 10)>(x);
-  if (W >= 4) x += swizzle<0x1F | (2 << 10)>(x);
-  x += swizzle<0x1F | (1 << 10)>(x);
+// Sum over each row of 16 lanes (lanes 16r .. 16r+15), result in every lane of
+// the row: a rotate-and-add butterfly on the DPP crossbar (no LDS traffic).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
   return x;
 }
 

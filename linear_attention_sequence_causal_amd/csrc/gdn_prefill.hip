@@ -51,7 +51,7 @@ constexpr int kThreads = 512;  // 8 waves
 constexpr int kWaves = 8;
 constexpr int kRowS = 136;     // bf16 row stride of [64 tok][128 d] tiles (272 B)
 constexpr int kTokS = 72;      // bf16 row stride of [128 d][64 tok] tiles (144 B)
-constexpr int kSqS = 68;       // row stride of [64][64] tiles (fp32 L/T, bf16 M/X)
+constexpr int kSqS = 68;       // bf16 row stride of [64][64] tiles (M, -L)
 
 constexpr int OFF_QH = 0;
 constexpr int OFF_QL = OFF_QH + 64 * kRowS * 2;
@@ -66,18 +66,21 @@ constexpr int OFF_BETA = OFF_CONVW + 384 * 4 * 4;
 constexpr int OFF_G = OFF_BETA + 64 * 4;
 constexpr int OFF_MDIAG = OFF_G + 64 * 4;
 constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
-constexpr int kLdsBytes = OFF_RMS + kWaves * 64 * 4;
-// reused regions after the gram products
-constexpr int OFF_L = OFF_KH;              // fp32 [64][68], then T in place
-constexpr int OFF_M = OFF_KL;              // bf16 [64][68]  M with zero diagonal
-constexpr int OFF_XW = OFF_QL;             // bf16 [64][68]  T diag(beta gamma)
-constexpr int OFF_XU = OFF_QL + 64 * kSqS * 2;  // bf16 [64][68]  (T - I) diag(beta)
-constexpr int OFF_W = OFF_KH;              // bf16 [64][136] -W (after T is consumed)
-static_assert(OFF_XU + 64 * kSqS * 2 <= OFF_KH, "X tiles overflow the Q-lo region");
-static_assert(64 * kSqS * 4 <= 64 * kRowS * 2, "L does not fit the K-hi region");
+constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;
+constexpr int OFF_CHG = OFF_INV + 64 * 4;       // fp32 [128] per-chunk log-decay (map)
+constexpr int kLdsBytes = OFF_CHG + 128 * 4;
+// regions reused after the gram products (Q-lo and K tiles are dead then)
+constexpr int kLdS = 17;                         // fp32 row stride of diagonal L blocks
+constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
+constexpr int OFF_LO = OFF_QL;                   // bf16 [64][68]  -L (strictly lower)
+constexpr int OFF_LD = OFF_LO + 64 * kSqS * 2;   // fp32 [4][16][17] diagonal L blocks
+constexpr int OFF_TD = OFF_LD + 4 * 16 * kLdS * 4;  // bf16 [4][16][24] T_bb - I
+constexpr int OFF_M = OFF_KL;                    // bf16 [64][68]  M with zero diagonal
+constexpr int OFF_W = OFF_KH;                    // bf16 [64][136] -W
+static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KH, "solve tiles overflow the Q-lo region");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
-enum Mode { kFull = 0, kMapA = 1, kMapB = 2 };
+enum Mode { kFull = 0, kMap = 1 };
 
 struct PrefillArgs {
   const void *q, *k, *v, *z;
@@ -123,17 +126,13 @@ template <> struct Raw<float> {
   }
 };
 
-__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
-  return (uint32_t)lo | ((uint32_t)hi << 16);
-}
-
 // hi/lo bf16 split of 8 floats, packed as two 16-byte words
 __device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint4 &lo) {
-  bf16_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) split_bf(x[i], h[i], l[i]);
-  hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-  lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+  for (int i = 0; i < 4; ++i) split_pk(x[2 * i], x[2 * i + 1], h[i], l[i]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // Width-4 causal conv + SiLU of NT tokens x 8 channels.  raw[r] holds the raw
@@ -156,12 +155,36 @@ __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>:
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += w[cc][j] * Raw<T>::get(raw[r + j], cc);
-      x[r][cc] = (tbase + r < nvalid) ? siluf_(acc) : 0.f;
+      x[r][cc] = (tbase + r < nvalid) ? silu_fast(acc) : 0.f;
     }
   }
 }
 
+// B operand (K = 32) from two 16x16 C-layout tiles: slot 8lg+j <-> row 4lg+j of
+// tile a (j < 4), row 4lg+j-4 of tile b (j >= 4).  Any A operand paired with it
+// reads its k index in the same order.
+__device__ __forceinline__ u16x8 pack_b(const f32x4 &a, const f32x4 &b) {
+  const uint32_t w0 = pk_bf16(a[0], a[1]), w1 = pk_bf16(a[2], a[3]);
+  const uint32_t w2 = pk_bf16(b[0], b[1]), w3 = pk_bf16(b[2], b[3]);
+  return __builtin_bit_cast(u16x8, make_uint4(w0, w1, w2, w3));
+}
+__device__ __forceinline__ u16x8 pack_b_half(const f32x4 &a) {  // tile b = 0
+  return __builtin_bit_cast(u16x8, make_uint4(pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]), 0u, 0u));
+}
+// A operand row fragment in the permuted k order: cols c0+4lg..+3 and c1+4lg..+3
+__device__ __forceinline__ u16x8 load_a_perm(const bf16_t *row, int c0, int c1, int lg) {
+  return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg),
+              *reinterpret_cast<const u16x4 *>(row + c1 + 4 * lg));
+}
+__device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int lg) {
+  const u16x4 z = {0, 0, 0, 0};
+  return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
+}
+
 // ------------------------------------------------------------ chunk kernel
+// MODE kFull: the whole mixer for one (segment, v head).  MODE kMap: the
+// segment's affine map; blockIdx selects the A half (state columns of the
+// identity) or the B half (columns of zero with the values written in).
 template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -169,9 +192,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   int wave = tid >> 6, lane = tid & 63;
   int ln = lane & 15, lg = lane >> 4;  // MFMA lane coordinates
   const int Hv = P.Hv, Hk = P.Hk;
-  const int h = blockIdx.x % Hv;
-  const int unit = blockIdx.x / Hv;  // segment (full) or map slot (map modes)
+  int h, unit, half = 0;
+  if (MODE == kFull) {
+    h = blockIdx.x % Hv;
+    unit = blockIdx.x / Hv;
+  } else {
+    half = blockIdx.x & 1;  // 0: A columns, 1: B columns
+    h = (blockIdx.x >> 1) % Hv;
+    unit = (blockIdx.x >> 1) / Hv;
+  }
   const int gq = h / (Hv / Hk);
+  const bool withV = MODE == kFull || half == 1;
 
   int segi;
   if (MODE == kFull) {
@@ -198,15 +229,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   float *const sG = reinterpret_cast<float *>(smem + OFF_G);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
   float *const sRms = reinterpret_cast<float *>(smem + OFF_RMS);
-  float *const sL = reinterpret_cast<float *>(smem + OFF_L);
+  float *const sInv = reinterpret_cast<float *>(smem + OFF_INV);
+  bf16_t *const sLo = reinterpret_cast<bf16_t *>(smem + OFF_LO);
+  float *const sLd = reinterpret_cast<float *>(smem + OFF_LD);
+  bf16_t *const sTd = reinterpret_cast<bf16_t *>(smem + OFF_TD);
   bf16_t *const sM = reinterpret_cast<bf16_t *>(smem + OFF_M);
-  bf16_t *const sXw = reinterpret_cast<bf16_t *>(smem + OFF_XW);
-  bf16_t *const sXu = reinterpret_cast<bf16_t *>(smem + OFF_XU);
   bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + OFF_W);
 
   // ---- roles of the prologue ----------------------------------------------------
   // threads 0..127: q, 128..255: k (8 channels x 8 tokens each),
-  // 256..511: v (8 channels x 4 tokens each).  Map mode A needs no q, v.
+  // 256..511: v (8 channels x 4 tokens each).  Map mode needs no q (and no v
+  // for the A half).
   const int role = tid < 128 ? 0 : (tid < 256 ? 1 : 2);
   const int ridx = role == 2 ? tid - 256 : (tid & 127);
   int cg = ridx & 15;                      // channels 8cg .. 8cg+7
@@ -229,7 +262,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   if (role == 0) cbase = (int64_t)gq * kD;
   else if (role == 1) cbase = (int64_t)Hk * kD + (int64_t)gq * kD;
   else cbase = 2LL * Hk * kD + (int64_t)h * kD;
-  const bool role_on = MODE == kFull || (role == 1) || (MODE == kMapB && role == 2);
+  const bool role_on = MODE == kFull || role == 1 || (role == 2 && withV);
 
   // conv weights of this head's 384 channels -> LDS (q 0..127, k 128..255, v 256..383)
   for (int i = tid; i < 384 * 4; i += kThreads) {
@@ -250,7 +283,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // raw rows for one chunk: rows tbase-3 .. tbase+NT-1 relative to the chunk start
   constexpr int RW = Raw<T>::W;
   uint32_t raw[11][RW];
-  float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 7)
+  float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 0)
   auto load_chunk = [&](int t0) {
     if (role_on) {
 #pragma unroll
@@ -268,7 +301,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
       }
     }
-    if (wave == 7) {
+    if (wave == 0) {
       const int tau = t0 + lane;
       if (tau < seg_end) {
         ga = P.a[(int64_t)tau * Hv + h];
@@ -293,18 +326,57 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         const int row = 16 * dt + 4 * lg + i, col = 16 * wave + ln;
         float x = 0.f;
         if (MODE == kFull) x = H0 ? H0[row * kD + col] : 0.f;
-        else if (MODE == kMapA) x = row == col ? 1.f : 0.f;
+        else if (half == 0) x = row == col ? 1.f : 0.f;
         Hacc[dt][i] = x;
       }
   }
 
   const float A_log_h = P.A_log[h], dt_bias_h = P.dt_bias[h];
+  const float wn = (MODE == kFull && P.norm_w) ? P.norm_w[16 * wave + ln] : 1.0f;
   const int nchunks = (seg.len + kChunk - 1) / kChunk;
   const bool last_seg = seg.idx == seg.nseg - 1;
-  if (nchunks > 0) load_chunk(seg.begin);
+
+  // Map mode: skip work whose contribution is provably below fp32 resolution.
+  // Each token multiplies the state by alpha_t (I - beta_t k_t k_t^T), whose
+  // 2-norm is <= alpha_t (beta in [0,1], |k| <= 1), so everything before chunk c
+  // reaches the segment end scaled by at most e^{S_c}, S_c = sum of g over
+  // chunks c.. of the segment.  With S_c <= -100 ln 2 that part is dropped: the
+  // B map starts at the last such chunk, and the A map is zero if S_0 is.
+  int c_begin = 0;
+  if (MODE == kMap) {
+    float *sChG = reinterpret_cast<float *>(smem + OFF_CHG);
+    for (int cc = wave; cc < nchunks; cc += kWaves) {  // chunk sums, fixed order
+      const int tau = seg.begin + cc * kChunk + lane;
+      float g = tau < seg_end ? log_decay(P.a[(int64_t)tau * Hv + h], A_log_h, dt_bias_h) : 0.f;
+      g = wave_sum(g);
+      if (lane == 0) sChG[cc] = g;
+    }
+    __syncthreads();
+    float S = 0.f;
+    const float thr = -69.31471805599453f;  // ln 2^-100
+    for (int cc = nchunks - 1; cc >= 0; --cc) {  // every thread, same order
+      S += sChG[cc];
+      if (S <= thr) {
+        c_begin = cc;
+        break;
+      }
+    }
+    if (half == 0) {
+      float tot = 0.f;
+      for (int cc = nchunks - 1; cc >= 0; --cc) tot += sChG[cc];
+      if (tot <= thr) {  // A map is zero to fp32 resolution
+        float *Hz = P.maps + (((int64_t)unit * Hv + h) * 2 + 0) * kD * kD;
+        for (int i = tid; i < kD * kD / 4; i += kThreads)
+          reinterpret_cast<f32x4 *>(Hz)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+      }
+      c_begin = 0;  // otherwise the A map needs every chunk
+    }
+  }
+  if (nchunks > 0) load_chunk(seg.begin + c_begin * kChunk);
   __syncthreads();  // conv weights
 
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = c_begin; c < nchunks; ++c) {
     refresh();
     const int t0 = seg.begin + c * kChunk;
     const int nvalid = min(kChunk, seg_end - t0);
@@ -321,7 +393,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           float ss = 0.f;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
-          ss = group_sum<16>(ss);
+          ss = row16_sum(ss);
           const float f = scale0 * rsqrtf(ss + P.l2_eps);
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
@@ -354,20 +426,20 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         conv_silu_rows<T, 4>(raw, wv, tbase, nvalid, x);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-          bf16_t hi[4], lo[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) split_bf(x[r][cc], hi[r], lo[r]);
+          uint32_t h0, l0, h1, l1;
+          split_pk(x[0][cc], x[1][cc], h0, l0);
+          split_pk(x[2][cc], x[3][cc], h1, l1);
           const int off = (cg * 8 + cc) * kTokS + tbase;
-          *reinterpret_cast<uint2 *>(sVTh + off) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-          *reinterpret_cast<uint2 *>(sVTl + off) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+          *reinterpret_cast<uint2 *>(sVTh + off) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2 *>(sVTl + off) = make_uint2(l0, l1);
         }
       }
     }
-    if (wave == 7) {  // gates of token `lane`, inclusive cumsum of g
+    if (wave == 0) {  // gates of token `lane`, inclusive cumsum of g
       float g = 0.f, be = 0.f;
       if (lane < nvalid) {
         g = log_decay(ga, A_log_h, dt_bias_h);
-        be = sigmoidf_(gb);
+        be = sigmoid_fast(gb);
       }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -380,7 +452,22 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     __syncthreads();  // (1) prologue tiles ready
     refresh();
 
-    // prefetch the next chunk's raw rows (consumed by the next prologue)
+    // this chunk's gate z (raw bits, consumed by the epilogue) and the next chunk's
+    // raw rows (consumed by the next prologue) stay in flight during the math; z is
+    // issued first so that waiting for it never waits for the prefetch
+    uint32_t zraw[4][4];
+    if (MODE == kFull) {
+      const T *zp = (const T *)P.z;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * lg + i;
+          // clamp instead of selecting on the loaded value, so nothing waits for it here
+          const int tk = min(tok, nvalid - 1);
+          zraw[mt][i] = Act<T>::bits(zp, ((int64_t)(t0 + tk) * Hv + h) * kD + 16 * wave + ln);
+        }
+    }
     if (c + 1 < nchunks) load_chunk(t0 + kChunk);
 
     // ================= gram products K K^T (and Q K^T) =========================
@@ -412,7 +499,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
       }
     }
-    __syncthreads();  // (2) K tiles consumed: L and M overwrite them
+    __syncthreads();  // (2) Q-lo and K tiles consumed: L, M overwrite them
     refresh();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -428,7 +515,9 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           const float Gi = sG[ri];
           const bool low = cj < ri;
           const float d = __expf(low ? Gi - Gj : 0.f);
-          sL[ri * kSqS + cj] = low ? sBeta[ri] * d * kk[s][i] : 0.f;
+          const float l = low ? sBeta[ri] * d * kk[s][i] : 0.f;
+          if (ti == tj) sLd[(ti * 16 + 4 * lg + i) * kLdS + ln] = l;
+          else sLo[ri * kSqS + cj] = f2bf(-l);
           if (MODE == kFull) {
             sM[ri * kSqS + cj] = f2bf(low ? d * qk[s][i] : 0.f);
             if (cj == ri) sMdiag[ri] = qk[s][i];
@@ -444,193 +533,126 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     __syncthreads();  // (3) L, M ready
     refresh();
 
-    // ================= triangular inverse (wave 0) | Q H, beta V (all) ============
-    if (wave == 0) {
-      // (a) 16x16 diagonal blocks by forward substitution; lane = (block, column)
-      {
-        const int bb = lg, cc = ln;
-        float *Lb = sL + (16 * bb) * kSqS + 16 * bb;
-        float xcol[16];
+    // ======== diagonal blocks (I + L_bb)^-1 (waves 0-3) | Q H, right-hand sides ========
+    if (wave < 4 && lane < 16) {
+      // forward substitution for column `lane` of block `wave`
+      const float *Lb = sLd + wave * 16 * kLdS;
+      float xcol[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sacc = (r == cc) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float s0 = (r == lane) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-          for (int j = 0; j < r; ++j) sacc -= Lb[r * kSqS + j] * xcol[j];
-          xcol[r] = sacc;
+        for (int j = 0; j < r; ++j) {
+          if (j & 1) s1 -= Lb[r * kLdS + j] * xcol[j];
+          else s0 -= Lb[r * kLdS + j] * xcol[j];
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Lb[r * kSqS + cc] = xcol[r];
+        xcol[r] = s0 + s1;
       }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      // (b) 16 -> 32: T[b1][b0] = -T[b1][b1] (L[b1][b0] T[b0][b0]) for (0,1) and (2,3)
+      bf16_t *Tb = sTd + wave * 16 * kTdS;
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int b0 = 2 * pr, b1 = 2 * pr + 1;
-        u16x8 A, B;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // natural k order, K = 16 real of 32
-          const int kx = 8 * lg + j;
-          A[j] = kx < 16 ? f2bf(sL[(16 * b1 + ln) * kSqS + 16 * b0 + kx]) : 0;
-          B[j] = kx < 16 ? f2bf(sL[(16 * b0 + kx) * kSqS + 16 * b0 + ln]) : 0;
-        }
-        f32x4 Pm = mfma16(A, B, f32x4{0, 0, 0, 0});  // P = L10 T00
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // k slot 8lg + j <-> k = 4lg + j (j < 4)
-          A[j] = j < 4 ? f2bf(sL[(16 * b1 + ln) * kSqS + 16 * b1 + 4 * lg + j]) : 0;
-          B[j] = j < 4 ? f2bf(Pm[j]) : 0;
-        }
-        f32x4 Tm = mfma16(A, B, f32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sL[(16 * b1 + 4 * lg + i) * kSqS + 16 * b0 + ln] = -Tm[i];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      // (c) 32 -> 64: T[23][01] = -T[23][23] (L[23][01] T[01][01])
-      {
-        f32x4 P2[2][2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int nj = 0; nj < 2; ++nj) {
-            u16x8 A, B;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int kx = 8 * lg + j;  // 0..31, natural
-              A[j] = f2bf(sL[(32 + 16 * mi + ln) * kSqS + kx]);
-              const bool zero = (nj == 1 && kx < 16);  // upper block T01 = 0
-              B[j] = zero ? 0 : f2bf(sL[kx * kSqS + 16 * nj + ln]);
-            }
-            P2[mi][nj] = mfma16(A, B, f32x4{0, 0, 0, 0});
-          }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int nj = 0; nj < 2; ++nj) {
-            u16x8 A, B;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              // k slot 8lg + j <-> k = 4lg + j (j < 4) or 16 + 4lg + (j - 4)
-              const int kx = j < 4 ? 4 * lg + j : 16 + 4 * lg + (j - 4);
-              const bool zero = (mi == 0 && kx >= 16);  // upper block T23 = 0
-              A[j] = zero ? 0 : f2bf(sL[(32 + 16 * mi + ln) * kSqS + 32 + kx]);
-              B[j] = f2bf(j < 4 ? P2[0][nj][j] : P2[1][nj][j - 4]);
-            }
-            f32x4 Tm = mfma16(A, B, f32x4{0, 0, 0, 0});
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sL[(32 + 16 * mi + 4 * lg + i) * kSqS + 16 * nj + ln] = -Tm[i];
-          }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      // (d) X_w = T diag(beta gamma), X_u = (T - I) diag(beta); lane = column
-      {
-        const int cc = lane;
-        const float bcol = sBeta[cc];
-        const float bgcol = bcol * __expf(sG[cc]);
-#pragma unroll 8
-        for (int r = 0; r < 64; ++r) {
-          const float t = (cc <= r) ? sL[r * kSqS + cc] : 0.f;
-          sXw[r * kSqS + cc] = f2bf(t * bgcol);
-          sXu[r * kSqS + cc] = f2bf(cc < r ? t * bcol : 0.f);
-        }
-      }
+      for (int r = 0; r < 16; ++r) Tb[r * kTdS + lane] = f2bf(r == lane ? 0.f : xcol[r]);
     }
 
     // H as bf16 B operands: Hb[kb] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb+16+4lg+j-4
     u16x8 Hb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Hb[kb][j] = f2bf(Hacc[2 * kb][j]);
-        Hb[kb][4 + j] = f2bf(Hacc[2 * kb + 1][j]);
-      }
-    f32x4 Oacc[4], Uacc[4];
-    int dvc = 16 * wave + ln;  // this lane's value column
+    for (int kb = 0; kb < 4; ++kb) Hb[kb] = pack_b(Hacc[2 * kb], Hacc[2 * kb + 1]);
+    f32x4 Oacc[4], Uacc[4], Wacc[4];
+    int dvc = 16 * wave + ln;  // this lane's value column (and dk column of W)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       Oacc[mt] = f32x4{0, 0, 0, 0};
-      Uacc[mt] = f32x4{0, 0, 0, 0};
       if (MODE == kFull) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const bf16_t *qrow = sQh + (16 * mt + ln) * kRowS + 32 * kb + 4 * lg;
-          const u16x8 aq = cat4(*reinterpret_cast<const u16x4 *>(qrow),
-                                *reinterpret_cast<const u16x4 *>(qrow + 16));
+          const u16x8 aq = load_a_perm(sQh + (16 * mt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
           Oacc[mt] = mfma16(aq, Hb[kb], Oacc[mt]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Oacc[mt][i] *= __expf(sG[16 * mt + 4 * lg + i]);
       }
-      if (MODE != kMapA) {  // identity part of Utilde: beta V, from V^T hi + lo
-        const int toff = dvc * kTokS + 16 * mt + 4 * lg;
-        const u16x4 vh = *reinterpret_cast<const u16x4 *>(sVTh + toff);
-        const u16x4 vl = *reinterpret_cast<const u16x4 *>(sVTl + toff);
+      // right-hand sides of the two triangular solves, fp32: beta V and beta gamma K
+      const int toff = dvc * kTokS + 16 * mt + 4 * lg;
+      const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
+      const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
+      u16x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
+      if (withV) {
+        vh = *reinterpret_cast<const u16x4 *>(sVTh + toff);
+        vl = *reinterpret_cast<const u16x4 *>(sVTl + toff);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Uacc[mt][i] = sBeta[16 * mt + 4 * lg + i] * (bf2f(vh[i]) + bf2f(vl[i]));
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * mt + 4 * lg + i;
+        const float be = sBeta[tok];
+        Uacc[mt][i] = be * (bf2f(vh[i]) + bf2f(vl[i]));
+        Wacc[mt][i] = be * __expf(sG[tok]) * (bf2f(kh[i]) + bf2f(kl[i]));
       }
     }
-    __syncthreads();  // (4) T, X_w, X_u ready; L consumed
+    __syncthreads();  // (4) T_bb - I ready
     refresh();
     dvc = 16 * wave + ln;
 
-    // ================= W = T diag(beta gamma) K (dk tile = wave); Utilde += X_u V ====
+    // ===== block forward substitution (I + L) X = R for W (dk tile = wave) and Utilde =====
+    //   X_i = (I + (T_ii - I)) (R_i - sum_{j<i} L_ij X_j), row blocks of 16 tokens
+    {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 wacc = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && mt < 2) continue;  // T is lower triangular
-        const bf16_t *xr = sXw + (16 * mt + ln) * kSqS + 32 * kb + 8 * lg;
-        const u16x8 ax = cat4(*reinterpret_cast<const u16x4 *>(xr),
-                              *reinterpret_cast<const u16x4 *>(xr + 4));
-        const u16x8 bk = *reinterpret_cast<const u16x8 *>(sKTh + dvc * kTokS + 32 * kb + 8 * lg);
-        wacc = mfma16(ax, bk, wacc);
-        if (MODE != kMapA) {
-          const bf16_t *ur = sXu + (16 * mt + ln) * kSqS + 32 * kb + 8 * lg;
-          const u16x8 au = cat4(*reinterpret_cast<const u16x4 *>(ur),
-                                *reinterpret_cast<const u16x4 *>(ur + 4));
-          const u16x8 bv = *reinterpret_cast<const u16x8 *>(sVTh + dvc * kTokS + 32 * kb + 8 * lg);
-          Uacc[mt] = mfma16(au, bv, Uacc[mt]);
+      for (int i = 0; i < 4; ++i) {
+        const bf16_t *lrow = sLo + (16 * i + ln) * kSqS;
+        if (i == 1) {
+          const u16x8 a = load_a_perm_half(lrow, 0, lg);
+          Wacc[1] = mfma16(a, pack_b_half(Wacc[0]), Wacc[1]);
+          if (withV) Uacc[1] = mfma16(a, pack_b_half(Uacc[0]), Uacc[1]);
+        } else if (i == 2) {
+          const u16x8 a = load_a_perm(lrow, 0, 16, lg);
+          Wacc[2] = mfma16(a, pack_b(Wacc[0], Wacc[1]), Wacc[2]);
+          if (withV) Uacc[2] = mfma16(a, pack_b(Uacc[0], Uacc[1]), Uacc[2]);
+        } else if (i == 3) {
+          const u16x8 a01 = load_a_perm(lrow, 0, 16, lg);
+          const u16x8 a2 = load_a_perm_half(lrow, 32, lg);
+          Wacc[3] = mfma16(a01, pack_b(Wacc[0], Wacc[1]), Wacc[3]);
+          Wacc[3] = mfma16(a2, pack_b_half(Wacc[2]), Wacc[3]);
+          if (withV) {
+            Uacc[3] = mfma16(a01, pack_b(Uacc[0], Uacc[1]), Uacc[3]);
+            Uacc[3] = mfma16(a2, pack_b_half(Uacc[2]), Uacc[3]);
+          }
         }
+        const u16x8 at = load_a_perm_half(sTd + (i * 16 + ln) * kTdS, 0, lg);
+        Wacc[i] = mfma16(at, pack_b_half(Wacc[i]), Wacc[i]);
+        if (withV) Uacc[i] = mfma16(at, pack_b_half(Uacc[i]), Uacc[i]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * kRowS + dvc] = f2bf(-wacc[i]);
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * kRowS + dvc] = f2bf(-Wacc[mt][i]);
     }
     __syncthreads();  // (5) -W ready
     refresh();
     dvc = 16 * wave + ln;
 
     // ================= chain: U = Utilde - W H; O += M U; H update ===============
+    {  // k-block outer, row tiles inner: four independent accumulators in flight
+      u16x8 aw[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) aw[0][mt] = load_a_perm(sW + (16 * mt + ln) * kRowS, 0, 16, lg);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16_t *wr = sW + (16 * mt + ln) * kRowS + 32 * kb + 4 * lg;
-        const u16x8 aw = cat4(*reinterpret_cast<const u16x4 *>(wr),
-                              *reinterpret_cast<const u16x4 *>(wr + 16));
-        Uacc[mt] = mfma16(aw, Hb[kb], Uacc[mt]);
-      }
-    // U as B operands (k = token): Ub[kb] slots <-> tokens 32kb + 4lg + j, 32kb+16+4lg+j-4
-    if (MODE == kFull) {
-      u16x8 Ub[2];
+        if (kb < 3) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Ub[kb][j] = f2bf(Uacc[2 * kb][j]);
-          Ub[kb][4 + j] = f2bf(Uacc[2 * kb + 1][j]);
+          for (int mt = 0; mt < 4; ++mt)
+            aw[(kb + 1) & 1][mt] = load_a_perm(sW + (16 * mt + ln) * kRowS, 32 * (kb + 1),
+                                               32 * (kb + 1) + 16, lg);
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Uacc[mt] = mfma16(aw[kb & 1][mt], Hb[kb], Uacc[mt]);
+      }
+    }
+    if (MODE == kFull) {
+      const u16x8 Ub0 = pack_b(Uacc[0], Uacc[1]), Ub1 = pack_b(Uacc[2], Uacc[3]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (kb == 1 && mt < 2) continue;
-          const bf16_t *mr = sM + (16 * mt + ln) * kSqS + 32 * kb + 4 * lg;
-          const u16x8 am = cat4(*reinterpret_cast<const u16x4 *>(mr),
-                                *reinterpret_cast<const u16x4 *>(mr + 16));
-          Oacc[mt] = mfma16(am, Ub[kb], Oacc[mt]);
-        }
+        const bf16_t *mrow = sM + (16 * mt + ln) * kSqS;
+        Oacc[mt] = mfma16(load_a_perm(mrow, 0, 16, lg), Ub0, Oacc[mt]);
+        if (mt >= 2) Oacc[mt] = mfma16(load_a_perm(mrow, 32, 48, lg), Ub1, Oacc[mt]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Oacc[mt][i] += sMdiag[16 * mt + 4 * lg + i] * Uacc[mt][i];
       }
@@ -639,34 +661,47 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     {
       const float GC = sG[63];
       const float gC = __expf(GC);
+      uint32_t uh[8], ul[8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = Uacc[mt][i] * __expf(GC - sG[16 * mt + 4 * lg + i]);
+        split_pk(u[0], u[1], uh[2 * mt], ul[2 * mt]);
+        split_pk(u[2], u[3], uh[2 * mt + 1], ul[2 * mt + 1]);
+      }
       u16x8 Uh[2], Ul[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int mt = 2 * kb + (j >> 2);
-          const int tok = 16 * mt + 4 * lg + (j & 3);
-          const float u = Uacc[mt][j & 3] * __expf(GC - sG[tok]);
-          bf16_t hi, lo;
-          split_bf(u, hi, lo);
-          Uh[kb][j] = hi;
-          Ul[kb][j] = lo;
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        Uh[kb] = __builtin_bit_cast(u16x8, make_uint4(uh[4 * kb], uh[4 * kb + 1], uh[4 * kb + 2],
+                                                      uh[4 * kb + 3]));
+        Ul[kb] = __builtin_bit_cast(u16x8, make_uint4(ul[4 * kb], ul[4 * kb + 1], ul[4 * kb + 2],
+                                                      ul[4 * kb + 3]));
+      }
       // the final state gets the split-precision update over its last two chunks
       const bool precise = MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2));
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Hacc[dt][i] *= gC;
+      if (!precise) {  // k-block outer, eight independent accumulators per block
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int off = (16 * dt + ln) * kTokS + 32 * kb + 4 * lg;
-          const u16x8 akh = cat4(*reinterpret_cast<const u16x4 *>(sKTh + off),
-                                 *reinterpret_cast<const u16x4 *>(sKTh + off + 16));
-          Hacc[dt] = mfma16(akh, Uh[kb], Hacc[dt]);
-          if (precise) {
-            const u16x8 akl = cat4(*reinterpret_cast<const u16x4 *>(sKTl + off),
-                                   *reinterpret_cast<const u16x4 *>(sKTl + off + 16));
+          u16x8 ak[8];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            ak[dt] = load_a_perm(sKTh + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) Hacc[dt] = mfma16(ak[dt], Uh[kb], Hacc[dt]);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const u16x8 akh = load_a_perm(sKTh + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
+            const u16x8 akl = load_a_perm(sKTl + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
+            Hacc[dt] = mfma16(akh, Uh[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akh, Ul[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akl, Uh[kb], Hacc[dt]);
           }
@@ -680,32 +715,36 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float s = group_sum<16>(Oacc[mt][i] * Oacc[mt][i]);
+          const float s = row16_sum(Oacc[mt][i] * Oacc[mt][i]);
           if (ln == 0) sRms[wave * 64 + 16 * mt + 4 * lg + i] = s;
         }
     }
-    __syncthreads();  // (6) partial sums ready; all LDS tiles of this chunk consumed
+    __syncthreads();  // (6) partial sums ready; this chunk's LDS tiles are consumed
     refresh();
     dvc = 16 * wave + ln;
     if (MODE == kFull) {
-      const float wn = P.norm_w ? P.norm_w[dvc] : 1.0f;
-      T *op = (T *)P.o;
-      const T *zp = (const T *)P.z;
+      if (wave == 0) {
+        float ss = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int w = 0; w < kWaves; ++w) ss += sRms[w * 64 + lane];
+        sInv[lane] = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
+      }
+      __syncthreads();  // (7) per-token 1/rms ready
+      refresh();
+      dvc = 16 * wave + ln;
+      T *op = (T *)P.o;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 inv = *reinterpret_cast<const f32x4 *>(sInv + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * lg + i;
           if (tok < nvalid) {
-            float ss = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) ss += sRms[w * 64 + tok];
-            const float inv = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
             const int64_t idx = ((int64_t)(t0 + tok) * Hv + h) * kD + dvc;
-            const float zv = Act<T>::load(zp, idx);
-            Act<T>::store(op, idx, Oacc[mt][i] * inv * wn * siluf_(zv));
+            Act<T>::store(op, idx, Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i])));
           }
         }
+      }
     }
   }
 
@@ -714,7 +753,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   if (MODE == kFull) {
     if (last_seg) Hout = P.final_state + ((int64_t)seg.seq * Hv + h) * kD * kD;
   } else {
-    Hout = P.maps + (((int64_t)unit * Hv + h) * 2 + (MODE == kMapA ? 0 : 1)) * kD * kD;
+    Hout = P.maps + (((int64_t)unit * Hv + h) * 2 + half) * kD * kD;
   }
   if (Hout) {
 #pragma unroll
@@ -924,10 +963,7 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     e = hipFuncSetAttribute((const void *)chunk_kernel<T, kFull>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)chunk_kernel<T, kMapA>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)chunk_kernel<T, kMapB>,
+    e = hipFuncSetAttribute((const void *)chunk_kernel<T, kMap>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -939,16 +975,15 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
   if (tm) tm->ran[0] = true;  // the segment table was launched by the caller
   mark(1);
   if (plan.max_maps > 0) {
-    dim3 g1((unsigned)(plan.max_maps * Hv));
-    hipLaunchKernelGGL((chunk_kernel<T, kMapA>), g1, dim3(kThreads), kLdsBytes, stream, args);
+    dim3 g1((unsigned)(plan.max_maps * Hv * 2));
+    hipLaunchKernelGGL((chunk_kernel<T, kMap>), g1, dim3(kThreads), kLdsBytes, stream, args);
     mark(2);
-    hipLaunchKernelGGL((chunk_kernel<T, kMapB>), g1, dim3(kThreads), kLdsBytes, stream, args);
     mark(3);
     dim3 g2((unsigned)(plan.max_segments * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
                        args.init_state, (const float *)args.maps, args.starts, Hv);
     mark(4);
-    if (tm) tm->ran[1] = tm->ran[2] = tm->ran[3] = true;
+    if (tm) tm->ran[1] = tm->ran[3] = true;
   } else {
     mark(2);
     mark(3);

@@ -113,6 +113,26 @@ def test_ragged_lengths_small_heads(T):
 
 
 @gpu
+@pytest.mark.parametrize("alog", [0.15, 0.03])
+def test_slow_decay_multi_segment(alog):
+    """Slow decay (alpha ~ 0.9 .. 0.98 per token): the segment maps are not
+    negligible, so the map pass computes A and B over every chunk and the
+    combine pass must carry the state across segment boundaries."""
+    import math
+    w = S.scaled(S.PREFILL_4K, lengths=(2600, 900), num_qk_heads=2, num_v_heads=4, seed=21,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    d["A_log"] = torch.full_like(d["A_log"], math.log(alog))
+    o, fs, _ = run_gpu(d)
+    o_ref, fs_ref, _, _ = run_oracle(d)
+    eo, es = rel_l2(S.to_f64(o), o_ref), rel_l2(S.to_f64(fs), fs_ref)
+    print(f"slow decay exp(A_log)={alog}: o rel-L2 {eo:.3e} final-state rel-L2 {es:.3e}")
+    # slow decay is a stress regime (the bars are set for the benchmark
+    # distributions); a broken map or combine would give errors of order 1
+    assert eo < 1e-2 and es < 1e-2
+
+
+@gpu
 def test_varlen_with_empty_and_short_sequences():
     w = S.scaled(S.PREFILL_4K, lengths=(5, 0, 1, 64, 2, 0, 129, 3, 600), num_qk_heads=2,
                  num_v_heads=4, seed=7, init_state_std=0.01, conv_history=True)
