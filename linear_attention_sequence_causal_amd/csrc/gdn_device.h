@@ -80,6 +80,30 @@ __device__ __forceinline__ float log_decay(float a, float A_log, float dt_bias) 
   return fmaxf(g, -200.0f);
 }
 
+// Log-decay with the hardware log/exp (absolute error ~1e-7 in softplus).
+__device__ __forceinline__ float log_decay_fast(float a, float A_log, float dt_bias) {
+  const float u = a + dt_bias;
+  const float sp = fmaxf(u, 0.0f) + __logf(1.0f + __expf(-fabsf(u)));
+  return fmaxf(-__expf(A_log) * sp, -200.0f);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shift-and-add inside each
+// row of 16 lanes on the DPP crossbar, then the row totals via readlane.
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const int row = (threadIdx.x & 63) >> 4;
+  if (row >= 1) x += r0;
+  if (row >= 2) x += r1;
+  if (row >= 3) x += r2;
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);

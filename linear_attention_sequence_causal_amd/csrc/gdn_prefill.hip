@@ -70,11 +70,12 @@ constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;
 constexpr int OFF_CHG = OFF_INV + 64 * 4;       // fp32 [128] per-chunk log-decay (map)
 constexpr int kLdsBytes = OFF_CHG + 128 * 4;
 // regions reused after the gram products (Q-lo and K tiles are dead then)
-constexpr int kLdS = 17;                         // fp32 row stride of diagonal L blocks
+constexpr int kLdS = 20;                         // fp32 row stride of diagonal L blocks
 constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
 constexpr int OFF_LO = OFF_QL;                   // bf16 [64][68]  -L (strictly lower)
-constexpr int OFF_LD = OFF_LO + 64 * kSqS * 2;   // fp32 [4][16][17] diagonal L blocks
+constexpr int OFF_LD = OFF_LO + 64 * kSqS * 2;   // fp32 [4][16][20] diagonal L blocks
 constexpr int OFF_TD = OFF_LD + 4 * 16 * kLdS * 4;  // bf16 [4][16][24] T_bb - I
+static_assert(OFF_LD % 16 == 0, "diagonal L blocks must be 16-byte aligned");
 constexpr int OFF_M = OFF_KL;                    // bf16 [64][68]  M with zero diagonal
 constexpr int OFF_W = OFF_KH;                    // bf16 [64][136] -W
 static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KH, "solve tiles overflow the Q-lo region");
@@ -138,7 +139,7 @@ __device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint
 // Width-4 causal conv + SiLU of NT tokens x 8 channels.  raw[r] holds the raw
 // inputs of token tbase - 3 + r of the chunk; wv the 8 x 4 taps (tap 3 = current
 // token).  Tokens at or past nvalid (the padded tail of a partial chunk) are 0.
-template <typename T, int NT>
+template <typename T, int NT, bool CHECK>
 __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>::W],
                                                const float *wv, int tbase, int nvalid,
                                                float (&x)[NT][8]) {
@@ -155,7 +156,7 @@ __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>:
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += w[cc][j] * Raw<T>::get(raw[r + j], cc);
-      x[r][cc] = (tbase + r < nvalid) ? silu_fast(acc) : 0.f;
+      x[r][cc] = (!CHECK || tbase + r < nvalid) ? silu_fast(acc) : 0.f;
     }
   }
 }
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // raw rows for one chunk: rows tbase-3 .. tbase+NT-1 relative to the chunk start
   constexpr int RW = Raw<T>::W;
   uint32_t raw[11][RW];
-  float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 0)
+  float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 1)
   auto load_chunk = [&](int t0) {
     if (role_on) {
 #pragma unroll
@@ -301,7 +302,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
       }
     }
-    if (wave == 0) {
+    if (wave == 1) {
       const int tau = t0 + lane;
       if (tau < seg_end) {
         ga = P.a[(int64_t)tau * Hv + h];
@@ -386,7 +387,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       const float *wv = sConvW + ((role * 128) + cg * 8) * 4;
       if (role < 2) {  // q or k: 8 tokens x 8 channels, L2 over the head's 128 channels
         float x[8][8];
-        conv_silu_rows<T, 8>(raw, wv, tbase, nvalid, x);
+        conv_silu_rows<T, 8, true>(raw, wv, tbase, nvalid, x);
         const float scale0 = role == 0 ? P.q_scale : 1.0f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -423,7 +424,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
       } else {  // v: 4 tokens x 8 channels -> V^T [dv][tok], 8 bytes per channel
         float x[4][8];
-        conv_silu_rows<T, 4>(raw, wv, tbase, nvalid, x);
+        conv_silu_rows<T, 4, true>(raw, wv, tbase, nvalid, x);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
           uint32_t h0, l0, h1, l1;
@@ -435,17 +436,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
       }
     }
-    if (wave == 0) {  // gates of token `lane`, inclusive cumsum of g
+    if (wave == 1) {  // gates of token `lane`, inclusive cumsum of g
       float g = 0.f, be = 0.f;
       if (lane < nvalid) {
-        g = log_decay(ga, A_log_h, dt_bias_h);
+        g = log_decay_fast(ga, A_log_h, dt_bias_h);
         be = sigmoid_fast(gb);
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_up(g, o, 64);
-        if (lane >= o) g += up;
-      }
+      g = wave_inclusive_sum(g);
       sBeta[lane] = be;
       sG[lane] = g;
     }
@@ -534,21 +531,30 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     refresh();
 
     // ======== diagonal blocks (I + L_bb)^-1 (waves 0-3) | Q H, right-hand sides ========
-    if (wave < 4 && lane < 16) {
-      // forward substitution for column `lane` of block `wave`
-      const float *Lb = sLd + wave * 16 * kLdS;
+    if (wave >= 4 && lane < 16) {
+      // forward substitution for column `lane` of diagonal block `wave - 4`
+      const int blk = wave - 4;
+      const float *Lb = sLd + blk * 16 * kLdS;
       float xcol[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        float lr[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (4 * q4 < r) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(Lb + r * kLdS + 4 * q4);
+            lr[4 * q4] = t.x; lr[4 * q4 + 1] = t.y; lr[4 * q4 + 2] = t.z; lr[4 * q4 + 3] = t.w;
+          }
+        }
         float s0 = (r == lane) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
         for (int j = 0; j < r; ++j) {
-          if (j & 1) s1 -= Lb[r * kLdS + j] * xcol[j];
-          else s0 -= Lb[r * kLdS + j] * xcol[j];
+          if (j & 1) s1 -= lr[j] * xcol[j];
+          else s0 -= lr[j] * xcol[j];
         }
         xcol[r] = s0 + s1;
       }
-      bf16_t *Tb = sTd + wave * 16 * kTdS;
+      bf16_t *Tb = sTd + blk * 16 * kTdS;
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tb[r * kTdS + lane] = f2bf(r == lane ? 0.f : xcol[r]);
     }
@@ -733,13 +739,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       refresh();
       dvc = 16 * wave + ln;
       T *op = (T *)P.o;
+      const bool full = nvalid == kChunk;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 inv = *reinterpret_cast<const f32x4 *>(sInv + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * lg + i;
-          if (tok < nvalid) {
+          if (full || tok < nvalid) {
             const int64_t idx = ((int64_t)(t0 + tok) * Hv + h) * kD + dvc;
             Act<T>::store(op, idx, Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i])));
           }
