@@ -193,14 +193,22 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   int wave = tid >> 6, lane = tid & 63;
   int ln = lane & 15, lg = lane >> 4;  // MFMA lane coordinates
   const int Hv = P.Hv, Hk = P.Hk;
+  // Workgroup ids go round-robin over the 8 XCDs (each with its own L2).  The
+  // r = Hv/Hk v heads that read the same q/k head get ids 8 apart, i.e. the same
+  // XCD at nearly the same time, so their shared q/k rows are fetched once.
   int h, unit, half = 0;
-  if (MODE == kFull) {
-    h = blockIdx.x % Hv;
-    unit = blockIdx.x / Hv;
-  } else {
-    half = blockIdx.x & 1;  // 0: A columns, 1: B columns
-    h = (blockIdx.x >> 1) % Hv;
-    unit = (blockIdx.x >> 1) / Hv;
+  {
+    int bid = blockIdx.x;
+    if (MODE == kMap) {
+      half = bid & 1;  // 0: A columns, 1: B columns
+      bid >>= 1;
+    }
+    const int r = Hv / Hk;
+    const int x = bid & 7, y = bid >> 3;
+    const int member = y % r;
+    const int pair = (y / r) * 8 + x;  // (unit, q/k head) index
+    h = (pair % Hk) * r + member;
+    unit = pair / Hk;
   }
   const int gq = h / (Hv / Hk);
   const bool withV = MODE == kFull || half == 1;
@@ -981,8 +989,13 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
   if (tm) for (int i = 0; i < kTimedKernels; ++i) tm->ran[i] = false;
   if (tm) tm->ran[0] = true;  // the segment table was launched by the caller
   mark(1);
+  // grids cover ceil(units * Hk / 8) * 8 * r ids (see the id mapping in chunk_kernel)
+  auto ids = [&](int64_t units) {
+    const int64_t pairs = units * args.Hk;
+    return ((pairs + 7) / 8) * 8 * (Hv / args.Hk);
+  };
   if (plan.max_maps > 0) {
-    dim3 g1((unsigned)(plan.max_maps * Hv * 2));
+    dim3 g1((unsigned)(ids(plan.max_maps) * 2));
     hipLaunchKernelGGL((chunk_kernel<T, kMap>), g1, dim3(kThreads), kLdsBytes, stream, args);
     mark(2);
     mark(3);
@@ -996,7 +1009,7 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     mark(3);
     mark(4);
   }
-  dim3 g3((unsigned)(plan.max_segments * Hv));
+  dim3 g3((unsigned)ids(plan.max_segments));
   hipLaunchKernelGGL((chunk_kernel<T, kFull>), g3, dim3(kThreads), kLdsBytes, stream, args);
   mark(5);
   if (tm) tm->ran[4] = true;
