@@ -182,6 +182,18 @@ __device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int
   return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
 }
 
+// Offset of (row, tok) in a [d][tok] tile (K^T, V^T).  Groups of 8 tokens are
+// XOR-swizzled with bits 3..5 of the row: the prologue writes rows 8 apart from
+// neighbouring lanes, which would otherwise fall into the same LDS banks.
+__device__ __forceinline__ int tok_off(int row, int tok) {
+  return row * kTokS + ((((tok >> 3) ^ (row >> 3)) & 7) << 3) + (tok & 7);
+}
+__device__ __forceinline__ u16x8 load_a_perm_tok(const bf16_t *tile, int row, int c0, int c1,
+                                                 int lg) {
+  return cat4(*reinterpret_cast<const u16x4 *>(tile + tok_off(row, c0 + 4 * lg)),
+              *reinterpret_cast<const u16x4 *>(tile + tok_off(row, c1 + 4 * lg)));
+}
+
 // ------------------------------------------------------------ chunk kernel
 // MODE kFull: the whole mixer for one (segment, v head).  MODE kMap: the
 // segment's affine map; blockIdx selects the A half (state columns of the
@@ -293,29 +305,26 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   constexpr int RW = Raw<T>::W;
   uint32_t raw[11][RW];
   float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 1)
+  // Loads are branch-free: out-of-range rows read a clamped in-range address and
+  // are zeroed when used (a select on a value still in flight would wait for it).
   auto load_chunk = [&](int t0) {
     if (role_on) {
+      const T *base = src + (int64_t)t0 * tok_stride + head_off;
 #pragma unroll
       for (int rr = 0; rr < 11; ++rr) {
         if (rr < NT + 3) {
           const int tau = t0 + tbase - 3 + rr;
-          if (tau >= seq_begin && tau < seg_end) {
-            Raw<T>::load(raw[rr], src + (int64_t)tau * tok_stride + head_off);
-          } else if (tau < seq_begin && hist) {
-            Raw<T>::load(raw[rr], hist + (int64_t)(3 + tau - seq_begin) * P.Cc);
-          } else {
-#pragma unroll
-            for (int w = 0; w < RW; ++w) raw[rr][w] = 0u;
-          }
+          const int tc = min(max(tau, seq_begin), seg_end - 1);
+          const T *p = (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
+                                                 : base + (int)((tc - t0) * (int)tok_stride);
+          Raw<T>::load(raw[rr], p);
         }
       }
     }
     if (wave == 1) {
-      const int tau = t0 + lane;
-      if (tau < seg_end) {
-        ga = P.a[(int64_t)tau * Hv + h];
-        gb = P.b[(int64_t)tau * Hv + h];
-      }
+      const int tc = min(t0 + lane, seg_end - 1);
+      ga = P.a[(int64_t)tc * Hv + h];
+      gb = P.b[(int64_t)tc * Hv + h];
     }
   };
 
@@ -393,6 +402,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     // ================= prologue: conv + SiLU (+ L2), gates -> LDS ================
     if (role_on) {
       const float *wv = sConvW + ((role * 128) + cg * 8) * 4;
+      if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
+#pragma unroll
+        for (int rr = 0; rr < 11; ++rr)
+          if (rr < NT + 3 && t0 + tbase - 3 + rr < seq_begin)
+#pragma unroll
+            for (int w = 0; w < RW; ++w) raw[rr][w] = 0u;
+      }
       if (role < 2) {  // q or k: 8 tokens x 8 channels, L2 over the head's 128 channels
         float x[8][8];
         conv_silu_rows<T, 8, true>(raw, wv, tbase, nvalid, x);
@@ -425,7 +441,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
             for (int r = 0; r < 8; ++r) col[r] = x[r][cc];
             uint4 hi, lo;
             split_pack8(col, hi, lo);
-            const int off = (cg * 8 + cc) * kTokS + tbase;
+            const int off = tok_off(cg * 8 + cc, tbase);
             *reinterpret_cast<uint4 *>(sKTh + off) = hi;
             *reinterpret_cast<uint4 *>(sKTl + off) = lo;
           }
@@ -438,7 +454,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           uint32_t h0, l0, h1, l1;
           split_pk(x[0][cc], x[1][cc], h0, l0);
           split_pk(x[2][cc], x[3][cc], h1, l1);
-          const int off = (cg * 8 + cc) * kTokS + tbase;
+          const int off = tok_off(cg * 8 + cc, tbase);
           *reinterpret_cast<uint2 *>(sVTh + off) = make_uint2(h0, h1);
           *reinterpret_cast<uint2 *>(sVTl + off) = make_uint2(l0, l1);
         }
@@ -586,7 +602,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         for (int i = 0; i < 4; ++i) Oacc[mt][i] *= __expf(sG[16 * mt + 4 * lg + i]);
       }
       // right-hand sides of the two triangular solves, fp32: beta V and beta gamma K
-      const int toff = dvc * kTokS + 16 * mt + 4 * lg;
+      const int toff = tok_off(dvc, 16 * mt + 4 * lg);
       const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
       const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
       u16x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
@@ -704,7 +720,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           u16x8 ak[8];
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
-            ak[dt] = load_a_perm(sKTh + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
+            ak[dt] = load_a_perm_tok(sKTh, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) Hacc[dt] = mfma16(ak[dt], Uh[kb], Hacc[dt]);
         }
@@ -713,8 +729,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const u16x8 akh = load_a_perm(sKTh + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
-            const u16x8 akl = load_a_perm(sKTl + (16 * dt + ln) * kTokS, 32 * kb, 32 * kb + 16, lg);
+            const u16x8 akh = load_a_perm_tok(sKTh, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
+            const u16x8 akl = load_a_perm_tok(sKTl, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
             Hacc[dt] = mfma16(akh, Uh[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akh, Ul[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akl, Uh[kb], Hacc[dt]);
