@@ -42,6 +42,31 @@ __device__ __forceinline__ f32x4 mfma16(u16x8 a, u16x8 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Raw buffer over [base, base + bytes) (uniform): loads past the end return 0
+// and stores past it are dropped, so ragged tails need no per-lane clamps.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t buf(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+template <typename T> struct BufIO;
+template <> struct BufIO<bf16_t> {
+  static __device__ __forceinline__ uint32_t bits(rsrc_t r, uint32_t off) {
+    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), r, off, 0, 0);
+  }
+};
+template <> struct BufIO<float> {
+  static __device__ __forceinline__ uint32_t bits(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+  }
+};
+
 __device__ __forceinline__ u16x8 cat4(u16x4 x, u16x4 y) {
   return u16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
@@ -62,20 +87,22 @@ constexpr int OFF_KTL = OFF_KTH + 128 * kTokS * 2;
 constexpr int OFF_VTH = OFF_KTL + 128 * kTokS * 2;
 constexpr int OFF_VTL = OFF_VTH + 128 * kTokS * 2;
 constexpr int OFF_CONVW = OFF_VTL + 128 * kTokS * 2;
-constexpr int OFF_BETA = OFF_CONVW + 384 * 4 * 4;
+constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no bank conflicts)
+constexpr int OFF_BETA = OFF_CONVW + 48 * kConvGS * 4;
 constexpr int OFF_G = OFF_BETA + 64 * 4;
-constexpr int OFF_MDIAG = OFF_G + 64 * 4;
+constexpr int OFF_GAM = OFF_G + 64 * 4;          // e^{G_t}
+constexpr int OFF_BG = OFF_GAM + 64 * 4;         // beta_t e^{G_t}
+constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
+constexpr int OFF_MDIAG = OFF_DEC + 64 * 4;
 constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
 constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;
 constexpr int OFF_CHG = OFF_INV + 64 * 4;       // fp32 [128] per-chunk log-decay (map)
 constexpr int kLdsBytes = OFF_CHG + 128 * 4;
 // regions reused after the gram products (Q-lo and K tiles are dead then)
-constexpr int kLdS = 20;                         // fp32 row stride of diagonal L blocks
 constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
 constexpr int OFF_LO = OFF_QL;                   // bf16 [64][68]  -L (strictly lower)
-constexpr int OFF_LD = OFF_LO + 64 * kSqS * 2;   // fp32 [4][16][20] diagonal L blocks
-constexpr int OFF_TD = OFF_LD + 4 * 16 * kLdS * 4;  // bf16 [4][16][24] T_bb - I
-static_assert(OFF_LD % 16 == 0, "diagonal L blocks must be 16-byte aligned");
+constexpr int OFF_TD = OFF_LO + 64 * kSqS * 2;   // bf16 [4][16][24] T_bb - I
+static_assert(OFF_TD % 16 == 0, "T_bb blocks must be 16-byte aligned");
 constexpr int OFF_M = OFF_KL;                    // bf16 [64][68]  M with zero diagonal
 constexpr int OFF_W = OFF_KH;                    // bf16 [64][136] -W
 static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KH, "solve tiles overflow the Q-lo region");
@@ -109,6 +136,10 @@ template <> struct Raw<bf16_t> {
     const uint4 t = *reinterpret_cast<const uint4 *>(p);
     dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
   }
+  static __device__ __forceinline__ void load_buf(uint32_t (&dst)[W], rsrc_t r, uint32_t off) {
+    const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
+  }
   static __device__ __forceinline__ float get(const uint32_t (&w)[W], int c) {
     const uint32_t word = w[c >> 1];
     return __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
@@ -119,6 +150,12 @@ template <> struct Raw<float> {
   static __device__ __forceinline__ void load(uint32_t (&dst)[W], const float *p) {
     const uint4 t0 = *reinterpret_cast<const uint4 *>(p);
     const uint4 t1 = *reinterpret_cast<const uint4 *>(p + 4);
+    dst[0] = t0.x; dst[1] = t0.y; dst[2] = t0.z; dst[3] = t0.w;
+    dst[4] = t1.x; dst[5] = t1.y; dst[6] = t1.z; dst[7] = t1.w;
+  }
+  static __device__ __forceinline__ void load_buf(uint32_t (&dst)[W], rsrc_t r, uint32_t off) {
+    const i32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const i32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
     dst[0] = t0.x; dst[1] = t0.y; dst[2] = t0.z; dst[3] = t0.w;
     dst[4] = t1.x; dst[5] = t1.y; dst[6] = t1.z; dst[7] = t1.w;
   }
@@ -138,11 +175,12 @@ __device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint
 
 // Width-4 causal conv + SiLU of NT tokens x 8 channels.  raw[r] holds the raw
 // inputs of token tbase - 3 + r of the chunk; wv the 8 x 4 taps (tap 3 = current
-// token).  Tokens at or past nvalid (the padded tail of a partial chunk) are 0.
-template <typename T, int NT, bool CHECK>
+// token).  Tokens past the end of a partial chunk come out as finite values that
+// never reach an output: their beta is 0, so their rows of L, W and Utilde (and
+// hence U) are exactly zero, and their o rows are not stored.
+template <typename T, int NT>
 __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>::W],
-                                               const float *wv, int tbase, int nvalid,
-                                               float (&x)[NT][8]) {
+                                               const float *wv, float (&x)[NT][8]) {
   float w[8][4];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
@@ -156,7 +194,7 @@ __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>:
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += w[cc][j] * Raw<T>::get(raw[r + j], cc);
-      x[r][cc] = (!CHECK || tbase + r < nvalid) ? silu_fast(acc) : 0.f;
+      x[r][cc] = silu_fast(acc);
     }
   }
 }
@@ -182,16 +220,88 @@ __device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int
   return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
 }
 
-// Offset of (row, tok) in a [d][tok] tile (K^T, V^T).  Groups of 8 tokens are
-// XOR-swizzled with bits 3..5 of the row: the prologue writes rows 8 apart from
-// neighbouring lanes, which would otherwise fall into the same LDS banks.
-__device__ __forceinline__ int tok_off(int row, int tok) {
-  return row * kTokS + ((((tok >> 3) ^ (row >> 3)) & 7) << 3) + (tok & 7);
+// [d][tok] tiles (K^T, V^T): groups of 8 tokens are XOR-swizzled with bits 4..6
+// of the row.  The prologue writes rows 8 apart from neighbouring lanes (which
+// would share LDS banks unswizzled); the MFMA reads take rows 16*rt + lane, for
+// which the swizzle is the constant rt, so their offsets fold to immediates.
+__device__ __forceinline__ int tok_swz(int row, int tok) {
+  return row * kTokS + ((((tok >> 3) ^ (row >> 4)) & 7) << 3) + (tok & 7);
 }
-__device__ __forceinline__ u16x8 load_a_perm_tok(const bf16_t *tile, int row, int c0, int c1,
-                                                 int lg) {
-  return cat4(*reinterpret_cast<const u16x4 *>(tile + tok_off(row, c0 + 4 * lg)),
-              *reinterpret_cast<const u16x4 *>(tile + tok_off(row, c1 + 4 * lg)));
+// Lane part of a read of tokens 16*tt + 4*lg .. +3 in row 16*rt + ln, for even
+// and odd rt; the rest is tok_rd_const(rt, tt).
+struct TokLane {
+  int b0, d;  // lane base for even rt; odd rt adds d (the flipped low group bit)
+  __device__ __forceinline__ TokLane(int ln, int lg) {
+    b0 = ln * kTokS + 4 * (lg & 1) + 8 * (lg >> 1);
+    d = 8 - 16 * (lg >> 1);
+  }
+  __device__ __forceinline__ int operator()(int rt, int tt) const {
+    return b0 + (rt & 1) * d + 16 * rt * kTokS + 8 * (((2 * tt) ^ rt) & 6);
+  }
+};
+// A operand of K^T U: rows 16rt + ln, tokens in the permuted k order of pack_b
+// (32kb + 4lg .. +3, then 32kb + 16 + 4lg .. +3)
+__device__ __forceinline__ u16x8 load_a_tok(const bf16_t *tile, const TokLane &tl, int rt,
+                                            int kb) {
+  return cat4(*reinterpret_cast<const u16x4 *>(tile + tl(rt, 2 * kb)),
+              *reinterpret_cast<const u16x4 *>(tile + tl(rt, 2 * kb + 1)));
+}
+
+// Lower 16x16 tiles (ti, tj), tj <= ti, of the chunk's 64x64 products: waves 0
+// and 1 take two off-diagonal tiles, waves 2 and 3 one, waves 4..7 the diagonal
+// tile wave - 4 (and that block's (I + L)^-1).
+__device__ __forceinline__ void gram_tile(int wave, int s, int &ti, int &tj) {
+  if (wave >= 4) {
+    ti = tj = wave - 4;
+  } else if (s == 1) {
+    ti = 3;
+    tj = wave;  // (3,0), (3,1)
+  } else {
+    ti = wave == 0 ? 1 : (wave == 3 ? 3 : 2);  // (1,0), (2,0), (2,1), (3,2)
+    tj = wave == 3 ? 2 : (wave == 2 ? 1 : 0);
+  }
+}
+
+// 16x16 operands with K = 16 in split precision, packed from a C-layout tile X:
+// as a B operand this is X, as an A operand it is the transpose of X.
+struct Split {
+  u16x8 h, l;
+};
+__device__ __forceinline__ Split split_half(const f32x4 &x) {
+  uint32_t h0, l0, h1, l1;
+  split_pk(x[0], x[1], h0, l0);
+  split_pk(x[2], x[3], h1, l1);
+  return {__builtin_bit_cast(u16x8, make_uint4(h0, h1, 0u, 0u)),
+          __builtin_bit_cast(u16x8, make_uint4(l0, l1, 0u, 0u))};
+}
+// c + A B with A = transpose of the tile packed in a, B = the tile packed in b
+__device__ __forceinline__ f32x4 mm_split(const Split &a, const Split &b, f32x4 c) {
+  c = mfma16(a.h, b.h, c);
+  c = mfma16(a.h, b.l, c);
+  return mfma16(a.l, b.h, c);
+}
+
+// Transpose of (I + L)^-1 for a strictly lower 16x16 block L, given the C-layout
+// tiles of M = -L^T (mc) and of M^T = -L (mt).  L is nilpotent (L^16 = 0), so
+// (I + L)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) with N = -L; the transpose is
+// the same product in M, and all factors commute.  Each product is formed from
+// split operands (about 16 bits), well below the bf16 rounding applied to T - I.
+__device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4 &mc, const f32x4 &mt, int ln,
+                                                      int lg) {
+  const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+  const Split sm = split_half(mc), smt = split_half(mt);
+  const f32x4 m2 = mm_split(smt, sm, Z), m2t = mm_split(sm, smt, Z);   // M^2, (M^2)^T
+  const Split sm2 = split_half(m2), sm2t = split_half(m2t);
+  const f32x4 m4 = mm_split(sm2t, sm2, Z), m4t = mm_split(sm2, sm2t, Z);  // M^4, (M^4)^T
+  const Split sm4 = split_half(m4), sm4t = split_half(m4t);
+  const f32x4 m8t = mm_split(sm4, sm4t, Z);                             // (M^8)^T
+  f32x4 t = mc;  // I + M
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * lg + i == ln) t[i] += 1.0f;
+  t = mm_split(sm2t, split_half(t), t);            // (I + M)(I + M^2)
+  t = mm_split(sm4t, split_half(t), t);            // ... (I + M^4)
+  return mm_split(split_half(m8t), split_half(t), t);  // ... (I + M^8)
 }
 
 // ------------------------------------------------------------ chunk kernel
@@ -202,7 +312,7 @@ template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int tid = threadIdx.x;
-  int wave = tid >> 6, lane = tid & 63;
+  int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   int ln = lane & 15, lg = lane >> 4;  // MFMA lane coordinates
   const int Hv = P.Hv, Hk = P.Hk;
   // Workgroup ids go round-robin over the 8 XCDs (each with its own L2).  The
@@ -248,11 +358,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   float *const sConvW = reinterpret_cast<float *>(smem + OFF_CONVW);
   float *const sBeta = reinterpret_cast<float *>(smem + OFF_BETA);
   float *const sG = reinterpret_cast<float *>(smem + OFF_G);
+  float *const sGam = reinterpret_cast<float *>(smem + OFF_GAM);
+  float *const sBG = reinterpret_cast<float *>(smem + OFF_BG);
+  float *const sDec = reinterpret_cast<float *>(smem + OFF_DEC);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
   float *const sRms = reinterpret_cast<float *>(smem + OFF_RMS);
   float *const sInv = reinterpret_cast<float *>(smem + OFF_INV);
   bf16_t *const sLo = reinterpret_cast<bf16_t *>(smem + OFF_LO);
-  float *const sLd = reinterpret_cast<float *>(smem + OFF_LD);
   bf16_t *const sTd = reinterpret_cast<bf16_t *>(smem + OFF_TD);
   bf16_t *const sM = reinterpret_cast<bf16_t *>(smem + OFF_M);
   bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + OFF_W);
@@ -261,7 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // threads 0..127: q, 128..255: k (8 channels x 8 tokens each),
   // 256..511: v (8 channels x 4 tokens each).  Map mode needs no q (and no v
   // for the A half).
-  const int role = tid < 128 ? 0 : (tid < 256 ? 1 : 2);
+  const int role = wave < 2 ? 0 : (wave < 4 ? 1 : 2);  // uniform per wave
   const int ridx = role == 2 ? tid - 256 : (tid & 127);
   int cg = ridx & 15;                      // channels 8cg .. 8cg+7
   const int tg = ridx >> 4;                // token group
@@ -272,7 +384,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // instead of being hoisted out of the chunk loop (and spilled).
   auto refresh = [&]() {
     tid = opaque(tid);
-    wave = tid >> 6;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane = tid & 63;
     ln = lane & 15;
     lg = lane >> 4;
@@ -292,12 +404,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     if (ch < 128) c = (int64_t)gq * kD + ch;
     else if (ch < 256) c = (int64_t)Hk * kD + (int64_t)gq * kD + (ch - 128);
     else c = 2LL * Hk * kD + (int64_t)h * kD + (ch - 256);
-    sConvW[i] = P.conv_w[c * 4 + tap];
+    sConvW[(ch >> 3) * kConvGS + (ch & 7) * 4 + tap] = P.conv_w[c * 4 + tap];
   }
 
-  const T *src = role == 0 ? (const T *)P.q : (role == 1 ? (const T *)P.k : (const T *)P.v);
-  const int64_t tok_stride = role == 2 ? (int64_t)Hv * kD : (int64_t)Hk * kD;
-  const int64_t head_off = (role == 2 ? (int64_t)h : (int64_t)gq) * kD + cg * 8;
+  // this wave's source columns (uniform) and token stride
+  const T *src = (role == 0 ? (const T *)P.q : (role == 1 ? (const T *)P.k : (const T *)P.v)) +
+                 (int64_t)(role == 2 ? h : gq) * kD;
+  const int tok_stride = role == 2 ? Hv * kD : Hk * kD;
   const T *hist = P.conv_in ? (const T *)P.conv_in + (int64_t)seg.seq * 3 * P.Cc + cbase + cg * 8
                             : nullptr;
 
@@ -309,20 +422,33 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // are zeroed when used (a select on a value still in flight would wait for it).
   auto load_chunk = [&](int t0) {
     if (role_on) {
-      const T *base = src + (int64_t)t0 * tok_stride + head_off;
+      if (t0 - 3 >= seq_begin) {
+        // rows t0-3+rr+tbase: one buffer per rr (uniform), rows at or past the
+        // segment end read as zero
+        const char *b = reinterpret_cast<const char *>(src + (int64_t)(t0 - 3) * tok_stride);
+        const int rowb = tok_stride * (int)sizeof(T);
+        const int nrows = min(seg_end - (t0 - 3), kChunk + 3);
+        const uint32_t lo = (uint32_t)(tbase * tok_stride + cg * 8) * (uint32_t)sizeof(T);
 #pragma unroll
-      for (int rr = 0; rr < 11; ++rr) {
-        if (rr < NT + 3) {
-          const int tau = t0 + tbase - 3 + rr;
-          const int tc = min(max(tau, seq_begin), seg_end - 1);
-          const T *p = (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
-                                                 : base + (int)((tc - t0) * (int)tok_stride);
-          Raw<T>::load(raw[rr], p);
+        for (int rr = 0; rr < 11; ++rr)
+          if (rr < NT + 3) Raw<T>::load_buf(raw[rr], buf(b + rr * rowb, max(nrows - rr, 0) * rowb), lo);
+      } else {
+        // rows before the sequence come from the conv history (or are zeroed at
+        // use); rows past the segment read a clamped in-range row (masked at use)
+#pragma unroll
+        for (int rr = 0; rr < 11; ++rr) {
+          if (rr < NT + 3) {
+            const int tau = t0 + tbase - 3 + rr;
+            const int tc = min(max(tau, seq_begin), seg_end - 1);
+            const T *p = (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
+                                                   : src + (int64_t)tc * tok_stride + cg * 8;
+            Raw<T>::load(raw[rr], p);
+          }
         }
       }
     }
     if (wave == 1) {
-      const int tc = min(t0 + lane, seg_end - 1);
+      const uint32_t tc = (uint32_t)min(t0 + lane, seg_end - 1);
       ga = P.a[(int64_t)tc * Hv + h];
       gb = P.b[(int64_t)tc * Hv + h];
     }
@@ -401,7 +527,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 
     // ================= prologue: conv + SiLU (+ L2), gates -> LDS ================
     if (role_on) {
-      const float *wv = sConvW + ((role * 128) + cg * 8) * 4;
+      const float *wv = sConvW + (role * 16 + cg) * kConvGS;
       if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
         for (int rr = 0; rr < 11; ++rr)
@@ -411,7 +537,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       }
       if (role < 2) {  // q or k: 8 tokens x 8 channels, L2 over the head's 128 channels
         float x[8][8];
-        conv_silu_rows<T, 8, true>(raw, wv, tbase, nvalid, x);
+        conv_silu_rows<T, 8>(raw, wv, x);
         const float scale0 = role == 0 ? P.q_scale : 1.0f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -425,36 +551,43 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         }
         bf16_t *dh = role == 0 ? sQh : sKh;
         bf16_t *dl = role == 0 ? sQl : sKl;
+        uint32_t hw[8][4], lw[8][4];  // row r: channels (2e, 2e+1) in word e
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          uint4 hi, lo;
-          split_pack8(x[r], hi, lo);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
           const int off = (tbase + r) * kRowS + cg * 8;
-          *reinterpret_cast<uint4 *>(dh + off) = hi;
-          *reinterpret_cast<uint4 *>(dl + off) = lo;
+          *reinterpret_cast<uint4 *>(dh + off) = make_uint4(hw[r][0], hw[r][1], hw[r][2], hw[r][3]);
+          *reinterpret_cast<uint4 *>(dl + off) = make_uint4(lw[r][0], lw[r][1], lw[r][2], lw[r][3]);
         }
-        if (role == 1) {  // K^T [dk][tok], 8 tokens per channel = 16 bytes
+        if (role == 1) {  // K^T [dk][tok]: the same halves regrouped by channel, 16 bytes
+          // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
+          const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            float col[8];
+            // tokens (2p, 2p+1) of channel cc: half (cc & 1) of word cc/2 of rows 2p, 2p+1
+            const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t th[4], tlo[4];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) col[r] = x[r][cc];
-            uint4 hi, lo;
-            split_pack8(col, hi, lo);
-            const int off = tok_off(cg * 8 + cc, tbase);
-            *reinterpret_cast<uint4 *>(sKTh + off) = hi;
-            *reinterpret_cast<uint4 *>(sKTl + off) = lo;
+            for (int p2 = 0; p2 < 4; ++p2) {
+              th[p2] = __builtin_amdgcn_perm(hw[2 * p2 + 1][cc >> 1], hw[2 * p2][cc >> 1], sel);
+              tlo[p2] = __builtin_amdgcn_perm(lw[2 * p2 + 1][cc >> 1], lw[2 * p2][cc >> 1], sel);
+            }
+            const int off = (cg * 8 + cc) * kTokS + swz;
+            *reinterpret_cast<uint4 *>(sKTh + off) = make_uint4(th[0], th[1], th[2], th[3]);
+            *reinterpret_cast<uint4 *>(sKTl + off) = make_uint4(tlo[0], tlo[1], tlo[2], tlo[3]);
           }
         }
       } else {  // v: 4 tokens x 8 channels -> V^T [dv][tok], 8 bytes per channel
         float x[4][8];
-        conv_silu_rows<T, 4, true>(raw, wv, tbase, nvalid, x);
+        conv_silu_rows<T, 4>(raw, wv, x);
+        const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
           uint32_t h0, l0, h1, l1;
           split_pk(x[0][cc], x[1][cc], h0, l0);
           split_pk(x[2][cc], x[3][cc], h1, l1);
-          const int off = tok_off(cg * 8 + cc, tbase);
+          const int off = (cg * 8 + cc) * kTokS + swz;
           *reinterpret_cast<uint2 *>(sVTh + off) = make_uint2(h0, h1);
           *reinterpret_cast<uint2 *>(sVTl + off) = make_uint2(l0, l1);
         }
@@ -467,8 +600,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         be = sigmoid_fast(gb);
       }
       g = wave_inclusive_sum(g);
+      const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
+      const float gam = __expf(g);
       sBeta[lane] = be;
       sG[lane] = g;
+      sGam[lane] = gam;
+      sBG[lane] = be * gam;
+      sDec[lane] = __expf(GC - g);
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
@@ -478,21 +616,23 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     // issued first so that waiting for it never waits for the prefetch
     uint32_t zraw[4][4];
     if (MODE == kFull) {
-      const T *zp = (const T *)P.z;
+      // token 16mt + 4lg + i, column 16 * wave + ln: one buffer per 16mt + i
+      // (uniform), tokens at or past nvalid read as zero
+      const int rowb = Hv * kD * (int)sizeof(T);
+      const char *zb = reinterpret_cast<const char *>(P.z) +
+                       (((int64_t)t0 * Hv + h) * kD + 16 * wave) * (int64_t)sizeof(T);
+      const uint32_t zl = 4 * lg * rowb + ln * (int)sizeof(T);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * mt + 4 * lg + i;
-          // clamp instead of selecting on the loaded value, so nothing waits for it here
-          const int tk = min(tok, nvalid - 1);
-          zraw[mt][i] = Act<T>::bits(zp, ((int64_t)(t0 + tk) * Hv + h) * kD + 16 * wave + ln);
+          const int r = 16 * mt + i;
+          zraw[mt][i] = BufIO<T>::bits(buf(zb + r * rowb, max(nvalid - r, 0) * rowb), zl);
         }
     }
     if (c + 1 < nchunks) load_chunk(t0 + kChunk);
 
     // ================= gram products K K^T (and Q K^T) =========================
-    // lower tiles (i, j), j <= i: wave w takes tile w, waves 0 and 1 also 8, 9
     f32x4 kk[2], qk[2];
     const int ntiles = wave < 2 ? 2 : 1;
 #pragma unroll
@@ -500,9 +640,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       kk[s] = f32x4{0, 0, 0, 0};
       qk[s] = f32x4{0, 0, 0, 0};
       if (s < ntiles) {
-        const int t = wave + 8 * s;
-        const int ti = (t >= 1) + (t >= 3) + (t >= 6);  // lower tiles in row order
-        const int tj = t - ti * (ti + 1) / 2;
+        int ti, tj;
+        gram_tile(wave, s, ti, tj);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const int col = 32 * kb + 8 * lg;
@@ -522,14 +661,15 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
     __syncthreads();  // (2) Q-lo and K tiles consumed: L, M overwrite them
     refresh();
+    // L, M tiles to LDS; the diagonal-tile waves form (I + L_bb)^-1 - I
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s < ntiles) {
-        const int t = wave + 8 * s;
-        const int ti = (t >= 1) + (t >= 3) + (t >= 6);
-        const int tj = t - ti * (ti + 1) / 2;
+        int ti, tj;
+        gram_tile(wave, s, ti, tj);
         const int cj = 16 * tj + ln;
         const float Gj = sG[cj];
+        f32x4 mc, mt;  // diagonal tile: C-layout tiles of -L^T and -L
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ri = 16 * ti + 4 * lg + i;
@@ -537,12 +677,26 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           const bool low = cj < ri;
           const float d = __expf(low ? Gi - Gj : 0.f);
           const float l = low ? sBeta[ri] * d * kk[s][i] : 0.f;
-          if (ti == tj) sLd[(ti * 16 + 4 * lg + i) * kLdS + ln] = l;
-          else sLo[ri * kSqS + cj] = f2bf(-l);
+          if (ti == tj) {
+            const bool up = ri < cj;
+            const float du = __expf(up ? Gj - Gi : 0.f);
+            mt[i] = -l;
+            mc[i] = up ? -(sBeta[cj] * du * kk[s][i]) : 0.f;
+          } else {
+            sLo[ri * kSqS + cj] = f2bf(-l);
+          }
           if (MODE == kFull) {
             sM[ri * kSqS + cj] = f2bf(low ? d * qk[s][i] : 0.f);
             if (cj == ri) sMdiag[ri] = qk[s][i];
           }
+        }
+        if (ti == tj) {
+          const f32x4 tt = unit_lower_inverse_t(mc, mt, ln, lg);  // row ln of T, cols 4lg..
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = tt[i] - (4 * lg + i == ln ? 1.0f : 0.0f);
+          *reinterpret_cast<uint2 *>(sTd + (16 * ti + ln) * kTdS + 4 * lg) =
+              make_uint2(pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]));
         }
       }
     }
@@ -551,38 +705,10 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sM[(16 * ti + 4 * lg + i) * kSqS + 16 * (ti + 1) + ln] = 0;
     }
-    __syncthreads();  // (3) L, M ready
+    __syncthreads();  // (3) -L, M and T_bb - I ready
     refresh();
 
-    // ======== diagonal blocks (I + L_bb)^-1 (waves 0-3) | Q H, right-hand sides ========
-    if (wave >= 4 && lane < 16) {
-      // forward substitution for column `lane` of diagonal block `wave - 4`
-      const int blk = wave - 4;
-      const float *Lb = sLd + blk * 16 * kLdS;
-      float xcol[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float lr[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (4 * q4 < r) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(Lb + r * kLdS + 4 * q4);
-            lr[4 * q4] = t.x; lr[4 * q4 + 1] = t.y; lr[4 * q4 + 2] = t.z; lr[4 * q4 + 3] = t.w;
-          }
-        }
-        float s0 = (r == lane) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < r; ++j) {
-          if (j & 1) s1 -= lr[j] * xcol[j];
-          else s0 -= lr[j] * xcol[j];
-        }
-        xcol[r] = s0 + s1;
-      }
-      bf16_t *Tb = sTd + blk * 16 * kTdS;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[r * kTdS + lane] = f2bf(r == lane ? 0.f : xcol[r]);
-    }
-
+    // ================= Q H, right-hand sides of the triangular solves =============
     // H as bf16 B operands: Hb[kb] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb+16+4lg+j-4
     u16x8 Hb[4];
 #pragma unroll
@@ -598,11 +724,12 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           const u16x8 aq = load_a_perm(sQh + (16 * mt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
           Oacc[mt] = mfma16(aq, Hb[kb], Oacc[mt]);
         }
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * mt + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Oacc[mt][i] *= __expf(sG[16 * mt + 4 * lg + i]);
+        for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gm[i];
       }
       // right-hand sides of the two triangular solves, fp32: beta V and beta gamma K
-      const int toff = tok_off(dvc, 16 * mt + 4 * lg);
+      const int toff = tok_swz(dvc, 16 * mt + 4 * lg);
       const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
       const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
       u16x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
@@ -610,17 +737,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         vh = *reinterpret_cast<const u16x4 *>(sVTh + toff);
         vl = *reinterpret_cast<const u16x4 *>(sVTl + toff);
       }
+      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBeta + 16 * mt + 4 * lg);
+      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * mt + 4 * lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * mt + 4 * lg + i;
-        const float be = sBeta[tok];
-        Uacc[mt][i] = be * (bf2f(vh[i]) + bf2f(vl[i]));
-        Wacc[mt][i] = be * __expf(sG[tok]) * (bf2f(kh[i]) + bf2f(kl[i]));
+        Uacc[mt][i] = be[i] * (bf2f(vh[i]) + bf2f(vl[i]));
+        Wacc[mt][i] = bg[i] * (bf2f(kh[i]) + bf2f(kl[i]));
       }
     }
-    __syncthreads();  // (4) T_bb - I ready
-    refresh();
-    dvc = 16 * wave + ln;
 
     // ===== block forward substitution (I + L) X = R for W (dk tile = wave) and Utilde =====
     //   X_i = (I + (T_ii - I)) (R_i - sum_{j<i} L_ij X_j), row blocks of 16 tokens
@@ -655,7 +779,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * kRowS + dvc] = f2bf(-Wacc[mt][i]);
     }
-    __syncthreads();  // (5) -W ready
+    __syncthreads();  // (4) -W ready
     refresh();
     dvc = 16 * wave + ln;
 
@@ -689,14 +813,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
     // state update H = gamma_C H + K^T diag(e^{G_C - G}) U
     {
-      const float GC = sG[63];
-      const float gC = __expf(GC);
+      const float gC = sGam[63];
       uint32_t uh[8], ul[8];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * mt + 4 * lg);
         float u[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = Uacc[mt][i] * __expf(GC - sG[16 * mt + 4 * lg + i]);
+        for (int i = 0; i < 4; ++i) u[i] = Uacc[mt][i] * dec[i];
         split_pk(u[0], u[1], uh[2 * mt], ul[2 * mt]);
         split_pk(u[2], u[3], uh[2 * mt + 1], ul[2 * mt + 1]);
       }
@@ -710,6 +834,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       }
       // the final state gets the split-precision update over its last two chunks
       const bool precise = MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2));
+      const TokLane tl(ln, lg);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -720,7 +845,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           u16x8 ak[8];
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
-            ak[dt] = load_a_perm_tok(sKTh, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
+            ak[dt] = load_a_tok(sKTh, tl, dt, kb);
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) Hacc[dt] = mfma16(ak[dt], Uh[kb], Hacc[dt]);
         }
@@ -729,8 +854,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const u16x8 akh = load_a_perm_tok(sKTh, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
-            const u16x8 akl = load_a_perm_tok(sKTl, 16 * dt + ln, 32 * kb, 32 * kb + 16, lg);
+            const u16x8 akh = load_a_tok(sKTh, tl, dt, kb);
+            const u16x8 akl = load_a_tok(sKTl, tl, dt, kb);
             Hacc[dt] = mfma16(akh, Uh[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akh, Ul[kb], Hacc[dt]);
             Hacc[dt] = mfma16(akl, Uh[kb], Hacc[dt]);
@@ -749,7 +874,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           if (ln == 0) sRms[wave * 64 + 16 * mt + 4 * lg + i] = s;
         }
     }
-    __syncthreads();  // (6) partial sums ready; this chunk's LDS tiles are consumed
+    __syncthreads();  // (5) partial sums ready; this chunk's LDS tiles are consumed
     refresh();
     dvc = 16 * wave + ln;
     if (MODE == kFull) {
@@ -759,21 +884,22 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
         for (int w = 0; w < kWaves; ++w) ss += sRms[w * 64 + lane];
         sInv[lane] = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
       }
-      __syncthreads();  // (7) per-token 1/rms ready
+      __syncthreads();  // (6) per-token 1/rms ready
       refresh();
       dvc = 16 * wave + ln;
-      T *op = (T *)P.o;
-      const bool full = nvalid == kChunk;
+      // same buffers as the z loads: stores of tokens at or past nvalid are dropped
+      const int rowb = Hv * kD * (int)sizeof(T);
+      char *ob = reinterpret_cast<char *>(P.o) +
+                 (((int64_t)t0 * Hv + h) * kD + 16 * wave) * (int64_t)sizeof(T);
+      const uint32_t ol = 4 * lg * rowb + ln * (int)sizeof(T);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 inv = *reinterpret_cast<const f32x4 *>(sInv + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * mt + 4 * lg + i;
-          if (full || tok < nvalid) {
-            const int64_t idx = ((int64_t)(t0 + tok) * Hv + h) * kD + dvc;
-            Act<T>::store(op, idx, Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i])));
-          }
+          const int r = 16 * mt + i;
+          const float val = Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i]));
+          BufIO<T>::store(buf(ob + r * rowb, max(nvalid - r, 0) * rowb), ol, val);
         }
       }
     }
