@@ -417,21 +417,20 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // raw rows for one chunk: rows tbase-3 .. tbase+NT-1 relative to the chunk start
   constexpr int RW = Raw<T>::W;
   uint32_t raw[11][RW];
-  float ga = 0.f, gb = 0.f;  // gate inputs of token `lane` (wave 1)
   // Loads are branch-free: out-of-range rows read a clamped in-range address and
   // are zeroed when used (a select on a value still in flight would wait for it).
   auto load_chunk = [&](int t0) {
     if (role_on) {
       if (t0 - 3 >= seq_begin) {
-        // rows t0-3+rr+tbase: one buffer per rr (uniform), rows at or past the
-        // segment end read as zero
-        const char *b = reinterpret_cast<const char *>(src + (int64_t)(t0 - 3) * tok_stride);
+        // rows t0-3+tbase+rr from one buffer starting at row t0-3 (uniform); rows
+        // at or past the segment end read as zero
         const int rowb = tok_stride * (int)sizeof(T);
-        const int nrows = min(seg_end - (t0 - 3), kChunk + 3);
-        const uint32_t lo = (uint32_t)(tbase * tok_stride + cg * 8) * (uint32_t)sizeof(T);
+        const rsrc_t rs = buf(src + (int64_t)(t0 - 3) * tok_stride,
+                              min(seg_end - (t0 - 3), kChunk + 3) * rowb);
+        const uint32_t lo = (uint32_t)(tbase * rowb + cg * 8 * (int)sizeof(T));
 #pragma unroll
         for (int rr = 0; rr < 11; ++rr)
-          if (rr < NT + 3) Raw<T>::load_buf(raw[rr], buf(b + rr * rowb, max(nrows - rr, 0) * rowb), lo);
+          if (rr < NT + 3) Raw<T>::load_buf(raw[rr], rs, lo + rr * rowb);
       } else {
         // rows before the sequence come from the conv history (or are zeroed at
         // use); rows past the segment read a clamped in-range row (masked at use)
@@ -446,11 +445,6 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           }
         }
       }
-    }
-    if (wave == 1) {
-      const uint32_t tc = (uint32_t)min(t0 + lane, seg_end - 1);
-      ga = P.a[(int64_t)tc * Hv + h];
-      gb = P.b[(int64_t)tc * Hv + h];
     }
   };
 
@@ -526,6 +520,13 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     const int nvalid = min(kChunk, seg_end - t0);
 
     // ================= prologue: conv + SiLU (+ L2), gates -> LDS ================
+    // gate inputs of token `lane` (wave 1), issued first and consumed last
+    float ga = 0.f, gb = 0.f;
+    if (wave == 1) {
+      const int tc = min(t0 + lane, seg_end - 1);
+      ga = P.a[(int64_t)tc * Hv + h];
+      gb = P.b[(int64_t)tc * Hv + h];
+    }
     if (role_on) {
       const float *wv = sConvW + (role * 16 + cg) * kConvGS;
       if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
@@ -616,21 +617,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     // issued first so that waiting for it never waits for the prefetch
     uint32_t zraw[4][4];
     if (MODE == kFull) {
-      // token 16mt + 4lg + i, column 16 * wave + ln: one buffer per 16mt + i
-      // (uniform), tokens at or past nvalid read as zero
+      // token 16mt + 4lg + i, column 16 * wave + ln, from one buffer over this
+      // chunk's rows (uniform); tokens at or past nvalid read as zero
       const int rowb = Hv * kD * (int)sizeof(T);
-      const char *zb = reinterpret_cast<const char *>(P.z) +
-                       (((int64_t)t0 * Hv + h) * kD + 16 * wave) * (int64_t)sizeof(T);
+      const rsrc_t zs = buf((const T *)P.z + (((int64_t)t0 * Hv + h) * kD + 16 * wave),
+                            nvalid * rowb);
       const uint32_t zl = 4 * lg * rowb + ln * (int)sizeof(T);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + i;
-          zraw[mt][i] = BufIO<T>::bits(buf(zb + r * rowb, max(nvalid - r, 0) * rowb), zl);
-        }
+        for (int i = 0; i < 4; ++i) zraw[mt][i] = BufIO<T>::bits(zs, zl + (16 * mt + i) * rowb);
     }
-    if (c + 1 < nchunks) load_chunk(t0 + kChunk);
 
     // ================= gram products K K^T (and Q K^T) =========================
     f32x4 kk[2], qk[2];
@@ -709,6 +706,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     refresh();
 
     // ================= Q H, right-hand sides of the triangular solves =============
+    if (c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
     // H as bf16 B operands: Hb[kb] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb+16+4lg+j-4
     u16x8 Hb[4];
 #pragma unroll
@@ -887,19 +885,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       __syncthreads();  // (6) per-token 1/rms ready
       refresh();
       dvc = 16 * wave + ln;
-      // same buffers as the z loads: stores of tokens at or past nvalid are dropped
+      // same layout as the z loads: stores of tokens at or past nvalid are dropped
       const int rowb = Hv * kD * (int)sizeof(T);
-      char *ob = reinterpret_cast<char *>(P.o) +
-                 (((int64_t)t0 * Hv + h) * kD + 16 * wave) * (int64_t)sizeof(T);
+      const rsrc_t os = buf((T *)P.o + (((int64_t)t0 * Hv + h) * kD + 16 * wave), nvalid * rowb);
       const uint32_t ol = 4 * lg * rowb + ln * (int)sizeof(T);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 inv = *reinterpret_cast<const f32x4 *>(sInv + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + i;
           const float val = Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i]));
-          BufIO<T>::store(buf(ob + r * rowb, max(nvalid - r, 0) * rowb), ol, val);
+          BufIO<T>::store(os, ol + (16 * mt + i) * rowb, val);
         }
       }
     }
