@@ -84,16 +84,18 @@ constexpr int OFF_KH = OFF_QL + 64 * kRowS * 2;
 constexpr int OFF_KL = OFF_KH + 64 * kRowS * 2;
 constexpr int OFF_KTH = OFF_KL + 64 * kRowS * 2;
 constexpr int OFF_KTL = OFF_KTH + 128 * kTokS * 2;
-constexpr int OFF_VTH = OFF_KTL + 128 * kTokS * 2;
-constexpr int OFF_VTL = OFF_VTH + 128 * kTokS * 2;
-constexpr int OFF_CONVW = OFF_VTL + 128 * kTokS * 2;
+constexpr int kVtS = 68;       // fp32 row stride of the [128 dv][64 tok] V^T tile (272 B)
+constexpr int OFF_VT = OFF_KTL + 128 * kTokS * 2;
+constexpr int OFF_CONVW = OFF_VT + 128 * kVtS * 4;
+constexpr float kConvScale = -1.4426950408889634f;  // -log2(e), folded into the conv taps
 constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no bank conflicts)
 constexpr int OFF_BETA = OFF_CONVW + 48 * kConvGS * 4;
 constexpr int OFF_G = OFF_BETA + 64 * 4;
 constexpr int OFF_GAM = OFF_G + 64 * 4;          // e^{G_t}
 constexpr int OFF_BG = OFF_GAM + 64 * 4;         // beta_t e^{G_t}
 constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
-constexpr int OFF_MDIAG = OFF_DEC + 64 * 4;
+constexpr int OFF_BV = OFF_DEC + 64 * 4;         // beta_t / kConvScale (multiplies scaled v)
+constexpr int OFF_MDIAG = OFF_BV + 64 * 4;
 constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
 constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;
 constexpr int OFF_CHG = OFF_INV + 64 * 4;       // fp32 [128] per-chunk log-decay (map)
@@ -175,8 +177,12 @@ __device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint
 
 // Width-4 causal conv + SiLU of NT tokens x 8 channels.  raw[r] holds the raw
 // inputs of token tbase - 3 + r of the chunk; wv the 8 x 4 taps (tap 3 = current
-// token).  Tokens past the end of a partial chunk come out as finite values that
-// never reach an output: their beta is 0, so their rows of L, W and Utilde (and
+// token) pre-multiplied by kConvScale = -log2(e), so that the conv output a is
+// -log2(e) u and SiLU(u) = u / (1 + e^-u) comes out as a / (1 + 2^a), i.e.
+// scaled by kConvScale: the L2 norm of q and k absorbs the scale (and its
+// sign), the beta that multiplies v in the right-hand side absorbs it for v.
+// Tokens past the end of a partial chunk come out as finite values that never
+// reach an output: their beta is 0, so their rows of L, W and Utilde (and
 // hence U) are exactly zero, and their o rows are not stored.
 template <typename T, int NT>
 __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>::W],
@@ -194,7 +200,7 @@ __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>:
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += w[cc][j] * Raw<T>::get(raw[r + j], cc);
-      x[r][cc] = silu_fast(acc);
+      x[r][cc] = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc));
     }
   }
 }
@@ -220,10 +226,11 @@ __device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int
   return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
 }
 
-// [d][tok] tiles (K^T, V^T): groups of 8 tokens are XOR-swizzled with bits 4..6
-// of the row.  The prologue writes rows 8 apart from neighbouring lanes (which
-// would share LDS banks unswizzled); the MFMA reads take rows 16*rt + lane, for
-// which the swizzle is the constant rt, so their offsets fold to immediates.
+// bf16 [dk][tok] tiles (K^T hi/lo): groups of 8 tokens are XOR-swizzled with
+// bits 4..6 of the row (the fp32 V^T tile does the same with groups of 4).
+// The prologue writes rows 8 apart from neighbouring lanes (which would share
+// LDS banks unswizzled); the MFMA reads take rows 16*rt + lane, for which the
+// swizzle is the constant rt, so their offsets fold to immediates.
 __device__ __forceinline__ int tok_swz(int row, int tok) {
   return row * kTokS + ((((tok >> 3) ^ (row >> 4)) & 7) << 3) + (tok & 7);
 }
@@ -353,14 +360,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   bf16_t *const sKl = reinterpret_cast<bf16_t *>(smem + OFF_KL);
   bf16_t *const sKTh = reinterpret_cast<bf16_t *>(smem + OFF_KTH);
   bf16_t *const sKTl = reinterpret_cast<bf16_t *>(smem + OFF_KTL);
-  bf16_t *const sVTh = reinterpret_cast<bf16_t *>(smem + OFF_VTH);
-  bf16_t *const sVTl = reinterpret_cast<bf16_t *>(smem + OFF_VTL);
+  float *const sVT = reinterpret_cast<float *>(smem + OFF_VT);
   float *const sConvW = reinterpret_cast<float *>(smem + OFF_CONVW);
   float *const sBeta = reinterpret_cast<float *>(smem + OFF_BETA);
   float *const sG = reinterpret_cast<float *>(smem + OFF_G);
   float *const sGam = reinterpret_cast<float *>(smem + OFF_GAM);
   float *const sBG = reinterpret_cast<float *>(smem + OFF_BG);
   float *const sDec = reinterpret_cast<float *>(smem + OFF_DEC);
+  float *const sBv = reinterpret_cast<float *>(smem + OFF_BV);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
   float *const sRms = reinterpret_cast<float *>(smem + OFF_RMS);
   float *const sInv = reinterpret_cast<float *>(smem + OFF_INV);
@@ -404,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     if (ch < 128) c = (int64_t)gq * kD + ch;
     else if (ch < 256) c = (int64_t)Hk * kD + (int64_t)gq * kD + (ch - 128);
     else c = 2LL * Hk * kD + (int64_t)h * kD + (ch - 256);
-    sConvW[(ch >> 3) * kConvGS + (ch & 7) * 4 + tap] = P.conv_w[c * 4 + tap];
+    sConvW[(ch >> 3) * kConvGS + (ch & 7) * 4 + tap] = P.conv_w[c * 4 + tap] * kConvScale;
   }
 
   // this wave's source columns (uniform) and token stride
@@ -539,14 +546,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       if (role < 2) {  // q or k: 8 tokens x 8 channels, L2 over the head's 128 channels
         float x[8][8];
         conv_silu_rows<T, 8>(raw, wv, x);
-        const float scale0 = role == 0 ? P.q_scale : 1.0f;
+        // x = kConvScale SiLU(u): dividing by the norm of x takes out |kConvScale|,
+        // the sign is applied here and eps scales with kConvScale^2
+        const float scale0 = -(role == 0 ? P.q_scale : 1.0f);
+        const float eps = P.l2_eps * (kConvScale * kConvScale);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           float ss = 0.f;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
           ss = row16_sum(ss);
-          const float f = scale0 * rsqrtf(ss + P.l2_eps);
+          const float f = scale0 * rsqrtf(ss + eps);
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
         }
@@ -579,19 +589,15 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
             *reinterpret_cast<uint4 *>(sKTl + off) = make_uint4(tlo[0], tlo[1], tlo[2], tlo[3]);
           }
         }
-      } else {  // v: 4 tokens x 8 channels -> V^T [dv][tok], 8 bytes per channel
+      } else {  // v: 4 tokens x 8 channels -> fp32 V^T [dv][tok], 16 bytes per channel
         float x[4][8];
         conv_silu_rows<T, 4>(raw, wv, x);
-        const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
+        // rows 8cg + cc share row >> 4 = cg >> 1; tbase = 4 * (4-token group)
+        const int swz = ((tbase >> 2) ^ (cg >> 1)) << 2;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          uint32_t h0, l0, h1, l1;
-          split_pk(x[0][cc], x[1][cc], h0, l0);
-          split_pk(x[2][cc], x[3][cc], h1, l1);
-          const int off = (cg * 8 + cc) * kTokS + swz;
-          *reinterpret_cast<uint2 *>(sVTh + off) = make_uint2(h0, h1);
-          *reinterpret_cast<uint2 *>(sVTl + off) = make_uint2(l0, l1);
-        }
+        for (int cc = 0; cc < 8; ++cc)
+          *reinterpret_cast<f32x4 *>(sVT + (cg * 8 + cc) * kVtS + swz) =
+              f32x4{x[0][cc], x[1][cc], x[2][cc], x[3][cc]};
       }
     }
     if (wave == 1) {  // gates of token `lane`, inclusive cumsum of g
@@ -608,6 +614,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       sGam[lane] = gam;
       sBG[lane] = be * gam;
       sDec[lane] = __expf(GC - g);
+      sBv[lane] = be * (1.0f / kConvScale);
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
@@ -730,16 +737,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       const int toff = tok_swz(dvc, 16 * mt + 4 * lg);
       const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
       const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
-      u16x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-      if (withV) {
-        vh = *reinterpret_cast<const u16x4 *>(sVTh + toff);
-        vl = *reinterpret_cast<const u16x4 *>(sVTl + toff);
-      }
-      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBeta + 16 * mt + 4 * lg);
+      f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+      if (withV)  // row dvc, 4-token group 4mt + lg swizzled with row >> 4 = wave
+        vv = *reinterpret_cast<const f32x4 *>(sVT + dvc * kVtS + (((4 * mt + lg) ^ (wave & 7)) << 2));
+      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * mt + 4 * lg);
       const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * mt + 4 * lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Uacc[mt][i] = be[i] * (bf2f(vh[i]) + bf2f(vl[i]));
+        Uacc[mt][i] = be[i] * vv[i];
         Wacc[mt][i] = bg[i] * (bf2f(kh[i]) + bf2f(kl[i]));
       }
     }
