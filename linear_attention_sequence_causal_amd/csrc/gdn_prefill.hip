@@ -131,52 +131,45 @@ struct PrefillArgs {
   int precise_all;         // split-precision state update on every chunk
 };
 
-template <typename T> struct Raw;  // 8 channels of one token as raw 32-bit words
-template <> struct Raw<bf16_t> {
-  static constexpr int W = 4;  // words per 8 channels
-  static __device__ __forceinline__ void load(uint32_t (&dst)[W], const bf16_t *p) {
-    const uint4 t = *reinterpret_cast<const uint4 *>(p);
-    dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
+// NC channels of one token as raw 32-bit words (bf16 pairs or fp32)
+template <typename T, int NC>
+struct RawN {
+  static constexpr int W = NC * (int)sizeof(T) / 4;
+  static_assert(W == 2 || W == 4 || W == 8, "row fragment of 8, 16 or 32 bytes");
+  static __device__ __forceinline__ void load(uint32_t (&dst)[W], const T *p) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+    if (W == 2) {
+      const uint2 t = *reinterpret_cast<const uint2 *>(q);
+      dst[0] = t.x; dst[1] = t.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        const uint4 t = *reinterpret_cast<const uint4 *>(q + i);
+        dst[i] = t.x; dst[i + 1] = t.y; dst[i + 2] = t.z; dst[i + 3] = t.w;
+      }
+    }
   }
   static __device__ __forceinline__ void load_buf(uint32_t (&dst)[W], rsrc_t r, uint32_t off) {
-    const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
+    if (W == 2) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      dst[0] = t[0]; dst[1] = t[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        dst[i] = t.x; dst[i + 1] = t.y; dst[i + 2] = t.z; dst[i + 3] = t.w;
+      }
+    }
   }
   static __device__ __forceinline__ float get(const uint32_t (&w)[W], int c) {
+    if (sizeof(T) == 4) return __uint_as_float(w[c]);
     const uint32_t word = w[c >> 1];
     return __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
   }
 };
-template <> struct Raw<float> {
-  static constexpr int W = 8;
-  static __device__ __forceinline__ void load(uint32_t (&dst)[W], const float *p) {
-    const uint4 t0 = *reinterpret_cast<const uint4 *>(p);
-    const uint4 t1 = *reinterpret_cast<const uint4 *>(p + 4);
-    dst[0] = t0.x; dst[1] = t0.y; dst[2] = t0.z; dst[3] = t0.w;
-    dst[4] = t1.x; dst[5] = t1.y; dst[6] = t1.z; dst[7] = t1.w;
-  }
-  static __device__ __forceinline__ void load_buf(uint32_t (&dst)[W], rsrc_t r, uint32_t off) {
-    const i32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    const i32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
-    dst[0] = t0.x; dst[1] = t0.y; dst[2] = t0.z; dst[3] = t0.w;
-    dst[4] = t1.x; dst[5] = t1.y; dst[6] = t1.z; dst[7] = t1.w;
-  }
-  static __device__ __forceinline__ float get(const uint32_t (&w)[W], int c) {
-    return __uint_as_float(w[c]);
-  }
-};
 
-// hi/lo bf16 split of 8 floats, packed as two 16-byte words
-__device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint4 &lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) split_pk(x[2 * i], x[2 * i + 1], h[i], l[i]);
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// Width-4 causal conv + SiLU of NT tokens x 8 channels.  raw[r] holds the raw
-// inputs of token tbase - 3 + r of the chunk; wv the 8 x 4 taps (tap 3 = current
+// Width-4 causal conv + SiLU of NT tokens x NC channels.  raw[r] holds the raw
+// inputs of token tbase - 3 + r of the chunk; wv the NC x 4 taps (tap 3 = current
 // token) pre-multiplied by kConvScale = -log2(e), so that the conv output a is
 // -log2(e) u and SiLU(u) = u / (1 + e^-u) comes out as a / (1 + 2^a), i.e.
 // scaled by kConvScale: the L2 norm of q and k absorbs the scale (and its
@@ -184,22 +177,22 @@ __device__ __forceinline__ void split_pack8(const float (&x)[8], uint4 &hi, uint
 // Tokens past the end of a partial chunk come out as finite values that never
 // reach an output: their beta is 0, so their rows of L, W and Utilde (and
 // hence U) are exactly zero, and their o rows are not stored.
-template <typename T, int NT>
-__device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[11][Raw<T>::W],
-                                               const float *wv, float (&x)[NT][8]) {
-  float w[8][4];
+template <typename T, int NT, int NC>
+__device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[NT + 3][RawN<T, NC>::W],
+                                               const float *wv, float (&x)[NT][NC]) {
+  float w[NC][4];
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
+  for (int cc = 0; cc < NC; ++cc) {
     const f32x4 t = *reinterpret_cast<const f32x4 *>(wv + cc * 4);
     w[cc][0] = t.x; w[cc][1] = t.y; w[cc][2] = t.z; w[cc][3] = t.w;
   }
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int cc = 0; cc < NC; ++cc) {
       float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc += w[cc][j] * Raw<T>::get(raw[r + j], cc);
+      for (int j = 0; j < 4; ++j) acc += w[cc][j] * RawN<T, NC>::get(raw[r + j], cc);
       x[r][cc] = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc));
     }
   }
@@ -377,15 +370,16 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + OFF_W);
 
   // ---- roles of the prologue ----------------------------------------------------
-  // threads 0..127: q, 128..255: k (8 channels x 8 tokens each),
-  // 256..511: v (8 channels x 4 tokens each).  Map mode needs no q (and no v
-  // for the A half).
-  const int role = wave < 2 ? 0 : (wave < 4 ? 1 : 2);  // uniform per wave
-  const int ridx = role == 2 ? tid - 256 : (tid & 127);
-  int cg = ridx & 15;                      // channels 8cg .. 8cg+7
-  const int tg = ridx >> 4;                // token group
-  const int NT = role == 2 ? 4 : 8;        // tokens per thread
-  int tbase = tg * NT;
+  // Before the first barrier every wave convolves q (waves 0-3) or k (waves 4-7):
+  // 4 tokens x 8 channels per thread, the 16 lanes of a token row spanning its
+  // 128 channels (for the L2 norm).  After it every thread convolves 4 tokens x
+  // 4 channels of v, which only the right-hand side (after barrier 3) reads.
+  // Map mode needs no q (and no v for the A half).
+  const int role = wave < 4 ? 0 : 1;   // uniform per wave
+  int cg = tid & 15;                   // q/k channels 8cg .. 8cg+7
+  int tbase = ((tid & 255) >> 4) * 4;  // q/k tokens tbase .. tbase+3
+  int cv = tid & 31;                   // v channels 4cv .. 4cv+3
+  int vbase = (tid >> 5) * 4;          // v tokens vbase .. vbase+3
   // Re-derive the lane coordinates behind an optimisation barrier after every
   // workgroup barrier, so that LDS addresses are formed next to their use
   // instead of being hoisted out of the chunk loop (and spilled).
@@ -397,12 +391,11 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     lg = lane >> 4;
     cg = opaque(cg);
     tbase = opaque(tbase);
+    cv = opaque(cv);
+    vbase = opaque(vbase);
   };
-  int64_t cbase;  // conv channel of this thread's first channel
-  if (role == 0) cbase = (int64_t)gq * kD;
-  else if (role == 1) cbase = (int64_t)Hk * kD + (int64_t)gq * kD;
-  else cbase = 2LL * Hk * kD + (int64_t)h * kD;
-  const bool role_on = MODE == kFull || role == 1 || (role == 2 && withV);
+  const bool qk_on = MODE == kFull || role == 1;
+  const bool v_on = withV;
 
   // conv weights of this head's 384 channels -> LDS (q 0..127, k 128..255, v 256..383)
   for (int i = tid; i < 384 * 4; i += kThreads) {
@@ -414,42 +407,56 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     sConvW[(ch >> 3) * kConvGS + (ch & 7) * 4 + tap] = P.conv_w[c * 4 + tap] * kConvScale;
   }
 
-  // this wave's source columns (uniform) and token stride
-  const T *src = (role == 0 ? (const T *)P.q : (role == 1 ? (const T *)P.k : (const T *)P.v)) +
-                 (int64_t)(role == 2 ? h : gq) * kD;
-  const int tok_stride = role == 2 ? Hv * kD : Hk * kD;
-  const T *hist = P.conv_in ? (const T *)P.conv_in + (int64_t)seg.seq * 3 * P.Cc + cbase + cg * 8
-                            : nullptr;
+  // this wave's q or k columns and the head's v columns (uniform), token strides
+  const T *src = (role == 0 ? (const T *)P.q : (const T *)P.k) + (int64_t)gq * kD;
+  const T *vsrc = (const T *)P.v + (int64_t)h * kD;
+  const int qk_stride = Hk * kD, v_stride = Hv * kD;
+  const T *hist = nullptr, *vhist = nullptr;
+  if (P.conv_in) {
+    const T *hs = (const T *)P.conv_in + (int64_t)seg.seq * 3 * P.Cc;
+    hist = hs + (int64_t)role * Hk * kD + (int64_t)gq * kD + cg * 8;
+    vhist = hs + 2LL * Hk * kD + (int64_t)h * kD + cv * 4;
+  }
 
-  // raw rows for one chunk: rows tbase-3 .. tbase+NT-1 relative to the chunk start
-  constexpr int RW = Raw<T>::W;
-  uint32_t raw[11][RW];
-  // Loads are branch-free: out-of-range rows read a clamped in-range address and
-  // are zeroed when used (a select on a value still in flight would wait for it).
+  // raw rows for one chunk: rows base-3 .. base+3 relative to the chunk start
+  typedef RawN<T, 8> RQ;
+  typedef RawN<T, 4> RV;
+  uint32_t raw[7][RQ::W], vraw[7][RV::W];
+  // Interior chunks use one buffer per stream (rows at or past the segment end
+  // read as zero); chunks that start within 3 rows of the sequence start take
+  // rows before it from the conv history (or zero them at use) and clamp rows
+  // past the segment (masked at use).
   auto load_chunk = [&](int t0) {
-    if (role_on) {
-      if (t0 - 3 >= seq_begin) {
-        // rows t0-3+tbase+rr from one buffer starting at row t0-3 (uniform); rows
-        // at or past the segment end read as zero
-        const int rowb = tok_stride * (int)sizeof(T);
-        const rsrc_t rs = buf(src + (int64_t)(t0 - 3) * tok_stride,
-                              min(seg_end - (t0 - 3), kChunk + 3) * rowb);
+    if (t0 - 3 >= seq_begin) {
+      const int nrows = min(seg_end - (t0 - 3), kChunk + 3);
+      if (qk_on) {
+        const int rowb = qk_stride * (int)sizeof(T);
+        const rsrc_t rs = buf(src + (int64_t)(t0 - 3) * qk_stride, nrows * rowb);
         const uint32_t lo = (uint32_t)(tbase * rowb + cg * 8 * (int)sizeof(T));
 #pragma unroll
-        for (int rr = 0; rr < 11; ++rr)
-          if (rr < NT + 3) Raw<T>::load_buf(raw[rr], rs, lo + rr * rowb);
-      } else {
-        // rows before the sequence come from the conv history (or are zeroed at
-        // use); rows past the segment read a clamped in-range row (masked at use)
+        for (int rr = 0; rr < 7; ++rr) RQ::load_buf(raw[rr], rs, lo + rr * rowb);
+      }
+      if (v_on) {
+        const int rowb = v_stride * (int)sizeof(T);
+        const rsrc_t rs = buf(vsrc + (int64_t)(t0 - 3) * v_stride, nrows * rowb);
+        const uint32_t lo = (uint32_t)(vbase * rowb + cv * 4 * (int)sizeof(T));
 #pragma unroll
-        for (int rr = 0; rr < 11; ++rr) {
-          if (rr < NT + 3) {
-            const int tau = t0 + tbase - 3 + rr;
-            const int tc = min(max(tau, seq_begin), seg_end - 1);
-            const T *p = (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
-                                                   : src + (int64_t)tc * tok_stride + cg * 8;
-            Raw<T>::load(raw[rr], p);
-          }
+        for (int rr = 0; rr < 7; ++rr) RV::load_buf(vraw[rr], rs, lo + rr * rowb);
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 7; ++rr) {
+        if (qk_on) {
+          const int tau = t0 + tbase - 3 + rr;
+          const int tc = min(max(tau, seq_begin), seg_end - 1);
+          RQ::load(raw[rr], (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
+                                                      : src + (int64_t)tc * qk_stride + cg * 8);
+        }
+        if (v_on) {
+          const int tau = t0 + vbase - 3 + rr;
+          const int tc = min(max(tau, seq_begin), seg_end - 1);
+          RV::load(vraw[rr], (tau < seq_begin && vhist) ? vhist + (3 + tau - seq_begin) * P.Cc
+                                                        : vsrc + (int64_t)tc * v_stride + cv * 4);
         }
       }
     }
@@ -534,70 +541,61 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       ga = P.a[(int64_t)tc * Hv + h];
       gb = P.b[(int64_t)tc * Hv + h];
     }
-    if (role_on) {
-      const float *wv = sConvW + (role * 16 + cg) * kConvGS;
-      if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
+    if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
-        for (int rr = 0; rr < 11; ++rr)
-          if (rr < NT + 3 && t0 + tbase - 3 + rr < seq_begin)
+      for (int rr = 0; rr < 7; ++rr) {
+        if (t0 + tbase - 3 + rr < seq_begin)
 #pragma unroll
-            for (int w = 0; w < RW; ++w) raw[rr][w] = 0u;
+          for (int w = 0; w < RQ::W; ++w) raw[rr][w] = 0u;
+        if (t0 + vbase - 3 + rr < seq_begin)
+#pragma unroll
+          for (int w = 0; w < RV::W; ++w) vraw[rr][w] = 0u;
       }
-      if (role < 2) {  // q or k: 8 tokens x 8 channels, L2 over the head's 128 channels
-        float x[8][8];
-        conv_silu_rows<T, 8>(raw, wv, x);
-        // x = kConvScale SiLU(u): dividing by the norm of x takes out |kConvScale|,
-        // the sign is applied here and eps scales with kConvScale^2
-        const float scale0 = -(role == 0 ? P.q_scale : 1.0f);
-        const float eps = P.l2_eps * (kConvScale * kConvScale);
+    }
+    if (qk_on) {  // q or k: 4 tokens x 8 channels, L2 over the head's 128 channels
+      float x[4][8];
+      conv_silu_rows<T, 4, 8>(raw, sConvW + (role * 16 + cg) * kConvGS, x);
+      // x = kConvScale SiLU(u): dividing by the norm of x takes out |kConvScale|,
+      // the sign is applied here and eps scales with kConvScale^2
+      const float scale0 = -(role == 0 ? P.q_scale : 1.0f);
+      const float eps = P.l2_eps * (kConvScale * kConvScale);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float ss = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        float ss = 0.f;
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
-          ss = row16_sum(ss);
-          const float f = scale0 * rsqrtf(ss + eps);
+        for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
+        ss = row16_sum(ss);
+        const float f = scale0 * rsqrtf(ss + eps);
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
+        for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
+      }
+      bf16_t *dh = role == 0 ? sQh : sKh;
+      bf16_t *dl = role == 0 ? sQl : sKl;
+      uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
+        const int off = (tbase + r) * kRowS + cg * 8;
+        *reinterpret_cast<uint4 *>(dh + off) = make_uint4(hw[r][0], hw[r][1], hw[r][2], hw[r][3]);
+        *reinterpret_cast<uint4 *>(dl + off) = make_uint4(lw[r][0], lw[r][1], lw[r][2], lw[r][3]);
+      }
+      if (role == 1) {  // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes
+        // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
+        const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          // tokens (2p, 2p+1) of channel cc: half (cc & 1) of word cc/2 of tokens 2p, 2p+1
+          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+          const int e = cc >> 1;
+          const int off = (cg * 8 + cc) * kTokS + swz;
+          *reinterpret_cast<uint2 *>(sKTh + off) =
+              make_uint2(__builtin_amdgcn_perm(hw[1][e], hw[0][e], sel),
+                         __builtin_amdgcn_perm(hw[3][e], hw[2][e], sel));
+          *reinterpret_cast<uint2 *>(sKTl + off) =
+              make_uint2(__builtin_amdgcn_perm(lw[1][e], lw[0][e], sel),
+                         __builtin_amdgcn_perm(lw[3][e], lw[2][e], sel));
         }
-        bf16_t *dh = role == 0 ? sQh : sKh;
-        bf16_t *dl = role == 0 ? sQl : sKl;
-        uint32_t hw[8][4], lw[8][4];  // row r: channels (2e, 2e+1) in word e
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
-          const int off = (tbase + r) * kRowS + cg * 8;
-          *reinterpret_cast<uint4 *>(dh + off) = make_uint4(hw[r][0], hw[r][1], hw[r][2], hw[r][3]);
-          *reinterpret_cast<uint4 *>(dl + off) = make_uint4(lw[r][0], lw[r][1], lw[r][2], lw[r][3]);
-        }
-        if (role == 1) {  // K^T [dk][tok]: the same halves regrouped by channel, 16 bytes
-          // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
-          const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            // tokens (2p, 2p+1) of channel cc: half (cc & 1) of word cc/2 of rows 2p, 2p+1
-            const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-            uint32_t th[4], tlo[4];
-#pragma unroll
-            for (int p2 = 0; p2 < 4; ++p2) {
-              th[p2] = __builtin_amdgcn_perm(hw[2 * p2 + 1][cc >> 1], hw[2 * p2][cc >> 1], sel);
-              tlo[p2] = __builtin_amdgcn_perm(lw[2 * p2 + 1][cc >> 1], lw[2 * p2][cc >> 1], sel);
-            }
-            const int off = (cg * 8 + cc) * kTokS + swz;
-            *reinterpret_cast<uint4 *>(sKTh + off) = make_uint4(th[0], th[1], th[2], th[3]);
-            *reinterpret_cast<uint4 *>(sKTl + off) = make_uint4(tlo[0], tlo[1], tlo[2], tlo[3]);
-          }
-        }
-      } else {  // v: 4 tokens x 8 channels -> fp32 V^T [dv][tok], 16 bytes per channel
-        float x[4][8];
-        conv_silu_rows<T, 4>(raw, wv, x);
-        // rows 8cg + cc share row >> 4 = cg >> 1; tbase = 4 * (4-token group)
-        const int swz = ((tbase >> 2) ^ (cg >> 1)) << 2;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc)
-          *reinterpret_cast<f32x4 *>(sVT + (cg * 8 + cc) * kVtS + swz) =
-              f32x4{x[0][cc], x[1][cc], x[2][cc], x[3][cc]};
       }
     }
     if (wave == 1) {  // gates of token `lane`, inclusive cumsum of g
@@ -618,6 +616,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
+
+    if (v_on) {  // v: 4 tokens x 4 channels -> fp32 V^T [dv][tok], 16 bytes per channel
+      float x[4][4];
+      conv_silu_rows<T, 4, 4>(vraw, sConvW + (32 + (cv >> 1)) * kConvGS + (cv & 1) * 16, x);
+      // rows 4cv + cc share row >> 4 = cv >> 2; vbase = 4 * (4-token group)
+      const int swz = ((vbase >> 2) ^ ((cv >> 2) & 7)) << 2;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<f32x4 *>(sVT + (cv * 4 + cc) * kVtS + swz) =
+            f32x4{x[0][cc], x[1][cc], x[2][cc], x[3][cc]};
+    }
 
     // this chunk's gate z (raw bits, consumed by the epilogue) and the next chunk's
     // raw rows (consumed by the next prologue) stay in flight during the math; z is
