@@ -121,6 +121,30 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Reduce-scatter over each row of 16 lanes: lane ln returns the sum over the
+// row of v[ln].  Four butterfly stages pair lanes that differ in bit 3, 2, 1,
+// 0 (partners ln^15, ln^7, ln^3, ln^1 on the DPP crossbar); at each stage a
+// lane keeps the half of its values selected by that bit and adds the other
+// half received from its partner.
+__device__ __forceinline__ float row16_reduce_scatter(const float (&v)[16], int ln) {
+  const bool b3 = ln & 8, b2 = ln & 4, b1 = ln & 2, b0 = ln & 1;
+  float a8[8], a4[4], a2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    a8[j] = (b3 ? v[j + 8] : v[j]) + dpp_f<0x140>(b3 ? v[j] : v[j + 8]);  // row_mirror
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    a4[j] = (b2 ? a8[j + 4] : a8[j]) + dpp_f<0x141>(b2 ? a8[j] : a8[j + 4]);  // row_half_mirror
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    a2[j] = (b1 ? a4[j + 2] : a4[j]) + dpp_f<0x1B>(b1 ? a4[j] : a4[j + 2]);  // quad_perm 3,2,1,0
+  return (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);            // quad_perm 1,0,3,2
+}
+
 // Value the optimiser cannot see through (keeps derived addresses local).
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));

@@ -680,17 +680,20 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       if (s < ntiles) {
         int ti, tj;
         gram_tile(wave, s, ti, tj);
+        const bool diag = s == 0 && ti == tj;  // the second tile is never diagonal
         const int cj = 16 * tj + ln;
         const float Gj = sG[cj];
+        const f32x4 Gr = *reinterpret_cast<const f32x4 *>(sG + 16 * ti + 4 * lg);
+        const f32x4 Br = *reinterpret_cast<const f32x4 *>(sBeta + 16 * ti + 4 * lg);
         f32x4 mc, mt;  // diagonal tile: C-layout tiles of -L^T and -L
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ri = 16 * ti + 4 * lg + i;
-          const float Gi = sG[ri];
+          const float Gi = Gr[i];
           const bool low = cj < ri;
           const float d = __expf(low ? Gi - Gj : 0.f);
-          const float l = low ? sBeta[ri] * d * kk[s][i] : 0.f;
-          if (ti == tj) {
+          const float l = low ? Br[i] * d * kk[s][i] : 0.f;
+          if (diag) {
             const bool up = ri < cj;
             const float du = __expf(up ? Gj - Gi : 0.f);
             mt[i] = -l;
@@ -703,7 +706,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
             if (cj == ri) sMdiag[ri] = qk[s][i];
           }
         }
-        if (ti == tj) {
+        if (diag) {
           const f32x4 tt = unit_lower_inverse_t(mc, mt, ln, lg);  // row ln of T, cols 4lg..
           float e[4];
 #pragma unroll
@@ -826,24 +829,21 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     // state update H = gamma_C H + K^T diag(e^{G_C - G}) U
     {
       const float gC = sGam[63];
-      uint32_t uh[8], ul[8];
+      float u[4][4];
+      uint32_t uh[8];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * mt + 4 * lg);
-        float u[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = Uacc[mt][i] * dec[i];
-        split_pk(u[0], u[1], uh[2 * mt], ul[2 * mt]);
-        split_pk(u[2], u[3], uh[2 * mt + 1], ul[2 * mt + 1]);
+        for (int i = 0; i < 4; ++i) u[mt][i] = Uacc[mt][i] * dec[i];
+        uh[2 * mt] = pk_bf16(u[mt][0], u[mt][1]);
+        uh[2 * mt + 1] = pk_bf16(u[mt][2], u[mt][3]);
       }
-      u16x8 Uh[2], Ul[2];
+      u16x8 Uh[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
         Uh[kb] = __builtin_bit_cast(u16x8, make_uint4(uh[4 * kb], uh[4 * kb + 1], uh[4 * kb + 2],
                                                       uh[4 * kb + 3]));
-        Ul[kb] = __builtin_bit_cast(u16x8, make_uint4(ul[4 * kb], ul[4 * kb + 1], ul[4 * kb + 2],
-                                                      ul[4 * kb + 3]));
-      }
       // the final state gets the split-precision update over its last two chunks
       const bool precise = MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2));
       const TokLane tl(ln, lg);
@@ -862,6 +862,20 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           for (int dt = 0; dt < 8; ++dt) Hacc[dt] = mfma16(ak[dt], Uh[kb], Hacc[dt]);
         }
       } else {
+        // lo parts of U: u - bf16(u)
+        u16x8 Ul[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          uint32_t ul[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int mt = 2 * kb + (q >> 1), i0 = 2 * (q & 1);
+            const uint32_t hw = uh[4 * kb + q];
+            ul[q] = pk_bf16(u[mt][i0] - __uint_as_float(hw << 16),
+                            u[mt][i0 + 1] - __uint_as_float(hw & 0xFFFF0000u));
+          }
+          Ul[kb] = __builtin_bit_cast(u16x8, make_uint4(ul[0], ul[1], ul[2], ul[3]));
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -877,14 +891,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
 
     // ================= epilogue: RMSNorm over 128 columns, SiLU(z) gate ============
-    if (MODE == kFull) {
+    if (MODE == kFull) {  // this wave's 16 columns of sum o^2, one token per lane
+      float sq[16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float s = row16_sum(Oacc[mt][i] * Oacc[mt][i]);
-          if (ln == 0) sRms[wave * 64 + 16 * mt + 4 * lg + i] = s;
-        }
+        for (int i = 0; i < 4; ++i) sq[4 * mt + i] = Oacc[mt][i] * Oacc[mt][i];
+      // lane ln gets value 4mt + i = ln, i.e. token 16(ln >> 2) + 4lg + (ln & 3)
+      sRms[wave * 64 + 16 * (ln >> 2) + 4 * lg + (ln & 3)] = row16_reduce_scatter(sq, ln);
     }
     __syncthreads();  // (5) partial sums ready; this chunk's LDS tiles are consumed
     refresh();
