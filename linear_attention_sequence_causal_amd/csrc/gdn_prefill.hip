@@ -97,8 +97,8 @@ constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
 constexpr int OFF_BV = OFF_DEC + 64 * 4;         // beta_t / kConvScale (multiplies scaled v)
 constexpr int OFF_MDIAG = OFF_BV + 64 * 4;
 constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
-constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;
-constexpr int OFF_CHG = OFF_INV + 64 * 4;       // fp32 [128] per-chunk log-decay (map)
+constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;  // fp32 [8 waves][64] 1/rms, per wave
+constexpr int OFF_CHG = OFF_INV + kWaves * 64 * 4;  // fp32 [128] per-chunk log-decay (map)
 constexpr int kLdsBytes = OFF_CHG + 128 * 4;
 // regions reused after the gram products (Q-lo and K tiles are dead then)
 constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
@@ -904,22 +904,22 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     refresh();
     dvc = 16 * wave + ln;
     if (MODE == kFull) {
-      if (wave == 0) {
+      // every wave forms 1/rms of the 64 tokens (token `lane`) in its own slot and
+      // reads it back: a wave's LDS accesses complete in order, so no barrier
+      float *inv_w = sInv + wave * 64;
+      {
         float ss = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) ss += sRms[w * 64 + lane];
-        sInv[lane] = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
+        inv_w[lane] = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
       }
-      __syncthreads();  // (6) per-token 1/rms ready
-      refresh();
-      dvc = 16 * wave + ln;
       // same layout as the z loads: stores of tokens at or past nvalid are dropped
       const int rowb = Hv * kD * (int)sizeof(T);
       const rsrc_t os = buf((T *)P.o + (((int64_t)t0 * Hv + h) * kD + 16 * wave), nvalid * rowb);
       const uint32_t ol = 4 * lg * rowb + ln * (int)sizeof(T);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 inv = *reinterpret_cast<const f32x4 *>(sInv + 16 * mt + 4 * lg);
+        const f32x4 inv = *reinterpret_cast<const f32x4 *>(inv_w + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float val = Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i]));
