@@ -125,6 +125,7 @@ struct PrefillArgs {
   const int32_t *hdr;      // [0] segments, [1] maps
   const int32_t *map_seg;  // map slot -> segment index
   float *maps;             // [max_maps][Hv][2][D][D]
+  int32_t *map_zero;       // [max_maps][Hv]: 1 if the A map is zero (not stored)
   float *starts;           // [max_segments][Hv][D][D]
   int Hk, Hv;
   int64_t Cc;
@@ -497,11 +498,22 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   int c_begin = 0;
   if (MODE == kMap) {
     float *sChG = reinterpret_cast<float *>(smem + OFF_CHG);
-    for (int cc = wave; cc < nchunks; cc += kWaves) {  // chunk sums, fixed order
+    // chunk sums, fixed order; segments hold at most 8192 tokens = 128 chunks,
+    // i.e. 16 per wave, whose gate loads are all issued before the first use
+    constexpr int kMaxChunksPerWave = 16;
+    float av[kMaxChunksPerWave];
+#pragma unroll
+    for (int j = 0; j < kMaxChunksPerWave; ++j) {
+      const int tau = min(seg.begin + (wave + kWaves * j) * kChunk + lane, seg_end - 1);
+      av[j] = P.a[(int64_t)tau * Hv + h];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxChunksPerWave; ++j) {
+      const int cc = wave + kWaves * j;
       const int tau = seg.begin + cc * kChunk + lane;
-      float g = tau < seg_end ? log_decay(P.a[(int64_t)tau * Hv + h], A_log_h, dt_bias_h) : 0.f;
+      float g = (cc < nchunks && tau < seg_end) ? log_decay(av[j], A_log_h, dt_bias_h) : 0.f;
       g = wave_sum(g);
-      if (lane == 0) sChG[cc] = g;
+      if (lane == 0 && cc < nchunks) sChG[cc] = g;
     }
     __syncthreads();
     float S = 0.f;
@@ -516,12 +528,9 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     if (half == 0) {
       float tot = 0.f;
       for (int cc = nchunks - 1; cc >= 0; --cc) tot += sChG[cc];
-      if (tot <= thr) {  // A map is zero to fp32 resolution
-        float *Hz = P.maps + (((int64_t)unit * Hv + h) * 2 + 0) * kD * kD;
-        for (int i = tid; i < kD * kD / 4; i += kThreads)
-          reinterpret_cast<f32x4 *>(Hz)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        return;
-      }
+      // A map zero to fp32 resolution: flag it instead of storing it
+      if (tid == 0) P.map_zero[(int64_t)unit * Hv + h] = tot <= thr ? 1 : 0;
+      if (tot <= thr) return;
       c_begin = 0;  // otherwise the A map needs every chunk
     }
   }
@@ -1024,7 +1033,8 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
 // written as the start state of every segment of a multi-segment sequence.
 __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const int32_t *hdr,
                                                       const float *init_state, const float *maps,
-                                                      float *starts, int Hv) {
+                                                      const int32_t *map_zero, float *starts,
+                                                      int Hv) {
   __shared__ float sH[kD][17];
   const int slice = blockIdx.x % 8;
   const int h = (blockIdx.x / 8) % Hv;
@@ -1047,6 +1057,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
     const int m = segs[segi + s].map;
     const float *A = maps + (((int64_t)m * Hv + h) * 2 + 0) * kD * kD;
     const float *B = maps + (((int64_t)m * Hv + h) * 2 + 1) * kD * kD;
+    if (map_zero[(int64_t)m * Hv + h]) {  // H_{s+1} = B_s
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hreg[j] = B[row * kD + col0 + j];
+      continue;
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) sH[row][c0 + j] = hreg[j];
@@ -1128,6 +1143,8 @@ PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_head
     off = align256(off + 2 * DD * (size_t)p.max_maps * num_v_heads);
     p.off_start = off;
     off = align256(off + DD * (size_t)p.max_segments * num_v_heads);
+    p.off_flags = off;
+    off = align256(off + sizeof(int32_t) * (size_t)p.max_maps * num_v_heads);
   }
   p.workspace_bytes = off;
   return p;
@@ -1167,7 +1184,7 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     mark(3);
     dim3 g2((unsigned)(plan.max_segments * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
-                       args.init_state, (const float *)args.maps, args.starts, Hv);
+                       args.init_state, (const float *)args.maps, args.map_zero, args.starts, Hv);
     mark(4);
     if (tm) tm->ran[1] = tm->ran[3] = true;
   } else {
@@ -1213,6 +1230,7 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   A.segs = segs; A.hdr = hdr; A.map_seg = map_seg;
   A.maps = plan.max_maps > 0 ? (float *)(ws + plan.off_maps) : nullptr;
   A.starts = plan.max_maps > 0 ? (float *)(ws + plan.off_start) : nullptr;
+  A.map_zero = plan.max_maps > 0 ? (int32_t *)(ws + plan.off_flags) : nullptr;
   A.Hk = p.num_qk_heads; A.Hv = p.num_v_heads;
   A.Cc = 2LL * p.num_qk_heads * kD + (int64_t)p.num_v_heads * kD;
   const char *ev = getenv("GDN_PRECISE_ALL");

@@ -40,7 +40,7 @@ struct PrefillPlan {
   int32_t seg_len = 0;       // tokens per segment (multiple of 64)
   int64_t max_segments = 0;  // upper bound of the segment count
   int64_t max_maps = 0;      // upper bound of the non-final segment count
-  size_t off_table = 0, off_maps = 0, off_start = 0;
+  size_t off_table = 0, off_maps = 0, off_start = 0, off_flags = 0;
   size_t workspace_bytes = 0;
 };
 
