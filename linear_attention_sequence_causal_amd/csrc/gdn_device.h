@@ -61,6 +61,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed fp16 pair (round to nearest even, one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
 // hi/lo split of a pair: a = bf16(hi.x) + bf16(lo.x) to ~2^-16, same for b
 __device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
   hi = pk_bf16(a, b);

@@ -15,12 +15,14 @@
 // beta = sigmoid(b)) and the gated RMSNorm epilogue are fused into the chunk
 // loop, so q/k/v/z/a/b are read once and o is written once.
 //
-// Precision plan (bf16 MFMA operands, fp32 accumulation, fp32 state):
-//   Q K^T and the state update K^T U use split operands x = hi + lo
-//   (hi*hi + hi*lo + lo*hi); K K^T, W, T V, W H, Q H and M U use one bf16
-//   pass; the identity part of T V (beta V) and the diagonal of M U are
-//   applied in fp32.  The triangular inverse is exact in fp32 on its 16x16
-//   diagonal blocks and merged with bf16 products.
+// Precision plan (fp32 accumulation, fp32 state):
+//   K K^T and Q K^T take one fp16 pass on the unit-norm q and k (q_scale is
+//   applied to the products); W, T V, W H, Q H and M U take one bf16 pass; the
+//   state update K^T U takes split bf16 operands x = hi + lo (hi*hi + hi*lo +
+//   lo*hi) over the last two chunks of a sequence and one pass before them;
+//   the identity part of T V (beta V, beta gamma K) and the diagonal of M U
+//   are applied in fp32.  The triangular inverse is formed per 16x16 diagonal
+//   block from split-precision products and merged with bf16 products.
 //
 // Work decomposition: one workgroup = 8 waves = one (segment, v head); wave w
 // owns value columns 16w..16w+15 of the state in MFMA accumulators.  Long
@@ -40,6 +42,12 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(u16x8 a, u16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// the same product with fp16 operands (same lane layout)
+__device__ __forceinline__ f32x4 mfma16h(u16x8 a, u16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // Raw buffer over [base, base + bytes) (uniform): loads past the end return 0
@@ -79,10 +87,10 @@ constexpr int kTokS = 72;      // bf16 row stride of [128 d][64 tok] tiles (144 
 constexpr int kSqS = 68;       // bf16 row stride of [64][64] tiles (M, -L)
 
 constexpr int OFF_QH = 0;
-constexpr int OFF_QL = OFF_QH + 64 * kRowS * 2;
-constexpr int OFF_KH = OFF_QL + 64 * kRowS * 2;
-constexpr int OFF_KL = OFF_KH + 64 * kRowS * 2;
-constexpr int OFF_KTH = OFF_KL + 64 * kRowS * 2;
+constexpr int OFF_QF = OFF_QH + 64 * kRowS * 2;  // fp16 unit-norm q (Q K^T)
+constexpr int OFF_KF = OFF_QF + 64 * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
+constexpr int OFF_MR = OFF_KF + 64 * kRowS * 2;  // M (written after the gram products)
+constexpr int OFF_KTH = OFF_MR + 64 * kRowS * 2;
 constexpr int OFF_KTL = OFF_KTH + 128 * kTokS * 2;
 constexpr int kVtS = 68;       // fp32 row stride of the [128 dv][64 tok] V^T tile (272 B)
 constexpr int OFF_VT = OFF_KTL + 128 * kTokS * 2;
@@ -95,19 +103,20 @@ constexpr int OFF_GAM = OFF_G + 64 * 4;          // e^{G_t}
 constexpr int OFF_BG = OFF_GAM + 64 * 4;         // beta_t e^{G_t}
 constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
 constexpr int OFF_BV = OFF_DEC + 64 * 4;         // beta_t / kConvScale (multiplies scaled v)
-constexpr int OFF_MDIAG = OFF_BV + 64 * 4;
+constexpr int OFF_GAMQ = OFF_BV + 64 * 4;        // q_scale e^{G_t} (multiplies Q H)
+constexpr int OFF_MDIAG = OFF_GAMQ + 64 * 4;
 constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
 constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;  // fp32 [8 waves][64] 1/rms, per wave
 constexpr int OFF_CHG = OFF_INV + kWaves * 64 * 4;  // fp32 [128] per-chunk log-decay (map)
 constexpr int kLdsBytes = OFF_CHG + 128 * 4;
 // regions reused after the gram products (Q-lo and K tiles are dead then)
 constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
-constexpr int OFF_LO = OFF_QL;                   // bf16 [64][68]  -L (strictly lower)
+constexpr int OFF_LO = OFF_QF;                   // bf16 [64][68]  -L (strictly lower)
 constexpr int OFF_TD = OFF_LO + 64 * kSqS * 2;   // bf16 [4][16][24] T_bb - I
 static_assert(OFF_TD % 16 == 0, "T_bb blocks must be 16-byte aligned");
-constexpr int OFF_M = OFF_KL;                    // bf16 [64][68]  M with zero diagonal
-constexpr int OFF_W = OFF_KH;                    // bf16 [64][136] -W
-static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KH, "solve tiles overflow the Q-lo region");
+constexpr int OFF_M = OFF_MR;                    // bf16 [64][68]  M with zero diagonal
+constexpr int OFF_W = OFF_KF;                    // bf16 [64][136] -W
+static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KF, "solve tiles overflow the fp16 Q region");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 enum Mode { kFull = 0, kMap = 1 };
@@ -349,9 +358,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   const int seg_end = seg.begin + seg.len;
 
   bf16_t *const sQh = reinterpret_cast<bf16_t *>(smem + OFF_QH);
-  bf16_t *const sQl = reinterpret_cast<bf16_t *>(smem + OFF_QL);
-  bf16_t *const sKh = reinterpret_cast<bf16_t *>(smem + OFF_KH);
-  bf16_t *const sKl = reinterpret_cast<bf16_t *>(smem + OFF_KL);
+  bf16_t *const sQf = reinterpret_cast<bf16_t *>(smem + OFF_QF);  // fp16 bits
+  bf16_t *const sKf = reinterpret_cast<bf16_t *>(smem + OFF_KF);  // fp16 bits
   bf16_t *const sKTh = reinterpret_cast<bf16_t *>(smem + OFF_KTH);
   bf16_t *const sKTl = reinterpret_cast<bf16_t *>(smem + OFF_KTL);
   float *const sVT = reinterpret_cast<float *>(smem + OFF_VT);
@@ -362,6 +370,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   float *const sBG = reinterpret_cast<float *>(smem + OFF_BG);
   float *const sDec = reinterpret_cast<float *>(smem + OFF_DEC);
   float *const sBv = reinterpret_cast<float *>(smem + OFF_BV);
+  float *const sGamQ = reinterpret_cast<float *>(smem + OFF_GAMQ);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
   float *const sRms = reinterpret_cast<float *>(smem + OFF_RMS);
   float *const sInv = reinterpret_cast<float *>(smem + OFF_INV);
@@ -565,8 +574,10 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       float x[4][8];
       conv_silu_rows<T, 4, 8>(raw, sConvW + (role * 16 + cg) * kConvGS, x);
       // x = kConvScale SiLU(u): dividing by the norm of x takes out |kConvScale|,
-      // the sign is applied here and eps scales with kConvScale^2
-      const float scale0 = -(role == 0 ? P.q_scale : 1.0f);
+      // the sign is applied here and eps scales with kConvScale^2.  q and k stay
+      // unit-norm (q_scale multiplies the products that use q instead), so their
+      // fp16 copies cannot overflow.
+      const float scale0 = -1.0f;
       const float eps = P.l2_eps * (kConvScale * kConvScale);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -578,18 +589,35 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
       }
-      bf16_t *dh = role == 0 ? sQh : sKh;
-      bf16_t *dl = role == 0 ? sQl : sKl;
-      uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
+      // fp16 rows of q or k (the gram products); bf16 rows of q (Q H); bf16 hi/lo
+      // halves of k regrouped into K^T (right-hand side and state update)
+      if (role == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r) {
+          uint32_t fw[4], bw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
-        const int off = (tbase + r) * kRowS + cg * 8;
-        *reinterpret_cast<uint4 *>(dh + off) = make_uint4(hw[r][0], hw[r][1], hw[r][2], hw[r][3]);
-        *reinterpret_cast<uint4 *>(dl + off) = make_uint4(lw[r][0], lw[r][1], lw[r][2], lw[r][3]);
-      }
-      if (role == 1) {  // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes
+          for (int e = 0; e < 4; ++e) {
+            fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
+            bw[e] = pk_bf16(x[r][2 * e], x[r][2 * e + 1]);
+          }
+          const int off = (tbase + r) * kRowS + cg * 8;
+          *reinterpret_cast<uint4 *>(sQf + off) = make_uint4(fw[0], fw[1], fw[2], fw[3]);
+          *reinterpret_cast<uint4 *>(sQh + off) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        }
+      } else {
+        uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t fw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
+            split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
+          }
+          *reinterpret_cast<uint4 *>(sKf + (tbase + r) * kRowS + cg * 8) =
+              make_uint4(fw[0], fw[1], fw[2], fw[3]);
+        }
+        // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes
         // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
         const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
 #pragma unroll
@@ -622,6 +650,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       sBG[lane] = be * gam;
       sDec[lane] = __expf(GC - g);
       sBv[lane] = be * (1.0f / kConvScale);
+      sGamQ[lane] = gam * P.q_scale;
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
@@ -667,16 +696,12 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const int col = 32 * kb + 8 * lg;
-          const u16x8 bk = *reinterpret_cast<const u16x8 *>(sKh + (16 * tj + ln) * kRowS + col);
-          const u16x8 ak = *reinterpret_cast<const u16x8 *>(sKh + (16 * ti + ln) * kRowS + col);
-          kk[s] = mfma16(ak, bk, kk[s]);
+          const u16x8 bk = *reinterpret_cast<const u16x8 *>(sKf + (16 * tj + ln) * kRowS + col);
+          const u16x8 ak = *reinterpret_cast<const u16x8 *>(sKf + (16 * ti + ln) * kRowS + col);
+          kk[s] = mfma16h(ak, bk, kk[s]);
           if (MODE == kFull) {
-            const u16x8 bkl = *reinterpret_cast<const u16x8 *>(sKl + (16 * tj + ln) * kRowS + col);
-            const u16x8 aqh = *reinterpret_cast<const u16x8 *>(sQh + (16 * ti + ln) * kRowS + col);
-            const u16x8 aql = *reinterpret_cast<const u16x8 *>(sQl + (16 * ti + ln) * kRowS + col);
-            qk[s] = mfma16(aqh, bk, qk[s]);
-            qk[s] = mfma16(aqh, bkl, qk[s]);
-            qk[s] = mfma16(aql, bk, qk[s]);
+            const u16x8 aq = *reinterpret_cast<const u16x8 *>(sQf + (16 * ti + ln) * kRowS + col);
+            qk[s] = mfma16h(aq, bk, qk[s]);
           }
         }
       }
@@ -711,8 +736,9 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
             sLo[ri * kSqS + cj] = f2bf(-l);
           }
           if (MODE == kFull) {
-            sM[ri * kSqS + cj] = f2bf(low ? d * qk[s][i] : 0.f);
-            if (cj == ri) sMdiag[ri] = qk[s][i];
+            const float qkq = qk[s][i] * P.q_scale;
+            sM[ri * kSqS + cj] = f2bf(low ? d * qkq : 0.f);
+            if (cj == ri) sMdiag[ri] = qkq;
           }
         }
         if (diag) {
@@ -750,7 +776,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           const u16x8 aq = load_a_perm(sQh + (16 * mt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
           Oacc[mt] = mfma16(aq, Hb[kb], Oacc[mt]);
         }
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * mt + 4 * lg);
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGamQ + 16 * mt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gm[i];
       }
