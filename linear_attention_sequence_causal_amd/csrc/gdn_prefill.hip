@@ -66,6 +66,23 @@ template <> struct BufIO<bf16_t> {
     __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), r, off, 0, 0);
   }
 };
+// 8 consecutive outputs of one row, rounded to T, as 16-byte buffer stores
+template <typename T> struct OutRow;
+template <> struct OutRow<bf16_t> {
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float *x) {
+    const i32x4 w = {(int)pk_bf16(x[0], x[1]), (int)pk_bf16(x[2], x[3]), (int)pk_bf16(x[4], x[5]),
+                     (int)pk_bf16(x[6], x[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+  }
+};
+template <> struct OutRow<float> {
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float *x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, f32x4{x[0], x[1], x[2], x[3]}),
+                                           r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, f32x4{x[4], x[5], x[6], x[7]}),
+                                           r, off + 16, 0, 0);
+  }
+};
 template <> struct BufIO<float> {
   static __device__ __forceinline__ uint32_t bits(rsrc_t r, uint32_t off) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
@@ -105,9 +122,13 @@ constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
 constexpr int OFF_BV = OFF_DEC + 64 * 4;         // beta_t / kConvScale (multiplies scaled v)
 constexpr int OFF_GAMQ = OFF_BV + 64 * 4;        // q_scale e^{G_t} (multiplies Q H)
 constexpr int OFF_MDIAG = OFF_GAMQ + 64 * 4;
-constexpr int OFF_RMS = OFF_MDIAG + 64 * 4;
-constexpr int OFF_INV = OFF_RMS + kWaves * 64 * 4;  // fp32 [8 waves][64] 1/rms, per wave
-constexpr int OFF_CHG = OFF_INV + kWaves * 64 * 4;  // fp32 [128] per-chunk log-decay (map)
+constexpr int OFF_NW = OFF_MDIAG + 64 * 4;       // fp32 [128] RMSNorm weight (1 if none)
+constexpr int OFF_CHG = OFF_NW + kD * 4;         // fp32 [128] per-chunk log-decay (map)
+// fp32 [64 tok][132] o tile for the epilogue, in the V^T region (dead after the
+// right-hand side; the next chunk writes V^T only after its first barrier)
+constexpr int kOS = 132;
+constexpr int OFF_O = OFF_VT;
+static_assert(64 * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
 constexpr int kLdsBytes = OFF_CHG + 128 * 4;
 // regions reused after the gram products (Q-lo and K tiles are dead then)
 constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
@@ -372,8 +393,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   float *const sBv = reinterpret_cast<float *>(smem + OFF_BV);
   float *const sGamQ = reinterpret_cast<float *>(smem + OFF_GAMQ);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
-  float *const sRms = reinterpret_cast<float *>(smem + OFF_RMS);
-  float *const sInv = reinterpret_cast<float *>(smem + OFF_INV);
+  float *const sNW = reinterpret_cast<float *>(smem + OFF_NW);
+  float *const sO = reinterpret_cast<float *>(smem + OFF_O);
   bf16_t *const sLo = reinterpret_cast<bf16_t *>(smem + OFF_LO);
   bf16_t *const sTd = reinterpret_cast<bf16_t *>(smem + OFF_TD);
   bf16_t *const sM = reinterpret_cast<bf16_t *>(smem + OFF_M);
@@ -494,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   }
 
   const float A_log_h = P.A_log[h], dt_bias_h = P.dt_bias[h];
-  const float wn = (MODE == kFull && P.norm_w) ? P.norm_w[16 * wave + ln] : 1.0f;
+  if (MODE == kFull && tid < kD) sNW[tid] = P.norm_w ? P.norm_w[tid] : 1.0f;
   const int nchunks = (seg.len + kChunk - 1) / kChunk;
   const bool last_seg = seg.idx == seg.nseg - 1;
 
@@ -669,18 +690,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     // this chunk's gate z (raw bits, consumed by the epilogue) and the next chunk's
     // raw rows (consumed by the next prologue) stay in flight during the math; z is
     // issued first so that waiting for it never waits for the prefetch
-    uint32_t zraw[4][4];
+    // epilogue layout: token tid >> 3, columns 8e..8e+7 and 64+8e..64+8e+7 with
+    // e = tid & 7 (two 16-byte bf16 blocks per thread for z and o)
+    typedef RawN<T, 8> RZ;
+    uint32_t zw[2][RZ::W];
     if (MODE == kFull) {
-      // token 16mt + 4lg + i, column 16 * wave + ln, from one buffer over this
-      // chunk's rows (uniform); tokens at or past nvalid read as zero
+      // one buffer over this chunk's rows (uniform); tokens at or past nvalid read as zero
       const int rowb = Hv * kD * (int)sizeof(T);
-      const rsrc_t zs = buf((const T *)P.z + (((int64_t)t0 * Hv + h) * kD + 16 * wave),
-                            nvalid * rowb);
-      const uint32_t zl = 4 * lg * rowb + ln * (int)sizeof(T);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zraw[mt][i] = BufIO<T>::bits(zs, zl + (16 * mt + i) * rowb);
+      const rsrc_t zs = buf((const T *)P.z + ((int64_t)t0 * Hv + h) * kD, nvalid * rowb);
+      const uint32_t zo = (uint32_t)((tid >> 3) * rowb + 8 * (tid & 7) * (int)sizeof(T));
+      RZ::load_buf(zw[0], zs, zo);
+      RZ::load_buf(zw[1], zs, zo + 64 * (int)sizeof(T));
     }
 
     // ================= gram products K K^T (and Q K^T) =========================
@@ -926,41 +946,53 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
 
     // ================= epilogue: RMSNorm over 128 columns, SiLU(z) gate ============
-    if (MODE == kFull) {  // this wave's 16 columns of sum o^2, one token per lane
-      float sq[16];
+    if (MODE == kFull) {  // this wave's 16 columns of o -> the fp32 o tile
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sq[4 * mt + i] = Oacc[mt][i] * Oacc[mt][i];
-      // lane ln gets value 4mt + i = ln, i.e. token 16(ln >> 2) + 4lg + (ln & 3)
-      sRms[wave * 64 + 16 * (ln >> 2) + 4 * lg + (ln & 3)] = row16_reduce_scatter(sq, ln);
+        for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * lg + i) * kOS + 16 * wave + ln] = Oacc[mt][i];
     }
-    __syncthreads();  // (5) partial sums ready; this chunk's LDS tiles are consumed
+    __syncthreads();  // (5) o tile ready; this chunk's other LDS tiles are consumed
     refresh();
-    dvc = 16 * wave + ln;
     if (MODE == kFull) {
-      // every wave forms 1/rms of the 64 tokens (token `lane`) in its own slot and
-      // reads it back: a wave's LDS accesses complete in order, so no barrier
-      float *inv_w = sInv + wave * 64;
+      // token tid >> 3 (8 lanes per token), columns 8e.. and 64+8e.. with e = tid & 7;
+      // the four 16-byte reads of a row are bank-conflict free with kOS = 132
+      const int etok = tid >> 3, e8 = 8 * (tid & 7);
+      const float *orow = sO + etok * kOS;
+      float ov[16], nw[16];
       {
-        float ss = 0.f;
+        const f32x4 r0 = *reinterpret_cast<const f32x4 *>(orow + e8);
+        const f32x4 r2 = *reinterpret_cast<const f32x4 *>(orow + 64 + e8);
+        const f32x4 r1 = *reinterpret_cast<const f32x4 *>(orow + e8 + 4);
+        const f32x4 r3 = *reinterpret_cast<const f32x4 *>(orow + 68 + e8);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(sNW + e8);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(sNW + e8 + 4);
+        const f32x4 w2 = *reinterpret_cast<const f32x4 *>(sNW + 64 + e8);
+        const f32x4 w3 = *reinterpret_cast<const f32x4 *>(sNW + 68 + e8);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) ss += sRms[w * 64 + lane];
-        inv_w[lane] = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
-      }
-      // same layout as the z loads: stores of tokens at or past nvalid are dropped
-      const int rowb = Hv * kD * (int)sizeof(T);
-      const rsrc_t os = buf((T *)P.o + (((int64_t)t0 * Hv + h) * kD + 16 * wave), nvalid * rowb);
-      const uint32_t ol = 4 * lg * rowb + ln * (int)sizeof(T);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 inv = *reinterpret_cast<const f32x4 *>(inv_w + 16 * mt + 4 * lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float val = Oacc[mt][i] * inv[i] * wn * silu_fast(Act<T>::from_bits(zraw[mt][i]));
-          BufIO<T>::store(os, ol + (16 * mt + i) * rowb, val);
+        for (int j = 0; j < 4; ++j) {
+          ov[j] = r0[j]; ov[4 + j] = r1[j]; ov[8 + j] = r2[j]; ov[12 + j] = r3[j];
+          nw[j] = w0[j]; nw[4 + j] = w1[j]; nw[8 + j] = w2[j]; nw[12 + j] = w3[j];
         }
       }
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss += ov[j] * ov[j];
+      // sum over the 8 lanes of the token: quad butterflies, then the other quad
+      ss += dpp_f<0xB1>(ss);  // quad_perm 1,0,3,2
+      ss += dpp_f<0x4E>(ss);  // quad_perm 2,3,0,1
+      ss += dpp_f<0x141>(ss);  // row_half_mirror
+      const float inv = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
+      float val[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        val[j] = ov[j] * inv * nw[j] * silu_fast(RZ::get(zw[j >> 3], j & 7));
+      // one buffer over this chunk's o rows: stores of tokens at or past nvalid are dropped
+      const int rowb = Hv * kD * (int)sizeof(T);
+      const rsrc_t os = buf((T *)P.o + ((int64_t)t0 * Hv + h) * kD, nvalid * rowb);
+      const uint32_t oo = (uint32_t)(etok * rowb + e8 * (int)sizeof(T));
+      OutRow<T>::store(os, oo, val);
+      OutRow<T>::store(os, oo + 64 * (int)sizeof(T), val + 8);
     }
   }
 
