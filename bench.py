@@ -177,7 +177,7 @@ def cpu_baseline_prefill(res, S, oracle):
     """fp64 oracle on the first `n` tokens of the same workload, all heads."""
     import numpy as np
     d = res["d"]
-    n = int(os.environ.get("GDN_BENCH_ORACLE_TOKENS", "8192"))
+    n = int(os.environ.get("GDN_BENCH_ORACLE_TOKENS", "65536"))
     f = lambda t: S.to_f64(t[:n]) if t is not None else None
     threads = min(oracle.default_threads(), d["v"].shape[1])
     t0 = time.perf_counter()
@@ -188,13 +188,13 @@ def cpu_baseline_prefill(res, S, oracle):
     dt = time.perf_counter() - t0
     err = rel_l2(S.to_f64(res["out"][:n]), o_ref)
     return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"first {n} tokens of the T=65536 workload, all 32 v heads, fp64, "
+                sample=f"first {n} of the 65536 tokens of the workload, all 32 v heads, fp64, "
                        f"{dt:.1f} s"), err
 
 
 def cpu_baseline_decode(dec, S, oracle):
     import numpy as np
-    n = int(os.environ.get("GDN_BENCH_ORACLE_DECODE_STEPS", "4"))
+    n = int(os.environ.get("GDN_BENCH_ORACLE_DECODE_STEPS", "32"))
     w, setup, toks = dec["w"], dec["setup"], dec["toks"]
     f = S.to_f64
     # fresh copies of the decode start state (the GPU run advanced its own)
