@@ -527,40 +527,38 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // B map starts at the last such chunk, and the A map is zero if S_0 is.
   int c_begin = 0;
   if (MODE == kMap) {
+    // Chunk sums of g from the segment end, eight chunks (one per wave) at a time,
+    // until the suffix sum S reaches the threshold.  g <= 0, so the first chunk
+    // where it does is the truncation point of the B map, and then the whole
+    // segment's sum is below the threshold too: the A map is zero.  Only if no
+    // suffix reaches it does the scan cover every chunk (A and B need them all).
     float *sChG = reinterpret_cast<float *>(smem + OFF_CHG);
-    // chunk sums, fixed order; segments hold at most 8192 tokens = 128 chunks,
-    // i.e. 16 per wave, whose gate loads are all issued before the first use
-    constexpr int kMaxChunksPerWave = 16;
-    float av[kMaxChunksPerWave];
-#pragma unroll
-    for (int j = 0; j < kMaxChunksPerWave; ++j) {
-      const int tau = min(seg.begin + (wave + kWaves * j) * kChunk + lane, seg_end - 1);
-      av[j] = P.a[(int64_t)tau * Hv + h];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxChunksPerWave; ++j) {
-      const int cc = wave + kWaves * j;
-      const int tau = seg.begin + cc * kChunk + lane;
-      float g = (cc < nchunks && tau < seg_end) ? log_decay(av[j], A_log_h, dt_bias_h) : 0.f;
-      g = wave_sum(g);
-      if (lane == 0 && cc < nchunks) sChG[cc] = g;
-    }
-    __syncthreads();
-    float S = 0.f;
     const float thr = -69.31471805599453f;  // ln 2^-100
-    for (int cc = nchunks - 1; cc >= 0; --cc) {  // every thread, same order
-      S += sChG[cc];
-      if (S <= thr) {
-        c_begin = cc;
-        break;
+    float S = 0.f;
+    bool reached = false;
+    for (int top = nchunks - 1; top >= 0 && !reached; top -= kWaves) {
+      const int cc = top - wave;
+      if (cc >= 0) {  // chunk sum, fixed order
+        const int tau = seg.begin + cc * kChunk + lane;
+        float g = tau < seg_end ? log_decay(P.a[(int64_t)tau * Hv + h], A_log_h, dt_bias_h) : 0.f;
+        g = wave_sum(g);
+        if (lane == 0) sChG[cc] = g;
       }
+      __syncthreads();
+      for (int k = 0; k < kWaves && top - k >= 0; ++k) {  // every thread, same order
+        S += sChG[top - k];
+        if (S <= thr) {
+          c_begin = top - k;
+          reached = true;
+          break;
+        }
+      }
+      __syncthreads();  // sChG reuse by the next batch
     }
     if (half == 0) {
-      float tot = 0.f;
-      for (int cc = nchunks - 1; cc >= 0; --cc) tot += sChG[cc];
       // A map zero to fp32 resolution: flag it instead of storing it
-      if (tid == 0) P.map_zero[(int64_t)unit * Hv + h] = tot <= thr ? 1 : 0;
-      if (tot <= thr) return;
+      if (tid == 0) P.map_zero[(int64_t)unit * Hv + h] = reached ? 1 : 0;
+      if (reached) return;
       c_begin = 0;  // otherwise the A map needs every chunk
     }
   }
