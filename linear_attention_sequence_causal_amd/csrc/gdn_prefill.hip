@@ -22,7 +22,7 @@
 //   lo*hi) over the last two chunks of a sequence and one pass before them;
 //   the identity part of T V (beta V, beta gamma K) and the diagonal of M U
 //   are applied in fp32.  The triangular inverse is formed per 16x16 diagonal
-//   block from split-precision products and merged with bf16 products.
+//   block from fp16 products and merged with bf16 products.
 //
 // Work decomposition: one workgroup = 8 waves = one (segment, v head); wave w
 // owns value columns 16w..16w+15 of the state in MFMA accumulators.  Long
@@ -293,46 +293,40 @@ __device__ __forceinline__ void gram_tile(int wave, int s, int &ti, int &tj) {
   }
 }
 
-// 16x16 operands with K = 16 in split precision, packed from a C-layout tile X:
-// as a B operand this is X, as an A operand it is the transpose of X.
-struct Split {
-  u16x8 h, l;
-};
-__device__ __forceinline__ Split split_half(const f32x4 &x) {
-  uint32_t h0, l0, h1, l1;
-  split_pk(x[0], x[1], h0, l0);
-  split_pk(x[2], x[3], h1, l1);
-  return {__builtin_bit_cast(u16x8, make_uint4(h0, h1, 0u, 0u)),
-          __builtin_bit_cast(u16x8, make_uint4(l0, l1, 0u, 0u))};
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+// 16x16 operand with K = 16 in fp16, packed from a C-layout tile X (lane ln, lg
+// holds rows 4lg..4lg+3 of column ln, which is the k order of the 16x16x16
+// product): as a B operand this is X, as an A operand it is the transpose of X.
+__device__ __forceinline__ f16x4_t h4(const f32x4 &x) {
+  return __builtin_bit_cast(f16x4_t, make_uint2(pk_f16(x[0], x[1]), pk_f16(x[2], x[3])));
 }
 // c + A B with A = transpose of the tile packed in a, B = the tile packed in b
-__device__ __forceinline__ f32x4 mm_split(const Split &a, const Split &b, f32x4 c) {
-  c = mfma16(a.h, b.h, c);
-  c = mfma16(a.h, b.l, c);
-  return mfma16(a.l, b.h, c);
+__device__ __forceinline__ f32x4 mm16(f16x4_t a, f16x4_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 // Transpose of (I + L)^-1 for a strictly lower 16x16 block L, given the C-layout
 // tiles of M = -L^T (mc) and of M^T = -L (mt).  L is nilpotent (L^16 = 0), so
 // (I + L)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) with N = -L; the transpose is
-// the same product in M, and all factors commute.  Each product is formed from
-// split operands (about 16 bits), well below the bf16 rounding applied to T - I.
+// the same product in M, and all factors commute.  |L_ij| <= 1 (beta <= 1, decay
+// <= 1, unit-norm keys), so every power and partial product has entries below
+// 2^15 and fits fp16; fp16 operands (11-bit significands) keep the products well
+// below the bf16 rounding applied to T - I.
 __device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4 &mc, const f32x4 &mt, int ln,
                                                       int lg) {
   const f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-  const Split sm = split_half(mc), smt = split_half(mt);
-  const f32x4 m2 = mm_split(smt, sm, Z), m2t = mm_split(sm, smt, Z);   // M^2, (M^2)^T
-  const Split sm2 = split_half(m2), sm2t = split_half(m2t);
-  const f32x4 m4 = mm_split(sm2t, sm2, Z), m4t = mm_split(sm2, sm2t, Z);  // M^4, (M^4)^T
-  const Split sm4 = split_half(m4), sm4t = split_half(m4t);
-  const f32x4 m8t = mm_split(sm4, sm4t, Z);                             // (M^8)^T
+  const f16x4_t sm = h4(mc), smt = h4(mt);
+  const f32x4 m2 = mm16(smt, sm, Z), m2t = mm16(sm, smt, Z);        // M^2, (M^2)^T
+  const f16x4_t sm2 = h4(m2), sm2t = h4(m2t);
+  const f32x4 m4 = mm16(sm2t, sm2, Z), m4t = mm16(sm2, sm2t, Z);    // M^4, (M^4)^T
+  const f32x4 m8t = mm16(h4(m4), h4(m4t), Z);                       // (M^8)^T
   f32x4 t = mc;  // I + M
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (4 * lg + i == ln) t[i] += 1.0f;
-  t = mm_split(sm2t, split_half(t), t);            // (I + M)(I + M^2)
-  t = mm_split(sm4t, split_half(t), t);            // ... (I + M^4)
-  return mm_split(split_half(m8t), split_half(t), t);  // ... (I + M^8)
+  t = mm16(sm2t, h4(t), t);        // (I + M)(I + M^2)
+  t = mm16(h4(m4t), h4(t), t);     // ... (I + M^4)
+  return mm16(h4(m8t), h4(t), t);  // ... (I + M^8)
 }
 
 // ------------------------------------------------------------ chunk kernel
@@ -980,11 +974,17 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       ss += dpp_f<0xB1>(ss);  // quad_perm 1,0,3,2
       ss += dpp_f<0x4E>(ss);  // quad_perm 2,3,0,1
       ss += dpp_f<0x141>(ss);  // row_half_mirror
-      const float inv = rsqrtf(ss * (1.0f / kD) + P.rms_eps);
+      // o * rsqrt(ms) * w * z * sigmoid(z) with the RMS folded into the sigmoid's
+      // denominator: 1 / (sd (1 + e^-z)), sd = sqrt(ms + eps)
+      const float ms = ss * (1.0f / kD) + P.rms_eps;
+      const float sd = ms * rsqrtf(ms);
       float val[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        val[j] = ov[j] * inv * nw[j] * silu_fast(RZ::get(zw[j >> 3], j & 7));
+      for (int j = 0; j < 16; ++j) {
+        const float zj = RZ::get(zw[j >> 3], j & 7);
+        const float e = __expf(-zj);
+        val[j] = ov[j] * zj * nw[j] * __builtin_amdgcn_rcpf(fmaf(e, sd, sd));
+      }
       // one buffer over this chunk's o rows: stores of tokens at or past nvalid are dropped
       const int rowb = Hv * kD * (int)sizeof(T);
       const rsrc_t os = buf((T *)P.o + ((int64_t)t0 * Hv + h) * kD, nvalid * rowb);
