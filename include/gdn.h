@@ -124,6 +124,30 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            const gdn_params *p, float *state, void *conv_state,
                            void *o, int32_t batch, void *stream);
 
+/* n_tokens new tokens per sequence on a cached state (multi-token decode; the
+ * verify and commit passes of speculative decoding).  The result is that of
+ * n_tokens gdn_decode_step calls in order (the field guide's six update
+ * operations per token, cutaway 02), but each fp32 state is read once and
+ * written at most once for all n_tokens.
+ *
+ *   q, k        [B, n, Hk, D] act dtype;  v, z [B, n, Hv, D] act dtype
+ *   a, b        [B, n, Hv] fp32
+ *   state       [B, Hv, D, D] fp32, in/out
+ *   conv_state  [B, 3, Cc] act dtype, in/out (oldest row first)
+ *   num_commit  [B] int32 device, or NULL: the state and the conv cache of
+ *               sequence b advance by num_commit[b] tokens (values are clamped
+ *               to 0..n; NULL means n for every sequence).  With 0 neither is
+ *               written (a verify pass); a later call with the accepted count
+ *               advances them.
+ *   o           [B, n, Hv, D] act dtype (out): outputs of all n tokens, token t
+ *               seeing tokens 0..t of this call whatever num_commit says
+ *   1 <= n_tokens <= 8.  Not transactional (as gdn_decode_step). */
+gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v,
+                             const float *a, const float *b, const void *z,
+                             const gdn_params *p, float *state, void *conv_state,
+                             const int32_t *num_commit, void *o, int32_t batch,
+                             int32_t n_tokens, void *stream);
+
 /* Diagnostics: per-kernel device time of the last gdn_prefill call made on
  * this thread while the environment had GDN_KERNEL_TIMING=1.  The library then
  * records HIP events on the caller's stream between its kernels (segment table,

@@ -25,7 +25,7 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
-            "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
+            "gdn_decode_tokens", "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
             "gdn_version")
 PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
 
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, sz, vp]
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32, vp]
+            L.gdn_decode_tokens.restype = ctypes.c_int
+            L.gdn_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, i32, i32,
+                                            vp]
             L.gdn_status_string.restype = ctypes.c_char_p
             L.gdn_status_string.argtypes = [ctypes.c_int]
             L.gdn_last_error.restype = ctypes.c_char_p
@@ -175,6 +178,27 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
     _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
                                  ctypes.byref(p), _ptr(state), _ptr(conv_state), _ptr(o), B,
                                  _stream()))
+    return o
+
+
+def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, *,
+                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None):
+    """n new tokens per sequence on a cached state; returns o [B, n, Hv, D].
+
+    q, k [B, n, Hk, D]; v, z [B, n, Hv, D]; a, b [B, n, Hv]; state [B, Hv, D, D] fp32 and
+    conv_state [B, 3, Cc] advance in place by num_commit[b] tokens (int32 [B] on the
+    device, clamped to 0..n; None = n).
+    """
+    B, n, Hk, D = q.shape
+    Hv = v.shape[2]
+    _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, num_commit)
+    if num_commit is not None and (num_commit.dtype != torch.int32 or num_commit.numel() != B):
+        raise ValueError("num_commit must be an int32 tensor of B elements")
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    o = torch.empty_like(v) if out is None else out
+    _check(lib().gdn_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
+                                   ctypes.byref(p), _ptr(state), _ptr(conv_state),
+                                   _ptr(num_commit), _ptr(o), B, n, _stream()))
     return o
 
 

@@ -23,6 +23,14 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          float rms_eps, float *state, void *conv_state, void *o, int batch,
                          int Hk, int Hv, hipStream_t stream);
 int decode_max_ratio();
+template <typename T>
+hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, const float *a,
+                                const float *b, const void *z, const float *conv_w,
+                                const float *A_log, const float *dt_bias, const float *norm_w,
+                                float q_scale, float l2_eps, float rms_eps, float *state,
+                                void *conv_state, const int32_t *num_commit, void *o, int batch,
+                                int n, int Hk, int Hv, hipStream_t stream);
+int decode_max_tokens();
 }  // namespace gdn
 
 namespace {
@@ -225,6 +233,43 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                                   conv_state, o, batch, p->num_qk_heads, p->num_v_heads,
                                   (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v, const float *a,
+                             const float *b, const void *z, const gdn_params *p, float *state,
+                             void *conv_state, const int32_t *num_commit, void *o, int32_t batch,
+                             int32_t n_tokens, void *stream) {
+  g_err[0] = 0;
+  gdn_status st = check_params(p);
+  if (st != GDN_OK) return st;
+  if (batch < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "batch (%d) must be >= 0", batch);
+  if (n_tokens < 1 || n_tokens > gdn::decode_max_tokens())
+    return fail(GDN_ERR_INVALID_ARGUMENT, "n_tokens (%d) must be in 1..%d", n_tokens,
+                gdn::decode_max_tokens());
+  if (p->num_v_heads / p->num_qk_heads > gdn::decode_max_ratio())
+    return fail(GDN_ERR_UNSUPPORTED, "num_v_heads / num_qk_heads above %d",
+                gdn::decode_max_ratio());
+  if (batch > 0 && (!q || !k || !v || !a || !b || !z || !state || !conv_state || !o))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "all tensor pointers except num_commit are required");
+  if ((int64_t)batch * p->num_qk_heads > (int64_t)INT32_MAX)
+    return fail(GDN_ERR_UNSUPPORTED, "batch * num_qk_heads too large");
+  if (o && (o == q || o == k || o == v || o == z))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "o must not alias an input");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e;
+  if (p->act_dtype == GDN_BF16)
+    e = gdn::launch_decode_tokens<gdn::bf16_t>(
+        q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias, p->norm_weight, p->q_scale,
+        p->l2_eps, p->rms_eps, state, conv_state, num_commit, o, batch, n_tokens,
+        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
+  else
+    e = gdn::launch_decode_tokens<float>(
+        q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias, p->norm_weight, p->q_scale,
+        p->l2_eps, p->rms_eps, state, conv_state, num_commit, o, batch, n_tokens,
+        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_tokens launch");
   return GDN_OK;
 }
 

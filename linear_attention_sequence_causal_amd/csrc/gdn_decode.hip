@@ -228,4 +228,248 @@ template hipError_t launch_decode<bf16_t>(const void *, const void *, const void
                                           const float *, float, float, float, float *, void *,
                                           void *, int, int, int, hipStream_t);
 
+// ---------------------------------------------------------------------------------
+// Multi-token step: n (1..8) new tokens per sequence on a cached state.  It is the
+// single step above applied to the tokens in order (per token the field guide's
+// six update operations, cutaway 02, and the same gates and epilogue), but each
+// fp32 state is read once and written at most once for all n tokens, so the bytes
+// per token drop n-fold.  Token t's output sees tokens 0..t.  The state and the
+// conv cache advance by commit = num_commit[b] tokens (clamped to 0..n; n when
+// num_commit is NULL): the state is written right after token commit - 1 and not
+// at all when commit = 0.  A speculative verify pass (commit 0) thus leaves both
+// untouched, and a second pass with the accepted count advances them.
+constexpr int kMaxStepTokens = 8;
+
+template <typename T>
+__global__ void __launch_bounds__(kDecThreads)
+decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+                     const float *__restrict__ a, const float *__restrict__ b,
+                     const T *__restrict__ z, const float *__restrict__ conv_w,
+                     const float *__restrict__ A_log, const float *__restrict__ dt_bias,
+                     const float *__restrict__ norm_w, float q_scale, float l2_eps,
+                     float rms_eps, float *__restrict__ state, T *__restrict__ conv_state,
+                     const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
+                     int n) {
+  const int g = blockIdx.x % Hk;
+  const int bseq = blockIdx.x / Hk;
+  const int r = Hv / Hk;
+  const int tid = threadIdx.x;
+  const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
+  const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
+
+  __shared__ float s_x[kMaxStepTokens][2 + kDecMaxRatio][kD];  // post-prologue q, k, v rows
+  __shared__ float s_red[8][2][kD];
+  __shared__ float s_e[kD];
+  __shared__ float s_y[kD];
+  __shared__ float s_kq[kMaxStepTokens];
+  __shared__ float s_ss[2];
+
+  const int col = (tid & 31) * 4;
+  const int rg = tid >> 5;
+  const int row0 = rg * 16;
+  auto head_ptr = [&](int j) {
+    return state + (((int64_t)bseq * Hv + r * g + j) * kD + row0) * kD + col;
+  };
+  f32x4 Hcur[16];
+  {
+    const float *Hp = head_ptr(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Hcur[i] = ld_nt4(Hp + i * kD);
+  }
+
+  // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
+  // raw[0..2] = cached rows (oldest first), raw[3 + t] = new token t
+  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+  const int c0 = (tid & 63) * 2;
+  const int sec = tid >> 6;
+  for (int pass = 0; pass == 0 || 2 + 4 * (pass - 1) < r; ++pass) {
+    int slot, jv = -1;
+    if (pass == 0) {
+      slot = sec;
+      if (sec >= 2) jv = sec - 2;
+    } else {
+      jv = 2 + 4 * (pass - 1) + sec;
+      slot = 2 + jv;
+    }
+    const bool active = jv < r;
+    int64_t cbase, hstride, sidx;
+    const T *src;
+    if (slot == 0) {
+      cbase = (int64_t)g * kD; src = q; hstride = (int64_t)Hk * kD;
+      sidx = ((int64_t)bseq * n * Hk + g) * kD;
+    } else if (slot == 1) {
+      cbase = (int64_t)Hk * kD + (int64_t)g * kD; src = k; hstride = (int64_t)Hk * kD;
+      sidx = ((int64_t)bseq * n * Hk + g) * kD;
+    } else {
+      cbase = 2LL * Hk * kD + (int64_t)(r * g + jv) * kD; src = v; hstride = (int64_t)Hv * kD;
+      sidx = ((int64_t)bseq * n * Hv + r * g + jv) * kD;
+    }
+    float xv[kMaxStepTokens][2];
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) xv[t][0] = xv[t][1] = 0.f;
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t ch = cbase + c0 + u;
+        float raw[3 + kMaxStepTokens];
+        raw[0] = Act<T>::load(cs, ch);
+        raw[1] = Act<T>::load(cs, Cc + ch);
+        raw[2] = Act<T>::load(cs, 2 * Cc + ch);
+#pragma unroll
+        for (int t = 0; t < kMaxStepTokens; ++t)
+          raw[3 + t] = t < n ? Act<T>::load(src, sidx + t * hstride + c0 + u) : 0.f;
+        const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
+#pragma unroll
+        for (int t = 0; t < kMaxStepTokens; ++t)
+          xv[t][u] = siluf_(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
+        // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
+        // (reads above precede these writes; this thread owns the channel)
+        if (commit > 0) {
+#pragma unroll
+          for (int s2 = 0; s2 < 3; ++s2) {
+            float x = raw[0];
+#pragma unroll
+            for (int i = 1; i < 3 + kMaxStepTokens; ++i)
+              if (i == commit + s2) x = raw[i];
+            Act<T>::store(cs, s2 * Cc + ch, x);
+          }
+        }
+      }
+    }
+    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token over 128 channels
+#pragma unroll
+      for (int t = 0; t < kMaxStepTokens; ++t) {
+        if (t < n) {
+          const float ss = wave_sum(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
+          const float f = (slot == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
+          xv[t][0] *= f;
+          xv[t][1] *= f;
+        }
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < kMaxStepTokens; ++t)
+        if (t < n) {
+          s_x[t][slot][c0] = xv[t][0];
+          s_x[t][slot][c0 + 1] = xv[t][1];
+        }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {  // k_t . q_t of each token
+    for (int t = 0; t < n; ++t) {
+      const float kq = wave_sum(s_x[t][0][2 * tid] * s_x[t][1][2 * tid] +
+                                s_x[t][0][2 * tid + 1] * s_x[t][1][2 * tid + 1]);
+      if (tid == 0) s_kq[t] = kq;
+    }
+  }
+  __syncthreads();
+
+  // ---- per v head: the state stays in registers across the n tokens ------------------
+  for (int j = 0; j < r; ++j) {
+    const int h = r * g + j;
+    f32x4 Hnext[16];
+    if (j + 1 < r) {
+      const float *Hn = head_ptr(j + 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Hnext[i] = ld_nt4(Hn + i * kD);
+    }
+    for (int t = 0; t < n; ++t) {
+      const int64_t gi = ((int64_t)bseq * n + t) * Hv + h;
+      const float alpha = __expf(log_decay(a[gi], A_log[h], dt_bias[h]));
+      const float beta = sigmoidf_(b[gi]);
+      float kr[16], qr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        kr[i] = s_x[t][1][row0 + i];
+        qr[i] = s_x[t][0][row0 + i];
+      }
+      float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sk[0] += Hcur[i].x * kr[i]; sk[1] += Hcur[i].y * kr[i];
+        sk[2] += Hcur[i].z * kr[i]; sk[3] += Hcur[i].w * kr[i];
+        sq[0] += Hcur[i].x * qr[i]; sq[1] += Hcur[i].y * qr[i];
+        sq[2] += Hcur[i].z * qr[i]; sq[3] += Hcur[i].w * qr[i];
+      }
+      *reinterpret_cast<f32x4 *>(&s_red[rg][0][col]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
+      *reinterpret_cast<f32x4 *>(&s_red[rg][1][col]) = f32x4{sq[0], sq[1], sq[2], sq[3]};
+      __syncthreads();
+      if (tid < kD) {
+        float vk = 0.f, vq = 0.f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          vk += s_red[p][0][tid];
+          vq += s_red[p][1][tid];
+        }
+        const float e = s_x[t][2 + j][tid] - alpha * vk;  // e = v - S'k
+        const float y = alpha * vq + beta * s_kq[t] * e;  // S'' q
+        s_e[tid] = e;
+        s_y[tid] = y;
+        const float ssum = wave_sum(y * y);
+        if ((tid & 63) == 0) s_ss[tid >> 6] = ssum;
+      }
+      __syncthreads();
+      float ec[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ec[c] = beta * s_e[col + c];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        Hcur[i].x = alpha * Hcur[i].x + kr[i] * ec[0];
+        Hcur[i].y = alpha * Hcur[i].y + kr[i] * ec[1];
+        Hcur[i].z = alpha * Hcur[i].z + kr[i] * ec[2];
+        Hcur[i].w = alpha * Hcur[i].w + kr[i] * ec[3];
+      }
+      if (t + 1 == commit) {
+        float *Hp = head_ptr(j);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st_nt4(Hp + i * kD, Hcur[i]);
+      }
+      if (tid < kD) {
+        const float inv = rsqrtf((s_ss[0] + s_ss[1]) * (1.0f / kD) + rms_eps);
+        const float w = norm_w ? norm_w[tid] : 1.0f;
+        const int64_t oi = gi * kD + tid;
+        Act<T>::store(o, oi, s_y[tid] * inv * w * siluf_(Act<T>::load(z, oi)));
+      }
+    }
+    __syncthreads();  // s_red, s_e, s_y, s_ss are reused by the next head
+    if (j + 1 < r) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Hcur[i] = Hnext[i];
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, const float *a,
+                                const float *b, const void *z, const float *conv_w,
+                                const float *A_log, const float *dt_bias, const float *norm_w,
+                                float q_scale, float l2_eps, float rms_eps, float *state,
+                                void *conv_state, const int32_t *num_commit, void *o, int batch,
+                                int n, int Hk, int Hv, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  dim3 grid((unsigned)batch * (unsigned)Hk);
+  hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kDecThreads), 0, stream,
+                     (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
+                     dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
+                     num_commit, (T *)o, Hk, Hv, n);
+  return hipGetLastError();
+}
+
+int decode_max_tokens() { return kMaxStepTokens; }
+
+template hipError_t launch_decode_tokens<float>(const void *, const void *, const void *,
+                                                const float *, const float *, const void *,
+                                                const float *, const float *, const float *,
+                                                const float *, float, float, float, float *,
+                                                void *, const int32_t *, void *, int, int, int,
+                                                int, hipStream_t);
+template hipError_t launch_decode_tokens<bf16_t>(const void *, const void *, const void *,
+                                                 const float *, const float *, const void *,
+                                                 const float *, const float *, const float *,
+                                                 const float *, float, float, float, float *,
+                                                 void *, const int32_t *, void *, int, int, int,
+                                                 int, hipStream_t);
+
 }  // namespace gdn

@@ -212,6 +212,39 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_ca
     return o, state, cache
 
 
+def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
+                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+    """n new tokens per sequence on a cached state (multi-token decode / verify / commit).
+
+    q, k [B, n, Hk, D]; v, z [B, n, Hv, D]; a, b [B, n, Hv].  Returns
+    (o [B, n, Hv, D], new_state, new_conv_cache): o holds the outputs of all n tokens
+    (token t after tokens 0..t, as n decode steps give them); the state and the cache
+    are those after the first num_commit[b] tokens (clamped to 0..n; None = n).
+
+    The token-by-token recurrence of the prefill oracle does both: the outputs are
+    one prefill of the n tokens of every sequence (packed, history = the cache,
+    initial state = the cached state), the committed state and cache one prefill of
+    each sequence's first num_commit[b] tokens.
+    """
+    q, k, v, a, b, z = map(_f64, (q, k, v, a, b, z))
+    B, n, Hk, D = q.shape
+    Hv = v.shape[2]
+    state, cache = _f64(state), _f64(conv_cache)
+    flat = lambda x: x.reshape((B * n,) + x.shape[2:])
+    kw = dict(q_scale=q_scale, l2_eps=l2_eps, rms_eps=rms_eps, nthreads=nthreads)
+    cu = np.arange(B + 1, dtype=np.int64) * n
+    o, _, _ = prefill(flat(q), flat(k), flat(v), flat(a), flat(b), flat(z), conv_w, A_log,
+                      dt_bias, norm_w, cu_seqlens=cu, init_state=state, conv_in=cache, **kw)
+    commit = np.full(B, n, dtype=np.int64) if num_commit is None else \
+        np.clip(np.asarray(num_commit, dtype=np.int64).reshape(B), 0, n)
+    sel = np.concatenate([np.arange(bb * n, bb * n + commit[bb]) for bb in range(B)]).astype(np.int64)
+    cuc = np.concatenate([[0], np.cumsum(commit)]).astype(np.int64)
+    _, fs, co = prefill(flat(q)[sel], flat(k)[sel], flat(v)[sel], flat(a)[sel], flat(b)[sel],
+                        flat(z)[sel], conv_w, A_log, dt_bias, norm_w, cu_seqlens=cuc,
+                        init_state=state, conv_in=cache, **kw)
+    return o.reshape(B, n, Hv, D), fs, co
+
+
 def select_heads(qk_heads, Hk: int, Hv: int, D: int):
     """Index helpers to run the oracle on a subset of q/k heads (and their v heads).
 

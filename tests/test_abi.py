@@ -65,6 +65,17 @@ def _decode(p, B=2, out=None, **over):
                                      ptr["cache"], ctypes.c_void_p(o.ctypes.data), B, None)
 
 
+def _tokens(p, B=2, n=4, out=None, **over):
+    bufs = {n_: _host(1 << 16) for n_ in ("q", "k", "v", "a", "b", "z", "state", "cache")}
+    o = out if out is not None else _host(1 << 16)
+    ptr = {n_: ctypes.c_void_p(x.ctypes.data) for n_, x in bufs.items()}
+    ptr.update(over)
+    return gdn.lib().gdn_decode_tokens(ptr["q"], ptr["k"], ptr["v"], ptr["a"], ptr["b"],
+                                       ptr["z"], ctypes.byref(p) if p is not None else None,
+                                       ptr["state"], ptr["cache"], None,
+                                       ctypes.c_void_p(o.ctypes.data), B, n, None)
+
+
 def _prefill(p, N=1, T=64, out=None, ws=None, ws_bytes=0, cu=True, **over):
     bufs = {n: _host(1 << 16) for n in ("q", "k", "v", "a", "b", "z", "fs")}
     o = out if out is not None else _host(1 << 16)
@@ -101,6 +112,22 @@ def test_decode_argument_errors_leave_outputs_untouched():
     p.conv_weight = None
     assert _decode(p, out=o) == INVALID
     assert np.all(o == 3.0)
+
+
+def test_decode_tokens_argument_errors_leave_outputs_untouched():
+    o = _host(1 << 16, fill=4.0)
+    p, h = _params()
+    assert _tokens(None, out=o) == INVALID
+    assert _tokens(p, n=0, out=o) == INVALID
+    assert _tokens(p, n=9, out=o) == INVALID
+    assert "n_tokens" in gdn.lib().gdn_last_error().decode()
+    assert _tokens(p, B=-1, out=o) == INVALID
+    assert _tokens(p, out=o, state=None) == INVALID
+    p, h = _params(Hk=1, Hv=16)
+    assert _tokens(p, out=o) == UNSUPPORTED
+    p, h = _params(D=64)
+    assert _tokens(p, out=o) == UNSUPPORTED
+    assert np.all(o == 4.0)
 
 
 def test_prefill_argument_errors():
@@ -140,6 +167,7 @@ def test_valid_calls_report_missing_device(monkeypatch):
         pytest.skip("a GPU is present")
     p, h = _params()
     assert _decode(p) == NO_DEVICE
+    assert _tokens(p) == NO_DEVICE
     n = gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 64)
     raw = np.zeros(n + 512, dtype=np.uint8)
     addr = (raw.ctypes.data + 255) // 256 * 256

@@ -1,0 +1,170 @@
+"""GPU parity of the multi-token step (n new tokens per sequence on a cached state)
+against the fp64 oracle.
+
+Bars as for decode: relative L2 <= 3e-3 on o (dominated by its bf16 rounding) and
+<= 1e-3 on the state; the arithmetic is fp32, so the state lands far below.  The
+conv cache holds raw inputs and must match bit for bit, and a verify pass
+(num_commit = 0) must leave state and cache bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as S
+import oracle
+
+gpu = pytest.mark.gpu
+
+O_TOL, STATE_TOL = 3e-3, 1e-3
+
+
+def rel_l2(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+
+
+def _case(w, n, dev="cuda"):
+    """Setup and n tokens per sequence in the [B, n, ...] layout."""
+    setup = S.decode_setup(w, dev)
+    toks = S.decode_tokens(w, setup, n, dev)
+    bn = {key: val.transpose(0, 1).contiguous() for key, val in toks.items()}
+    return setup, bn
+
+
+def _gpu(setup, t, state, cache, num_commit=None):
+    import linear_attention_sequence_causal_amd as gdn
+    o = gdn.decode_tokens(t["q"], t["k"], t["v"], t["a"], t["b"], t["z"], setup["conv_w"],
+                          setup["A_log"], setup["dt_bias"], setup["norm_w"], state, cache,
+                          num_commit=num_commit)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(setup, t, state, cache, sel=slice(None), num_commit=None):
+    f = S.to_f64
+    return oracle.decode_tokens(f(t["q"][sel]), f(t["k"][sel]), f(t["v"][sel]), f(t["a"][sel]),
+                                f(t["b"][sel]), f(t["z"][sel]), f(setup["conv_w"]),
+                                f(setup["A_log"]), f(setup["dt_bias"]), f(setup["norm_w"]),
+                                f(state[sel]), f(cache[sel]), num_commit=num_commit)
+
+
+def _check(setup, t, n, sel=slice(None), num_commit=None, label=""):
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    commit_dev = None
+    if num_commit is not None:
+        commit_dev = torch.tensor(num_commit, dtype=torch.int32, device="cuda")
+    o = _gpu(setup, t, setup["state"], setup["conv_cache"], commit_dev)
+    o_ref, st_ref, cc_ref = _oracle(setup, t, st0, cc0, sel, num_commit)
+    f = S.to_f64
+    eo, es = rel_l2(f(o[sel]), o_ref), rel_l2(f(setup["state"][sel]), st_ref)
+    print(f"{label}: o rel-L2 {eo:.3e} state rel-L2 {es:.3e}")
+    assert eo < O_TOL
+    assert es < 1e-5
+    assert np.array_equal(f(setup["conv_cache"][sel]), cc_ref)
+    return o, st0, cc0
+
+
+@gpu
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_tokens_match_oracle_bf16(n):
+    w = S.scaled(S.DECODE_B256, decode_batch=4, seed=60 + n)
+    setup, t = _case(w, n)
+    _check(setup, t, n, label=f"decode_tokens n={n} Hk=16 Hv=32")
+
+
+@gpu
+def test_tokens_fp32_small_heads():
+    w = S.scaled(S.DECODE_B256, decode_batch=3, num_qk_heads=1, num_v_heads=2,
+                 act_dtype=torch.float32, seed=70)
+    setup, t = _case(w, 4)
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    o = _gpu(setup, t, setup["state"], setup["conv_cache"])
+    o_ref, st_ref, cc_ref = _oracle(setup, t, st0, cc0)
+    assert rel_l2(S.to_f64(o), o_ref) < 1e-5
+    assert rel_l2(S.to_f64(setup["state"]), st_ref) < 1e-5
+    assert np.array_equal(S.to_f64(setup["conv_cache"]), cc_ref)
+
+
+@gpu
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8)])
+def test_tokens_head_layouts(hk, hv):
+    w = S.scaled(S.DECODE_B256, decode_batch=5, num_qk_heads=hk, num_v_heads=hv, seed=71 + hv)
+    setup, t = _case(w, 3)
+    _check(setup, t, 3, label=f"decode_tokens n=3 Hk={hk} Hv={hv}")
+
+
+@gpu
+def test_tokens_commit_counts():
+    """Per-sequence commit counts (0, partial, all, clamped): o of all n tokens; state
+    and cache advanced by the count; count 0 leaves both bit for bit."""
+    n = 5
+    w = S.scaled(S.DECODE_B256, decode_batch=6, seed=80)
+    setup, t = _case(w, n)
+    commit = [0, 1, 5, 3, 2, 7]
+    o, st0, cc0 = _check(setup, t, n, num_commit=commit, label="decode_tokens commit")
+    assert torch.equal(setup["state"][0], st0[0])
+    assert torch.equal(setup["conv_cache"][0], cc0[0])
+
+
+@gpu
+def test_verify_then_commit():
+    """Speculative flow: a verify pass (commit 0) changes nothing; the commit pass with
+    the accepted counts gives the same outputs bit for bit and the oracle's state."""
+    n = 4
+    w = S.scaled(S.DECODE_B256, decode_batch=4, seed=81)
+    setup, t = _case(w, n)
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    zeros = torch.zeros(4, dtype=torch.int32, device="cuda")
+    o1 = _gpu(setup, t, setup["state"], setup["conv_cache"], zeros)
+    assert torch.equal(setup["state"], st0) and torch.equal(setup["conv_cache"], cc0)
+    accepted = [4, 0, 2, 1]
+    o2 = _gpu(setup, t, setup["state"], setup["conv_cache"],
+              torch.tensor(accepted, dtype=torch.int32, device="cuda"))
+    assert torch.equal(o1, o2)
+    _, st_ref, cc_ref = _oracle(setup, t, st0, cc0, num_commit=accepted)
+    assert rel_l2(S.to_f64(setup["state"]), st_ref) < 1e-5
+    assert np.array_equal(S.to_f64(setup["conv_cache"]), cc_ref)
+
+
+@gpu
+def test_tokens_equal_successive_single_steps():
+    """n tokens at once against n single decode steps on the GPU."""
+    import linear_attention_sequence_causal_amd as gdn
+    n = 6
+    w = S.scaled(S.DECODE_B256, decode_batch=3, seed=82)
+    setup, t = _case(w, n)
+    st1, cc1 = setup["state"].clone(), setup["conv_cache"].clone()
+    o = _gpu(setup, t, setup["state"], setup["conv_cache"])
+    outs = []
+    for i in range(n):
+        outs.append(gdn.decode_step(t["q"][:, i].contiguous(), t["k"][:, i].contiguous(),
+                                    t["v"][:, i].contiguous(), t["a"][:, i].contiguous(),
+                                    t["b"][:, i].contiguous(), t["z"][:, i].contiguous(),
+                                    setup["conv_w"], setup["A_log"], setup["dt_bias"],
+                                    setup["norm_w"], st1, cc1))
+    torch.cuda.synchronize()
+    f = S.to_f64
+    assert rel_l2(f(o), np.stack([f(x) for x in outs], 1)) < 1e-4
+    assert rel_l2(f(setup["state"]), f(st1)) < 1e-6
+    assert torch.equal(setup["conv_cache"], cc1)
+
+
+@gpu
+def test_tokens_full_batch_sampled_sequences():
+    """B=256, 16/32 heads, n=4 in the launch configuration the benchmark times; the
+    oracle recomputes 6 sampled sequences (all heads and tokens)."""
+    n = 4
+    w = S.DECODE_B256
+    setup, t = _case(w, n)
+    sample = [0, 1, 77, 128, 200, 255]
+    _check(setup, t, n, sel=sample, label="decode_tokens B=256 n=4 sampled")
+
+
+@gpu
+def test_tokens_zero_batch_is_a_no_op():
+    w = S.scaled(S.DECODE_B256, decode_batch=1, seed=83)
+    setup, t = _case(w, 2)
+    empty = {key: val[:0] for key, val in t.items()}
+    o = _gpu(setup, empty, setup["state"][:0], setup["conv_cache"][:0])
+    assert o.numel() == 0

@@ -455,3 +455,81 @@ def test_no_nan_at_extreme_gates():
     c["A_log"][1] = -np.inf
     o, fs, _ = _run(c)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(fs))
+
+
+# ----------------------------------------------- multi-token step (decode n tokens)
+
+def _token_batch(rng, B, n, Hk=2, Hv=4, D=16):
+    """B sequences with a cached state and conv cache, n new tokens each ([B, n, ...])."""
+    c = _mixer_case(rng, [n] * B, Hk, Hv, D)
+    sh = lambda x: x.reshape((B, n) + x.shape[1:])
+    return dict(q=sh(c["q"]), k=sh(c["k"]), v=sh(c["v"]), a=sh(c["a"]), b=sh(c["b"]),
+                z=sh(c["z"]), conv_w=c["conv_w"], A_log=c["A_log"], dt_bias=c["dt_bias"],
+                norm_w=c["norm_w"], state=c["init"], cache=c["hist"])
+
+
+def _tokens(t, num_commit=None):
+    return oracle.decode_tokens(t["q"], t["k"], t["v"], t["a"], t["b"], t["z"], t["conv_w"],
+                                t["A_log"], t["dt_bias"], t["norm_w"], t["state"], t["cache"],
+                                num_commit=num_commit)
+
+
+def _steps(t, count):
+    """`count` single decode steps of every sequence: outputs per step, state, cache."""
+    st, cache, outs = t["state"], t["cache"], []
+    for i in range(count):
+        o_i, st, cache = oracle.decode_step(
+            t["q"][:, i], t["k"][:, i], t["v"][:, i], t["a"][:, i], t["b"][:, i], t["z"][:, i],
+            t["conv_w"], t["A_log"], t["dt_bias"], t["norm_w"], st, cache)
+        outs.append(o_i)
+    return outs, st, cache
+
+
+def test_decode_tokens_equals_successive_single_steps():
+    """n tokens at once = n single steps in order (outputs, state and cache), bitwise."""
+    rng = np.random.default_rng(41)
+    for n in (1, 2, 5):
+        t = _token_batch(rng, 3, n)
+        o, st, cache = _tokens(t)
+        outs, st1, cache1 = _steps(t, n)
+        for i in range(n):
+            assert np.array_equal(o[:, i], outs[i])
+        assert np.array_equal(st, st1)
+        assert np.array_equal(cache, cache1)
+
+
+def test_decode_tokens_commit_prefix():
+    """num_commit[b] = c: outputs of all n tokens, state and cache after the first c
+    (c = 0 leaves both bit for bit; out-of-range counts clamp to 0..n)."""
+    rng = np.random.default_rng(42)
+    n = 5
+    t = _token_batch(rng, 5, n)
+    commit = [0, 2, 5, 3, 9]
+    o, st, cache = _tokens(t, commit)
+    o_all, _, _ = _tokens(t)
+    assert np.array_equal(o, o_all)
+    for bb, c in enumerate(commit):
+        c = min(max(c, 0), n)
+        one = {key: (val[bb:bb + 1] if key in ("q", "k", "v", "a", "b", "z", "state", "cache")
+                     else val) for key, val in t.items()}
+        _, st1, cache1 = _steps(one, c)
+        assert np.array_equal(st[bb], st1[0])
+        assert np.array_equal(cache[bb], cache1[0])
+    assert np.array_equal(st[0], t["state"][0]) and np.array_equal(cache[0], t["cache"][0])
+
+
+def test_decode_tokens_after_prefill_is_the_longer_prefill():
+    """prefill(T) then n tokens on its state and cache = prefill(T + n), bitwise."""
+    rng = np.random.default_rng(43)
+    T, n = 11, 4
+    c = _mixer_case(rng, [T + n])
+    o_full, fs_full, co_full = _run(c)
+    _, st, cache = _run(c, sl=slice(0, T), cu=[0, T])
+    sl = slice(T, T + n)
+    o, st2, cache2 = oracle.decode_tokens(
+        c["q"][None, sl], c["k"][None, sl], c["v"][None, sl], c["a"][None, sl],
+        c["b"][None, sl], c["z"][None, sl], c["conv_w"], c["A_log"], c["dt_bias"],
+        c["norm_w"], st, cache)
+    assert np.array_equal(o[0], o_full[sl])
+    assert np.array_equal(st2, fs_full)
+    assert np.array_equal(cache2, co_full)
