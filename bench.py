@@ -14,6 +14,8 @@ choose to do):
   prefill bytes/token = 2*(2*Hk*D + 3*Hv*D) + 2*4*Hv   (+ initial and final state)
   decode bytes/step  = B*Hv*D*D*4*2 (state read + write) + B*33,024 (tokens)
                        + B*3*Cc*2*2 (conv cache read + write)
+  n-token step bytes = the same with n*B*33,024 token bytes (commit pass); a
+                       verify pass (commit 0) reads the state and cache only
 Peaks: MI355X dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s.
 """
 from __future__ import annotations
@@ -173,6 +175,64 @@ def bench_decode(args, torch, gdn, S):
                 w=w, setup=setup, toks=toks)
 
 
+def decode_tokens_alg_bytes(B, n, Hk, Hv, D, act_bytes=2, commit=True):
+    Cc = 2 * Hk * D + Hv * D
+    rw = 2 if commit else 1
+    state = B * Hv * D * D * 4 * rw
+    tokens = n * B * (act_bytes * (2 * Hk * D + 3 * Hv * D) + 2 * 4 * Hv)
+    cache = B * 3 * Cc * act_bytes * rw
+    return state + tokens + cache
+
+
+def bench_decode_tokens(args, torch, gdn, S, dec=None):
+    """n new tokens per sequence per call (B=256, 16/32 heads): commit passes that
+    advance the state, and verify passes (commit 0) that only read it."""
+    w, n, calls = S.DECODE_B256, args.tokens_n, args.tokens_calls
+    B, Hk, Hv, D = w.decode_batch, w.num_qk_heads, w.num_v_heads, w.head_dim
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, calls * n, "cuda")
+    bn = {k_: v_.reshape((calls, n) + tuple(v_.shape[1:])).transpose(1, 2).contiguous()
+          for k_, v_ in toks.items()}
+    del toks
+    state, cache = setup["state"], setup["conv_cache"]
+    o = torch.empty((B, n, Hv, D), dtype=torch.bfloat16, device="cuda")
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def one(c, commit):
+        gdn.decode_tokens(bn["q"][c], bn["k"][c], bn["v"][c], bn["a"][c], bn["b"][c],
+                          bn["z"][c], setup["conv_w"], setup["A_log"], setup["dt_bias"],
+                          setup["norm_w"], state, cache, num_commit=commit, out=o)
+
+    res = {}
+    for name, commit in (("verify", zeros), ("commit", None)):
+        for c in range(min(args.warmup, calls)):
+            one(c, commit)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in range(calls):
+            one(c, commit)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / calls
+    nb_c = decode_tokens_alg_bytes(B, n, Hk, Hv, D, commit=True)
+    nb_v = decode_tokens_alg_bytes(B, n, Hk, Hv, D, commit=False)
+    t = res["commit"] * 1e-3
+    gbs = nb_c / t / 1e9
+    return {"value": B * n / t, "unit": "tokens/s", "ms_per_step": res["commit"],
+            "calls": calls,
+            "config": {"workload": f"decode_tokens_B{B}_n{n}_hk{Hk}_hv{Hv}_d{D}_bf16",
+                       "batch": B, "n_tokens": n, "calls": calls},
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens (commit all)",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": stored_traffic("decode_tokens_bytes_per_launch"),
+                         "alg_bytes_per_launch": nb_c, "launch_ms": res["commit"]},
+            "verify": {"ms_per_step": res["verify"], "tokens_per_s": B * n / (res["verify"] * 1e-3),
+                       "alg_bytes_per_launch": nb_v,
+                       "hbm_frac": nb_v / (res["verify"] * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+
 def cpu_baseline_prefill(res, S, oracle):
     """fp64 oracle on the first `n` tokens of the same workload, all heads."""
     import numpy as np
@@ -220,7 +280,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20, help="timed prefill calls")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "tokens"), default="all")
+    ap.add_argument("--tokens-n", type=int, default=4,
+                    help="new tokens per sequence of the n-token step leg (1..8)")
+    ap.add_argument("--tokens-calls", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a device copy of this many GiB (PMC scale factor)")
@@ -300,7 +363,15 @@ def main():
                          "roofline": dline["roofline"]})
         else:
             line["decode"] = dline
-    if not args.no_cpu_baseline:
+    if args.only in ("all", "tokens"):
+        tl = bench_decode_tokens(args, torch, gdn, S)
+        if args.only == "tokens":
+            line.update({"value": tl["value"], "unit": "tokens/s",
+                         "ms_per_step": tl["ms_per_step"], "config": tl["config"],
+                         "roofline": tl["roofline"], "verify": tl["verify"]})
+        else:
+            line["decode_tokens"] = tl
+    if not args.no_cpu_baseline and args.only != "tokens":
         import oracle
         if args.only in ("all", "prefill"):
             cb, err = cpu_baseline_prefill(pre, S, oracle)

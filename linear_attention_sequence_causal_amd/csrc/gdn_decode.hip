@@ -53,6 +53,10 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   auto head_ptr = [&](int j) {
     return state + (((int64_t)bseq * Hv + r * g + j) * kD + row0) * kD + col;
   };
+  // Small inputs go out before the state: vector-memory waits are in issue order,
+  // so a wait for one of them never queues behind a state prefetch.
+  const float nwv = (norm_w && tid < kD) ? norm_w[tid] : 1.0f;
+  float zcur = tid < kD ? Act<T>::load(z, ((int64_t)bseq * Hv + r * g) * kD + tid) : 0.f;
   // Start streaming the first head's state before the prologue.
   f32x4 Hcur[16];
   {
@@ -139,6 +143,8 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   // ---- 3./4. per v head: state stream and epilogue ---------------------------------
   for (int j = 0; j < r; ++j) {
     const int h = r * g + j;
+    const float zg = siluf_(zcur);
+    if (j + 1 < r && tid < kD) zcur = Act<T>::load(z, ((int64_t)bseq * Hv + h + 1) * kD + tid);
     f32x4 Hnext[16];
     if (j + 1 < r) {
       const float *Hn = head_ptr(j + 1);
@@ -188,9 +194,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     }
     if (tid < kD) {
       const float inv = rsqrtf((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
-      const float w = norm_w ? norm_w[tid] : 1.0f;
-      const int64_t oi = ((int64_t)bseq * Hv + h) * kD + tid;
-      Act<T>::store(o, oi, s_y[tid] * inv * w * siluf_(Act<T>::load(z, oi)));
+      Act<T>::store(o, ((int64_t)bseq * Hv + h) * kD + tid, s_y[tid] * inv * nwv * zg);
     }
     __syncthreads();  // s_red, s_e, s_y, s_misc are reused by the next head
     if (j + 1 < r) {
@@ -256,6 +260,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   const int tid = threadIdx.x;
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
+  const float nwv = (norm_w && tid < kD) ? norm_w[tid] : 1.0f;  // loaded before the state
 
   __shared__ float s_x[kMaxStepTokens][2 + kDecMaxRatio][kD];  // post-prologue q, k, v rows
   __shared__ float s_red[8][2][kD];
@@ -367,18 +372,43 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   __syncthreads();
 
   // ---- per v head: the state stays in registers across the n tokens ------------------
+  // Gate inputs and z of every token of a head are loaded before its token loop, so
+  // no global load latency sits between two tokens.
+  float ga[kMaxStepTokens], gb[kMaxStepTokens], zr[kMaxStepTokens];
+  auto load_head_inputs = [&](int h) {
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) {
+      const int64_t gi = ((int64_t)bseq * n + min(t, n - 1)) * Hv + h;
+      ga[t] = a[gi];
+      gb[t] = b[gi];
+      zr[t] = tid < kD ? Act<T>::load(z, gi * kD + tid) : 0.f;
+    }
+  };
+  load_head_inputs(r * g);
   for (int j = 0; j < r; ++j) {
     const int h = r * g + j;
+    float alph[kMaxStepTokens], bet[kMaxStepTokens], zg[kMaxStepTokens];
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) {
+      alph[t] = __expf(log_decay(ga[t], A_log[h], dt_bias[h]));
+      bet[t] = sigmoidf_(gb[t]);
+      zg[t] = siluf_(zr[t]);
+    }
+    // the next head's small inputs, then its state: vector-memory waits are in
+    // issue order, so nothing waited on in the token loop queues behind the state
+    if (j + 1 < r) load_head_inputs(h + 1);
     f32x4 Hnext[16];
     if (j + 1 < r) {
       const float *Hn = head_ptr(j + 1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) Hnext[i] = ld_nt4(Hn + i * kD);
     }
-    for (int t = 0; t < n; ++t) {
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) {
+      if (t >= n) break;
       const int64_t gi = ((int64_t)bseq * n + t) * Hv + h;
-      const float alpha = __expf(log_decay(a[gi], A_log[h], dt_bias[h]));
-      const float beta = sigmoidf_(b[gi]);
+      const float alpha = alph[t];
+      const float beta = bet[t];
       float kr[16], qr[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -428,9 +458,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       }
       if (tid < kD) {
         const float inv = rsqrtf((s_ss[0] + s_ss[1]) * (1.0f / kD) + rms_eps);
-        const float w = norm_w ? norm_w[tid] : 1.0f;
-        const int64_t oi = gi * kD + tid;
-        Act<T>::store(o, oi, s_y[tid] * inv * w * siluf_(Act<T>::load(z, oi)));
+        Act<T>::store(o, gi * kD + tid, s_y[tid] * inv * nwv * zg[t]);
       }
     }
     __syncthreads();  // s_red, s_e, s_y, s_ss are reused by the next head
