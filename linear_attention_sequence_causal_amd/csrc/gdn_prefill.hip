@@ -403,7 +403,10 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   const int role = wave < 4 ? 0 : 1;   // uniform per wave
   int cg = tid & 15;                   // q/k channels 8cg .. 8cg+7
   int tbase = ((tid & 255) >> 4) * 4;  // q/k tokens tbase .. tbase+3
-  int cv = tid & 31;                   // v channels 4cv .. 4cv+3
+  // v channels 4cv .. 4cv+3; cv rotates the 5 lane bits so that the 8 lanes of one
+  // 16-byte LDS write cycle take cv values 4 apart: their V^T rows 4cv + cc lie in
+  // 8 different 16-row blocks, which the tile's swizzle spreads over all banks
+  int cv = ((tid & 7) << 2) | ((tid >> 3) & 3);
   int vbase = (tid >> 5) * 4;          // v tokens vbase .. vbase+3
   // Re-derive the lane coordinates behind an optimisation barrier after every
   // workgroup barrier, so that LDS addresses are formed next to their use
