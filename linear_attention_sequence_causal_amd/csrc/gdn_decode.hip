@@ -244,8 +244,26 @@ template hipError_t launch_decode<bf16_t>(const void *, const void *, const void
 // untouched, and a second pass with the accepted count advances them.
 constexpr int kMaxStepTokens = 8;
 
+// Sum of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of a
+// wave), left in all four: two row swaps on the gfx950 permlane crossbar.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// One workgroup per (sequence, q/k head, pair of its v heads): wave w holds
+// v head 2p + (w >> 1), value columns 64 (w & 1) + 4 cg .. + 3 (cg = lane & 15)
+// and key rows 32 rg .. + 31 (rg = lane >> 4) of the fp32 state, 128 values per
+// lane.  A token's S k and S q sums are finished across the four row lanes with
+// permlane swaps, so the token loop needs no LDS round trip and no barrier; the
+// RMS of each token's y (split over the two waves of a head) is taken once after
+// the loop.
 template <typename T>
-__global__ void __launch_bounds__(kDecThreads)
+__global__ void __launch_bounds__(kDecThreads, 2)
 decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                      const float *__restrict__ a, const float *__restrict__ b,
                      const T *__restrict__ z, const float *__restrict__ conv_w,
@@ -254,49 +272,59 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
                      float rms_eps, float *__restrict__ state, T *__restrict__ conv_state,
                      const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
                      int n) {
-  const int g = blockIdx.x % Hk;
-  const int bseq = blockIdx.x / Hk;
   const int r = Hv / Hk;
-  const int tid = threadIdx.x;
+  const int npair = (r + 1) / 2;
+  const int pair = blockIdx.x % npair;
+  const int g = (blockIdx.x / npair) % Hk;
+  const int bseq = blockIdx.x / npair / Hk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
-  const float nwv = (norm_w && tid < kD) ? norm_w[tid] : 1.0f;  // loaded before the state
 
-  __shared__ float s_x[kMaxStepTokens][2 + kDecMaxRatio][kD];  // post-prologue q, k, v rows
-  __shared__ float s_red[8][2][kD];
-  __shared__ float s_e[kD];
-  __shared__ float s_y[kD];
+  const int hl = wave >> 1;                       // head of the pair
+  const int jh = 2 * pair + hl;                   // v head within the q/k group
+  const bool head_on = jh < r;
+  const int h = r * g + min(jh, r - 1);
+  const int cg = lane & 15, rg = lane >> 4;
+  const int col0 = 64 * (wave & 1) + 4 * cg;      // 4 value columns
+  const int row0 = 32 * rg;                       // 32 key rows
+  const int ocol = col0 + rg;                     // the column this lane outputs
+
+  __shared__ float s_x[kMaxStepTokens][4][kD];    // post-prologue q, k, v0, v1 rows
   __shared__ float s_kq[kMaxStepTokens];
-  __shared__ float s_ss[2];
+  __shared__ float s_ss[4][kMaxStepTokens];       // per-wave partial sums of y^2
+  __shared__ float s_ab[2][kMaxStepTokens][2];    // alpha, beta of each head and token
+  __shared__ float s_y[4][kMaxStepTokens][64];    // y of each lane's output column
 
-  const int col = (tid & 31) * 4;
-  const int rg = tid >> 5;
-  const int row0 = rg * 16;
-  auto head_ptr = [&](int j) {
-    return state + (((int64_t)bseq * Hv + r * g + j) * kD + row0) * kD + col;
-  };
-  f32x4 Hcur[16];
-  {
-    const float *Hp = head_ptr(0);
+  // small inputs first (vector-memory waits are in issue order), then the state
+  const float nwv = norm_w ? norm_w[ocol] : 1.0f;
+  float zr[kMaxStepTokens];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Hcur[i] = ld_nt4(Hp + i * kD);
+  for (int t = 0; t < kMaxStepTokens; ++t)
+    zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
+  float ga = 0.f, gb = 0.f;  // gate inputs of (head tid >> 3, token tid & 7)
+  const int gh = r * g + min(2 * pair + (tid >> 3), r - 1), gt = tid & 7;
+  if (tid < 16 && gt < n) {
+    const int64_t gi = ((int64_t)bseq * n + gt) * Hv + gh;
+    ga = a[gi];
+    gb = b[gi];
   }
+  float *Hp = state + (((int64_t)bseq * Hv + h) * kD + row0) * kD + col0;
+  f32x4 Hs[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) Hs[i] = ld_nt4(Hp + i * kD);
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
-  // raw[0..2] = cached rows (oldest first), raw[3 + t] = new token t
-  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
-  const int c0 = (tid & 63) * 2;
-  const int sec = tid >> 6;
-  for (int pass = 0; pass == 0 || 2 + 4 * (pass - 1) < r; ++pass) {
-    int slot, jv = -1;
-    if (pass == 0) {
-      slot = sec;
-      if (sec >= 2) jv = sec - 2;
-    } else {
-      jv = 2 + 4 * (pass - 1) + sec;
-      slot = 2 + jv;
-    }
-    const bool active = jv < r;
+  // section = wave: q, k, v of head 2p, v of head 2p + 1.  raw[0..2] = cached rows
+  // (oldest first), raw[3 + t] = new token t.  The q/k cache channels belong to the
+  // pair-0 workgroup, a v head's to the workgroup of its pair.
+  {
+    T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+    const int c0 = lane * 2;
+    const int slot = wave;
+    const int jv = 2 * pair + (slot - 2);
+    const bool active = slot < 2 || jv < r;
+    const bool owner = slot < 2 ? pair == 0 : true;
     int64_t cbase, hstride, sidx;
     const T *src;
     if (slot == 0) {
@@ -306,8 +334,9 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       cbase = (int64_t)Hk * kD + (int64_t)g * kD; src = k; hstride = (int64_t)Hk * kD;
       sidx = ((int64_t)bseq * n * Hk + g) * kD;
     } else {
-      cbase = 2LL * Hk * kD + (int64_t)(r * g + jv) * kD; src = v; hstride = (int64_t)Hv * kD;
-      sidx = ((int64_t)bseq * n * Hv + r * g + jv) * kD;
+      const int jj = min(jv, r - 1);
+      cbase = 2LL * Hk * kD + (int64_t)(r * g + jj) * kD; src = v; hstride = (int64_t)Hv * kD;
+      sidx = ((int64_t)bseq * n * Hv + r * g + jj) * kD;
     }
     float xv[kMaxStepTokens][2];
 #pragma unroll
@@ -328,8 +357,8 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         for (int t = 0; t < kMaxStepTokens; ++t)
           xv[t][u] = siluf_(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
         // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
-        // (reads above precede these writes; this thread owns the channel)
-        if (commit > 0) {
+        // (the reads above precede these writes, and only this thread touches ch)
+        if (owner && commit > 0) {
 #pragma unroll
           for (int s2 = 0; s2 < 3; ++s2) {
             float x = raw[0];
@@ -341,7 +370,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         }
       }
     }
-    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token over 128 channels
+    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token
 #pragma unroll
       for (int t = 0; t < kMaxStepTokens; ++t) {
         if (t < n) {
@@ -352,119 +381,106 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         }
       }
     }
-    if (active) {
 #pragma unroll
-      for (int t = 0; t < kMaxStepTokens; ++t)
-        if (t < n) {
-          s_x[t][slot][c0] = xv[t][0];
-          s_x[t][slot][c0 + 1] = xv[t][1];
-        }
-    }
+    for (int t = 0; t < kMaxStepTokens; ++t)
+      if (t < n) {
+        s_x[t][slot][c0] = xv[t][0];
+        s_x[t][slot][c0 + 1] = xv[t][1];
+      }
+  }
+  if (tid < 16 && gt < n) {
+    s_ab[tid >> 3][gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
+    s_ab[tid >> 3][gt][1] = sigmoidf_(gb);
   }
   __syncthreads();
-  if (tid < 64) {  // k_t . q_t of each token
+  if (wave == 0) {  // k_t . q_t of each token
     for (int t = 0; t < n; ++t) {
-      const float kq = wave_sum(s_x[t][0][2 * tid] * s_x[t][1][2 * tid] +
-                                s_x[t][0][2 * tid + 1] * s_x[t][1][2 * tid + 1]);
-      if (tid == 0) s_kq[t] = kq;
+      const float kq = wave_sum(s_x[t][0][2 * lane] * s_x[t][1][2 * lane] +
+                                s_x[t][0][2 * lane + 1] * s_x[t][1][2 * lane + 1]);
+      if (lane == 0) s_kq[t] = kq;
     }
   }
   __syncthreads();
 
-  // ---- per v head: the state stays in registers across the n tokens ------------------
-  // Gate inputs and z of every token of a head are loaded before its token loop, so
-  // no global load latency sits between two tokens.
-  float ga[kMaxStepTokens], gb[kMaxStepTokens], zr[kMaxStepTokens];
-  auto load_head_inputs = [&](int h) {
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) {
-      const int64_t gi = ((int64_t)bseq * n + min(t, n - 1)) * Hv + h;
-      ga[t] = a[gi];
-      gb[t] = b[gi];
-      zr[t] = tid < kD ? Act<T>::load(z, gi * kD + tid) : 0.f;
-    }
-  };
-  load_head_inputs(r * g);
-  for (int j = 0; j < r; ++j) {
-    const int h = r * g + j;
-    float alph[kMaxStepTokens], bet[kMaxStepTokens], zg[kMaxStepTokens];
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) {
-      alph[t] = __expf(log_decay(ga[t], A_log[h], dt_bias[h]));
-      bet[t] = sigmoidf_(gb[t]);
-      zg[t] = siluf_(zr[t]);
-    }
-    // the next head's small inputs, then its state: vector-memory waits are in
-    // issue order, so nothing waited on in the token loop queues behind the state
-    if (j + 1 < r) load_head_inputs(h + 1);
-    f32x4 Hnext[16];
-    if (j + 1 < r) {
-      const float *Hn = head_ptr(j + 1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Hnext[i] = ld_nt4(Hn + i * kD);
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) {
-      if (t >= n) break;
-      const int64_t gi = ((int64_t)bseq * n + t) * Hv + h;
-      const float alpha = alph[t];
-      const float beta = bet[t];
-      float kr[16], qr[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        kr[i] = s_x[t][1][row0 + i];
-        qr[i] = s_x[t][0][row0 + i];
-      }
+  // ---- token loop: the state stays in registers, no barrier -----------------------------
+#pragma unroll 1
+  for (int t = 0; t < n; ++t) {
+    {
+      const float alpha = s_ab[hl][t][0];
+      const float beta = s_ab[hl][t][1];
+      // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
+      // within each 16-lane row); k again for the update, to keep registers low
       float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sk[0] += Hcur[i].x * kr[i]; sk[1] += Hcur[i].y * kr[i];
-        sk[2] += Hcur[i].z * kr[i]; sk[3] += Hcur[i].w * kr[i];
-        sq[0] += Hcur[i].x * qr[i]; sq[1] += Hcur[i].y * qr[i];
-        sq[2] += Hcur[i].z * qr[i]; sq[3] += Hcur[i].w * qr[i];
-      }
-      *reinterpret_cast<f32x4 *>(&s_red[rg][0][col]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
-      *reinterpret_cast<f32x4 *>(&s_red[rg][1][col]) = f32x4{sq[0], sq[1], sq[2], sq[3]};
-      __syncthreads();
-      if (tid < kD) {
-        float vk = 0.f, vq = 0.f;
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
+        const f32x4 qq = *reinterpret_cast<const f32x4 *>(&s_x[t][0][row0 + i]);
+        const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          vk += s_red[p][0][tid];
-          vq += s_red[p][1][tid];
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 hv = Hs[i + u];
+          sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
+          sk[2] += hv.z * kv[u]; sk[3] += hv.w * kv[u];
+          sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
+          sq[2] += hv.z * qv[u]; sq[3] += hv.w * qv[u];
         }
-        const float e = s_x[t][2 + j][tid] - alpha * vk;  // e = v - S'k
-        const float y = alpha * vq + beta * s_kq[t] * e;  // S'' q
-        s_e[tid] = e;
-        s_y[tid] = y;
-        const float ssum = wave_sum(y * y);
-        if ((tid & 63) == 0) s_ss[tid >> 6] = ssum;
       }
-      __syncthreads();
-      float ec[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ec[c] = beta * s_e[col + c];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        Hcur[i].x = alpha * Hcur[i].x + kr[i] * ec[0];
-        Hcur[i].y = alpha * Hcur[i].y + kr[i] * ec[1];
-        Hcur[i].z = alpha * Hcur[i].z + kr[i] * ec[2];
-        Hcur[i].w = alpha * Hcur[i].w + kr[i] * ec[3];
+      for (int c = 0; c < 4; ++c) {
+        sk[c] = rows4_sum(sk[c]);
+        sq[c] = rows4_sum(sq[c]);
       }
-      if (t + 1 == commit) {
-        float *Hp = head_ptr(j);
+      const f32x4 vv = *reinterpret_cast<const f32x4 *>(&s_x[t][2 + hl][col0]);
+      const float kq = s_kq[t];
+      float be[4];
+      float y[4];
+      const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st_nt4(Hp + i * kD, Hcur[i]);
+      for (int c = 0; c < 4; ++c) {
+        const float e = vs[c] - alpha * sk[c];  // e = v - S'k
+        y[c] = alpha * sq[c] + beta * kq * e;   // S'' q
+        be[c] = beta * e;
       }
-      if (tid < kD) {
-        const float inv = rsqrtf((s_ss[0] + s_ss[1]) * (1.0f / kD) + rms_eps);
-        Act<T>::store(o, gi * kD + tid, s_y[tid] * inv * nwv * zg[t]);
+      s_y[wave][t][lane] = rg == 0 ? y[0] : rg == 1 ? y[1] : rg == 2 ? y[2] : y[3];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
+        const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Hs[i + u].x = alpha * Hs[i + u].x + kv[u] * be[0];
+          Hs[i + u].y = alpha * Hs[i + u].y + kv[u] * be[1];
+          Hs[i + u].z = alpha * Hs[i + u].z + kv[u] * be[2];
+          Hs[i + u].w = alpha * Hs[i + u].w + kv[u] * be[3];
+        }
+      }
+      if (t + 1 == commit && head_on) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) st_nt4(Hp + i * kD, Hs[i]);
       }
     }
-    __syncthreads();  // s_red, s_e, s_y, s_ss are reused by the next head
-    if (j + 1 < r) {
+  }
+
+  // ---- epilogue: RMS over the head's 128 columns (two waves), SiLU(z) gate ------------
+  float yown[kMaxStepTokens];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hcur[i] = Hnext[i];
+  for (int t = 0; t < kMaxStepTokens; ++t) {
+    yown[t] = t < n ? s_y[wave][t][lane] : 0.f;  // this lane's own writes: no barrier
+    if (t < n) {
+      // each column sits in one lane of its group of four: sum over the wave's 64
+      const float ssum = wave_sum(yown[t] * yown[t]);
+      if (lane == 0) s_ss[wave][t] = ssum;
+    }
+  }
+  __syncthreads();
+  if (head_on) {
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) {
+      if (t < n) {
+        const float inv = rsqrtf((s_ss[2 * hl][t] + s_ss[2 * hl + 1][t]) * (1.0f / kD) + rms_eps);
+        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
+        Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
+      }
     }
   }
 }
@@ -477,7 +493,8 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 void *conv_state, const int32_t *num_commit, void *o, int batch,
                                 int n, int Hk, int Hv, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  dim3 grid((unsigned)batch * (unsigned)Hk);
+  const unsigned npair = (unsigned)((Hv / Hk + 1) / 2);
+  dim3 grid((unsigned)batch * (unsigned)Hk * npair);
   hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kDecThreads), 0, stream,
                      (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
                      dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
