@@ -771,11 +771,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sM[(16 * ti + 4 * lg + i) * kSqS + 16 * (ti + 1) + ln] = 0;
     }
+    // next chunk's raw rows: the q waves, which have slack here, go first so that the
+    // k waves' loads after the barrier do not queue behind theirs
+    if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);
     __syncthreads();  // (3) -L, M and T_bb - I ready
     refresh();
 
     // ================= Q H, right-hand sides of the triangular solves =============
-    if (c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
+    if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
     // H as bf16 B operands: Hb[kb] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb+16+4lg+j-4
     u16x8 Hb[4];
 #pragma unroll
