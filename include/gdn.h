@@ -124,6 +124,18 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            const gdn_params *p, float *state, void *conv_state,
                            void *o, int32_t batch, void *stream);
 
+/* gdn_decode_step with the state stored in bf16: state is [B, Hv, D, D] bf16
+ * (uint16 bit patterns), read once per step, widened to fp32 for the step's
+ * arithmetic (identical to gdn_decode_step's), and written back rounded to
+ * nearest even.  Halves the state bytes that dominate a decode step.  This is a
+ * reduced-precision storage mode beside the pages' fp32 state: the stored state
+ * carries one bf16 rounding per step (its own tolerance; see the tests).  Other
+ * arguments and errors as gdn_decode_step. */
+gdn_status gdn_decode_step_bf16_state(const void *q, const void *k, const void *v,
+                                      const float *a, const float *b, const void *z,
+                                      const gdn_params *p, void *state, void *conv_state,
+                                      void *o, int32_t batch, void *stream);
+
 /* n_tokens new tokens per sequence on a cached state (multi-token decode; the
  * verify and commit passes of speculative decoding).  The result is that of
  * n_tokens gdn_decode_step calls in order (the field guide's six update

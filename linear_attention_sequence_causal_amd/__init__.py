@@ -25,7 +25,7 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
-            "gdn_decode_tokens", "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
+            "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
             "gdn_version")
 PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
 
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, sz, vp]
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32, vp]
+            L.gdn_decode_step_bf16_state.restype = ctypes.c_int
+            L.gdn_decode_step_bf16_state.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32,
+                                                     vp]
             L.gdn_decode_tokens.restype = ctypes.c_int
             L.gdn_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, i32, i32,
                                             vp]
@@ -167,7 +170,8 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
                 q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None):
     """One decode step; updates `state` and `conv_state` in place, returns o.
 
-    q, k [B, Hk, D]; v, z [B, Hv, D]; a, b [B, Hv]; state [B, Hv, D, D] fp32;
+    q, k [B, Hk, D]; v, z [B, Hv, D]; a, b [B, Hv]; state [B, Hv, D, D] fp32, or bf16
+    for the reduced-precision storage mode (fp32 arithmetic, state rounded on store);
     conv_state [B, 3, Cc] in the activation dtype.
     """
     B, Hk, D = q.shape
@@ -175,9 +179,14 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
     _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state)
     p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
     o = torch.empty_like(v) if out is None else out
-    _check(lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
-                                 ctypes.byref(p), _ptr(state), _ptr(conv_state), _ptr(o), B,
-                                 _stream()))
+    if state.dtype == torch.bfloat16:  # reduced-precision storage of the state
+        fn = lib().gdn_decode_step_bf16_state
+    elif state.dtype == torch.float32:
+        fn = lib().gdn_decode_step
+    else:
+        raise ValueError("state must be float32 or bfloat16")
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z), ctypes.byref(p), _ptr(state),
+              _ptr(conv_state), _ptr(o), B, _stream()))
     return o
 
 

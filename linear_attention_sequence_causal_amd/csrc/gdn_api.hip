@@ -20,8 +20,8 @@ template <typename T>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *a,
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
-                         float rms_eps, float *state, void *conv_state, void *o, int batch,
-                         int Hk, int Hv, hipStream_t stream);
+                         float rms_eps, void *state, bool state_bf16, void *conv_state, void *o,
+                         int batch, int Hk, int Hv, hipStream_t stream);
 int decode_max_ratio();
 template <typename T>
 hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, const float *a,
@@ -203,9 +203,13 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
   return GDN_OK;
 }
 
-gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *a,
-                           const float *b, const void *z, const gdn_params *p, float *state,
-                           void *conv_state, void *o, int32_t batch, void *stream) {
+}  // extern "C"
+
+namespace {
+gdn_status decode_step_impl(const void *q, const void *k, const void *v, const float *a,
+                            const float *b, const void *z, const gdn_params *p, void *state,
+                            bool state_bf16, void *conv_state, void *o, int32_t batch,
+                            void *stream) {
   g_err[0] = 0;
   gdn_status st = check_params(p);
   if (st != GDN_OK) return st;
@@ -225,15 +229,31 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
   if (p->act_dtype == GDN_BF16)
     e = gdn::launch_decode<gdn::bf16_t>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                         p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
-                                        conv_state, o, batch, p->num_qk_heads, p->num_v_heads,
-                                        (hipStream_t)stream);
+                                        state_bf16, conv_state, o, batch, p->num_qk_heads,
+                                        p->num_v_heads, (hipStream_t)stream);
   else
     e = gdn::launch_decode<float>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                   p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
-                                  conv_state, o, batch, p->num_qk_heads, p->num_v_heads,
-                                  (hipStream_t)stream);
+                                  state_bf16, conv_state, o, batch, p->num_qk_heads,
+                                  p->num_v_heads, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *a,
+                           const float *b, const void *z, const gdn_params *p, float *state,
+                           void *conv_state, void *o, int32_t batch, void *stream) {
+  return decode_step_impl(q, k, v, a, b, z, p, state, false, conv_state, o, batch, stream);
+}
+
+gdn_status gdn_decode_step_bf16_state(const void *q, const void *k, const void *v,
+                                      const float *a, const float *b, const void *z,
+                                      const gdn_params *p, void *state, void *conv_state,
+                                      void *o, int32_t batch, void *stream) {
+  return decode_step_impl(q, k, v, a, b, z, p, state, true, conv_state, o, batch, stream);
 }
 
 gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v, const float *a,

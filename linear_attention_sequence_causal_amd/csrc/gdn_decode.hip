@@ -25,14 +25,35 @@ namespace gdn {
 constexpr int kDecThreads = 256;
 constexpr int kDecMaxRatio = 8;  // largest Hv / Hk the decode kernel accepts
 
-template <typename T>
+// Stored state: fp32, or bf16 (rounded to nearest even on every store) with the
+// step itself computed in fp32.  Four consecutive columns per access, streamed
+// once (non-temporal).
+template <typename S> struct StateIO;
+template <> struct StateIO<float> {
+  static __device__ __forceinline__ f32x4 load(const float *p) { return ld_nt4(p); }
+  static __device__ __forceinline__ void store(float *p, f32x4 x) { st_nt4(p, x); }
+};
+template <> struct StateIO<bf16_t> {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x4 load(const bf16_t *p) {
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+  static __device__ __forceinline__ void store(bf16_t *p, f32x4 x) {
+    const u32x2 w = {pk_bf16(x.x, x.y), pk_bf16(x.z, x.w)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+  }
+};
+
+template <typename T, typename S>
 __global__ void __launch_bounds__(kDecThreads)
 decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                    const float *__restrict__ a, const float *__restrict__ b,
                    const T *__restrict__ z, const float *__restrict__ conv_w,
                    const float *__restrict__ A_log, const float *__restrict__ dt_bias,
                    const float *__restrict__ norm_w, float q_scale, float l2_eps, float rms_eps,
-                   float *__restrict__ state, T *__restrict__ conv_state, T *__restrict__ o,
+                   S *__restrict__ state, T *__restrict__ conv_state, T *__restrict__ o,
                    int Hk, int Hv) {
   const int g = blockIdx.x % Hk;
   const int bseq = blockIdx.x / Hk;
@@ -60,9 +81,9 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   // Start streaming the first head's state before the prologue.
   f32x4 Hcur[16];
   {
-    const float *Hp = head_ptr(0);
+    const S *Hp = head_ptr(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Hcur[i] = ld_nt4(Hp + i * kD);
+    for (int i = 0; i < 16; ++i) Hcur[i] = StateIO<S>::load(Hp + i * kD);
   }
 
   // ---- 1. prologue --------------------------------------------------------------
@@ -147,9 +168,9 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     if (j + 1 < r && tid < kD) zcur = Act<T>::load(z, ((int64_t)bseq * Hv + h + 1) * kD + tid);
     f32x4 Hnext[16];
     if (j + 1 < r) {
-      const float *Hn = head_ptr(j + 1);
+      const S *Hn = head_ptr(j + 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hnext[i] = ld_nt4(Hn + i * kD);
+      for (int i = 0; i < 16; ++i) Hnext[i] = StateIO<S>::load(Hn + i * kD);
     }
     const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
     const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
@@ -182,7 +203,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     float ec[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ec[c] = beta * s_e[col + c];
-    float *Hp = head_ptr(j);
+    S *Hp = head_ptr(j);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       f32x4 hn;
@@ -190,7 +211,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       hn.y = alpha * Hcur[i].y + kr[i] * ec[1];
       hn.z = alpha * Hcur[i].z + kr[i] * ec[2];
       hn.w = alpha * Hcur[i].w + kr[i] * ec[3];
-      st_nt4(Hp + i * kD, hn);
+      StateIO<S>::store(Hp + i * kD, hn);
     }
     if (tid < kD) {
       const float inv = rsqrtf((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
@@ -204,18 +225,25 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   }
 }
 
+// state_bf16: the state is bf16 storage (void * either way)
 template <typename T>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *a,
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
-                         float rms_eps, float *state, void *conv_state, void *o, int batch,
-                         int Hk, int Hv, hipStream_t stream) {
+                         float rms_eps, void *state, bool state_bf16, void *conv_state, void *o,
+                         int batch, int Hk, int Hv, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   dim3 grid((unsigned)batch * (unsigned)Hk);
-  hipLaunchKernelGGL((decode_step_kernel<T>), grid, dim3(kDecThreads), 0, stream,
-                     (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
-                     dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state, (T *)o,
-                     Hk, Hv);
+  if (state_bf16)
+    hipLaunchKernelGGL((decode_step_kernel<T, bf16_t>), grid, dim3(kDecThreads), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
+                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, (bf16_t *)state,
+                       (T *)conv_state, (T *)o, Hk, Hv);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<T, float>), grid, dim3(kDecThreads), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
+                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, (float *)state,
+                       (T *)conv_state, (T *)o, Hk, Hv);
   return hipGetLastError();
 }
 
@@ -224,13 +252,13 @@ int decode_max_ratio() { return kDecMaxRatio; }
 template hipError_t launch_decode<float>(const void *, const void *, const void *, const float *,
                                          const float *, const void *, const float *,
                                          const float *, const float *, const float *, float,
-                                         float, float, float *, void *, void *, int, int, int,
-                                         hipStream_t);
+                                         float, float, void *, bool, void *, void *, int, int,
+                                         int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(const void *, const void *, const void *,
                                           const float *, const float *, const void *,
                                           const float *, const float *, const float *,
-                                          const float *, float, float, float, float *, void *,
-                                          void *, int, int, int, hipStream_t);
+                                          const float *, float, float, float, void *, bool,
+                                          void *, void *, int, int, int, hipStream_t);
 
 // ---------------------------------------------------------------------------------
 // Multi-token step: n (1..8) new tokens per sequence on a cached state.  It is the

@@ -212,6 +212,25 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_ca
     return o, state, cache
 
 
+def round_bf16(x):
+    """Nearest bf16 value of each fp64 element (8 significant bits, ties to even),
+    returned as fp64.  Normal range only: x = m 2^e with 0.5 <= |m| < 1, and m is
+    rounded to a multiple of 2^-8."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def decode_step_bf16_state(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache,
+                           **kw):
+    """One decode step with the state stored in bf16: the step in fp64 on the stored
+    (bf16-valued) state, then the new state rounded to the nearest bf16 value.
+    Returns (o, new_state, new_conv_cache)."""
+    o, st, cache = decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state,
+                               conv_cache, **kw)
+    return o, round_bf16(st), cache
+
+
 def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
                   num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
     """n new tokens per sequence on a cached state (multi-token decode / verify / commit).

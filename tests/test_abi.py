@@ -22,7 +22,7 @@ HEADER = os.path.join(ROOT, "include", "gdn.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -168,6 +168,11 @@ def test_valid_calls_report_missing_device(monkeypatch):
     p, h = _params()
     assert _decode(p) == NO_DEVICE
     assert _tokens(p) == NO_DEVICE
+    bufs = {n: _host(1 << 16) for n in ("q", "k", "v", "a", "b", "z", "state", "cache", "o")}
+    ptr = {n: ctypes.c_void_p(x.ctypes.data) for n, x in bufs.items()}
+    assert gdn.lib().gdn_decode_step_bf16_state(
+        ptr["q"], ptr["k"], ptr["v"], ptr["a"], ptr["b"], ptr["z"], ctypes.byref(p),
+        ptr["state"], ptr["cache"], ptr["o"], 2, None) == NO_DEVICE
     n = gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 64)
     raw = np.zeros(n + 512, dtype=np.uint8)
     addr = (raw.ctypes.data + 255) // 256 * 256

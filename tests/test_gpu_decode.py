@@ -123,3 +123,87 @@ def test_decode_identity_gates_keep_state_bitwise():
                     setup["conv_cache"])
     torch.cuda.synchronize()
     assert torch.equal(st0, setup["state"])
+
+
+# ------------------------------------------- reduced-precision (bf16) state storage
+
+def _run_decode_bf16_state(w, steps, seq_sample=None):
+    """GPU decode with bf16 state storage, the bf16-storage oracle, and the fp32-storage
+    oracle from the same (bf16-rounded) start."""
+    import linear_attention_sequence_causal_amd as gdn
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, steps, "cuda")
+    state = setup["state"].to(torch.bfloat16)
+    cache = setup["conv_cache"]
+    st0, cc0 = state.clone(), cache.clone()
+    outs = []
+    for s in range(steps):
+        outs.append(gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s],
+                                    toks["b"][s], toks["z"][s], setup["conv_w"], setup["A_log"],
+                                    setup["dt_bias"], setup["norm_w"], state, cache))
+    torch.cuda.synchronize()
+    sel = slice(None) if seq_sample is None else seq_sample
+    f = S.to_f64
+    sb, cb = f(st0[sel]), f(cc0[sel])
+    sx, cx = sb.copy(), cb.copy()
+    ob, ox = [], []
+    for s in range(steps):
+        args = (f(toks["q"][s][sel]), f(toks["k"][s][sel]), f(toks["v"][s][sel]),
+                f(toks["a"][s][sel]), f(toks["b"][s][sel]), f(toks["z"][s][sel]),
+                f(setup["conv_w"]), f(setup["A_log"]), f(setup["dt_bias"]), f(setup["norm_w"]))
+        o_s, sb, cb = oracle.decode_step_bf16_state(*args, sb, cb)
+        ob.append(o_s)
+        o_s, sx, cx = oracle.decode_step(*args, sx, cx)
+        ox.append(o_s)
+    return (np.stack([f(o[sel]) for o in outs]), f(state[sel]), f(cache[sel]),
+            np.stack(ob), sb, cb, np.stack(ox), sx)
+
+
+@gpu
+@pytest.mark.parametrize("hk,hv", [(16, 32), (2, 8)])
+def test_decode_bf16_state_matches_its_oracle(hk, hv):
+    """Against the oracle of the same storage (fp64 step, state rounded to bf16 each
+    step) only the fp32 arithmetic differs: a stored element moves by one bf16 unit
+    where fp32 and fp64 fall on two sides of a rounding midpoint."""
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=hk, num_v_heads=hv, seed=90 + hv)
+    o, st, cc, o_b, st_b, cc_b, o_x, st_x = _run_decode_bf16_state(w, steps=8)
+    eo, es = rel_l2(o, o_b), rel_l2(st, st_b)
+    print(f"decode bf16 state Hk={hk} Hv={hv}: o rel-L2 {eo:.3e} state rel-L2 {es:.3e} "
+          f"(vs fp32 storage: o {rel_l2(o, o_x):.3e} state {rel_l2(st, st_x):.3e})")
+    assert eo < O_TOL
+    assert es < 1e-4
+    assert np.array_equal(cc, cc_b)
+
+
+@gpu
+def test_decode_bf16_state_full_batch_precision_cost():
+    """B=256, 16/32 heads, 40 steps: parity with the bf16-storage oracle on 6 sampled
+    sequences, and the cost of the storage against fp32 storage (the mode's own
+    tolerance, 1e-2 on o and on the state: one rounding of 2^-9 per step, damped by
+    the decay)."""
+    w = S.DECODE_B256
+    sample = [0, 5, 99, 128, 201, 255]
+    o, st, cc, o_b, st_b, cc_b, o_x, st_x = _run_decode_bf16_state(w, 40, seq_sample=sample)
+    eo, es, ex_o, ex_s = rel_l2(o, o_b), rel_l2(st, st_b), rel_l2(o, o_x), rel_l2(st, st_x)
+    print(f"decode bf16 state B=256 sampled: o rel-L2 {eo:.3e} state rel-L2 {es:.3e}; "
+          f"vs fp32 storage o {ex_o:.3e} state {ex_s:.3e}")
+    assert eo < O_TOL and es < 1e-4
+    assert ex_o < 1e-2 and ex_s < 1e-2
+    assert np.array_equal(cc, cc_b)
+
+
+@gpu
+def test_decode_bf16_state_identity_gates_keep_state_bitwise():
+    import linear_attention_sequence_causal_amd as gdn
+    w = S.scaled(S.DECODE_B256, decode_batch=3, seed=92)
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, 1, "cuda")
+    state = setup["state"].to(torch.bfloat16)
+    st0 = state.clone()
+    b = torch.full_like(toks["b"][0], -float("inf"))
+    A_log = torch.full_like(setup["A_log"], -float("inf"))
+    gdn.decode_step(toks["q"][0], toks["k"][0], toks["v"][0], toks["a"][0], b, toks["z"][0],
+                    setup["conv_w"], A_log, setup["dt_bias"], setup["norm_w"], state,
+                    setup["conv_cache"])
+    torch.cuda.synchronize()
+    assert torch.equal(st0, state)

@@ -533,3 +533,52 @@ def test_decode_tokens_after_prefill_is_the_longer_prefill():
     assert np.array_equal(o[0], o_full[sl])
     assert np.array_equal(st2, fs_full)
     assert np.array_equal(cache2, co_full)
+
+
+# ------------------------------------------------ bf16 storage of the decode state
+
+def test_round_bf16_hand_values_and_ties():
+    one = 1.0
+    assert oracle.round_bf16(one + 2.0 ** -8) == 1.0                  # tie -> even (1.0)
+    assert oracle.round_bf16(one + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie -> even mantissa
+    assert oracle.round_bf16(one + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert oracle.round_bf16(-3.0) == -3.0 and oracle.round_bf16(0.0) == 0.0
+    assert oracle.round_bf16(0.1) == 0.10009765625                   # 0x3DCD
+    assert np.isinf(oracle.round_bf16(np.inf))
+
+
+def test_round_bf16_matches_the_fp32_to_bf16_conversion():
+    """For fp32 inputs (a single rounding either way) it is torch's RNE cast."""
+    import torch
+    rng = np.random.default_rng(44)
+    x = (rng.standard_normal(100_000) * np.exp(rng.uniform(-20, 20, 100_000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_bf16_state_step_keeps_a_frozen_state_bit_for_bit():
+    """beta = 0, alpha = 1: the stored (bf16-valued) state comes back unchanged."""
+    rng = np.random.default_rng(45)
+    t = _token_batch(rng, 2, 1)
+    st0 = oracle.round_bf16(t["state"])
+    _, st, _ = oracle.decode_step_bf16_state(
+        t["q"][:, 0], t["k"][:, 0], t["v"][:, 0], t["a"][:, 0], np.full_like(t["b"][:, 0], -np.inf),
+        t["z"][:, 0], t["conv_w"], np.full_like(t["A_log"], -np.inf), t["dt_bias"], t["norm_w"],
+        st0, t["cache"])
+    assert np.array_equal(st, st0)
+
+
+def test_bf16_state_step_is_the_exact_step_rounded():
+    """Same outputs and cache as the fp32-storage step; the state is its rounding, so
+    it lies within half a bf16 unit (2^-9 relative) of the exact one."""
+    rng = np.random.default_rng(46)
+    t = _token_batch(rng, 3, 1)
+    st0 = oracle.round_bf16(t["state"])
+    args = (t["q"][:, 0], t["k"][:, 0], t["v"][:, 0], t["a"][:, 0], t["b"][:, 0], t["z"][:, 0],
+            t["conv_w"], t["A_log"], t["dt_bias"], t["norm_w"], st0, t["cache"])
+    o1, s1, c1 = oracle.decode_step(*args)
+    o2, s2, c2 = oracle.decode_step_bf16_state(*args)
+    assert np.array_equal(o1, o2) and np.array_equal(c1, c2)
+    nz = s1 != 0
+    assert np.all(np.abs(s2[nz] - s1[nz]) <= np.abs(s1[nz]) * 2.0 ** -8)
+    assert not np.array_equal(s1, s2)  # the rounding is real
