@@ -14,6 +14,7 @@ choose to do):
   prefill bytes/token = 2*(2*Hk*D + 3*Hv*D) + 2*4*Hv   (+ initial and final state)
   decode bytes/step  = B*Hv*D*D*4*2 (state read + write) + B*33,024 (tokens)
                        + B*3*Cc*2*2 (conv cache read + write)
+  bf16-state decode  = the same with 2-byte state elements
   n-token step bytes = the same with n*B*33,024 token bytes (commit pass); a
                        verify pass (commit 0) reads the state and cache only
 Peaks: MI355X dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s.
@@ -47,9 +48,9 @@ def prefill_alg_bytes(T, N, Hk, Hv, D, act_bytes=2, init=True):
     return T * per_tok + states
 
 
-def decode_alg_bytes(B, Hk, Hv, D, act_bytes=2):
+def decode_alg_bytes(B, Hk, Hv, D, act_bytes=2, state_bytes=4):
     Cc = 2 * Hk * D + Hv * D
-    state = B * Hv * D * D * 4 * 2
+    state = B * Hv * D * D * state_bytes * 2
     tokens = B * (act_bytes * (2 * Hk * D + 3 * Hv * D) + 2 * 4 * Hv)
     cache = B * 3 * Cc * act_bytes * 2
     return state + tokens + cache
@@ -144,12 +145,15 @@ def bench_prefill(args, torch, gdn, S):
     return res
 
 
-def bench_decode(args, torch, gdn, S):
+def bench_decode(args, torch, gdn, S, state_bf16=False, toks=None):
     w = S.DECODE_B256
     steps = args.decode_steps
     setup = S.decode_setup(w, "cuda")
-    toks = S.decode_tokens(w, setup, steps, "cuda")
+    if toks is None:
+        toks = S.decode_tokens(w, setup, steps, "cuda")
     state, cache = setup["state"], setup["conv_cache"]
+    if state_bf16:  # reduced-precision storage of the same start state
+        state = state.to(torch.bfloat16)
     o = torch.empty((w.decode_batch, w.num_v_heads, w.head_dim), dtype=torch.bfloat16,
                     device="cuda")
 
@@ -170,7 +174,8 @@ def bench_decode(args, torch, gdn, S):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = e0.elapsed_time(e1)
-    nbytes = decode_alg_bytes(w.decode_batch, w.num_qk_heads, w.num_v_heads, w.head_dim)
+    nbytes = decode_alg_bytes(w.decode_batch, w.num_qk_heads, w.num_v_heads, w.head_dim,
+                              state_bytes=2 if state_bf16 else 4)
     return dict(steps=steps, wall_s=wall, ms_per_step=ev_ms / steps, bytes=nbytes,
                 w=w, setup=setup, toks=toks)
 
@@ -357,10 +362,19 @@ def main():
                               "traffic": stored_traffic("decode_bytes_per_launch"),
                               "alg_bytes_per_launch": dec["bytes"],
                               "launch_ms": dec["ms_per_step"]}}
+        # the same steps with the state stored in bf16 (fp32 arithmetic; its own tolerance)
+        d16 = bench_decode(args, torch, gdn, S, state_bf16=True, toks=dec["toks"])
+        t16 = d16["ms_per_step"] * 1e-3
+        g16 = d16["bytes"] / t16 / 1e9
+        dline["bf16_state"] = {
+            "value": 1.0 / t16, "unit": "steps/s", "ms_per_step": d16["ms_per_step"],
+            "roofline": {"bound": "hbm", "kernel": "decode_step (bf16 state)", "achieved": g16,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g16 / PEAK_HBM_GBS,
+                         "alg_bytes_per_launch": d16["bytes"], "launch_ms": d16["ms_per_step"]}}
         if args.only == "decode":
             line.update({"value": dline["value"], "unit": "steps/s",
                          "ms_per_step": dline["ms_per_step"], "config": dline["config"],
-                         "roofline": dline["roofline"]})
+                         "roofline": dline["roofline"], "bf16_state": dline["bf16_state"]})
         else:
             line["decode"] = dline
     if args.only in ("all", "tokens"):

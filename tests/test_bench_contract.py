@@ -22,6 +22,7 @@ def test_algorithmic_counts():
     assert bench.prefill_alg_bytes(1, 1, 16, 32, 128, init=False) - 32 * 128 * 128 * 4 == 33_024
     assert bench.prefill_alg_bytes(65536, 1, 16, 32, 128, init=True) == 65536 * 33_024 + 2 * 32 * 128 * 128 * 4
     assert bench.decode_alg_bytes(256, 16, 32, 128) == 1_107_361_792
+    assert bench.decode_alg_bytes(256, 16, 32, 128, state_bytes=2) == 1_107_361_792 - 256 * 32 * 128 * 128 * 4
     # the n-token step: one state read + write per call, n tokens per sequence
     assert bench.decode_tokens_alg_bytes(256, 1, 16, 32, 128) == 1_107_361_792
     assert bench.decode_tokens_alg_bytes(256, 4, 16, 32, 128) == 1_107_361_792 + 3 * 256 * 33_024
