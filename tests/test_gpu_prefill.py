@@ -297,3 +297,47 @@ def test_decode_after_prefill_matches_longer_prefill():
     o2 = torch.cat(outs)
     assert rel_l2(S.to_f64(o2), S.to_f64(o_all)) < O_TOL
     assert rel_l2(S.to_f64(st), S.to_f64(fs_all)) < STATE_TOL
+
+
+@gpu
+def test_delta_rule_write_reproduces_the_last_value():
+    """beta = 1 (b = +inf), alpha = 1 (A_log = -inf): the last write makes the state map the
+    last key to the last value, S_T k_T = v_T with the post-prologue k and v.
+
+    No decay is a stress regime: nothing damps the rounding of the bf16 MFMA operands, so
+    o and the state land near 4e-3 (an fp64 emulation of the same rounded products gives
+    4.7e-3 and 4.0e-3; no single product dominates).  The bar here is the stress bar of
+    the slow-decay test, 1e-2; a wrong write gives errors of order 1."""
+    w = S.scaled(S.PREFILL_4K, lengths=(200,), num_qk_heads=1, num_v_heads=2, seed=13,
+                 init_state_std=0.0)
+    d = S.prefill_inputs(w, "cuda")
+    d["b"] = torch.full_like(d["b"], float("inf"))
+    d["A_log"] = torch.full_like(d["A_log"], -float("inf"))
+    o, fs, _ = run_gpu(d)
+    o_ref, fs_ref, _, _ = run_oracle(d)
+    eo, es = rel_l2(S.to_f64(o), o_ref), rel_l2(S.to_f64(fs), fs_ref)
+    f = S.to_f64
+    wr = []
+    for h in range(2):
+        _, kk, vv = oracle.prologue(f(d["q"]), f(d["k"]), f(d["v"]), f(d["conv_w"]), h)
+        Sk = f(fs[0, h]).T @ kk[-1]  # stored H = S^T
+        wr.append(np.linalg.norm(Sk - vv[-1]) / np.linalg.norm(vv[-1]))
+        # the oracle's own state meets it to rounding (pinned on the CPU as P2)
+        assert np.linalg.norm(fs_ref[0, h].T @ kk[-1] - vv[-1]) <= 1e-6 * np.linalg.norm(vv[-1])
+    print(f"beta=1 alpha=1: o rel-L2 {eo:.3e} final-state rel-L2 {es:.3e}; "
+          f"|S k - v|/|v| {max(wr):.3e}")
+    assert eo < 1e-2 and es < 1e-2 and max(wr) < 1e-2
+
+
+@gpu
+def test_extreme_gates_stay_finite_and_match():
+    """alpha -> 0 on some heads (A_log = 100: e^g underflows), beta in {0, 1} on others
+    (b = -inf, +inf): no NaN, and o and the final state match the oracle."""
+    w = S.scaled(S.PREFILL_4K, lengths=(300,), num_qk_heads=2, num_v_heads=4, seed=14)
+    d = S.prefill_inputs(w, "cuda")
+    d["A_log"][0] = 100.0
+    d["b"][:, 1] = float("inf")
+    d["b"][:, 2] = -float("inf")
+    d["A_log"][3] = 100.0
+    d["b"][::7, 3] = -float("inf")
+    check_parity(d, tag="extreme gates")
