@@ -19,7 +19,8 @@
 //   K K^T and Q K^T take one fp16 pass on the unit-norm q and k (q_scale is
 //   applied to the products); W, T V, W H, Q H and M U take one bf16 pass; the
 //   state update K^T U takes split bf16 operands x = hi + lo (hi*hi + hi*lo +
-//   lo*hi) over the last two chunks of a sequence and one pass before them;
+//   lo*hi) over the last two chunks of a sequence and on chunks whose decay keeps
+//   more than 2^-8 of the state, one pass elsewhere;
 //   the identity part of T V (beta V, beta gamma K) and the diagonal of M U
 //   are applied in fp32.  The triangular inverse is formed per 16x16 diagonal
 //   block from fp16 products and merged with bf16 products.
@@ -897,8 +898,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       for (int kb = 0; kb < 2; ++kb)
         Uh[kb] = __builtin_bit_cast(u16x8, make_uint4(uh[4 * kb], uh[4 * kb + 1], uh[4 * kb + 2],
                                                       uh[4 * kb + 3]));
-      // the final state gets the split-precision update over its last two chunks
-      const bool precise = MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2));
+      // Split precision for the state update: on the last two chunks of a sequence (the
+      // final state) and on every chunk whose decay leaves more than 2^-8 of the state
+      // (nothing would damp the rounding of a one-pass update there; fast-decaying heads
+      // never take it).  gC is the same in every lane.
+      const bool slow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >=
+                        (1.0f / 256.0f);
+      const bool precise =
+          slow || (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2)));
       const TokLane tl(ln, lg);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)

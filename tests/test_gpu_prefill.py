@@ -127,9 +127,9 @@ def test_slow_decay_multi_segment(alog):
     o_ref, fs_ref, _, _ = run_oracle(d)
     eo, es = rel_l2(S.to_f64(o), o_ref), rel_l2(S.to_f64(fs), fs_ref)
     print(f"slow decay exp(A_log)={alog}: o rel-L2 {eo:.3e} final-state rel-L2 {es:.3e}")
-    # slow decay is a stress regime (the bars are set for the benchmark
-    # distributions); a broken map or combine would give errors of order 1
-    assert eo < 1e-2 and es < 1e-2
+    # slow decay takes the split-precision state update on every chunk (the chunk decay
+    # leaves more than 2^-8 of the state), which keeps it within the main bars
+    assert eo <= O_TOL and es <= STATE_TOL
 
 
 @gpu
