@@ -180,6 +180,40 @@ def bench_decode(args, torch, gdn, S, state_bf16=False, toks=None):
                 w=w, setup=setup, toks=toks)
 
 
+def bench_prefill_config(args, torch, gdn, S, w):
+    """Whole-call time of one of the other prefill workloads (T=4096; varlen N=64)."""
+    d = S.prefill_inputs(w, "cuda")
+    T = d["q"].shape[0]
+    N = d["cu_seqlens"].numel() - 1
+    Hk, Hv, D = w.num_qk_heads, w.num_v_heads, w.head_dim
+    out = torch.empty_like(d["v"])
+    fs = torch.empty((N, Hv, D, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        gdn.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["z"], d["conv_w"], d["A_log"],
+                    d["dt_bias"], d["norm_w"], init_state=d["init_state"],
+                    cu_seqlens=d["cu_seqlens"], out=out, final_state=fs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    reps = max(3, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = prefill_alg_flops_per_token(Hk, Hv, D) * T
+    nbytes = prefill_alg_bytes(T, N, Hk, Hv, D, init=d["init_state"] is not None)
+    del d, out, fs
+    return {"value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "calls": reps,
+            "config": {"workload": w.name, "num_seqs": N, "total_tokens": T},
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def decode_tokens_alg_bytes(B, n, Hk, Hv, D, act_bytes=2, commit=True):
     Cc = 2 * Hk * D + Hv * D
     rw = 2 if commit else 1
@@ -349,6 +383,9 @@ def main():
                 "alg_bytes": pre["bytes"], "per_kernel_ms": pre["per_kernel_ms"],
             },
         })
+        # the other prefill workloads (parity configs), tokens/s of the whole call
+        line["prefill_configs"] = {w.name: bench_prefill_config(args, torch, gdn, S, w)
+                                   for w in (S.PREFILL_4K, S.VARLEN_64)}
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, S)
         t = dec["ms_per_step"] * 1e-3
