@@ -35,10 +35,16 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-CHUNK = 64
+# The unit of prefill work is the chunk-64 WY/UT form's FLOP count per token
+# (5,242,880 at 16/32 heads, d = 128), fixed whatever chunk the kernel runs: the
+# kernel's 32-token chunks execute fewer intra-chunk products (the same formula at
+# C = 32 gives 4,194,304), so the MFMA fraction below is the token rate expressed
+# in that fixed unit, not a count of the products issued.
+ALG_CHUNK = 64
+KERNEL_CHUNK = 32
 
 
-def prefill_alg_flops_per_token(Hk, Hv, D, C=CHUNK):
+def prefill_alg_flops_per_token(Hk, Hv, D, C=ALG_CHUNK):
     return Hk * 4 * C * D + Hv * (6 * C * D + 6 * D * D)
 
 
@@ -367,13 +373,16 @@ def main():
             "ms_per_step": pre["ms_per_step"],
             "config": {"workload": "prefill_T65536_hk16_hv32_d128_bf16", "num_seqs": 1,
                        "seq_len": pre["T"], "num_qk_heads": 16, "num_v_heads": 32,
-                       "head_dim": 128, "chunk": CHUNK, "state": "fp32"},
+                       "head_dim": 128, "chunk": KERNEL_CHUNK, "state": "fp32"},
             "roofline": {
                 "bound": "mfma", "kernel": f"prefill {pre['dominant']} pass",
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS,
                 "traffic": stored_traffic("prefill_full_bytes_per_launch"),
                 "alg_flops_per_launch": pre["flops"],
+                # the same formula at the kernel's own chunk size (what its products amount to)
+                "chunk32_form_flops_per_launch":
+                    prefill_alg_flops_per_token(16, 32, 128, C=KERNEL_CHUNK) * pre["T"],
                 "launch_ms": pre["dominant_ms"],
             },
             "prefill_path": {

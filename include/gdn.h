@@ -80,7 +80,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_params *p, int32_t num_seqs,
 
 /* Chunked prefill of num_seqs packed sequences (the whole mixer; the state
  * update follows the model card's chunk form state*chunk_decay + key^T v_new,
- * with chunks of 64 tokens aligned to each sequence's start).
+ * with chunks of 32 tokens aligned to each sequence's start).
  *
  *   q, k          [T, Hk, D] act dtype        T = total_tokens
  *   v, z          [T, Hv, D] act dtype

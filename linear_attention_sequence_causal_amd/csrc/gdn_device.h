@@ -7,7 +7,7 @@
 namespace gdn {
 
 constexpr int kD = 128;     // head dim the kernels are built for
-constexpr int kChunk = 64;  // tokens per chunk of the prefill
+constexpr int kChunk = 32;  // tokens per chunk of the prefill
 
 typedef uint16_t bf16_t;  // storage of a bf16 value
 typedef float f32x4 __attribute__((ext_vector_type(4)));

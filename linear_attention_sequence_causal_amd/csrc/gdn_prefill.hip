@@ -1,6 +1,6 @@
 // gdn_prefill.hip -- chunked prefill of the Gated DeltaNet mixer on gfx950.
 //
-// Method (rows = tokens of one 64-token chunk, H = S^T [dk][dv] the state the
+// Method (rows = tokens of one 32-token chunk, H = S^T [dk][dv] the state the
 // chunk enters with, g = log alpha, G = chunk-local cumsum of g, gamma = e^G):
 //   L[i][j] = beta_i e^{G_i-G_j} (k_i . k_j)  (j < i)      T = (I + L)^-1
 //   W       = T diag(beta gamma) K                         Utilde = T diag(beta) V
@@ -19,18 +19,20 @@
 //   K K^T and Q K^T take one fp16 pass on the unit-norm q and k (q_scale is
 //   applied to the products); W, T V, W H, Q H and M U take one bf16 pass; the
 //   state update K^T U takes split bf16 operands x = hi + lo (hi*hi + hi*lo +
-//   lo*hi) over the last two chunks of a sequence and on chunks whose decay keeps
-//   more than 2^-8 of the state, one pass elsewhere;
+//   lo*hi) over the last 128 tokens of a sequence and on chunks whose decay keeps
+//   more than 2^-4 of the state (2^-8 per 64 tokens), one pass elsewhere;
 //   the identity part of T V (beta V, beta gamma K) and the diagonal of M U
 //   are applied in fp32.  The triangular inverse is formed per 16x16 diagonal
 //   block from fp16 products and merged with bf16 products.
 //
-// Work decomposition: one workgroup = 8 waves = one (segment, v head); wave w
-// owns value columns 16w..16w+15 of the state in MFMA accumulators.  Long
-// sequences are cut into segments: pass 1 computes each non-final segment's
-// affine map H -> A H + B (the same chunk loop run on the columns of A = I and
-// B = 0), pass 2 chains the maps into segment start states, pass 3 runs the
-// full chunk loop of every segment from its start state.
+// Work decomposition: one workgroup = 4 waves = one (segment, v head); wave w
+// owns value columns 32w..32w+31 of the state in MFMA accumulators, and two
+// workgroups share a compute unit (75-80 KB of LDS and <= 256 VGPRs each), so
+// one's VALU-bound prologue and epilogue overlap the other's LDS- and MFMA-bound
+// chain.  Long sequences are cut into segments: pass 1 computes each non-final
+// segment's affine map H -> A H + B (the same chunk loop run on the columns of
+// A = I and B = 0), pass 2 chains the maps into segment start states, pass 3
+// runs the full chunk loop of every segment from its start state.
 #include "gdn_device.h"
 #include "gdn_prefill_plan.h"
 
@@ -98,48 +100,54 @@ __device__ __forceinline__ u16x8 cat4(u16x4 x, u16x4 y) {
 }
 
 // --------------------------------------------------------------------- LDS
-constexpr int kThreads = 512;  // 8 waves
-constexpr int kWaves = 8;
-constexpr int kRowS = 136;     // bf16 row stride of [64 tok][128 d] tiles (272 B)
-constexpr int kTokS = 72;      // bf16 row stride of [128 d][64 tok] tiles (144 B)
-constexpr int kSqS = 68;       // bf16 row stride of [64][64] tiles (M, -L)
+// One workgroup = 4 waves; two workgroups share a compute unit (LDS <= 80 KB and
+// <= 256 VGPRs each), so one's VALU-heavy prologue/epilogue overlaps the other's
+// LDS- and MFMA-heavy chain.
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = 4;
+constexpr int kRowS = 136;     // bf16 row stride of [32 tok][128 d] tiles (272 B)
+constexpr int kTokS = 36;      // bf16 row stride of [128 d][32 tok] tiles (72 B)
+constexpr int kSqS = 36;       // bf16 row stride of [32][32] tiles (M, -L)
 
 constexpr int OFF_QH = 0;
-constexpr int OFF_QF = OFF_QH + 64 * kRowS * 2;  // fp16 unit-norm q (Q K^T)
-constexpr int OFF_KF = OFF_QF + 64 * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
-constexpr int OFF_MR = OFF_KF + 64 * kRowS * 2;  // M (written after the gram products)
-constexpr int OFF_KTH = OFF_MR + 64 * kRowS * 2;
+constexpr int OFF_QF = OFF_QH + kChunk * kRowS * 2;  // fp16 unit-norm q (Q K^T)
+constexpr int OFF_KF = OFF_QF + kChunk * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
+constexpr int OFF_M = OFF_KF + kChunk * kRowS * 2;   // bf16 [32][36] M with zero diagonal
+constexpr int OFF_KTH = OFF_M + kChunk * kSqS * 2;
 constexpr int OFF_KTL = OFF_KTH + 128 * kTokS * 2;
-constexpr int kVtS = 68;       // fp32 row stride of the [128 dv][64 tok] V^T tile (272 B)
+constexpr int kVtS = 36;       // fp32 row stride of the [128 dv][32 tok] V^T tile (144 B)
 constexpr int OFF_VT = OFF_KTL + 128 * kTokS * 2;
 constexpr int OFF_CONVW = OFF_VT + 128 * kVtS * 4;
 constexpr float kConvScale = -1.4426950408889634f;  // -log2(e), folded into the conv taps
 constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no bank conflicts)
-constexpr int OFF_BETA = OFF_CONVW + 48 * kConvGS * 4;
-constexpr int OFF_G = OFF_BETA + 64 * 4;
-constexpr int OFF_GAM = OFF_G + 64 * 4;          // e^{G_t}
-constexpr int OFF_BG = OFF_GAM + 64 * 4;         // beta_t e^{G_t}
-constexpr int OFF_DEC = OFF_BG + 64 * 4;         // e^{G_C - G_t}
-constexpr int OFF_BV = OFF_DEC + 64 * 4;         // beta_t / kConvScale (multiplies scaled v)
-constexpr int OFF_GAMQ = OFF_BV + 64 * 4;        // q_scale e^{G_t} (multiplies Q H)
-constexpr int OFF_MDIAG = OFF_GAMQ + 64 * 4;
-constexpr int OFF_NW = OFF_MDIAG + 64 * 4;       // fp32 [128] RMSNorm weight (1 if none)
-constexpr int OFF_CHG = OFF_NW + kD * 4;         // fp32 [128] per-chunk log-decay (map)
-// fp32 [64 tok][132] o tile for the epilogue, in the V^T region (dead after the
+// Per-token gate vectors of a chunk, two buffers (chunk parity): the next chunk's
+// are written while this chunk's are in use.  Vector k of a buffer starts at float
+// k * kChunk: beta, G (cumsum of g), gamma = e^G, beta gamma, e^{G_C - G},
+// beta / kConvScale (multiplies scaled v), q_scale gamma (multiplies Q H).
+enum { GB_BETA = 0, GB_G, GB_GAM, GB_BG, GB_DEC, GB_BV, GB_GAMQ, GB_N };
+constexpr int kGateN = GB_N * kChunk;                // floats per buffer
+constexpr int OFF_GATES = OFF_CONVW + 48 * kConvGS * 4;
+constexpr int OFF_MDIAG = OFF_GATES + 2 * kGateN * 4;
+constexpr int OFF_NW = OFF_MDIAG + kChunk * 4;       // fp32 [128] RMSNorm weight (1 if none)
+// -L and the diagonal blocks of T have their own regions, so the waves that form
+// them need not wait for the gram products of the others
+constexpr int kTdS = 24;                             // bf16 row stride of (T_bb - I) blocks
+constexpr int OFF_LO = OFF_NW + kD * 4;              // bf16 [32][36]  -L (strictly lower)
+constexpr int OFF_TD = OFF_LO + kChunk * kSqS * 2;   // bf16 [2][16][24] T_bb - I
+static_assert(OFF_TD % 16 == 0, "T_bb blocks must be 16-byte aligned");
+constexpr int kLdsBytes = OFF_TD + 2 * 16 * kTdS * 2;
+// fp32 [32 tok][132] o tile for the epilogue, in the V^T region (dead after the
 // right-hand side; the next chunk writes V^T only after its first barrier)
 constexpr int kOS = 132;
 constexpr int OFF_O = OFF_VT;
-static_assert(64 * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
-constexpr int kLdsBytes = OFF_CHG + 128 * 4;
-// regions reused after the gram products (Q-lo and K tiles are dead then)
-constexpr int kTdS = 24;                         // bf16 row stride of (T_bb - I) blocks
-constexpr int OFF_LO = OFF_QF;                   // bf16 [64][68]  -L (strictly lower)
-constexpr int OFF_TD = OFF_LO + 64 * kSqS * 2;   // bf16 [4][16][24] T_bb - I
-static_assert(OFF_TD % 16 == 0, "T_bb blocks must be 16-byte aligned");
-constexpr int OFF_M = OFF_MR;                    // bf16 [64][68]  M with zero diagonal
-constexpr int OFF_W = OFF_KF;                    // bf16 [64][136] -W
-static_assert(OFF_TD + 4 * 16 * kTdS * 2 <= OFF_KF, "solve tiles overflow the fp16 Q region");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kChunk * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
+// map mode's per-chunk log-decays (before the chunk loop), also in the V^T region
+constexpr int OFF_CHG = OFF_VT;
+constexpr int kMaxSegChunks = 256;                   // segments hold at most 8192 tokens
+static_assert(kMaxSegChunks * 4 <= 128 * kVtS * 4, "chunk sums overflow the V^T region");
+constexpr int OFF_W = OFF_KF;                        // bf16 [32][136] -W (K tile dead then)
+static_assert(2 * kLdsBytes <= 160 * 1024, "LDS budget of two workgroups per compute unit");
+static_assert(kChunk == 32, "the tile code below is written for 32-token chunks");
 
 enum Mode { kFull = 0, kMap = 1 };
 
@@ -251,47 +259,32 @@ __device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int
   return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
 }
 
-// bf16 [dk][tok] tiles (K^T hi/lo): groups of 8 tokens are XOR-swizzled with
-// bits 4..6 of the row (the fp32 V^T tile does the same with groups of 4).
-// The prologue writes rows 8 apart from neighbouring lanes (which would share
-// LDS banks unswizzled); the MFMA reads take rows 16*rt + lane, for which the
-// swizzle is the constant rt, so their offsets fold to immediates.
-__device__ __forceinline__ int tok_swz(int row, int tok) {
-  return row * kTokS + ((((tok >> 3) ^ (row >> 4)) & 7) << 3) + (tok & 7);
+// [row][tok] tiles over the chunk's 32 tokens (bf16 K^T hi/lo, fp32 V^T): the
+// eight 4-token groups of a row are XOR-swizzled with bits 4..6 of the row.  The
+// prologue writes rows 8 (K^T) or 16 (V^T) apart from neighbouring lanes, which
+// the swizzle spreads over all banks; the MFMA reads take rows 16*rt + lane, for
+// which the swizzle is the constant rt.
+__device__ __forceinline__ int tok_swz(int row, int tok, int stride) {
+  return row * stride + ((((tok >> 2) ^ (row >> 4)) & 7) << 2) + (tok & 3);
 }
-// Lane part of a read of tokens 16*tt + 4*lg .. +3 in row 16*rt + ln, for even
-// and odd rt; the rest is tok_rd_const(rt, tt).
+// Lane part of the K^T reads of rows 16*rt + ln, tokens 4lg..4lg+3 (half 0) and
+// 16+4lg..16+4lg+3 (half 1): with lg < 4 the swizzled group is (lg ^ (rt & 3))
+// plus a constant, so four lane bases cover every rt.
 struct TokLane {
-  int b0, d;  // lane base for even rt; odd rt adds d (the flipped low group bit)
+  int base[4];
   __device__ __forceinline__ TokLane(int ln, int lg) {
-    b0 = ln * kTokS + 4 * (lg & 1) + 8 * (lg >> 1);
-    d = 8 - 16 * (lg >> 1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) base[d] = ln * kTokS + 4 * (lg ^ d);
   }
-  __device__ __forceinline__ int operator()(int rt, int tt) const {
-    return b0 + (rt & 1) * d + 16 * rt * kTokS + 8 * (((2 * tt) ^ rt) & 6);
+  __device__ __forceinline__ int operator()(int rt, int half) const {
+    return base[rt & 3] + 16 * rt * kTokS + 4 * (half ? 4 - (rt & 4) : (rt & 4));
   }
 };
 // A operand of K^T U: rows 16rt + ln, tokens in the permuted k order of pack_b
-// (32kb + 4lg .. +3, then 32kb + 16 + 4lg .. +3)
-__device__ __forceinline__ u16x8 load_a_tok(const bf16_t *tile, const TokLane &tl, int rt,
-                                            int kb) {
-  return cat4(*reinterpret_cast<const u16x4 *>(tile + tl(rt, 2 * kb)),
-              *reinterpret_cast<const u16x4 *>(tile + tl(rt, 2 * kb + 1)));
-}
-
-// Lower 16x16 tiles (ti, tj), tj <= ti, of the chunk's 64x64 products: waves 0
-// and 1 take two off-diagonal tiles, waves 2 and 3 one, waves 4..7 the diagonal
-// tile wave - 4 (and that block's (I + L)^-1).
-__device__ __forceinline__ void gram_tile(int wave, int s, int &ti, int &tj) {
-  if (wave >= 4) {
-    ti = tj = wave - 4;
-  } else if (s == 1) {
-    ti = 3;
-    tj = wave;  // (3,0), (3,1)
-  } else {
-    ti = wave == 0 ? 1 : (wave == 3 ? 3 : 2);  // (1,0), (2,0), (2,1), (3,2)
-    tj = wave == 3 ? 2 : (wave == 2 ? 1 : 0);
-  }
+// (4lg .. +3, then 16 + 4lg .. +3)
+__device__ __forceinline__ u16x8 load_a_tok(const bf16_t *tile, const TokLane &tl, int rt) {
+  return cat4(*reinterpret_cast<const u16x4 *>(tile + tl(rt, 0)),
+              *reinterpret_cast<const u16x4 *>(tile + tl(rt, 1)));
 }
 
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -335,7 +328,7 @@ __device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4 &mc, const f32
 // segment's affine map; blockIdx selects the A half (state columns of the
 // identity) or the B half (columns of zero with the values written in).
 template <typename T, int MODE>
-__global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
+__global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int tid = threadIdx.x;
   int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -380,13 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   bf16_t *const sKTl = reinterpret_cast<bf16_t *>(smem + OFF_KTL);
   float *const sVT = reinterpret_cast<float *>(smem + OFF_VT);
   float *const sConvW = reinterpret_cast<float *>(smem + OFF_CONVW);
-  float *const sBeta = reinterpret_cast<float *>(smem + OFF_BETA);
-  float *const sG = reinterpret_cast<float *>(smem + OFF_G);
-  float *const sGam = reinterpret_cast<float *>(smem + OFF_GAM);
-  float *const sBG = reinterpret_cast<float *>(smem + OFF_BG);
-  float *const sDec = reinterpret_cast<float *>(smem + OFF_DEC);
-  float *const sBv = reinterpret_cast<float *>(smem + OFF_BV);
-  float *const sGamQ = reinterpret_cast<float *>(smem + OFF_GAMQ);
+  float *const sGates = reinterpret_cast<float *>(smem + OFF_GATES);
   float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
   float *const sNW = reinterpret_cast<float *>(smem + OFF_NW);
   float *const sO = reinterpret_cast<float *>(smem + OFF_O);
@@ -396,14 +383,14 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + OFF_W);
 
   // ---- roles of the prologue ----------------------------------------------------
-  // Before the first barrier every wave convolves q (waves 0-3) or k (waves 4-7):
+  // Before the first barrier every wave convolves q (waves 0-1) or k (waves 2-3):
   // 4 tokens x 8 channels per thread, the 16 lanes of a token row spanning its
   // 128 channels (for the L2 norm).  After it every thread convolves 4 tokens x
   // 4 channels of v, which only the right-hand side (after barrier 3) reads.
   // Map mode needs no q (and no v for the A half).
-  const int role = wave < 4 ? 0 : 1;   // uniform per wave
+  const int role = wave < 2 ? 0 : 1;   // uniform per wave
   int cg = tid & 15;                   // q/k channels 8cg .. 8cg+7
-  int tbase = ((tid & 255) >> 4) * 4;  // q/k tokens tbase .. tbase+3
+  int tbase = ((tid & 127) >> 4) * 4;  // q/k tokens tbase .. tbase+3
   // v channels 4cv .. 4cv+3; cv rotates the 5 lane bits so that the 8 lanes of one
   // 16-byte LDS write cycle take cv values 4 apart: their V^T rows 4cv + cc lie in
   // 8 different 16-row blocks, which the tile's swizzle spreads over all banks
@@ -492,27 +479,63 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   };
 
   // ---- state accumulators ---------------------------------------------------------
-  // Hacc[dt]: rows (dk) 16dt + 4lg + i, column (dv) 16*wave + ln.
-  f32x4 Hacc[8];
+  // Hacc[dt][ct]: rows (dk) 16dt + 4lg + i, column (dv) 32*wave + 16ct + ln.
+  f32x4 Hacc[8][2];
   {
     const float *H0 = nullptr;
     if (MODE == kFull) {
-      if (seg.nseg > 1) H0 = P.starts + ((int64_t)segi * Hv + h) * kD * kD;
-      else if (P.init_state) H0 = P.init_state + ((int64_t)seg.seq * Hv + h) * kD * kD;
+      if (seg.idx > 0) {
+        // start state after the previous segment: its B map itself when that
+        // segment's A map is zero, else what the combine pass wrote
+        const int64_t m = P.segs[segi - 1].map;
+        H0 = P.map_zero[m * Hv + h] ? P.maps + ((m * Hv + h) * 2 + 1) * kD * kD
+                                    : P.starts + ((int64_t)segi * Hv + h) * kD * kD;
+      } else if (P.init_state) {
+        H0 = P.init_state + ((int64_t)seg.seq * Hv + h) * kD * kD;
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * dt + 4 * lg + i, col = 16 * wave + ln;
-        float x = 0.f;
-        if (MODE == kFull) x = H0 ? H0[row * kD + col] : 0.f;
-        else if (half == 0) x = row == col ? 1.f : 0.f;
-        Hacc[dt][i] = x;
-      }
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * dt + 4 * lg + i, col = 32 * wave + 16 * ct + ln;
+          float x = 0.f;
+          if (MODE == kFull) x = H0 ? H0[row * kD + col] : 0.f;
+          else if (half == 0) x = row == col ? 1.f : 0.f;
+          Hacc[dt][ct][i] = x;
+        }
   }
 
   const float A_log_h = P.A_log[h], dt_bias_h = P.dt_bias[h];
+  // Gates of one chunk, computed by wave 3 one chunk ahead (where it has slack):
+  // inputs of token `lane` of the chunk starting at t0g, then the gate vectors of
+  // its nv tokens (tokens past nv get g = 0, beta = 0) into buffer gbuf.
+  auto load_gates = [&](int t0g, float &ga, float &gb) {
+    const int tc = min(t0g + lane, seg_end - 1);
+    ga = P.a[(int64_t)tc * Hv + h];
+    gb = P.b[(int64_t)tc * Hv + h];
+  };
+  auto write_gates = [&](float *gbuf, int nv, float ga, float gb) {
+    float g = 0.f, be = 0.f;
+    if (lane < nv) {
+      g = log_decay_fast(ga, A_log_h, dt_bias_h);
+      be = sigmoid_fast(gb);
+    }
+    g = wave_inclusive_sum(g);  // G: inclusive cumsum of g
+    const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
+    if (lane < kChunk) {
+      const float gam = __expf(g);
+      gbuf[GB_BETA * kChunk + lane] = be;
+      gbuf[GB_G * kChunk + lane] = g;
+      gbuf[GB_GAM * kChunk + lane] = gam;
+      gbuf[GB_BG * kChunk + lane] = be * gam;
+      gbuf[GB_DEC * kChunk + lane] = __expf(GC - g);
+      gbuf[GB_BV * kChunk + lane] = be * (1.0f / kConvScale);
+      gbuf[GB_GAMQ * kChunk + lane] = gam * P.q_scale;
+    }
+  };
   if (MODE == kFull && tid < kD) sNW[tid] = P.norm_w ? P.norm_w[tid] : 1.0f;
   const int nchunks = (seg.len + kChunk - 1) / kChunk;
   const bool last_seg = seg.idx == seg.nseg - 1;
@@ -525,7 +548,7 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
   // B map starts at the last such chunk, and the A map is zero if S_0 is.
   int c_begin = 0;
   if (MODE == kMap) {
-    // Chunk sums of g from the segment end, eight chunks (one per wave) at a time,
+    // Chunk sums of g from the segment end, four chunks (one per wave) at a time,
     // until the suffix sum S reaches the threshold.  g <= 0, so the first chunk
     // where it does is the truncation point of the B map, and then the whole
     // segment's sum is below the threshold too: the A map is zero.  Only if no
@@ -538,7 +561,8 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
       const int cc = top - wave;
       if (cc >= 0) {  // chunk sum, fixed order
         const int tau = seg.begin + cc * kChunk + lane;
-        float g = tau < seg_end ? log_decay(P.a[(int64_t)tau * Hv + h], A_log_h, dt_bias_h) : 0.f;
+        float g = (lane < kChunk && tau < seg_end)
+                      ? log_decay(P.a[(int64_t)tau * Hv + h], A_log_h, dt_bias_h) : 0.f;
         g = wave_sum(g);
         if (lane == 0) sChG[cc] = g;
       }
@@ -561,21 +585,31 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
   }
   if (nchunks > 0) load_chunk(seg.begin + c_begin * kChunk);
-  __syncthreads();  // conv weights
+  if (wave == 3 && c_begin < nchunks) {  // the first chunk's gates
+    float ga, gb;
+    load_gates(seg.begin + c_begin * kChunk, ga, gb);
+    write_gates(sGates + (c_begin & 1) * kGateN, min(kChunk, seg_end - seg.begin - c_begin * kChunk),
+                ga, gb);
+  }
+  __syncthreads();  // conv weights, first gates
 
   for (int c = c_begin; c < nchunks; ++c) {
     refresh();
     const int t0 = seg.begin + c * kChunk;
     const int nvalid = min(kChunk, seg_end - t0);
 
-    // ================= prologue: conv + SiLU (+ L2), gates -> LDS ================
-    // gate inputs of token `lane` (wave 1), issued first and consumed last
+    // this chunk's gate vectors (written one chunk ahead)
+    const float *const gcur = sGates + (c & 1) * kGateN;
+    const float *const sBeta = gcur + GB_BETA * kChunk, *const sG = gcur + GB_G * kChunk;
+    const float *const sGam = gcur + GB_GAM * kChunk, *const sBG = gcur + GB_BG * kChunk;
+    const float *const sDec = gcur + GB_DEC * kChunk, *const sBv = gcur + GB_BV * kChunk;
+    const float *const sGamQ = gcur + GB_GAMQ * kChunk;
+    // the next chunk's gate inputs (wave 3), issued first and consumed after barrier 2
     float ga = 0.f, gb = 0.f;
-    if (wave == 1) {
-      const int tc = min(t0 + lane, seg_end - 1);
-      ga = P.a[(int64_t)tc * Hv + h];
-      gb = P.b[(int64_t)tc * Hv + h];
-    }
+    const bool gates_next = wave == 3 && c + 1 < nchunks;
+    if (gates_next) load_gates(t0 + kChunk, ga, gb);
+
+    // ================= prologue: conv + SiLU (+ L2) -> LDS ========================
     if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
       for (int rr = 0; rr < 7; ++rr) {
@@ -634,9 +668,9 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
           *reinterpret_cast<uint4 *>(sKf + (tbase + r) * kRowS + cg * 8) =
               make_uint4(fw[0], fw[1], fw[2], fw[3]);
         }
-        // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes
-        // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
-        const int swz = ((((tbase >> 3) ^ (cg >> 1)) & 7) << 3) + (tbase & 7);
+        // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes (4 tokens) per
+        // row; rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
+        const int swz = (((tbase >> 2) ^ (cg >> 1)) & 7) << 2;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
           // tokens (2p, 2p+1) of channel cc: half (cc & 1) of word cc/2 of tokens 2p, 2p+1
@@ -651,23 +685,6 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
                          __builtin_amdgcn_perm(lw[3][e], lw[2][e], sel));
         }
       }
-    }
-    if (wave == 1) {  // gates of token `lane`, inclusive cumsum of g
-      float g = 0.f, be = 0.f;
-      if (lane < nvalid) {
-        g = log_decay_fast(ga, A_log_h, dt_bias_h);
-        be = sigmoid_fast(gb);
-      }
-      g = wave_inclusive_sum(g);
-      const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
-      const float gam = __expf(g);
-      sBeta[lane] = be;
-      sG[lane] = g;
-      sGam[lane] = gam;
-      sBG[lane] = be * gam;
-      sDec[lane] = __expf(GC - g);
-      sBv[lane] = be * (1.0f / kConvScale);
-      sGamQ[lane] = gam * P.q_scale;
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
@@ -700,262 +717,271 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
     }
 
     // ================= gram products K K^T (and Q K^T) =========================
-    f32x4 kk[2], qk[2];
-    const int ntiles = wave < 2 ? 2 : 1;
+    // lower 16x16 tiles of the 32x32 products: wave 0 (0,0), wave 1 (1,1), wave 2
+    // (1,0); the diagonal-tile waves also form that block's (I + L)^-1
+    const bool gram_on = wave < 3;
+    const int ti = wave == 0 ? 0 : 1, tj = wave == 1 ? 1 : 0;
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+    if (gram_on) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      kk[s] = f32x4{0, 0, 0, 0};
-      qk[s] = f32x4{0, 0, 0, 0};
-      if (s < ntiles) {
-        int ti, tj;
-        gram_tile(wave, s, ti, tj);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int col = 32 * kb + 8 * lg;
-          const u16x8 bk = *reinterpret_cast<const u16x8 *>(sKf + (16 * tj + ln) * kRowS + col);
-          const u16x8 ak = *reinterpret_cast<const u16x8 *>(sKf + (16 * ti + ln) * kRowS + col);
-          kk[s] = mfma16h(ak, bk, kk[s]);
-          if (MODE == kFull) {
-            const u16x8 aq = *reinterpret_cast<const u16x8 *>(sQf + (16 * ti + ln) * kRowS + col);
-            qk[s] = mfma16h(aq, bk, qk[s]);
-          }
+      for (int kb = 0; kb < 4; ++kb) {
+        const int col = 32 * kb + 8 * lg;
+        const u16x8 bk = *reinterpret_cast<const u16x8 *>(sKf + (16 * tj + ln) * kRowS + col);
+        const u16x8 ak = *reinterpret_cast<const u16x8 *>(sKf + (16 * ti + ln) * kRowS + col);
+        kk = mfma16h(ak, bk, kk);
+        if (MODE == kFull) {
+          const u16x8 aq = *reinterpret_cast<const u16x8 *>(sQf + (16 * ti + ln) * kRowS + col);
+          qk = mfma16h(aq, bk, qk);
         }
       }
     }
-    __syncthreads();  // (2) Q-lo and K tiles consumed: L, M overwrite them
-    refresh();
-    // L, M tiles to LDS; the diagonal-tile waves form (I + L_bb)^-1 - I
+    // L, M tiles to LDS; the diagonal-tile waves form (I + L_bb)^-1 - I.  The gates
+    // were written a chunk ahead, -L, T_bb - I and M have regions of their own: no
+    // barrier after the gram products
+    if (gram_on) {
+      const int cj = 16 * tj + ln;
+      const float Gj = sG[cj];
+      const f32x4 Gr = *reinterpret_cast<const f32x4 *>(sG + 16 * ti + 4 * lg);
+      const f32x4 Br = *reinterpret_cast<const f32x4 *>(sBeta + 16 * ti + 4 * lg);
+      float l[4], d[4];  // L and the decay e^{G_i - G_j} (j < i; 0 and 1 elsewhere)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < ntiles) {
-        int ti, tj;
-        gram_tile(wave, s, ti, tj);
-        const bool diag = s == 0 && ti == tj;  // the second tile is never diagonal
-        const int cj = 16 * tj + ln;
-        const float Gj = sG[cj];
-        const f32x4 Gr = *reinterpret_cast<const f32x4 *>(sG + 16 * ti + 4 * lg);
-        const f32x4 Br = *reinterpret_cast<const f32x4 *>(sBeta + 16 * ti + 4 * lg);
-        f32x4 mc, mt;  // diagonal tile: C-layout tiles of -L^T and -L
+      for (int i = 0; i < 4; ++i) {
+        const bool low = cj < 16 * ti + 4 * lg + i;
+        d[i] = __expf(low ? Gr[i] - Gj : 0.f);
+        l[i] = low ? Br[i] * d[i] * kk[i] : 0.f;
+      }
+      if (MODE == kFull) {  // M with zero diagonal and upper part
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int ri = 16 * ti + 4 * lg + i;
-          const float Gi = Gr[i];
-          const bool low = cj < ri;
-          const float d = __expf(low ? Gi - Gj : 0.f);
-          const float l = low ? Br[i] * d * kk[s][i] : 0.f;
-          if (diag) {
-            const bool up = ri < cj;
-            const float du = __expf(up ? Gj - Gi : 0.f);
-            mt[i] = -l;
-            mc[i] = up ? -(sBeta[cj] * du * kk[s][i]) : 0.f;
-          } else {
-            sLo[ri * kSqS + cj] = f2bf(-l);
-          }
-          if (MODE == kFull) {
-            const float qkq = qk[s][i] * P.q_scale;
-            sM[ri * kSqS + cj] = f2bf(low ? d * qkq : 0.f);
-            if (cj == ri) sMdiag[ri] = qkq;
-          }
-        }
-        if (diag) {
-          const f32x4 tt = unit_lower_inverse_t(mc, mt, ln, lg);  // row ln of T, cols 4lg..
-          float e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = tt[i] - (4 * lg + i == ln ? 1.0f : 0.0f);
-          *reinterpret_cast<uint2 *>(sTd + (16 * ti + ln) * kTdS + 4 * lg) =
-              make_uint2(pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]));
+          const bool low = cj < 16 * ti + 4 * lg + i;
+          sM[(16 * ti + 4 * lg + i) * kSqS + cj] = f2bf(low ? d[i] * (qk[i] * P.q_scale) : 0.f);
         }
       }
-    }
-    if (MODE == kFull && wave < 2) {  // zero upper tiles (0,1) and (2,3) of M read by M U
-      const int ti = wave == 0 ? 0 : 2;
+      if (ti != tj) {  // wave 2: the off-diagonal block of -L
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sM[(16 * ti + 4 * lg + i) * kSqS + 16 * (ti + 1) + ln] = 0;
+        for (int i = 0; i < 4; ++i) sLo[(16 * ti + 4 * lg + i) * kSqS + cj] = f2bf(-l[i]);
+      } else {
+        // diagonal block: M's diagonal (fp32) and (I + L_bb)^-1 - I from the C-layout
+        // tiles of -L^T (mc) and -L (mt)
+        if (MODE == kFull) {
+          const int di = ln - 4 * lg;  // the lane's diagonal element, if any
+          if (di >= 0 && di < 4) {
+            const float qd = di == 0 ? qk[0] : (di == 1 ? qk[1] : (di == 2 ? qk[2] : qk[3]));
+            sMdiag[cj] = qd * P.q_scale;
+          }
+        }
+        const float Bj = sBeta[cj];
+        f32x4 mc, mt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool up = 16 * ti + 4 * lg + i < cj;
+          const float du = __expf(up ? Gj - Gr[i] : 0.f);
+          mt[i] = -l[i];
+          mc[i] = up ? -(Bj * du * kk[i]) : 0.f;
+        }
+        const f32x4 tt = unit_lower_inverse_t(mc, mt, ln, lg);  // row ln of T, cols 4lg..
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = tt[i] - (4 * lg + i == ln ? 1.0f : 0.0f);
+        *reinterpret_cast<uint2 *>(sTd + (16 * ti + ln) * kTdS + 4 * lg) =
+            make_uint2(pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]));
+      }
     }
-    // next chunk's raw rows: the q waves, which have slack here, go first so that the
-    // k waves' loads after the barrier do not queue behind theirs
-    if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);
-    __syncthreads();  // (3) -L, M and T_bb - I ready
+    if (MODE == kFull && wave == 3) {  // zero the upper tile (0,1) of M read by M U
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sM[(4 * lg + i) * kSqS + 16 + ln] = 0;
+    }
+    // the next chunk's gates (wave 3, which has no diagonal tile)
+    if (gates_next)
+      write_gates(sGates + ((c + 1) & 1) * kGateN, min(kChunk, seg_end - t0 - kChunk), ga, gb);
+    // next chunk's raw rows: the k waves (off the diagonal tiles) go first so that
+    // the q waves' loads after the barrier do not queue behind theirs
+    if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);
+    __syncthreads();  // (3) -L, M, T_bb - I and the next gates ready; Q and K consumed
     refresh();
+    if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
 
-    // ================= Q H, right-hand sides of the triangular solves =============
-    if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
-    // H as bf16 B operands: Hb[kb] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb+16+4lg+j-4
-    u16x8 Hb[4];
+    // ================= right-hand sides and the triangular solves =================
+    // fp32 right-hand sides beta V and beta gamma K of this wave's columns
+    f32x4 Uacc[2][2], Wacc[2][2];  // [row tile of 16 tokens][column tile]
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Hb[kb] = pack_b(Hacc[2 * kb], Hacc[2 * kb + 1]);
-    f32x4 Oacc[4], Uacc[4], Wacc[4];
-    int dvc = 16 * wave + ln;  // this lane's value column (and dk column of W)
+    for (int rt = 0; rt < 2; ++rt) {
+      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
+      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * rt + 4 * lg);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Oacc[mt] = f32x4{0, 0, 0, 0};
-      if (MODE == kFull) {
+      for (int ct = 0; ct < 2; ++ct) {
+        const int dcol = 32 * wave + 16 * ct + ln;
+        const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
+        const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
+        const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
+        f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+        if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const u16x8 aq = load_a_perm(sQh + (16 * mt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
-          Oacc[mt] = mfma16(aq, Hb[kb], Oacc[mt]);
+        for (int i = 0; i < 4; ++i) {
+          Uacc[rt][ct][i] = be[i] * vv[i];
+          Wacc[rt][ct][i] = bg[i] * (bf2f(kh[i]) + bf2f(kl[i]));
         }
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGamQ + 16 * mt + 4 * lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Oacc[mt][i] *= gm[i];
-      }
-      // right-hand sides of the two triangular solves, fp32: beta V and beta gamma K
-      const int toff = tok_swz(dvc, 16 * mt + 4 * lg);
-      const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
-      const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
-      f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-      if (withV)  // row dvc, 4-token group 4mt + lg swizzled with row >> 4 = wave
-        vv = *reinterpret_cast<const f32x4 *>(sVT + dvc * kVtS + (((4 * mt + lg) ^ (wave & 7)) << 2));
-      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * mt + 4 * lg);
-      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * mt + 4 * lg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Uacc[mt][i] = be[i] * vv[i];
-        Wacc[mt][i] = bg[i] * (bf2f(kh[i]) + bf2f(kl[i]));
       }
     }
-
-    // ===== block forward substitution (I + L) X = R for W (dk tile = wave) and Utilde =====
-    //   X_i = (I + (T_ii - I)) (R_i - sum_{j<i} L_ij X_j), row blocks of 16 tokens
+    // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
+    //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
     {
+      const u16x8 at0 = load_a_perm_half(sTd + ln * kTdS, 0, lg);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16_t *lrow = sLo + (16 * i + ln) * kSqS;
-        if (i == 1) {
-          const u16x8 a = load_a_perm_half(lrow, 0, lg);
-          Wacc[1] = mfma16(a, pack_b_half(Wacc[0]), Wacc[1]);
-          if (withV) Uacc[1] = mfma16(a, pack_b_half(Uacc[0]), Uacc[1]);
-        } else if (i == 2) {
-          const u16x8 a = load_a_perm(lrow, 0, 16, lg);
-          Wacc[2] = mfma16(a, pack_b(Wacc[0], Wacc[1]), Wacc[2]);
-          if (withV) Uacc[2] = mfma16(a, pack_b(Uacc[0], Uacc[1]), Uacc[2]);
-        } else if (i == 3) {
-          const u16x8 a01 = load_a_perm(lrow, 0, 16, lg);
-          const u16x8 a2 = load_a_perm_half(lrow, 32, lg);
-          Wacc[3] = mfma16(a01, pack_b(Wacc[0], Wacc[1]), Wacc[3]);
-          Wacc[3] = mfma16(a2, pack_b_half(Wacc[2]), Wacc[3]);
-          if (withV) {
-            Uacc[3] = mfma16(a01, pack_b(Uacc[0], Uacc[1]), Uacc[3]);
-            Uacc[3] = mfma16(a2, pack_b_half(Uacc[2]), Uacc[3]);
-          }
-        }
-        const u16x8 at = load_a_perm_half(sTd + (i * 16 + ln) * kTdS, 0, lg);
-        Wacc[i] = mfma16(at, pack_b_half(Wacc[i]), Wacc[i]);
-        if (withV) Uacc[i] = mfma16(at, pack_b_half(Uacc[i]), Uacc[i]);
+      for (int ct = 0; ct < 2; ++ct) {
+        Wacc[0][ct] = mfma16(at0, pack_b_half(Wacc[0][ct]), Wacc[0][ct]);
+        if (withV) Uacc[0][ct] = mfma16(at0, pack_b_half(Uacc[0][ct]), Uacc[0][ct]);
+      }
+      const u16x8 a10 = load_a_perm_half(sLo + (16 + ln) * kSqS, 0, lg);  // -L_10
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        Wacc[1][ct] = mfma16(a10, pack_b_half(Wacc[0][ct]), Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mfma16(a10, pack_b_half(Uacc[0][ct]), Uacc[1][ct]);
+      }
+      const u16x8 at1 = load_a_perm_half(sTd + (16 + ln) * kTdS, 0, lg);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        Wacc[1][ct] = mfma16(at1, pack_b_half(Wacc[1][ct]), Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mfma16(at1, pack_b_half(Uacc[1][ct]), Uacc[1][ct]);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * kRowS + dvc] = f2bf(-Wacc[mt][i]);
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sW[(16 * rt + 4 * lg + i) * kRowS + 32 * wave + 16 * ct + ln] = f2bf(-Wacc[rt][ct][i]);
     }
     __syncthreads();  // (4) -W ready
     refresh();
-    dvc = 16 * wave + ln;
 
-    // ================= chain: U = Utilde - W H; O += M U; H update ===============
-    {  // k-block outer, row tiles inner: four independent accumulators in flight
-      u16x8 aw[2][4];
+    // ================= Q H, U = Utilde - W H, O += M U, H update ==================
+    // H as bf16 B operands: Hb[kb][ct] slots 8lg+j <-> dk 32kb + 4lg + j (j<4),
+    // 32kb + 16 + 4lg + j - 4 (j >= 4)
+    f32x4 Oacc[2][2];
+    {
+      u16x8 Hb[4][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) aw[0][mt] = load_a_perm(sW + (16 * mt + ln) * kRowS, 0, 16, lg);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Hb[kb][ct] = pack_b(Hacc[2 * kb][ct], Hacc[2 * kb + 1][ct]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Oacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // k-block outer: four independent accumulators per product and block
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            aw[(kb + 1) & 1][mt] = load_a_perm(sW + (16 * mt + ln) * kRowS, 32 * (kb + 1),
-                                               32 * (kb + 1) + 16, lg);
+        for (int rt = 0; rt < 2; ++rt) {
+          const u16x8 aw = load_a_perm(sW + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) Uacc[rt][ct] = mfma16(aw, Hb[kb][ct], Uacc[rt][ct]);
+          if (MODE == kFull) {
+            const u16x8 aq = load_a_perm(sQh + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) Oacc[rt][ct] = mfma16(aq, Hb[kb][ct], Oacc[rt][ct]);
+          }
         }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) Uacc[mt] = mfma16(aw[kb & 1][mt], Hb[kb], Uacc[mt]);
       }
     }
     if (MODE == kFull) {
-      const u16x8 Ub0 = pack_b(Uacc[0], Uacc[1]), Ub1 = pack_b(Uacc[2], Uacc[3]);
+      u16x8 Ub[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16_t *mrow = sM + (16 * mt + ln) * kSqS;
-        Oacc[mt] = mfma16(load_a_perm(mrow, 0, 16, lg), Ub0, Oacc[mt]);
-        if (mt >= 2) Oacc[mt] = mfma16(load_a_perm(mrow, 32, 48, lg), Ub1, Oacc[mt]);
+      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_b(Uacc[0][ct], Uacc[1][ct]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Oacc[mt][i] += sMdiag[16 * mt + 4 * lg + i] * Uacc[mt][i];
+      for (int rt = 0; rt < 2; ++rt) {
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGamQ + 16 * rt + 4 * lg);
+        const f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
+        const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Oacc[rt][ct][i] = fmaf(md[i], Uacc[rt][ct][i], Oacc[rt][ct][i] * gm[i]);
+          Oacc[rt][ct] = mfma16(am, Ub[ct], Oacc[rt][ct]);
+        }
       }
     }
     // state update H = gamma_C H + K^T diag(e^{G_C - G}) U
     {
-      const float gC = sGam[63];
-      float u[4][4];
-      uint32_t uh[8];
+      const float gC = sGam[kChunk - 1];
+      float u[2][2][4];
+      uint32_t uh[2][4];  // [ct]: tokens 4lg.. of row tile 0, then of row tile 1
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * mt + 4 * lg);
+      for (int rt = 0; rt < 2; ++rt) {
+        const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * rt + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[mt][i] = Uacc[mt][i] * dec[i];
-        uh[2 * mt] = pk_bf16(u[mt][0], u[mt][1]);
-        uh[2 * mt + 1] = pk_bf16(u[mt][2], u[mt][3]);
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[rt][ct][i] = Uacc[rt][ct][i] * dec[i];
+          uh[ct][2 * rt] = pk_bf16(u[rt][ct][0], u[rt][ct][1]);
+          uh[ct][2 * rt + 1] = pk_bf16(u[rt][ct][2], u[rt][ct][3]);
+        }
       }
       u16x8 Uh[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        Uh[kb] = __builtin_bit_cast(u16x8, make_uint4(uh[4 * kb], uh[4 * kb + 1], uh[4 * kb + 2],
-                                                      uh[4 * kb + 3]));
-      // Split precision for the state update: on the last two chunks of a sequence (the
-      // final state) and on every chunk whose decay leaves more than 2^-8 of the state
-      // (nothing would damp the rounding of a one-pass update there; fast-decaying heads
-      // never take it).  gC is the same in every lane.
+      for (int ct = 0; ct < 2; ++ct)
+        Uh[ct] = __builtin_bit_cast(u16x8, make_uint4(uh[ct][0], uh[ct][1], uh[ct][2], uh[ct][3]));
+      // Split precision for the state update: on a sequence's last 128 tokens (the
+      // final state) and on every chunk whose decay leaves more than 2^-4 of the
+      // state (nothing would damp the rounding of a one-pass update there;
+      // fast-decaying heads never take it).  gC is the same in every lane.
       const bool slow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >=
-                        (1.0f / 256.0f);
+                        (1.0f / 16.0f);
       const bool precise =
-          slow || (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 2)));
+          slow || (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 4)));
       const TokLane tl(ln, lg);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Hacc[dt][i] *= gC;
-      if (!precise) {  // k-block outer, eight independent accumulators per block
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          u16x8 ak[8];
+          for (int i = 0; i < 4; ++i) Hacc[dt][ct][i] *= gC;
+      if (!precise) {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            ak[dt] = load_a_tok(sKTh, tl, dt, kb);
+        for (int dt = 0; dt < 8; ++dt) {
+          const u16x8 ak = load_a_tok(sKTh, tl, dt);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) Hacc[dt] = mfma16(ak[dt], Uh[kb], Hacc[dt]);
+          for (int ct = 0; ct < 2; ++ct) Hacc[dt][ct] = mfma16(ak, Uh[ct], Hacc[dt][ct]);
         }
       } else {
         // lo parts of U: u - bf16(u)
         u16x8 Ul[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int ct = 0; ct < 2; ++ct) {
           uint32_t ul[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int mt = 2 * kb + (q >> 1), i0 = 2 * (q & 1);
-            const uint32_t hw = uh[4 * kb + q];
-            ul[q] = pk_bf16(u[mt][i0] - __uint_as_float(hw << 16),
-                            u[mt][i0 + 1] - __uint_as_float(hw & 0xFFFF0000u));
+            const int rt = q >> 1, i0 = 2 * (q & 1);
+            const uint32_t hw = uh[ct][q];
+            ul[q] = pk_bf16(u[rt][ct][i0] - __uint_as_float(hw << 16),
+                            u[rt][ct][i0 + 1] - __uint_as_float(hw & 0xFFFF0000u));
           }
-          Ul[kb] = __builtin_bit_cast(u16x8, make_uint4(ul[0], ul[1], ul[2], ul[3]));
+          Ul[ct] = __builtin_bit_cast(u16x8, make_uint4(ul[0], ul[1], ul[2], ul[3]));
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
+          const u16x8 akh = load_a_tok(sKTh, tl, dt);
+          const u16x8 akl = load_a_tok(sKTl, tl, dt);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const u16x8 akh = load_a_tok(sKTh, tl, dt, kb);
-            const u16x8 akl = load_a_tok(sKTl, tl, dt, kb);
-            Hacc[dt] = mfma16(akh, Uh[kb], Hacc[dt]);
-            Hacc[dt] = mfma16(akh, Ul[kb], Hacc[dt]);
-            Hacc[dt] = mfma16(akl, Uh[kb], Hacc[dt]);
+          for (int ct = 0; ct < 2; ++ct) {
+            Hacc[dt][ct] = mfma16(akh, Uh[ct], Hacc[dt][ct]);
+            Hacc[dt][ct] = mfma16(akh, Ul[ct], Hacc[dt][ct]);
+            Hacc[dt][ct] = mfma16(akl, Uh[ct], Hacc[dt][ct]);
           }
         }
       }
     }
 
     // ================= epilogue: RMSNorm over 128 columns, SiLU(z) gate ============
-    if (MODE == kFull) {  // this wave's 16 columns of o -> the fp32 o tile
+    if (MODE == kFull) {  // this wave's 32 columns of o -> the fp32 o tile
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sO[(16 * mt + 4 * lg + i) * kOS + 16 * wave + ln] = Oacc[mt][i];
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sO[(16 * rt + 4 * lg + i) * kOS + 32 * wave + 16 * ct + ln] = Oacc[rt][ct][i];
     }
     __syncthreads();  // (5) o tile ready; this chunk's other LDS tiles are consumed
     refresh();
@@ -1018,7 +1044,10 @@ __global__ void __launch_bounds__(kThreads, 1) chunk_kernel(PrefillArgs P) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Hout[(16 * dt + 4 * lg + i) * kD + 16 * wave + ln] = Hacc[dt][i];
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Hout[(16 * dt + 4 * lg + i) * kD + 32 * wave + 16 * ct + ln] = Hacc[dt][ct][i];
   }
 }
 
@@ -1098,8 +1127,10 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
 }
 
 // ------------------------------------------------------------ combine (pass 2)
-// Per (sequence, v head, 16-column slice): H_0 = init; H_{s+1} = A_s H_s + B_s,
-// written as the start state of every segment of a multi-segment sequence.
+// Per (sequence, v head, 16-column slice): H_0 = init; H_{s+1} = A_s H_s + B_s.
+// Where A_s is zero (flagged by the map pass) H_{s+1} = B_s, which the full pass
+// reads from the map itself; only the start states after a non-zero A map are
+// computed and written here.
 __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const int32_t *hdr,
                                                       const float *init_state, const float *maps,
                                                       const int32_t *map_zero, float *starts,
@@ -1115,22 +1146,23 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
   const int row = tid >> 1, c0 = (tid & 1) * 8;  // 8 outputs per thread
   const int col0 = slice * 16 + c0;
   float hreg[8];
-  const float *H0 = init_state ? init_state + ((int64_t)s0.seq * Hv + h) * kD * kD : nullptr;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) hreg[j] = H0 ? H0[row * kD + col0 + j] : 0.f;
-  for (int s = 0; s < s0.nseg; ++s) {
-    float *dst = starts + ((int64_t)(segi + s) * Hv + h) * kD * kD;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[row * kD + col0 + j] = hreg[j];
-    if (s == s0.nseg - 1) break;
-    const int m = segs[segi + s].map;
-    const float *A = maps + (((int64_t)m * Hv + h) * 2 + 0) * kD * kD;
-    const float *B = maps + (((int64_t)m * Hv + h) * 2 + 1) * kD * kD;
-    if (map_zero[(int64_t)m * Hv + h]) {  // H_{s+1} = B_s
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hreg[j] = B[row * kD + col0 + j];
+  // H_s lives in hreg once loaded (have), else it is src (NULL: zeros)
+  const float *src = init_state ? init_state + ((int64_t)s0.seq * Hv + h) * kD * kD : nullptr;
+  bool have = false;
+  for (int s = 0; s + 1 < s0.nseg; ++s) {
+    const int64_t m = segs[segi + s].map;
+    const float *B = maps + ((m * Hv + h) * 2 + 1) * kD * kD;
+    if (map_zero[m * Hv + h]) {  // H_{s+1} = B_s
+      src = B;
+      have = false;
       continue;
     }
+    if (!have) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hreg[j] = src ? src[row * kD + col0 + j] : 0.f;
+      have = true;
+    }
+    const float *A = maps + ((m * Hv + h) * 2 + 0) * kD * kD;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) sH[row][c0 + j] = hreg[j];
@@ -1143,8 +1175,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] += a * sH[kx][c0 + j];
     }
+    float *dst = starts + ((int64_t)(segi + s + 1) * Hv + h) * kD * kD;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) hreg[j] = acc[j];
+    for (int j = 0; j < 8; ++j) {
+      hreg[j] = acc[j];
+      dst[row * kD + col0 + j] = acc[j];
+    }
   }
 }
 
@@ -1182,11 +1218,11 @@ __global__ void conv_out_kernel(const int32_t *cu, int N, int64_t T_total, const
 // ------------------------------------------------------------ host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Segment length: the smallest power of two >= 512 (at most 8192 tokens)
-// that still gives about one workgroup per compute unit over all v heads.
+// Segment length: the smallest power of two >= 256 (at most 8192 tokens)
+// that still gives about two workgroups per compute unit over all v heads.
 static int32_t pick_seg_len(int64_t T, int32_t Hv) {
-  int64_t target = T * (int64_t)Hv / 256;
-  int32_t s = 512;
+  int64_t target = T * (int64_t)Hv / 512;
+  int32_t s = 256;
   while (s < 8192 && s < target) s *= 2;
   return s;
 }

@@ -1,14 +1,16 @@
 // gdn_prefill_plan.h -- launch plan of the chunked prefill (host side).
 //
 // Long sequences are cut into segments of `seg_len` tokens (a multiple of the
-// 64-token chunk) so that several workgroups per v head run at once:
+// 32-token chunk) so that several workgroups per v head run at once:
 //   pass 1  (map):     per non-final segment s, the affine map of its chunks,
 //                      H_end = A_s H_start + B_s  (A_s, B_s fp32 [D][D])
 //   pass 2  (combine): per sequence, the start state of every segment,
-//                      H_{s+1} = A_s H_s + B_s, sequential over segments
+//                      H_{s+1} = A_s H_s + B_s, sequential over segments; where
+//                      A_s is zero (flagged by pass 1) H_{s+1} is B_s itself
 //   pass 3  (full):    per segment, the chunk recurrence from its start state
-//                      with the fused prologue and epilogue; writes o and,
-//                      for the last segment, the final state.
+//                      (the initial state, B_{s-1}, or what pass 2 wrote) with
+//                      the fused prologue and epilogue; writes o and, for the
+//                      last segment, the final state.
 // A sequence that fits in one segment runs pass 3 only.  The segment table is
 // built on the device from cu_seqlens, so the host needs only N and T.
 #pragma once
@@ -37,7 +39,7 @@ struct PrefillPlan {
   int32_t num_seqs = 0;
   int64_t total_tokens = 0;
   int32_t num_v_heads = 0;
-  int32_t seg_len = 0;       // tokens per segment (multiple of 64)
+  int32_t seg_len = 0;       // tokens per segment (multiple of 32)
   int64_t max_segments = 0;  // upper bound of the segment count
   int64_t max_maps = 0;      // upper bound of the non-final segment count
   size_t off_table = 0, off_maps = 0, off_start = 0, off_flags = 0;

@@ -36,7 +36,7 @@ def _case(rng, T, D, gate="typical"):
     return q, k, v, alpha, beta
 
 
-@pytest.mark.parametrize("chunk", [1, 16, 64])
+@pytest.mark.parametrize("chunk", [1, 16, 32, 64])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
 @pytest.mark.parametrize("gate", ["typical", "slow", "mixed"])
 def test_chunk_form_matches_recurrence(chunk, T, gate):
