@@ -431,11 +431,27 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   __syncthreads();
 
   // ---- token loop: the state stays in registers, no barrier -----------------------------
+  // The registers hold the state divided by the running decay product of this call,
+  // S = Gam * Hs, so a token costs one FMA per state element for the update instead
+  // of a decay multiply and an FMA: with Gam_t = alpha_t Gam_{t-1},
+  //   alpha_t S_{t-1} k = Gam_t (Hs k),  S_t = Gam_t (Hs + (beta e / Gam_t) k^T).
+  // When Gam_t falls below 2^-60 it is folded into Hs (and taken as 1), which also
+  // covers alpha = 0.  Gam is uniform per wave (one head per wave).
+  float Gam = 1.0f;
 #pragma unroll 1
   for (int t = 0; t < n; ++t) {
     {
       const float alpha = s_ab[hl][t][0];
       const float beta = s_ab[hl][t][1];
+      float Gt = Gam * alpha;
+      if (Gt < 0x1p-60f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          Hs[i].x *= Gt; Hs[i].y *= Gt; Hs[i].z *= Gt; Hs[i].w *= Gt;
+        }
+        Gt = 1.0f;
+      }
+      Gam = Gt;
       // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
       // within each 16-lane row); k again for the update, to keep registers low
       float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
@@ -463,11 +479,12 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       float be[4];
       float y[4];
       const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+      const float rG = 1.0f / Gt;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float e = vs[c] - alpha * sk[c];  // e = v - S'k
-        y[c] = alpha * sq[c] + beta * kq * e;   // S'' q
-        be[c] = beta * e;
+        const float e = vs[c] - Gt * sk[c];   // e = v - S'k
+        y[c] = Gt * sq[c] + beta * kq * e;    // S_t q
+        be[c] = beta * e * rG;
       }
       s_y[wave][t][lane] = rg == 0 ? y[0] : rg == 1 ? y[1] : rg == 2 ? y[2] : y[3];
 #pragma unroll
@@ -476,15 +493,16 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          Hs[i + u].x = alpha * Hs[i + u].x + kv[u] * be[0];
-          Hs[i + u].y = alpha * Hs[i + u].y + kv[u] * be[1];
-          Hs[i + u].z = alpha * Hs[i + u].z + kv[u] * be[2];
-          Hs[i + u].w = alpha * Hs[i + u].w + kv[u] * be[3];
+          Hs[i + u].x = fmaf(kv[u], be[0], Hs[i + u].x);
+          Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
+          Hs[i + u].z = fmaf(kv[u], be[2], Hs[i + u].z);
+          Hs[i + u].w = fmaf(kv[u], be[3], Hs[i + u].w);
         }
       }
       if (t + 1 == commit && head_on) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) st_nt4(Hp + i * kD, Hs[i]);
+        for (int i = 0; i < 32; ++i)
+          st_nt4(Hp + i * kD, f32x4{Gam * Hs[i].x, Gam * Hs[i].y, Gam * Hs[i].z, Gam * Hs[i].w});
       }
     }
   }

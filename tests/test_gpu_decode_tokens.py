@@ -162,6 +162,25 @@ def test_tokens_full_batch_sampled_sequences():
 
 
 @gpu
+def test_tokens_extreme_gates():
+    """alpha = 0 (A_log = 100: e^g underflows), alpha = 1 (A_log = -inf), beta in {0, 1}
+    (b = -inf, +inf), and a decay of about e^-80 per token, whose product over the call
+    underflows: the state carried divided by the running decay product (and rescaled
+    when that product gets small) still matches the oracle."""
+    import math
+    n = 8
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=2, num_v_heads=8, seed=83)
+    setup, t = _case(w, n)
+    setup["A_log"][0] = 100.0
+    setup["A_log"][1] = -float("inf")
+    setup["A_log"][2] = math.log(16.0)
+    t["a"][:, :, 2] = 5.0
+    t["b"][:, :, 3] = float("inf")
+    t["b"][:, :, 4] = -float("inf")
+    _check(setup, t, n, label="decode_tokens extreme gates")
+
+
+@gpu
 def test_tokens_zero_batch_is_a_no_op():
     w = S.scaled(S.DECODE_B256, decode_batch=1, seed=83)
     setup, t = _case(w, 2)
