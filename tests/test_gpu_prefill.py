@@ -134,6 +134,38 @@ def test_slow_decay_multi_segment(alog):
 
 
 @gpu
+def test_segment_maps_alternate_zero_and_nonzero():
+    """Along one sequence the decay switches between almost none and strong from one
+    segment to the next, so the segments' A maps alternate between negligible (flagged
+    zero: the next segment starts from the B map itself) and not (the combine pass
+    chains them, reloading the state from a B map after a zero one).  Two of the four
+    heads take the pattern in opposite phase.
+
+    The weak segments are the no-decay stress regime (nothing damps the rounding of the
+    bf16 products, see the delta-rule test), so the state is held to that test's stress
+    bar, 1e-2; a wrong start state gives errors of order 0.1-1.  o meets the main bar."""
+    T = 3000
+    w = S.scaled(S.PREFILL_4K, lengths=(T,), num_qk_heads=2, num_v_heads=4, seed=22,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    d["A_log"] = torch.zeros_like(d["A_log"])      # g = -softplus(a + dt_bias)
+    d["dt_bias"] = torch.zeros_like(d["dt_bias"])
+    # segments of 256 tokens for T = 3000 and 4 v heads (the last two are 224 tokens)
+    blk = (torch.arange(T, device="cuda") // 256) % 2
+    weak = torch.full((T,), -12.0, device="cuda")   # g ~ -6e-6 per token
+    strong = torch.full((T,), 3.0, device="cuda")   # g ~ -3 per token
+    for h in range(4):
+        phase = blk if h % 2 == 0 else 1 - blk
+        d["a"][:, h] = torch.where(phase == 1, strong, weak)
+    o, fs, _ = run_gpu(d)
+    o_ref, fs_ref, _, vi = run_oracle(d)
+    eo, es = rel_l2(S.to_f64(o)[:, vi], o_ref), rel_l2(S.to_f64(fs)[:, vi], fs_ref)
+    print(f"alternating zero/non-zero segment maps: o rel-L2 {eo:.3e} final-state rel-L2 "
+          f"{es:.3e}")
+    assert eo <= O_TOL and es <= 1e-2
+
+
+@gpu
 def test_varlen_with_empty_and_short_sequences():
     w = S.scaled(S.PREFILL_4K, lengths=(5, 0, 1, 64, 2, 0, 129, 3, 600), num_qk_heads=2,
                  num_v_heads=4, seed=7, init_state_std=0.01, conv_history=True)
