@@ -27,19 +27,27 @@ constexpr int kDecMaxRatio = 8;  // largest Hv / Hk the decode kernel accepts
 
 // Stored state: fp32, or bf16 (rounded to nearest even on every store) with the
 // step itself computed in fp32.  Four consecutive columns per access, streamed
-// once (non-temporal).
+// once (non-temporal).  A prefetched head is kept in its stored form (Raw) until
+// it is used, so bf16 storage needs half the registers for it.
 template <typename S> struct StateIO;
 template <> struct StateIO<float> {
+  typedef f32x4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const float *p) { return ld_nt4(p); }
+  static __device__ __forceinline__ f32x4 widen(Raw x) { return x; }
   static __device__ __forceinline__ f32x4 load(const float *p) { return ld_nt4(p); }
   static __device__ __forceinline__ void store(float *p, f32x4 x) { st_nt4(p, x); }
 };
 template <> struct StateIO<bf16_t> {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  static __device__ __forceinline__ f32x4 load(const bf16_t *p) {
-    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  typedef u32x2 Raw;
+  static __device__ __forceinline__ Raw load_raw(const bf16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  }
+  static __device__ __forceinline__ f32x4 widen(Raw w) {
     return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
   }
+  static __device__ __forceinline__ f32x4 load(const bf16_t *p) { return widen(load_raw(p)); }
   static __device__ __forceinline__ void store(bf16_t *p, f32x4 x) {
     const u32x2 w = {pk_bf16(x.x, x.y), pk_bf16(x.z, x.w)};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
@@ -79,11 +87,11 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   const float nwv = (norm_w && tid < kD) ? norm_w[tid] : 1.0f;
   float zcur = tid < kD ? Act<T>::load(z, ((int64_t)bseq * Hv + r * g) * kD + tid) : 0.f;
   // Start streaming the first head's state before the prologue.
-  f32x4 Hcur[16];
+  typename StateIO<S>::Raw Hraw[16];
   {
     const S *Hp = head_ptr(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Hcur[i] = StateIO<S>::load(Hp + i * kD);
+    for (int i = 0; i < 16; ++i) Hraw[i] = StateIO<S>::load_raw(Hp + i * kD);
   }
 
   // ---- 1. prologue --------------------------------------------------------------
@@ -166,12 +174,17 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     const int h = r * g + j;
     const float zg = siluf_(zcur);
     if (j + 1 < r && tid < kD) zcur = Act<T>::load(z, ((int64_t)bseq * Hv + h + 1) * kD + tid);
-    f32x4 Hnext[16];
+    // the next head's loads go out first (vector-memory waits are in issue order, so
+    // waiting for this head's state does not wait for them)
+    typename StateIO<S>::Raw Hnext[16];
     if (j + 1 < r) {
       const S *Hn = head_ptr(j + 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hnext[i] = StateIO<S>::load(Hn + i * kD);
+      for (int i = 0; i < 16; ++i) Hnext[i] = StateIO<S>::load_raw(Hn + i * kD);
     }
+    f32x4 Hcur[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Hcur[i] = StateIO<S>::widen(Hraw[i]);
     const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
     const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
     float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
@@ -220,7 +233,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     __syncthreads();  // s_red, s_e, s_y, s_misc are reused by the next head
     if (j + 1 < r) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hcur[i] = Hnext[i];
+      for (int i = 0; i < 16; ++i) Hraw[i] = Hnext[i];
     }
   }
 }
