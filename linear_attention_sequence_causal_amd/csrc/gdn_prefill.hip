@@ -341,8 +341,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   {
     int bid = blockIdx.x;
     if (MODE == kMap) {
-      half = bid & 1;  // 0: A columns, 1: B columns
-      bid >>= 1;
+      // the B halves (which walk the chunks) take the first half of the grid and
+      // start at once; the A halves mostly stop after the decay scan
+      const int hgrid = (int)(gridDim.x >> 1);
+      half = bid < hgrid ? 1 : 0;  // 0: A columns, 1: B columns
+      bid -= half ? 0 : hgrid;
     }
     const int r = Hv / Hk;
     const int x = bid & 7, y = bid >> 3;
