@@ -163,6 +163,7 @@ struct PrefillArgs {
   const SegInfo *segs;
   const int32_t *hdr;      // [0] segments, [1] maps
   const int32_t *map_seg;  // map slot -> segment index
+  const int32_t *seq_first;  // sequence -> index of its first segment
   float *maps;             // [max_maps][Hv][2][D][D]
   int32_t *map_zero;       // [max_maps][Hv]: 1 if the A map is zero (not stored)
   float *starts;           // [max_segments][Hv][D][D]
@@ -1058,7 +1059,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 // One workgroup: sequence lengths -> segments (prefix sums over sequences).
 __global__ void __launch_bounds__(1024) segment_table_kernel(
     const int32_t *cu, int N, int64_t T, int seg_len, int64_t max_segments, int64_t max_maps,
-    SegInfo *segs, int32_t *hdr, int32_t *map_seg) {
+    SegInfo *segs, int32_t *hdr, int32_t *map_seg, int32_t *seq_first) {
   __shared__ int s_nseg[1024], s_nmap[1024];
   __shared__ int s_base_seg, s_base_map;
   const int tid = threadIdx.x;
@@ -1094,6 +1095,7 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
     const int first = s_base_seg + s_nseg[tid] - ns;
     const int firstmap = s_base_map + s_nmap[tid] - nm;
     if (n < N) {
+      seq_first[n] = first;
       // chunks are spread evenly over the segments (the first nch % ns get one
       // more), so every segment of a split sequence holds >= 4 full chunks
       const int q = nch / ns, rem = nch % ns;
@@ -1135,16 +1137,19 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
 // reads from the map itself; only the start states after a non-zero A map are
 // computed and written here.
 __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const int32_t *hdr,
+                                                      const int32_t *seq_first, int N,
                                                       const float *init_state, const float *maps,
                                                       const int32_t *map_zero, float *starts,
                                                       int Hv) {
   __shared__ float sH[kD][17];
   const int slice = blockIdx.x % 8;
   const int h = (blockIdx.x / 8) % Hv;
-  const int segi = blockIdx.x / (8 * Hv);  // candidate first segment
-  if (segi >= hdr[0]) return;
+  const int n = blockIdx.x / (8 * Hv);  // sequence
+  if (n >= N) return;
+  const int segi = seq_first[n];  // its first segment
+  if (segi < 0 || segi >= hdr[0]) return;  // (no segments when the table was invalid)
   const SegInfo s0 = segs[segi];
-  if (s0.idx != 0 || s0.nseg < 2) return;
+  if (s0.nseg < 2) return;
   const int tid = threadIdx.x;
   const int row = tid >> 1, c0 = (tid & 1) * 8;  // 8 outputs per thread
   const int col0 = slice * 16 + c0;
@@ -1152,37 +1157,49 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
   // H_s lives in hreg once loaded (have), else it is src (NULL: zeros)
   const float *src = init_state ? init_state + ((int64_t)s0.seq * Hv + h) * kD * kD : nullptr;
   bool have = false;
-  for (int s = 0; s + 1 < s0.nseg; ++s) {
-    const int64_t m = segs[segi + s].map;
-    const float *B = maps + ((m * Hv + h) * 2 + 1) * kD * kD;
-    if (map_zero[m * Hv + h]) {  // H_{s+1} = B_s
-      src = B;
-      have = false;
-      continue;
+  // the maps' slots and zero flags, 256 segments at a time, loaded in parallel
+  __shared__ int sMap[256], sZero[256];
+  for (int sb = 0; sb + 1 < s0.nseg; sb += 256) {
+    const int nb = min(256, s0.nseg - 1 - sb);
+    __syncthreads();  // previous batch consumed
+    if (tid < nb) {
+      const int m = segs[segi + sb + tid].map;
+      sMap[tid] = m;
+      sZero[tid] = map_zero[(int64_t)m * Hv + h];
     }
-    if (!have) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hreg[j] = src ? src[row * kD + col0 + j] : 0.f;
-      have = true;
-    }
-    const float *A = maps + ((m * Hv + h) * 2 + 0) * kD * kD;
     __syncthreads();
+    for (int s = sb; s < sb + nb; ++s) {
+      const int64_t m = sMap[s - sb];
+      const float *B = maps + ((m * Hv + h) * 2 + 1) * kD * kD;
+      if (sZero[s - sb]) {  // H_{s+1} = B_s
+        src = B;
+        have = false;
+        continue;
+      }
+      if (!have) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sH[row][c0 + j] = hreg[j];
-    __syncthreads();
-    float acc[8];
+        for (int j = 0; j < 8; ++j) hreg[j] = src ? src[row * kD + col0 + j] : 0.f;
+        have = true;
+      }
+      const float *A = maps + ((m * Hv + h) * 2 + 0) * kD * kD;
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = B[row * kD + col0 + j];
-    for (int kx = 0; kx < kD; ++kx) {
-      const float a = A[row * kD + kx];
+      for (int j = 0; j < 8; ++j) sH[row][c0 + j] = hreg[j];
+      __syncthreads();
+      float acc[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += a * sH[kx][c0 + j];
-    }
-    float *dst = starts + ((int64_t)(segi + s + 1) * Hv + h) * kD * kD;
+      for (int j = 0; j < 8; ++j) acc[j] = B[row * kD + col0 + j];
+      for (int kx = 0; kx < kD; ++kx) {
+        const float a = A[row * kD + kx];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      hreg[j] = acc[j];
-      dst[row * kD + col0 + j] = acc[j];
+        for (int j = 0; j < 8; ++j) acc[j] += a * sH[kx][c0 + j];
+      }
+      float *dst = starts + ((int64_t)(segi + s + 1) * Hv + h) * kD * kD;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hreg[j] = acc[j];
+        dst[row * kD + col0 + j] = acc[j];
+      }
     }
   }
 }
@@ -1245,7 +1262,7 @@ PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_head
   size_t off = 0;
   p.off_table = off;
   off = align256(off + sizeof(int32_t) * 16 + sizeof(SegInfo) * (size_t)p.max_segments +
-                 sizeof(int32_t) * (size_t)(p.max_maps + 1));
+                 sizeof(int32_t) * (size_t)(p.max_maps + 1) + sizeof(int32_t) * (size_t)num_seqs);
   if (p.max_maps > 0) {
     p.off_maps = off;
     off = align256(off + 2 * DD * (size_t)p.max_maps * num_v_heads);
@@ -1290,9 +1307,10 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     hipLaunchKernelGGL((chunk_kernel<T, kMap>), g1, dim3(kThreads), kLdsBytes, stream, args);
     mark(2);
     mark(3);
-    dim3 g2((unsigned)(plan.max_segments * Hv * 8));
+    dim3 g2((unsigned)((int64_t)N * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
-                       args.init_state, (const float *)args.maps, args.map_zero, args.starts, Hv);
+                       args.seq_first, N, args.init_state, (const float *)args.maps,
+                       args.map_zero, args.starts, Hv);
     mark(4);
     if (tm) tm->ran[1] = tm->ran[3] = true;
   } else {
@@ -1327,15 +1345,16 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   int32_t *hdr = (int32_t *)(ws + plan.off_table);
   SegInfo *segs = (SegInfo *)(ws + plan.off_table + 16 * sizeof(int32_t));
   int32_t *map_seg = (int32_t *)(segs + plan.max_segments);
+  int32_t *seq_first = map_seg + plan.max_maps + 1;
   hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, num_seqs,
                      total_tokens, plan.seg_len, plan.max_segments, plan.max_maps, segs, hdr,
-                     map_seg);
+                     map_seg, seq_first);
   PrefillArgs A;
   A.q = q; A.k = k; A.v = v; A.z = z; A.a = a; A.b = b;
   A.conv_w = p.conv_weight; A.A_log = p.A_log; A.dt_bias = p.dt_bias; A.norm_w = p.norm_weight;
   A.q_scale = p.q_scale; A.l2_eps = p.l2_eps; A.rms_eps = p.rms_eps;
   A.init_state = init_state; A.conv_in = conv_state_in; A.o = o; A.final_state = final_state;
-  A.segs = segs; A.hdr = hdr; A.map_seg = map_seg;
+  A.segs = segs; A.hdr = hdr; A.map_seg = map_seg; A.seq_first = seq_first;
   A.maps = plan.max_maps > 0 ? (float *)(ws + plan.off_maps) : nullptr;
   A.starts = plan.max_maps > 0 ? (float *)(ws + plan.off_start) : nullptr;
   A.map_zero = plan.max_maps > 0 ? (int32_t *)(ws + plan.off_flags) : nullptr;
