@@ -84,8 +84,12 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   };
   // Small inputs go out before the state: vector-memory waits are in issue order,
   // so a wait for one of them never queues behind a state prefetch.
-  const float nwv = (norm_w && tid < kD) ? norm_w[tid] : 1.0f;
-  float zcur = tid < kD ? Act<T>::load(z, ((int64_t)bseq * Hv + r * g) * kD + tid) : 0.f;
+  // (unconditional, as bit patterns widened at first use: a conditional load would be
+  // widened, and waited for, before the state loads are issued; threads >= kD read a
+  // valid element and ignore it)
+  const int ztid = tid & (kD - 1);
+  const float nwv = norm_w ? norm_w[ztid] : 1.0f;
+  uint32_t zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + r * g) * kD + ztid);
   // Start streaming the first head's state before the prologue.
   typename StateIO<S>::Raw Hraw[16];
   {
@@ -172,8 +176,8 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   // ---- 3./4. per v head: state stream and epilogue ---------------------------------
   for (int j = 0; j < r; ++j) {
     const int h = r * g + j;
-    const float zg = siluf_(zcur);
-    if (j + 1 < r && tid < kD) zcur = Act<T>::load(z, ((int64_t)bseq * Hv + h + 1) * kD + tid);
+    const float zg = siluf_(Act<T>::from_bits(zbits));
+    if (j + 1 < r) zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + h + 1) * kD + ztid);
     // the next head's loads go out first (vector-memory waits are in issue order, so
     // waiting for this head's state does not wait for them)
     typename StateIO<S>::Raw Hnext[16];
