@@ -608,7 +608,16 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     const float *const sGam = gcur + GB_GAM * kChunk, *const sBG = gcur + GB_BG * kChunk;
     const float *const sDec = gcur + GB_DEC * kChunk, *const sBv = gcur + GB_BV * kChunk;
     const float *const sGamQ = gcur + GB_GAMQ * kChunk;
-    // the next chunk's gate inputs (wave 3), issued first and consumed after barrier 2
+    // Split precision for the state update, and the lo half of K^T that it and the
+    // exact right-hand side beta gamma K use: on a sequence's last 128 tokens (the
+    // final state) and on every chunk whose decay leaves more than 2^-4 of the state
+    // (nothing would damp the rounding of a one-pass update there; fast-decaying
+    // heads never take it).  gC is the same in every lane.
+    const float gC = sGam[kChunk - 1];
+    const bool precise =
+        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >= (1.0f / 16.0f) ||
+        (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 4)));
+    // the next chunk's gate inputs (wave 3), issued first and consumed in the gram phase
     float ga = 0.f, gb = 0.f;
     const bool gates_next = wave == 3 && c + 1 < nchunks;
     if (gates_next) load_gates(t0 + kChunk, ga, gb);
@@ -660,33 +669,42 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
           *reinterpret_cast<uint4 *>(sQh + off) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
         }
       } else {
-        uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
+        // K^T [dk][tok]: the halves regrouped by channel, 8 bytes (4 tokens) per row;
+        // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1.  Tokens (2p, 2p+1) of
+        // channel cc are half (cc & 1) of word cc/2 of tokens 2p, 2p+1.
+        const int swz = (((tbase >> 2) ^ (cg >> 1)) & 7) << 2;
+        auto put_kt = [&](bf16_t *tile, const uint32_t (&w)[4][4]) {
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+            const int e = cc >> 1;
+            *reinterpret_cast<uint2 *>(tile + (cg * 8 + cc) * kTokS + swz) =
+                make_uint2(__builtin_amdgcn_perm(w[1][e], w[0][e], sel),
+                           __builtin_amdgcn_perm(w[3][e], w[2][e], sel));
+          }
+        };
+        uint32_t hw[4][4];  // token r: channels (2e, 2e+1) in word e
+        if (precise) {  // hi and lo halves
+          uint32_t lw[4][4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
+          put_kt(sKTl, lw);
+        } else {  // hi halves only
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hw[r][e] = pk_bf16(x[r][2 * e], x[r][2 * e + 1]);
+        }
+        put_kt(sKTh, hw);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           uint32_t fw[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
-            split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
-          }
+          for (int e = 0; e < 4; ++e) fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
           *reinterpret_cast<uint4 *>(sKf + (tbase + r) * kRowS + cg * 8) =
               make_uint4(fw[0], fw[1], fw[2], fw[3]);
-        }
-        // K^T [dk][tok]: the same halves regrouped by channel, 8 bytes (4 tokens) per
-        // row; rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1
-        const int swz = (((tbase >> 2) ^ (cg >> 1)) & 7) << 2;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          // tokens (2p, 2p+1) of channel cc: half (cc & 1) of word cc/2 of tokens 2p, 2p+1
-          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-          const int e = cc >> 1;
-          const int off = (cg * 8 + cc) * kTokS + swz;
-          *reinterpret_cast<uint2 *>(sKTh + off) =
-              make_uint2(__builtin_amdgcn_perm(hw[1][e], hw[0][e], sel),
-                         __builtin_amdgcn_perm(hw[3][e], hw[2][e], sel));
-          *reinterpret_cast<uint2 *>(sKTl + off) =
-              make_uint2(__builtin_amdgcn_perm(lw[1][e], lw[0][e], sel),
-                         __builtin_amdgcn_perm(lw[3][e], lw[2][e], sel));
         }
       }
     }
@@ -817,7 +835,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         const int dcol = 32 * wave + 16 * ct + ln;
         const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
         const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
-        const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
+        u16x4 kl = {0, 0, 0, 0};  // beta gamma K in fp32 where the lo halves exist
+        if (precise) kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
         f32x4 vv = {0.f, 0.f, 0.f, 0.f};
         if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
 #pragma unroll
@@ -908,7 +927,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     }
     // state update H = gamma_C H + K^T diag(e^{G_C - G}) U
     {
-      const float gC = sGam[kChunk - 1];
       float u[2][2][4];
       uint32_t uh[2][4];  // [ct]: tokens 4lg.. of row tile 0, then of row tile 1
 #pragma unroll
@@ -926,14 +944,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
         Uh[ct] = __builtin_bit_cast(u16x8, make_uint4(uh[ct][0], uh[ct][1], uh[ct][2], uh[ct][3]));
-      // Split precision for the state update: on a sequence's last 128 tokens (the
-      // final state) and on every chunk whose decay leaves more than 2^-4 of the
-      // state (nothing would damp the rounding of a one-pass update there;
-      // fast-decaying heads never take it).  gC is the same in every lane.
-      const bool slow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >=
-                        (1.0f / 16.0f);
-      const bool precise =
-          slow || (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 4)));
       const TokLane tl(ln, lg);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
