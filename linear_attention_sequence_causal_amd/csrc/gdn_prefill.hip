@@ -617,8 +617,10 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     const bool precise =
         __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >= (1.0f / 16.0f) ||
         (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 4)));
-    // the next chunk's gate inputs (wave 3), issued first and consumed in the gram phase
-    float ga = 0.f, gb = 0.f;
+    // the next chunk's gate inputs (wave 3), issued first and consumed in the gram
+    // phase under the same condition (left undefined otherwise, so that no select
+    // waits for the loads here)
+    float ga, gb;
     const bool gates_next = wave == 3 && c + 1 < nchunks;
     if (gates_next) load_gates(t0 + kChunk, ga, gb);
 
