@@ -90,6 +90,17 @@ def test_prefill_4k_full_parity():
 
 
 @gpu
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 3)])
+def test_head_layouts(hk, hv):
+    """One v head per q/k head (r = 1), four (r = 4), and a head count that is not a
+    multiple of the workgroup id groups of 8; multi-segment (T = 2000)."""
+    w = S.scaled(S.PREFILL_4K, lengths=(2000, 300), num_qk_heads=hk, num_v_heads=hv,
+                 seed=30 + hv, init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    check_parity(d, tag=f"Hk={hk} Hv={hv} T=2300")
+
+
+@gpu
 def test_prefill_64k_sampled_heads():
     d = S.prefill_inputs(S.PREFILL_64K, "cuda")
     check_parity(d, qk_heads=[0, 15], tag="T=65536 bf16, v heads 0,1,30,31")
