@@ -24,10 +24,12 @@ def rel_l2(x, ref):
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
 
 
-def _run_decode(w, steps, seq_sample=None):
+def _run_decode(w, steps, seq_sample=None, q_scale=1.0, norm_w=None):
     import linear_attention_sequence_causal_amd as gdn
     dev = "cuda"
     setup = S.decode_setup(w, dev)
+    if norm_w is not None:
+        setup["norm_w"] = norm_w
     toks = S.decode_tokens(w, setup, steps, dev)
     st0 = setup["state"].clone()
     cc0 = setup["conv_cache"].clone()
@@ -37,7 +39,7 @@ def _run_decode(w, steps, seq_sample=None):
     for s in range(steps):
         o = gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s], toks["b"][s],
                             toks["z"][s], setup["conv_w"], setup["A_log"], setup["dt_bias"],
-                            setup["norm_w"], state, cache)
+                            setup["norm_w"], state, cache, q_scale=q_scale)
         outs.append(o)
     torch.cuda.synchronize()
     sel = slice(None) if seq_sample is None else seq_sample
@@ -50,10 +52,26 @@ def _run_decode(w, steps, seq_sample=None):
             f(toks["q"][s][sel]), f(toks["k"][s][sel]), f(toks["v"][s][sel]),
             f(toks["a"][s][sel]), f(toks["b"][s][sel]), f(toks["z"][s][sel]),
             f(setup["conv_w"]), f(setup["A_log"]), f(setup["dt_bias"]), f(setup["norm_w"]),
-            ost, occ)
+            ost, occ, q_scale=q_scale)
         o_ref.append(o_s)
     o_gpu = np.stack([f(o[sel]) for o in outs])
     return o_gpu, np.stack(o_ref), f(state[sel]), ost, f(cache[sel]), occ
+
+
+@gpu
+def test_decode_q_scale_and_norm_weight():
+    """q_scale = 1/sqrt(128) and a non-uniform RMSNorm weight (the workloads use 1 and
+    ones)."""
+    import math
+    w = S.scaled(S.DECODE_B256, decode_batch=8, num_qk_heads=4, num_v_heads=8, seed=42)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(43)
+    nw = torch.rand(128, generator=g, device="cuda") + 0.5
+    o, o_ref, st, st_ref, cc, cc_ref = _run_decode(w, 5, q_scale=1.0 / math.sqrt(128), norm_w=nw)
+    eo, es = rel_l2(o, o_ref), rel_l2(st, st_ref)
+    print(f"decode q_scale 1/sqrt(128), random norm weight: o rel-L2 {eo:.3e} state {es:.3e}")
+    assert eo < O_TOL and es < 1e-5
+    assert np.array_equal(cc, cc_ref)
 
 
 @gpu

@@ -32,21 +32,22 @@ def _case(w, n, dev="cuda"):
     return setup, bn
 
 
-def _gpu(setup, t, state, cache, num_commit=None):
+def _gpu(setup, t, state, cache, num_commit=None, q_scale=1.0):
     import linear_attention_sequence_causal_amd as gdn
     o = gdn.decode_tokens(t["q"], t["k"], t["v"], t["a"], t["b"], t["z"], setup["conv_w"],
                           setup["A_log"], setup["dt_bias"], setup["norm_w"], state, cache,
-                          num_commit=num_commit)
+                          num_commit=num_commit, q_scale=q_scale)
     torch.cuda.synchronize()
     return o
 
 
-def _oracle(setup, t, state, cache, sel=slice(None), num_commit=None):
+def _oracle(setup, t, state, cache, sel=slice(None), num_commit=None, q_scale=1.0):
     f = S.to_f64
     return oracle.decode_tokens(f(t["q"][sel]), f(t["k"][sel]), f(t["v"][sel]), f(t["a"][sel]),
                                 f(t["b"][sel]), f(t["z"][sel]), f(setup["conv_w"]),
                                 f(setup["A_log"]), f(setup["dt_bias"]), f(setup["norm_w"]),
-                                f(state[sel]), f(cache[sel]), num_commit=num_commit)
+                                f(state[sel]), f(cache[sel]), num_commit=num_commit,
+                                q_scale=q_scale)
 
 
 def _check(setup, t, n, sel=slice(None), num_commit=None, label=""):
@@ -178,6 +179,28 @@ def test_tokens_extreme_gates():
     t["b"][:, :, 3] = float("inf")
     t["b"][:, :, 4] = -float("inf")
     _check(setup, t, n, label="decode_tokens extreme gates")
+
+
+@gpu
+def test_tokens_q_scale_and_norm_weight():
+    """q_scale = 1/sqrt(128) and a non-uniform RMSNorm weight (the workloads use 1 and
+    ones)."""
+    import math
+    n = 4
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=2, num_v_heads=8, seed=84)
+    setup, t = _case(w, n)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(85)
+    setup["norm_w"] = torch.rand(128, generator=g, device="cuda") + 0.5
+    qs = 1.0 / math.sqrt(128)
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    o = _gpu(setup, t, setup["state"], setup["conv_cache"], q_scale=qs)
+    o_ref, st_ref, cc_ref = _oracle(setup, t, st0, cc0, q_scale=qs)
+    f = S.to_f64
+    eo, es = rel_l2(f(o), o_ref), rel_l2(f(setup["state"]), st_ref)
+    print(f"decode_tokens q_scale 1/sqrt(128), random norm weight: o {eo:.3e} state {es:.3e}")
+    assert eo < O_TOL and es < 1e-5
+    assert np.array_equal(f(setup["conv_cache"]), cc_ref)
 
 
 @gpu

@@ -40,7 +40,7 @@ def run_gpu(d, cu=True, **kw):
     return out
 
 
-def run_oracle(d, qk_heads=None):
+def run_oracle(d, qk_heads=None, q_scale=1.0):
     """Oracle on the given q/k heads (and their v heads); returns (o, fs, v_idx)."""
     f = S.to_f64
     Hk = d["q"].shape[1]
@@ -60,7 +60,7 @@ def run_oracle(d, qk_heads=None):
         sel(d["b"], vi_t), sel(d["z"], vi_t), sel(d["conv_w"], ch_t, 0), sel(d["A_log"], vi_t, 0),
         sel(d["dt_bias"], vi_t, 0), f(d["norm_w"]), cu_seqlens=d["cu_seqlens"].cpu().numpy(),
         init_state=None if init is None else sel(init, vi_t),
-        conv_in=None if conv_in is None else sel(conv_in, ch_t, 2))
+        conv_in=None if conv_in is None else sel(conv_in, ch_t, 2), q_scale=q_scale)
     return o, fs, co, vi
 
 
@@ -98,6 +98,25 @@ def test_head_layouts(hk, hv):
                  seed=30 + hv, init_state_std=0.01, conv_history=True)
     d = S.prefill_inputs(w, "cuda")
     check_parity(d, tag=f"Hk={hk} Hv={hv} T=2300")
+
+
+@gpu
+def test_q_scale_and_norm_weight():
+    """q_scale = 1/sqrt(128) and a non-uniform RMSNorm weight (the workloads use 1 and
+    ones): q_scale reaches M, its fp32 diagonal and Q H; the weight the epilogue."""
+    import math
+    w = S.scaled(S.PREFILL_4K, lengths=(700, 333), num_qk_heads=2, num_v_heads=4, seed=40,
+                 init_state_std=0.01)
+    d = S.prefill_inputs(w, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(41)
+    d["norm_w"] = torch.rand(128, generator=g, device="cuda") + 0.5
+    qs = 1.0 / math.sqrt(128)
+    o, fs, _ = run_gpu(d, q_scale=qs)
+    o_ref, fs_ref, _, vi = run_oracle(d, q_scale=qs)
+    eo, es = rel_l2(S.to_f64(o)[:, vi], o_ref), rel_l2(S.to_f64(fs)[:, vi], fs_ref)
+    print(f"q_scale 1/sqrt(128), random norm weight: o rel-L2 {eo:.3e} state rel-L2 {es:.3e}")
+    assert eo <= O_TOL and es <= STATE_TOL
 
 
 @gpu
