@@ -300,15 +300,36 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One workgroup per (sequence, q/k head, pair of its v heads): wave w holds
-// v head 2p + (w >> 1), value columns 64 (w & 1) + 4 cg .. + 3 (cg = lane & 15)
-// and key rows 32 rg .. + 31 (rg = lane >> 4) of the fp32 state, 128 values per
-// lane.  A token's S k and S q sums are finished across the four row lanes with
-// permlane swaps, so the token loop needs no LDS round trip and no barrier; the
-// RMS of each token's y (split over the two waves of a head) is taken once after
-// the loop.
+// One workgroup of eight waves per (sequence, q/k head, pair of its v heads): wave
+// w holds v head 2p + (w >> 2), value columns 32 (w & 3) + 2 cg, + 1 (cg = lane & 15)
+// and key rows 32 rg .. + 31 (rg = lane >> 4) of the fp32 state, 64 values per
+// lane, so that four waves fit on a SIMD and the state reads of some workgroups
+// overlap the token loops of others.  A token's S k and S q sums are finished
+// across the four row lanes with permlane swaps, so the token loop needs no LDS
+// round trip and no barrier; the RMS of each token's y (split over the four waves
+// of a head) is taken once after the loop.
+constexpr int kTokThreads = 512;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// One v head's fp32 state as a raw buffer: each lane's 8-byte pieces are addressed by
+// its own offset plus a uniform row offset, so no per-row 64-bit addresses are kept
+// in registers.  Cache policy non-temporal (the state is touched once per call).
+constexpr int kNtPolicy = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_buf(float *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kD * kD * (int)sizeof(float),
+                                           0x00020000);
+}
+__device__ __forceinline__ f32x2 ld_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, row_off, kNtPolicy));
+}
+__device__ __forceinline__ void st_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off,
+                                        f32x2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, x), r, off, row_off,
+                                        kNtPolicy);
+}
+
 template <typename T>
-__global__ void __launch_bounds__(kDecThreads, 2)
+__global__ void __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                      const float *__restrict__ a, const float *__restrict__ b,
                      const T *__restrict__ z, const float *__restrict__ conv_w,
@@ -326,27 +347,24 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
 
-  const int hl = wave >> 1;                       // head of the pair
+  const int hl = wave >> 2;                       // head of the pair
   const int jh = 2 * pair + hl;                   // v head within the q/k group
   const bool head_on = jh < r;
   const int h = r * g + min(jh, r - 1);
   const int cg = lane & 15, rg = lane >> 4;
-  const int col0 = 64 * (wave & 1) + 4 * cg;      // 4 value columns
+  const int col0 = 32 * (wave & 3) + 2 * cg;      // 2 value columns
   const int row0 = 32 * rg;                       // 32 key rows
-  const int ocol = col0 + rg;                     // the column this lane outputs
+  const int ocol = col0 + (rg & 1);               // the column this lane outputs
+  const bool out_lane = rg < 2;                   // rows 2, 3 repeat rows 0, 1
 
   __shared__ float s_x[kMaxStepTokens][4][kD];    // post-prologue q, k, v0, v1 rows
   __shared__ float s_kq[kMaxStepTokens];
-  __shared__ float s_ss[4][kMaxStepTokens];       // per-wave partial sums of y^2
+  __shared__ float s_ss[8][kMaxStepTokens];       // per-wave partial sums of y^2
   __shared__ float s_ab[2][kMaxStepTokens][2];    // alpha, beta of each head and token
-  __shared__ float s_y[4][kMaxStepTokens][64];    // y of each lane's output column
+  __shared__ float s_y[8][kMaxStepTokens][64];    // y of each lane's output column
 
-  // small inputs first (vector-memory waits are in issue order), then the state
-  const float nwv = norm_w ? norm_w[ocol] : 1.0f;
-  float zr[kMaxStepTokens];
-#pragma unroll
-  for (int t = 0; t < kMaxStepTokens; ++t)
-    zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
+  // the gate inputs first; the state is read after the prologue, whose registers it
+  // would otherwise share (four waves per SIMD need at most 128 registers per lane)
   float ga = 0.f, gb = 0.f;  // gate inputs of (head tid >> 3, token tid & 7)
   const int gh = r * g + min(2 * pair + (tid >> 3), r - 1), gt = tid & 7;
   if (tid < 16 && gt < n) {
@@ -354,13 +372,12 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     ga = a[gi];
     gb = b[gi];
   }
-  float *Hp = state + (((int64_t)bseq * Hv + h) * kD + row0) * kD + col0;
-  f32x4 Hs[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) Hs[i] = ld_nt4(Hp + i * kD);
+  const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
+  const uint32_t hoff = (uint32_t)(row0 * kD + col0) * (uint32_t)sizeof(float);
+  f32x2 Hs[32];
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
-  // section = wave: q, k, v of head 2p, v of head 2p + 1.  raw[0..2] = cached rows
+  // section = wave (waves 0-3): q, k, v of head 2p, v of head 2p + 1.  raw[0..2] = cached rows
   // (oldest first), raw[3 + t] = new token t.  The q/k cache channels belong to the
   // pair-0 workgroup, a v head's to the workgroup of its pair.
   {
@@ -368,7 +385,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     const int c0 = lane * 2;
     const int slot = wave;
     const int jv = 2 * pair + (slot - 2);
-    const bool active = slot < 2 || jv < r;
+    const bool active = slot < 2 || (slot < 4 && jv < r);
     const bool owner = slot < 2 ? pair == 0 : true;
     int64_t cbase, hstride, sidx;
     const T *src;
@@ -379,7 +396,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       cbase = (int64_t)Hk * kD + (int64_t)g * kD; src = k; hstride = (int64_t)Hk * kD;
       sidx = ((int64_t)bseq * n * Hk + g) * kD;
     } else {
-      const int jj = min(jv, r - 1);
+      const int jj = min(max(jv, 0), r - 1);
       cbase = 2LL * Hk * kD + (int64_t)(r * g + jj) * kD; src = v; hstride = (int64_t)Hv * kD;
       sidx = ((int64_t)bseq * n * Hv + r * g + jj) * kD;
     }
@@ -426,13 +443,18 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         }
       }
     }
+    if (slot < 4) {
 #pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t)
-      if (t < n) {
-        s_x[t][slot][c0] = xv[t][0];
-        s_x[t][slot][c0 + 1] = xv[t][1];
-      }
+      for (int t = 0; t < kMaxStepTokens; ++t)
+        if (t < n) {
+          s_x[t][slot][c0] = xv[t][0];
+          s_x[t][slot][c0 + 1] = xv[t][1];
+        }
+    }
   }
+  // the state (the barriers below do not wait for these loads)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
   if (tid < 16 && gt < n) {
     s_ab[tid >> 3][gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
     s_ab[tid >> 3][gt][1] = sigmoidf_(gb);
@@ -464,14 +486,14 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       if (Gt < 0x1p-60f) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          Hs[i].x *= Gt; Hs[i].y *= Gt; Hs[i].z *= Gt; Hs[i].w *= Gt;
+          Hs[i].x *= Gt; Hs[i].y *= Gt;
         }
         Gt = 1.0f;
       }
       Gam = Gt;
       // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
       // within each 16-lane row); k again for the update, to keep registers low
-      float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
+      float sk[2] = {0, 0}, sq[2] = {0, 0};
 #pragma unroll
       for (int i = 0; i < 32; i += 4) {
         const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
@@ -479,31 +501,29 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const f32x4 hv = Hs[i + u];
+          const f32x2 hv = Hs[i + u];
           sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
-          sk[2] += hv.z * kv[u]; sk[3] += hv.w * kv[u];
           sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
-          sq[2] += hv.z * qv[u]; sq[3] += hv.w * qv[u];
         }
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
         sk[c] = rows4_sum(sk[c]);
         sq[c] = rows4_sum(sq[c]);
       }
-      const f32x4 vv = *reinterpret_cast<const f32x4 *>(&s_x[t][2 + hl][col0]);
+      const f32x2 vv = *reinterpret_cast<const f32x2 *>(&s_x[t][2 + hl][col0]);
       const float kq = s_kq[t];
-      float be[4];
-      float y[4];
-      const float vs[4] = {vv.x, vv.y, vv.z, vv.w};
+      float be[2];
+      float y[2];
+      const float vs[2] = {vv.x, vv.y};
       const float rG = 1.0f / Gt;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
         const float e = vs[c] - Gt * sk[c];   // e = v - S'k
         y[c] = Gt * sq[c] + beta * kq * e;    // S_t q
         be[c] = beta * e * rG;
       }
-      s_y[wave][t][lane] = rg == 0 ? y[0] : rg == 1 ? y[1] : rg == 2 ? y[2] : y[3];
+      s_y[wave][t][lane] = (rg & 1) ? y[1] : y[0];
 #pragma unroll
       for (int i = 0; i < 32; i += 4) {
         const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
@@ -512,35 +532,40 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         for (int u = 0; u < 4; ++u) {
           Hs[i + u].x = fmaf(kv[u], be[0], Hs[i + u].x);
           Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
-          Hs[i + u].z = fmaf(kv[u], be[2], Hs[i + u].z);
-          Hs[i + u].w = fmaf(kv[u], be[3], Hs[i + u].w);
         }
       }
       if (t + 1 == commit && head_on) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-          st_nt4(Hp + i * kD, f32x4{Gam * Hs[i].x, Gam * Hs[i].y, Gam * Hs[i].z, Gam * Hs[i].w});
+          st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2{Gam * Hs[i].x, Gam * Hs[i].y});
       }
     }
   }
 
-  // ---- epilogue: RMS over the head's 128 columns (two waves), SiLU(z) gate ------------
+  // ---- epilogue: RMS over the head's 128 columns (four waves), SiLU(z) gate -----------
+  const float nwv = norm_w ? norm_w[ocol] : 1.0f;
+  float zr[kMaxStepTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxStepTokens; ++t)
+    zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
   float yown[kMaxStepTokens];
 #pragma unroll
   for (int t = 0; t < kMaxStepTokens; ++t) {
     yown[t] = t < n ? s_y[wave][t][lane] : 0.f;  // this lane's own writes: no barrier
     if (t < n) {
-      // each column sits in one lane of its group of four: sum over the wave's 64
-      const float ssum = wave_sum(yown[t] * yown[t]);
+      // each column sits in one of the lanes with rg < 2: sum over those
+      const float ssum = wave_sum(out_lane ? yown[t] * yown[t] : 0.f);
       if (lane == 0) s_ss[wave][t] = ssum;
     }
   }
   __syncthreads();
-  if (head_on) {
+  if (head_on && out_lane) {
 #pragma unroll
     for (int t = 0; t < kMaxStepTokens; ++t) {
       if (t < n) {
-        const float inv = rsqrtf((s_ss[2 * hl][t] + s_ss[2 * hl + 1][t]) * (1.0f / kD) + rms_eps);
+        const float ssh = (s_ss[4 * hl][t] + s_ss[4 * hl + 1][t]) +
+                          (s_ss[4 * hl + 2][t] + s_ss[4 * hl + 3][t]);
+        const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
         const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
         Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
       }
@@ -558,7 +583,7 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
   if (batch == 0) return hipSuccess;
   const unsigned npair = (unsigned)((Hv / Hk + 1) / 2);
   dim3 grid((unsigned)batch * (unsigned)Hk * npair);
-  hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kDecThreads), 0, stream,
+  hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kTokThreads), 0, stream,
                      (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
                      dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
                      num_commit, (T *)o, Hk, Hv, n);
