@@ -309,7 +309,6 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // round trip and no barrier; the RMS of each token's y (split over the four waves
 // of a head) is taken once after the loop.
 constexpr int kTokThreads = 512;
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // One v head's fp32 state as a raw buffer: each lane's 8-byte pieces are addressed by
 // its own offset plus a uniform row offset, so no per-row 64-bit addresses are kept
@@ -319,11 +318,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_buf(float *base) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kD * kD * (int)sizeof(float),
                                            0x00020000);
 }
-__device__ __forceinline__ f32x2 ld_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off) {
-  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, row_off, kNtPolicy));
+__device__ __forceinline__ f32x2_t ld_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off) {
+  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, row_off, kNtPolicy));
 }
 __device__ __forceinline__ void st_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off,
-                                        f32x2 x) {
+                                        f32x2_t x) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, x), r, off, row_off,
                                         kNtPolicy);
 }
@@ -374,7 +373,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   }
   const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
   const uint32_t hoff = (uint32_t)(row0 * kD + col0) * (uint32_t)sizeof(float);
-  f32x2 Hs[32];
+  f32x2_t Hs[32];
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
   // section = wave (waves 0-3): q, k, v of head 2p, v of head 2p + 1.  raw[0..2] = cached rows
@@ -501,7 +500,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const f32x2 hv = Hs[i + u];
+          const f32x2_t hv = Hs[i + u];
           sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
           sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
         }
@@ -511,7 +510,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         sk[c] = rows4_sum(sk[c]);
         sq[c] = rows4_sum(sq[c]);
       }
-      const f32x2 vv = *reinterpret_cast<const f32x2 *>(&s_x[t][2 + hl][col0]);
+      const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_x[t][2 + hl][col0]);
       const float kq = s_kq[t];
       float be[2];
       float y[2];
@@ -537,7 +536,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       if (t + 1 == commit && head_on) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-          st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2{Gam * Hs[i].x, Gam * Hs[i].y});
+          st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2_t{Gam * Hs[i].x, Gam * Hs[i].y});
       }
     }
   }

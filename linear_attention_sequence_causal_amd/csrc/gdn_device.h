@@ -26,11 +26,6 @@ __device__ __forceinline__ bf16_t f2bf(float x) {
 }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// hi = bf16(x), lo = bf16(x - hi): x = hi + lo to ~2^-16 relative.
-__device__ __forceinline__ void split_bf(float x, bf16_t &hi, bf16_t &lo) {
-  hi = f2bf(x);
-  lo = f2bf(x - bf2f(hi));
-}
 
 template <typename T> struct Act;
 template <> struct Act<float> {
@@ -49,11 +44,10 @@ template <> struct Act<bf16_t> {
 };
 
 __device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
-// sigmoid / SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
+// sigmoid with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
 __device__ __forceinline__ float sigmoid_fast(float u) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-u));
 }
-__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -114,8 +108,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
-// Sum over lanes that differ only in bits below `width` (width a power of 2).
-// (W <= 32; uses the LDS swizzle unit in bit-mask mode, lane ^ o within 32 lanes)
 // Sum over each row of 16 lanes (lanes 16r .. 16r+15), result in every lane of
 // the row: a rotate-and-add butterfly on the DPP crossbar (no LDS traffic).
 __device__ __forceinline__ float row16_sum(float x) {
@@ -130,26 +122,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// Reduce-scatter over each row of 16 lanes: lane ln returns the sum over the
-// row of v[ln].  Four butterfly stages pair lanes that differ in bit 3, 2, 1,
-// 0 (partners ln^15, ln^7, ln^3, ln^1 on the DPP crossbar); at each stage a
-// lane keeps the half of its values selected by that bit and adds the other
-// half received from its partner.
-__device__ __forceinline__ float row16_reduce_scatter(const float (&v)[16], int ln) {
-  const bool b3 = ln & 8, b2 = ln & 4, b1 = ln & 2, b0 = ln & 1;
-  float a8[8], a4[4], a2[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    a8[j] = (b3 ? v[j + 8] : v[j]) + dpp_f<0x140>(b3 ? v[j] : v[j + 8]);  // row_mirror
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    a4[j] = (b2 ? a8[j + 4] : a8[j]) + dpp_f<0x141>(b2 ? a8[j] : a8[j + 4]);  // row_half_mirror
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    a2[j] = (b1 ? a4[j + 2] : a4[j]) + dpp_f<0x1B>(b1 ? a4[j] : a4[j + 2]);  // quad_perm 3,2,1,0
-  return (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);            // quad_perm 1,0,3,2
-}
-
 // Value the optimiser cannot see through (keeps derived addresses local).
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
