@@ -88,8 +88,10 @@ def test_tokens_fp32_small_heads():
 
 
 @gpu
-@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8)])
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 9), (1, 1)])
 def test_tokens_head_layouts(hk, hv):
+    """One, four and three v heads per q/k head: an odd count leaves the second head
+    of the last pair empty (its waves compute but store nothing)."""
     w = S.scaled(S.DECODE_B256, decode_batch=5, num_qk_heads=hk, num_v_heads=hv, seed=71 + hv)
     setup, t = _case(w, 3)
     _check(setup, t, 3, label=f"decode_tokens n=3 Hk={hk} Hv={hv}")
