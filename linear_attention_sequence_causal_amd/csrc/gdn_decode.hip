@@ -300,15 +300,15 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One workgroup of eight waves per (sequence, q/k head, pair of its v heads): wave
-// w holds v head 2p + (w >> 2), value columns 32 (w & 3) + 2 cg, + 1 (cg = lane & 15)
-// and key rows 32 rg .. + 31 (rg = lane >> 4) of the fp32 state, 64 values per
-// lane, so that four waves fit on a SIMD and the state reads of some workgroups
-// overlap the token loops of others.  A token's S k and S q sums are finished
-// across the four row lanes with permlane swaps, so the token loop needs no LDS
-// round trip and no barrier; the RMS of each token's y (split over the four waves
-// of a head) is taken once after the loop.
-constexpr int kTokThreads = 512;
+// One workgroup of four waves per (sequence, v head): wave w holds value columns
+// 32 w + 2 cg, + 1 (cg = lane & 15) and key rows 32 rg .. + 31 (rg = lane >> 4) of the
+// fp32 state, 64 values per lane, so that four waves fit on a SIMD and the state
+// reads of some workgroups overlap the token loops of others.  The r workgroups of a
+// q/k head each convolve its q and k rows (the first of them advances their conv
+// cache).  A token's S k and S q sums are finished across the four row lanes with
+// permlane swaps, so the token loop needs no LDS round trip and no barrier; the RMS
+// of each token's y (split over the four waves) is taken once after the loop.
+constexpr int kTokThreads = 256;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // One v head's fp32 state as a raw buffer: each lane's 8-byte pieces are addressed by
 // its own offset plus a uniform row offset, so no per-row 64-bit addresses are kept
@@ -338,17 +338,14 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
                      const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
                      int n) {
   const int r = Hv / Hk;
-  const int npair = (r + 1) / 2;
-  const int pair = blockIdx.x % npair;
-  const int g = (blockIdx.x / npair) % Hk;
-  const int bseq = blockIdx.x / npair / Hk;
+  const int jh = blockIdx.x % r;                  // v head within its q/k group
+  const int g = (blockIdx.x / r) % Hk;            // q/k head
+  const int bseq = blockIdx.x / r / Hk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
 
-  const int hl = wave >> 2;                       // head of the pair
-  const int jh = 2 * pair + hl;                   // v head within the q/k group
-  const bool head_on = jh < r;
+  // v head (the clamp is a no-op; in this form the kernel fits 128 registers unspilled)
   const int h = r * g + min(jh, r - 1);
   const int cg = lane & 15, rg = lane >> 4;
   const int col0 = 32 * (wave & 3) + 2 * cg;      // 2 value columns
@@ -356,17 +353,17 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   const int ocol = col0 + (rg & 1);               // the column this lane outputs
   const bool out_lane = rg < 2;                   // rows 2, 3 repeat rows 0, 1
 
-  __shared__ float s_x[kMaxStepTokens][4][kD];    // post-prologue q, k, v0, v1 rows
+  __shared__ float s_x[kMaxStepTokens][3][kD];    // post-prologue q, k, v rows
   __shared__ float s_kq[kMaxStepTokens];
-  __shared__ float s_ss[8][kMaxStepTokens];       // per-wave partial sums of y^2
-  __shared__ float s_ab[2][kMaxStepTokens][2];    // alpha, beta of each head and token
-  __shared__ float s_y[8][kMaxStepTokens][64];    // y of each lane's output column
+  __shared__ float s_ss[4][kMaxStepTokens];       // per-wave partial sums of y^2
+  __shared__ float s_ab[kMaxStepTokens][2];       // alpha, beta of each token
+  __shared__ float s_y[4][kMaxStepTokens][64];    // y of each lane's output column
 
   // the gate inputs first; the state is read after the prologue, whose registers it
   // would otherwise share (four waves per SIMD need at most 128 registers per lane)
-  float ga = 0.f, gb = 0.f;  // gate inputs of (head tid >> 3, token tid & 7)
-  const int gh = r * g + min(2 * pair + (tid >> 3), r - 1), gt = tid & 7;
-  if (tid < 16 && gt < n) {
+  float ga = 0.f, gb = 0.f;  // gate inputs of token gt (tid < 8)
+  const int gh = r * g + jh, gt = tid & 7;  // gh = h
+  if (tid < 8 && gt < n) {
     const int64_t gi = ((int64_t)bseq * n + gt) * Hv + gh;
     ga = a[gi];
     gb = b[gi];
@@ -376,16 +373,15 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   f32x2_t Hs[32];
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
-  // section = wave (waves 0-3): q, k, v of head 2p, v of head 2p + 1.  raw[0..2] = cached rows
-  // (oldest first), raw[3 + t] = new token t.  The q/k cache channels belong to the
-  // pair-0 workgroup, a v head's to the workgroup of its pair.
+  // section = wave (waves 0-2): q, k, v.  raw[0..2] = cached rows (oldest first),
+  // raw[3 + t] = new token t.  The q/k cache channels belong to the workgroup of the
+  // group's first v head, the v channels to their head's workgroup.
   {
     T *cs = conv_state + (int64_t)bseq * 3 * Cc;
     const int c0 = lane * 2;
     const int slot = wave;
-    const int jv = 2 * pair + (slot - 2);
-    const bool active = slot < 2 || (slot < 4 && jv < r);
-    const bool owner = slot < 2 ? pair == 0 : true;
+    const bool active = slot < 3;
+    const bool owner = slot < 2 ? jh == 0 : true;
     int64_t cbase, hstride, sidx;
     const T *src;
     if (slot == 0) {
@@ -395,9 +391,8 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       cbase = (int64_t)Hk * kD + (int64_t)g * kD; src = k; hstride = (int64_t)Hk * kD;
       sidx = ((int64_t)bseq * n * Hk + g) * kD;
     } else {
-      const int jj = min(max(jv, 0), r - 1);
-      cbase = 2LL * Hk * kD + (int64_t)(r * g + jj) * kD; src = v; hstride = (int64_t)Hv * kD;
-      sidx = ((int64_t)bseq * n * Hv + r * g + jj) * kD;
+      cbase = 2LL * Hk * kD + (int64_t)h * kD; src = v; hstride = (int64_t)Hv * kD;
+      sidx = ((int64_t)bseq * n * Hv + h) * kD;
     }
     float xv[kMaxStepTokens][2];
 #pragma unroll
@@ -442,7 +437,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         }
       }
     }
-    if (slot < 4) {
+    if (slot < 3) {
 #pragma unroll
       for (int t = 0; t < kMaxStepTokens; ++t)
         if (t < n) {
@@ -454,9 +449,9 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   // the state (the barriers below do not wait for these loads)
 #pragma unroll
   for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
-  if (tid < 16 && gt < n) {
-    s_ab[tid >> 3][gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
-    s_ab[tid >> 3][gt][1] = sigmoidf_(gb);
+  if (tid < 8 && gt < n) {
+    s_ab[gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
+    s_ab[gt][1] = sigmoidf_(gb);
   }
   __syncthreads();
   if (wave == 0) {  // k_t . q_t of each token
@@ -474,13 +469,13 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   // of a decay multiply and an FMA: with Gam_t = alpha_t Gam_{t-1},
   //   alpha_t S_{t-1} k = Gam_t (Hs k),  S_t = Gam_t (Hs + (beta e / Gam_t) k^T).
   // When Gam_t falls below 2^-60 it is folded into Hs (and taken as 1), which also
-  // covers alpha = 0.  Gam is uniform per wave (one head per wave).
+  // covers alpha = 0.  Gam is uniform (one head per workgroup).
   float Gam = 1.0f;
 #pragma unroll 1
   for (int t = 0; t < n; ++t) {
     {
-      const float alpha = s_ab[hl][t][0];
-      const float beta = s_ab[hl][t][1];
+      const float alpha = s_ab[t][0];
+      const float beta = s_ab[t][1];
       float Gt = Gam * alpha;
       if (Gt < 0x1p-60f) {
 #pragma unroll
@@ -510,7 +505,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         sk[c] = rows4_sum(sk[c]);
         sq[c] = rows4_sum(sq[c]);
       }
-      const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_x[t][2 + hl][col0]);
+      const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_x[t][2][col0]);
       const float kq = s_kq[t];
       float be[2];
       float y[2];
@@ -533,7 +528,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
           Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
         }
       }
-      if (t + 1 == commit && head_on) {
+      if (t + 1 == commit) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)
           st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2_t{Gam * Hs[i].x, Gam * Hs[i].y});
@@ -558,12 +553,11 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     }
   }
   __syncthreads();
-  if (head_on && out_lane) {
+  if (out_lane) {
 #pragma unroll
     for (int t = 0; t < kMaxStepTokens; ++t) {
       if (t < n) {
-        const float ssh = (s_ss[4 * hl][t] + s_ss[4 * hl + 1][t]) +
-                          (s_ss[4 * hl + 2][t] + s_ss[4 * hl + 3][t]);
+        const float ssh = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
         const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
         const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
         Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
@@ -580,8 +574,7 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 void *conv_state, const int32_t *num_commit, void *o, int batch,
                                 int n, int Hk, int Hv, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  const unsigned npair = (unsigned)((Hv / Hk + 1) / 2);
-  dim3 grid((unsigned)batch * (unsigned)Hk * npair);
+  dim3 grid((unsigned)batch * (unsigned)Hv);
   hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kTokThreads), 0, stream,
                      (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
                      dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
