@@ -712,6 +712,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     }
     __syncthreads();  // (1) prologue tiles ready
     refresh();
+    // the diagonal-tile waves (gram tile, L/M and the 16x16 inverse) are this phase's
+    // critical path: they take issue priority over the other waves on their SIMD
+    if (MODE == kFull && wave < 2) __builtin_amdgcn_s_setprio(1);
 
     if (v_on) {  // v: 4 tokens x 4 channels -> fp32 V^T [dv][tok], 16 bytes per channel
       float x[4][4];
@@ -821,6 +824,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     // next chunk's raw rows: the k waves (off the diagonal tiles) go first so that
     // the q waves' loads after the barrier do not queue behind theirs
     if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (3) -L, M, T_bb - I and the next gates ready; Q and K consumed
     refresh();
     if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
