@@ -625,6 +625,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     if (gates_next) load_gates(t0 + kChunk, ga, gb);
 
     // ================= prologue: conv + SiLU (+ L2) -> LDS ========================
+    // Issue priority follows each phase's longest waves: here the k waves (K^T
+    // regrouping, the lo halves), from barrier 1 to barrier 4 waves 0 and 1 (their
+    // diagonal gram tiles, L/M, the 16x16 inverses, then the q waves' prefetch).
+    // Between them the two workgroups on a compute unit fill the SIMDs.
+    if (MODE == kFull && wave >= 2) __builtin_amdgcn_s_setprio(1);
     if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
       for (int rr = 0; rr < 7; ++rr) {
@@ -710,10 +715,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (1) prologue tiles ready
     refresh();
-    // the diagonal-tile waves (gram tile, L/M and the 16x16 inverse) are this phase's
-    // critical path: they take issue priority over the other waves on their SIMD
     if (MODE == kFull && wave < 2) __builtin_amdgcn_s_setprio(1);
 
     if (v_on) {  // v: 4 tokens x 4 channels -> fp32 V^T [dv][tok], 16 bytes per channel
@@ -824,7 +828,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     // next chunk's raw rows: the k waves (off the diagonal tiles) go first so that
     // the q waves' loads after the barrier do not queue behind theirs
     if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);
-    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (3) -L, M, T_bb - I and the next gates ready; Q and K consumed
     refresh();
     if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
@@ -881,6 +884,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
           for (int i = 0; i < 4; ++i)
             sW[(16 * rt + 4 * lg + i) * kRowS + 32 * wave + 16 * ct + ln] = f2bf(-Wacc[rt][ct][i]);
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (4) -W ready
     refresh();
 
