@@ -87,14 +87,22 @@ size_t gdn_prefill_workspace_bytes(const gdn_params *p, int32_t num_seqs,
  *   a, b          [T, Hv] fp32
  *   init_state    [N, Hv, D, D] fp32, or NULL for zeros
  *   cu_seqlens    [N+1] int32 device: cu[0] = 0, non-decreasing, cu[N] = T;
- *                 may be NULL when N = 1.  Contents are not validated unless
- *                 the environment sets GDN_VALIDATE=1 (then the call copies
- *                 them to the host synchronously and checks them).
+ *                 may be NULL when N = 1.  The host does not read the contents
+ *                 (no synchronisation); the first kernel checks them on the
+ *                 device, and for an invalid table runs nothing else (o and
+ *                 final_state are left unwritten) and sets a per-device error
+ *                 flag that gdn_check_device_errors() reports.  With the
+ *                 environment variable GDN_VALIDATE=1 the call instead
+ *                 synchronises, reports a flag left by an earlier call, copies
+ *                 cu_seqlens to the host and checks it before launching.
  *                 Zero-length sequences are allowed: their final state equals
  *                 their initial state bit for bit.
  *   conv_state_in [N, 3, Cc] act dtype, or NULL for zeros
  *   o             [T, Hv, D] act dtype (out); must not alias an input
- *   final_state   [N, Hv, D, D] fp32 (out); may alias init_state
+ *   final_state   [N, Hv, D, D] fp32 (out); may alias init_state (a sequence
+ *                 split over several workgroups starts from a copy of its
+ *                 initial state taken in the workspace before any final state
+ *                 is written)
  *   conv_state_out[N, 3, Cc] act dtype (out), or NULL; may alias conv_state_in
  *   workspace     device memory of at least gdn_prefill_workspace_bytes()
  *                 bytes (may be NULL when that is 0), 256-byte aligned.
@@ -106,6 +114,12 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v,
                        int64_t total_tokens, const void *conv_state_in,
                        void *o, float *final_state, void *conv_state_out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Reports, and clears, an error that a kernel of an earlier call on the current
+ * device found in device-resident arguments: today an invalid cu_seqlens table
+ * passed to gdn_prefill (GDN_ERR_INVALID_ARGUMENT).  Synchronises `stream` first
+ * (host synchronisation).  GDN_OK when no such error is pending. */
+gdn_status gdn_check_device_errors(void *stream);
 
 /* One decode step (one new token) for `batch` independent sequences: the
  * field guide's six update operations applied once per (sequence, v head),

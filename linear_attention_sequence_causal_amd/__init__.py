@@ -25,8 +25,8 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
-            "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times", "gdn_status_string", "gdn_last_error",
-            "gdn_version")
+            "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times",
+            "gdn_check_device_errors", "gdn_status_string", "gdn_last_error", "gdn_version")
 PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
             L.gdn_last_error.argtypes = []
             L.gdn_version.restype = ctypes.c_char_p
             L.gdn_version.argtypes = []
+            L.gdn_check_device_errors.restype = ctypes.c_int
+            L.gdn_check_device_errors.argtypes = [vp]
             L.gdn_prefill_last_kernel_times.restype = ctypes.c_int
             L.gdn_prefill_last_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                         ctypes.c_int]
@@ -209,6 +211,13 @@ def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_
                                    ctypes.byref(p), _ptr(state), _ptr(conv_state),
                                    _ptr(num_commit), _ptr(o), B, n, _stream()))
     return o
+
+
+def check_device_errors():
+    """Raise GdnError if a kernel of an earlier call on the current device found invalid
+    device-resident arguments (an invalid cu_seqlens table); clears the flag.
+    Synchronises torch's current stream."""
+    _check(lib().gdn_check_device_errors(_stream()))
 
 
 def last_kernel_times():

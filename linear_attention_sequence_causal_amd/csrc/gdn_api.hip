@@ -131,7 +131,23 @@ int gdn_prefill_last_kernel_times(float *ms, int max_kernels) {
   return n;
 }
 
-const char *gdn_version(void) { return "gdn-gfx950 0.1"; }
+const char *gdn_version(void) { return "gdn-gfx950 0.2"; }
+
+gdn_status gdn_check_device_errors(void *stream) {
+  g_err[0] = 0;
+  gdn_status st = check_device();
+  if (st != GDN_OK) return st;
+  if (hipError_t e = hipStreamSynchronize((hipStream_t)stream); e != hipSuccess)
+    return hip_fail(e, "stream synchronisation");
+  int flag = 0;
+  if (hipError_t e = gdn::take_prefill_error(&flag); e != hipSuccess)
+    return hip_fail(e, "reading the device error flag");
+  if (flag)
+    return fail(GDN_ERR_INVALID_ARGUMENT,
+                "a gdn_prefill call on this device had invalid cu_seqlens contents (its o and "
+                "final states were not written)");
+  return GDN_OK;
+}
 
 size_t gdn_prefill_workspace_bytes(const gdn_params *p, int32_t num_seqs, int64_t total_tokens) {
   if (check_params(p) != GDN_OK || num_seqs < 0 || total_tokens < 0) return (size_t)-1;
@@ -171,6 +187,17 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
   if (st != GDN_OK) return st;
   if (num_seqs == 0) return GDN_OK;
 
+  if (const char *ev = getenv("GDN_VALIDATE"); ev && ev[0] == '1') {
+    // report an invalid table met by an earlier call first
+    if (hipError_t e = hipStreamSynchronize((hipStream_t)stream); e != hipSuccess)
+      return hip_fail(e, "GDN_VALIDATE stream synchronisation");
+    int flag = 0;
+    if (hipError_t e = gdn::take_prefill_error(&flag); e != hipSuccess)
+      return hip_fail(e, "GDN_VALIDATE error flag");
+    if (flag)
+      return fail(GDN_ERR_INVALID_ARGUMENT,
+                  "an earlier gdn_prefill call on this device had invalid cu_seqlens");
+  }
   if (const char *ev = getenv("GDN_VALIDATE"); ev && ev[0] == '1' && cu_seqlens) {
     std::vector<int32_t> cu(num_seqs + 1);
     hipError_t e = hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (num_seqs + 1),

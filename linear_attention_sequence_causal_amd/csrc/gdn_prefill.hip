@@ -169,7 +169,6 @@ struct PrefillArgs {
   float *starts;           // [max_segments][Hv][D][D]
   int Hk, Hv;
   int64_t Cc;
-  int precise_all;         // split-precision state update on every chunk
 };
 
 // NC channels of one token as raw 32-bit words (bf16 pairs or fp32)
@@ -495,7 +494,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         H0 = P.map_zero[m * Hv + h] ? P.maps + ((m * Hv + h) * 2 + 1) * kD * kD
                                     : P.starts + ((int64_t)segi * Hv + h) * kD * kD;
       } else if (P.init_state) {
-        H0 = P.init_state + ((int64_t)seg.seq * Hv + h) * kD * kD;
+        // A sequence of several segments starts from the copy of its initial state that
+        // the combine pass made: its last segment writes final_state in this launch,
+        // and final_state may alias init_state.
+        H0 = seg.nseg > 1 ? P.starts + ((int64_t)segi * Hv + h) * kD * kD
+                          : P.init_state + ((int64_t)seg.seq * Hv + h) * kD * kD;
       }
     }
 #pragma unroll
@@ -608,15 +611,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     const float *const sGam = gcur + GB_GAM * kChunk, *const sBG = gcur + GB_BG * kChunk;
     const float *const sDec = gcur + GB_DEC * kChunk, *const sBv = gcur + GB_BV * kChunk;
     const float *const sGamQ = gcur + GB_GAMQ * kChunk;
-    // Split precision for the state update, and the lo half of K^T that it and the
-    // exact right-hand side beta gamma K use: on a sequence's last 128 tokens (the
-    // final state) and on every chunk whose decay leaves more than 2^-4 of the state
-    // (nothing would damp the rounding of a one-pass update there; fast-decaying
-    // heads never take it).  gC is the same in every lane.
+    // gC = gamma_C, the chunk's decay (the same in every lane)
     const float gC = sGam[kChunk - 1];
-    const bool precise =
-        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gC))) >= (1.0f / 16.0f) ||
-        (MODE == kFull && (P.precise_all || (last_seg && c >= nchunks - 4)));
     // the next chunk's gate inputs (wave 3), issued first and consumed in the gram
     // phase under the same condition (left undefined otherwise, so that no select
     // waits for the loads here)
@@ -690,20 +686,12 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
                            __builtin_amdgcn_perm(w[3][e], w[2][e], sel));
           }
         };
-        uint32_t hw[4][4];  // token r: channels (2e, 2e+1) in word e
-        if (precise) {  // hi and lo halves
-          uint32_t lw[4][4];
+        uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
-          put_kt(sKTl, lw);
-        } else {  // hi halves only
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hw[r][e] = pk_bf16(x[r][2 * e], x[r][2 * e + 1]);
-        }
+          for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
+        put_kt(sKTl, lw);
         put_kt(sKTh, hw);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -844,8 +832,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         const int dcol = 32 * wave + 16 * ct + ln;
         const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
         const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
-        u16x4 kl = {0, 0, 0, 0};  // beta gamma K in fp32 where the lo halves exist
-        if (precise) kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);
+        const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);  // beta gamma K in fp32
         f32x4 vv = {0.f, 0.f, 0.f, 0.f};
         if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
 #pragma unroll
@@ -961,14 +948,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) Hacc[dt][ct][i] *= gC;
-      if (!precise) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const u16x8 ak = load_a_tok(sKTh, tl, dt);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Hacc[dt][ct] = mfma16(ak, Uh[ct], Hacc[dt][ct]);
-        }
-      } else {
+      {
         // lo parts of U: u - bf16(u)
         u16x8 Ul[2];
 #pragma unroll
@@ -1076,18 +1056,41 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 }
 
 // ------------------------------------------------------------ segment table
+// Set (to 1) by the segment table when cu_seqlens is invalid; read and cleared by
+// the host (gdn_check_device_errors).  One copy per device.
+__device__ int g_prefill_bad_cu = 0;
+
 // One workgroup: sequence lengths -> segments (prefix sums over sequences).
+// cu_seqlens must have cu[0] = 0, cu[i] <= cu[i+1] and cu[N] = T; otherwise the
+// table is left empty (no segment runs, o and the final states are not written)
+// and g_prefill_bad_cu is set.
 __global__ void __launch_bounds__(1024) segment_table_kernel(
     const int32_t *cu, int N, int64_t T, int seg_len, int64_t max_segments, int64_t max_maps,
     SegInfo *segs, int32_t *hdr, int32_t *map_seg, int32_t *seq_first) {
   __shared__ int s_nseg[1024], s_nmap[1024];
-  __shared__ int s_base_seg, s_base_map;
+  __shared__ int s_base_seg, s_base_map, s_bad;
   const int tid = threadIdx.x;
   if (tid == 0) {
     s_base_seg = 0;
     s_base_map = 0;
+    s_bad = 0;
   }
   __syncthreads();
+  if (cu) {  // validate the whole table first
+    for (int n = tid; n < N; n += 1024) {
+      const int b0 = cu[n], e0 = cu[n + 1];
+      if (e0 < b0 || (n == 0 && b0 != 0) || (n == N - 1 && (int64_t)e0 != T)) s_bad = 1;
+    }
+    __syncthreads();
+    if (s_bad) {
+      if (tid == 0) {
+        hdr[0] = 0;
+        hdr[1] = 0;
+        g_prefill_bad_cu = 1;
+      }
+      return;
+    }
+  }
   for (int n0 = 0; n0 < N; n0 += 1024) {
     const int n = n0 + tid;
     int b = 0, e = 0, ns = 0, nm = 0, nch = 0;
@@ -1143,12 +1146,29 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
     __syncthreads();
   }
   if (tid == 0) {
-    // More segments than the bound means cu_seqlens was invalid (overlapping or
-    // not ending at T): run nothing rather than index past the tables.
+    // (cannot happen for a valid table; kept so that no segment index ever passes
+    // the workspace tables)
     const bool ok = s_base_seg <= max_segments && s_base_map <= max_maps;
     hdr[0] = ok ? s_base_seg : 0;
     hdr[1] = ok ? s_base_map : 0;
+    if (!ok) g_prefill_bad_cu = 1;
   }
+}
+
+// Host side: read and clear the current device's invalid-cu_seqlens flag
+// (synchronous; the caller has synchronised the stream that ran the prefill).
+hipError_t take_prefill_error(int *flag) {
+  int v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_prefill_bad_cu), sizeof(int), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *flag = v;
+  if (v) {
+    const int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_prefill_bad_cu), &zero, sizeof(int), 0,
+                          hipMemcpyHostToDevice);
+  }
+  return e;
 }
 
 // ------------------------------------------------------------ combine (pass 2)
@@ -1177,6 +1197,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
   // H_s lives in hreg once loaded (have), else it is src (NULL: zeros)
   const float *src = init_state ? init_state + ((int64_t)s0.seq * Hv + h) * kD * kD : nullptr;
   bool have = false;
+  if (src) {
+    // The first segment's start state: a copy of the initial state, which the full
+    // pass reads instead of init_state (final_state, written by the sequence's last
+    // segment in that pass, may alias init_state).
+    float *dst = starts + ((int64_t)segi * Hv + h) * kD * kD;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hreg[j] = src[row * kD + col0 + j];
+      dst[row * kD + col0 + j] = hreg[j];
+    }
+    have = true;
+  }
   // the maps' slots and zero flags, 256 segments at a time, loaded in parallel
   __shared__ int sMap[256], sZero[256];
   for (int sb = 0; sb + 1 < s0.nseg; sb += 256) {
@@ -1380,8 +1412,6 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   A.map_zero = plan.max_maps > 0 ? (int32_t *)(ws + plan.off_flags) : nullptr;
   A.Hk = p.num_qk_heads; A.Hv = p.num_v_heads;
   A.Cc = 2LL * p.num_qk_heads * kD + (int64_t)p.num_v_heads * kD;
-  const char *ev = getenv("GDN_PRECISE_ALL");
-  A.precise_all = (ev && ev[0] == '1') ? 1 : 0;
   if (p.act_dtype == GDN_BF16)
     return launch_typed<bf16_t>(plan, A, cu_seqlens, num_seqs, total_tokens, conv_state_out,
                                 stream, tm);

@@ -56,6 +56,10 @@ struct PrefillTiming {
   bool ran[kTimedKernels];
 };
 
+// Reads and clears this device's flag for invalid cu_seqlens contents (set by the
+// segment table of an earlier gdn_prefill call).  Synchronous.
+hipError_t take_prefill_error(int *flag);
+
 hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k, const void *v,
                           const float *a, const float *b, const void *z, const gdn_params &p,
                           const float *init_state, const int32_t *cu_seqlens, int32_t num_seqs,

@@ -110,6 +110,56 @@ def test_decode_full_batch_sampled_sequences():
 
 
 @gpu
+def test_decode_1000_steps_full_length():
+    """The decode workload as specified: B = 256, 16/32 heads, 1000 consecutive steps
+    with fresh inputs, in the launch configuration the benchmark times.  o of all
+    1000 steps and the state and cache after step 1000 are checked on 64 sequences
+    (every fourth, all heads).  The oracle's reference for n consecutive decode steps
+    is one prefill of the n tokens from the cached state and history (decode after
+    prefill equals the longer prefill, pinned bitwise on the CPU), run on 16
+    sequences at a time."""
+    import linear_attention_sequence_causal_amd as gdn
+    w = S.DECODE_B256
+    steps, B = 1000, w.decode_batch
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, steps, "cuda")
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    sample = torch.arange(0, B, 4, device="cuda")
+    o_s = torch.empty((steps, sample.numel(), w.num_v_heads, w.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    o = torch.empty((B, w.num_v_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    for s in range(steps):
+        gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s], toks["b"][s],
+                        toks["z"][s], setup["conv_w"], setup["A_log"], setup["dt_bias"],
+                        setup["norm_w"], setup["state"], setup["conv_cache"], out=o)
+        o_s[s] = o.index_select(0, sample)
+    torch.cuda.synchronize()
+    f = S.to_f64
+    num_o = den_o = num_s = den_s = 0.0
+    for i in range(0, sample.numel(), 16):
+        sel = sample[i:i + 16]
+        nb = sel.numel()
+        seqs = lambda t: t.index_select(1, sel).transpose(0, 1).reshape((nb * steps,) + tuple(t.shape[2:]))
+        cu = np.arange(nb + 1, dtype=np.int64) * steps
+        o_ref, st_ref, cc_ref = oracle.prefill(
+            f(seqs(toks["q"])), f(seqs(toks["k"])), f(seqs(toks["v"])), f(seqs(toks["a"])),
+            f(seqs(toks["b"])), f(seqs(toks["z"])), f(setup["conv_w"]), f(setup["A_log"]),
+            f(setup["dt_bias"]), f(setup["norm_w"]), cu_seqlens=cu,
+            init_state=f(st0.index_select(0, sel)), conv_in=f(cc0.index_select(0, sel)))
+        o_g = f(o_s[:, i:i + nb].transpose(0, 1).reshape(o_ref.shape))
+        st_g = f(setup["state"].index_select(0, sel))
+        num_o += float(np.sum((o_g - o_ref) ** 2))
+        den_o += float(np.sum(o_ref ** 2))
+        num_s += float(np.sum((st_g - st_ref) ** 2))
+        den_s += float(np.sum(st_ref ** 2))
+        assert np.array_equal(f(setup["conv_cache"].index_select(0, sel)), cc_ref)
+        del o_ref, o_g
+    eo, es = (num_o / den_o) ** 0.5, (num_s / den_s) ** 0.5
+    print(f"decode B=256 x 1000 steps, 64 sequences: o rel-L2 {eo:.3e} state rel-L2 {es:.3e}")
+    assert eo < O_TOL and es < STATE_TOL
+
+
+@gpu
 def test_decode_zero_batch_is_a_no_op():
     import linear_attention_sequence_causal_amd as gdn
     w = S.scaled(S.DECODE_B256, decode_batch=1, seed=50)

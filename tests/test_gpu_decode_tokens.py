@@ -90,8 +90,9 @@ def test_tokens_fp32_small_heads():
 @gpu
 @pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 9), (1, 1)])
 def test_tokens_head_layouts(hk, hv):
-    """One, four and three v heads per q/k head: an odd count leaves the second head
-    of the last pair empty (its waves compute but store nothing)."""
+    """One, four and three v heads per q/k head: the v heads of a q/k head run in rounds
+    of two, and an odd count leaves the last round's second slot empty (its waves
+    compute nothing and store nothing)."""
     w = S.scaled(S.DECODE_B256, decode_batch=5, num_qk_heads=hk, num_v_heads=hv, seed=71 + hv)
     setup, t = _case(w, 3)
     _check(setup, t, 3, label=f"decode_tokens n=3 Hk={hk} Hv={hv}")
@@ -154,14 +155,17 @@ def test_tokens_equal_successive_single_steps():
 
 
 @gpu
-def test_tokens_full_batch_sampled_sequences():
-    """B=256, 16/32 heads, n=4 in the launch configuration the benchmark times; the
-    oracle recomputes 6 sampled sequences (all heads and tokens)."""
+@pytest.mark.parametrize("commit", [None, "mixed"])
+def test_tokens_full_batch_all_sequences(commit):
+    """B=256, 16/32 heads, n=4 in the launch configuration the benchmark times, every
+    sequence, head and token against the oracle; with all tokens committed and with
+    per-sequence commit counts 0..4 (the cache channels of a q/k head are read and
+    advanced by one workgroup only, so no sequence sees another's advance)."""
     n = 4
     w = S.DECODE_B256
     setup, t = _case(w, n)
-    sample = [0, 1, 77, 128, 200, 255]
-    _check(setup, t, n, sel=sample, label="decode_tokens B=256 n=4 sampled")
+    nc = None if commit is None else [i % (n + 1) for i in range(w.decode_batch)]
+    _check(setup, t, n, num_commit=nc, label=f"decode_tokens B=256 n=4 commit={commit}")
 
 
 @gpu
