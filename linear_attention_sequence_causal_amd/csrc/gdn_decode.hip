@@ -300,18 +300,19 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One workgroup per (sequence b, q/k head g).  It owns the conv-cache channels of q/k
-// head g and of the r = Hv/Hk v heads that read it, so no other workgroup of the
-// launch reads or writes them (each channel is read and then advanced by one thread).
-// The v heads run in rounds of P = min(r, 2), four waves per v head: wave w of a head
-// holds value columns 32 (w & 3) + 2 cg, + 1 (cg = lane & 15) and key rows
-// 32 rg .. + 31 (rg = lane >> 4) of its fp32 state, 64 values per lane, so that four
-// waves fit on a SIMD and the state reads of some workgroups overlap the token loops
-// of others.  q and k are convolved once per workgroup, before the first round; each
-// round's v heads after it.  A token's S k and S q sums are finished across the four
-// row lanes with permlane swaps, so the token loop needs no LDS round trip and no
-// barrier; the RMS of each token's y (split over the head's four waves) is taken once
-// after the loop.
+// One workgroup of four waves per (sequence, v head): wave w holds value columns
+// 32 w + 2 cg, + 1 (cg = lane & 15) and key rows 32 rg .. + 31 (rg = lane >> 4) of the
+// fp32 state, 64 values per lane, so that four waves fit on a SIMD and the state
+// reads of some workgroups overlap the token loops of others.  The r workgroups of a
+// q/k head each convolve its q and k rows from the cache and only read the cache's
+// q/k channels; a second kernel on the same stream advances those channels after
+// every workgroup has read them (qk_cache_advance_kernel), so no workgroup reads a
+// cache word that another one of the same launch writes.  The v channels of a head
+// are read and advanced by the thread that convolves them, in its head's workgroup.
+// A token's S k and S q sums are finished across the four row lanes with permlane
+// swaps, so the token loop needs no LDS round trip and no barrier; the RMS of each
+// token's y (split over the four waves) is taken once after the loop.
+constexpr int kTokThreads = 256;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // One v head's fp32 state as a raw buffer: each lane's 8-byte pieces are addressed by
 // its own offset plus a uniform row offset, so no per-row 64-bit addresses are kept
@@ -330,47 +331,8 @@ __device__ __forceinline__ void st_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, 
                                         kNtPolicy);
 }
 
-// Width-4 causal conv + SiLU of channels cbase + c0, + 1 over the three cached rows and
-// the n new tokens (raw row t of the call at src[sidx + t * hstride]), then the
-// in-place advance of those two cache channels by `commit` tokens.  The calling thread
-// is the only one in the launch that reads or writes them.
 template <typename T>
-__device__ __forceinline__ void conv2_advance(T *cs, int64_t Cc, const T *src, int64_t sidx,
-                                              int64_t hstride, int64_t cbase, int c0,
-                                              const float *conv_w, int n, int commit,
-                                              float (&xv)[kMaxStepTokens][2]) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t ch = cbase + c0 + u;
-    float raw[3 + kMaxStepTokens];
-    raw[0] = Act<T>::load(cs, ch);
-    raw[1] = Act<T>::load(cs, Cc + ch);
-    raw[2] = Act<T>::load(cs, 2 * Cc + ch);
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t)
-      raw[3 + t] = t < n ? Act<T>::load(src, sidx + t * hstride + c0 + u) : 0.f;
-    const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t)
-      xv[t][u] = siluf_(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
-    // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
-    if (commit > 0) {
-#pragma unroll
-      for (int s2 = 0; s2 < 3; ++s2) {
-        float x = raw[0];
-#pragma unroll
-        for (int i = 1; i < 3 + kMaxStepTokens; ++i)
-          if (i == commit + s2) x = raw[i];
-        Act<T>::store(cs, s2 * Cc + ch, x);
-      }
-    }
-  }
-}
-
-// MULTI: more than one round (r > P); the one-round form keeps every value of the
-// token loop in registers.
-template <typename T, int P, bool MULTI>
-__global__ void __launch_bounds__(256 * P) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ void __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                      const float *__restrict__ a, const float *__restrict__ b,
                      const T *__restrict__ z, const float *__restrict__ conv_w,
@@ -380,211 +342,266 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
                      const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
                      int n) {
   const int r = Hv / Hk;
-  const int g = blockIdx.x % Hk;                  // q/k head
-  const int bseq = blockIdx.x / Hk;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
-  const int hw = wave & 3;                        // wave within its v head
-  const int jp = wave >> 2;                       // v head slot of a round (0 .. P-1)
+  const int jh = blockIdx.x % r;                  // v head within its q/k group
+  const int g = (blockIdx.x / r) % Hk;            // q/k head
+  const int bseq = blockIdx.x / r / Hk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
 
+  // v head (the clamp is a no-op; in this form the kernel fits 128 registers unspilled)
+  const int h = r * g + min(jh, r - 1);
   const int cg = lane & 15, rg = lane >> 4;
-  const int col0 = 32 * hw + 2 * cg;              // 2 value columns
+  const int col0 = 32 * (wave & 3) + 2 * cg;      // 2 value columns
   const int row0 = 32 * rg;                       // 32 key rows
   const int ocol = col0 + (rg & 1);               // the column this lane outputs
   const bool out_lane = rg < 2;                   // rows 2, 3 repeat rows 0, 1
-  // prologue sections: q and k (first round only), then the round's v heads; with
-  // P = 2 they are spread over both heads' waves (q 0, v0 1, k 4, v1 5)
-  const int sec_q = 0, sec_k = P == 2 ? 4 : 1;
-  const int vslot = P == 2 ? ((wave & 3) == 1 ? jp : -1) : (wave == 2 ? 0 : -1);
 
-  __shared__ float s_qk[kMaxStepTokens][2][kD];   // post-prologue q, k rows
-  __shared__ float s_v[P][kMaxStepTokens][kD];    // post-prologue v rows of the round
+  __shared__ float s_x[kMaxStepTokens][3][kD];    // post-prologue q, k, v rows
   __shared__ float s_kq[kMaxStepTokens];
-  __shared__ float s_ss[4 * P][kMaxStepTokens];   // per-wave partial sums of y^2
-  __shared__ float s_ab[P][kMaxStepTokens][2];    // alpha, beta of each token
-  __shared__ float s_y[4 * P][kMaxStepTokens][64];  // y of each lane's output column
+  __shared__ float s_ss[4][kMaxStepTokens];       // per-wave partial sums of y^2
+  __shared__ float s_ab[kMaxStepTokens][2];       // alpha, beta of each token
+  __shared__ float s_y[4][kMaxStepTokens][64];    // y of each lane's output column
 
-  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
-  const int c0 = lane * 2;
+  // the gate inputs first; the state is read after the prologue, whose registers it
+  // would otherwise share (four waves per SIMD need at most 128 registers per lane)
+  float ga = 0.f, gb = 0.f;  // gate inputs of token gt (tid < 8)
+  const int gh = r * g + jh, gt = tid & 7;  // gh = h
+  if (tid < 8 && gt < n) {
+    const int64_t gi = ((int64_t)bseq * n + gt) * Hv + gh;
+    ga = a[gi];
+    gb = b[gi];
+  }
+  const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
+  const uint32_t hoff = (uint32_t)(row0 * kD + col0) * (uint32_t)sizeof(float);
+  f32x2_t Hs[32];
 
-  for (int j0 = 0; j0 < (MULTI ? r : 1); j0 += P) {
-    const int jh = j0 + jp;
-    const bool head_on = jh < r;                  // uniform per wave
-    const int h = r * g + min(jh, r - 1);
-    // the gate inputs first; the state is read after the prologue, whose registers it
-    // would otherwise share (four waves per SIMD need at most 128 registers per lane)
-    float ga = 0.f, gb = 0.f;                     // gate inputs of token gt
-    const int gt = lane & 7;
-    const bool gate_lane = hw == 0 && lane < 8 && gt < n && head_on;
-    if (gate_lane) {
-      const int64_t gi = ((int64_t)bseq * n + gt) * Hv + h;
-      ga = a[gi];
-      gb = b[gi];
+  // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
+  // section = wave (waves 0-2): q, k, v.  raw[0..2] = cached rows (oldest first),
+  // raw[3 + t] = new token t.  Only the v channels are advanced here (by their head's
+  // workgroup); the q/k channels are advanced by qk_cache_advance_kernel afterwards.
+  {
+    T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+    const int c0 = lane * 2;
+    const int slot = wave;
+    const bool active = slot < 3;
+    const bool owner = slot == 2;  // v channels only
+    int64_t cbase, hstride, sidx;
+    const T *src;
+    if (slot == 0) {
+      cbase = (int64_t)g * kD; src = q; hstride = (int64_t)Hk * kD;
+      sidx = ((int64_t)bseq * n * Hk + g) * kD;
+    } else if (slot == 1) {
+      cbase = (int64_t)Hk * kD + (int64_t)g * kD; src = k; hstride = (int64_t)Hk * kD;
+      sidx = ((int64_t)bseq * n * Hk + g) * kD;
+    } else {
+      cbase = 2LL * Hk * kD + (int64_t)h * kD; src = v; hstride = (int64_t)Hv * kD;
+      sidx = ((int64_t)bseq * n * Hv + h) * kD;
     }
-    const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
-    const uint32_t hoff = (uint32_t)(row0 * kD + col0) * (uint32_t)sizeof(float);
-    f32x2_t Hs[32];
-
-    // ---- prologue: conv + SiLU of every new token, 2 channels per thread --------------
-    // one section per wave (one code path: q, k or a v head), q and k L2-normalised
-    {
-      int sec = -1;  // 0 q, 1 k, 2 v (uniform per wave)
-      if (j0 == 0 && wave == sec_q) sec = 0;
-      else if (j0 == 0 && wave == sec_k) sec = 1;
-      else if (vslot >= 0 && j0 + vslot < r) sec = 2;
-      if (sec >= 0) {
-        const int hv = r * g + j0 + max(vslot, 0);
-        const T *src = sec == 0 ? q : sec == 1 ? k : v;
-        const int64_t hstride = sec == 2 ? (int64_t)Hv * kD : (int64_t)Hk * kD;
-        const int64_t sidx = sec == 2 ? ((int64_t)bseq * n * Hv + hv) * kD
-                                      : ((int64_t)bseq * n * Hk + g) * kD;
-        const int64_t cbase = sec == 2 ? 2LL * Hk * kD + (int64_t)hv * kD
-                                       : (int64_t)sec * Hk * kD + (int64_t)g * kD;
-        float xv[kMaxStepTokens][2];
-        conv2_advance<T>(cs, Cc, src, sidx, hstride, cbase, c0, conv_w, n, commit, xv);
-        float *dst = sec == 2 ? &s_v[max(vslot, 0)][0][0] : &s_qk[0][sec][0];
-        const int tstride = sec == 2 ? kD : 2 * kD;  // floats between tokens
+    float xv[kMaxStepTokens][2];
 #pragma unroll
-        for (int t = 0; t < kMaxStepTokens; ++t) {
-          if (t < n) {
-            float f = 1.0f;
-            if (sec < 2) {
-              const float ss = wave_sum(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
-              f = (sec == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
-            }
-            dst[t * tstride + c0] = xv[t][0] * f;
-            dst[t * tstride + c0 + 1] = xv[t][1] * f;
+    for (int t = 0; t < kMaxStepTokens; ++t) xv[t][0] = xv[t][1] = 0.f;
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t ch = cbase + c0 + u;
+        float raw[3 + kMaxStepTokens];
+        raw[0] = Act<T>::load(cs, ch);
+        raw[1] = Act<T>::load(cs, Cc + ch);
+        raw[2] = Act<T>::load(cs, 2 * Cc + ch);
+#pragma unroll
+        for (int t = 0; t < kMaxStepTokens; ++t)
+          raw[3 + t] = t < n ? Act<T>::load(src, sidx + t * hstride + c0 + u) : 0.f;
+        const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
+#pragma unroll
+        for (int t = 0; t < kMaxStepTokens; ++t)
+          xv[t][u] = siluf_(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
+        // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
+        // (the reads above precede these writes, and only this thread touches ch)
+        if (owner && commit > 0) {
+#pragma unroll
+          for (int s2 = 0; s2 < 3; ++s2) {
+            float x = raw[0];
+#pragma unroll
+            for (int i = 1; i < 3 + kMaxStepTokens; ++i)
+              if (i == commit + s2) x = raw[i];
+            Act<T>::store(cs, s2 * Cc + ch, x);
           }
         }
       }
     }
-    // the state (the barriers below do not wait for these loads)
-    if (head_on) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
-    }
-    if (gate_lane) {
-      s_ab[jp][gt][0] = __expf(log_decay(ga, A_log[h], dt_bias[h]));
-      s_ab[jp][gt][1] = sigmoidf_(gb);
-    }
-    __syncthreads();
-    if (j0 == 0) {
-      if (wave == 0) {  // k_t . q_t of each token
-        for (int t = 0; t < n; ++t) {
-          const float kq = wave_sum(s_qk[t][0][2 * lane] * s_qk[t][1][2 * lane] +
-                                    s_qk[t][0][2 * lane + 1] * s_qk[t][1][2 * lane + 1]);
-          if (lane == 0) s_kq[t] = kq;
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---- token loop: the state stays in registers, no barrier ---------------------------
-    // The registers hold the state divided by the running decay product of this call,
-    // S = Gam * Hs, so a token costs one FMA per state element for the update instead
-    // of a decay multiply and an FMA: with Gam_t = alpha_t Gam_{t-1},
-    //   alpha_t S_{t-1} k = Gam_t (Hs k),  S_t = Gam_t (Hs + (beta e / Gam_t) k^T).
-    // When Gam_t falls below 2^-60 it is folded into Hs (and taken as 1), which also
-    // covers alpha = 0.  Gam is uniform (one head per wave).
-    if (head_on) {
-      float Gam = 1.0f;
-#pragma unroll 1
-      for (int t = 0; t < n; ++t) {
-        const float alpha = s_ab[jp][t][0];
-        const float beta = s_ab[jp][t][1];
-        float Gt = Gam * alpha;
-        if (Gt < 0x1p-60f) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            Hs[i].x *= Gt; Hs[i].y *= Gt;
-          }
-          Gt = 1.0f;
-        }
-        Gam = Gt;
-        // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
-        // within each 16-lane row); k again for the update, to keep registers low
-        float sk[2] = {0, 0}, sq[2] = {0, 0};
-#pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-          const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_qk[t][1][row0 + i]);
-          const f32x4 qq = *reinterpret_cast<const f32x4 *>(&s_qk[t][0][row0 + i]);
-          const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const f32x2_t hv = Hs[i + u];
-            sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
-            sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          sk[c] = rows4_sum(sk[c]);
-          sq[c] = rows4_sum(sq[c]);
-        }
-        const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_v[jp][t][col0]);
-        const float kq = s_kq[t];
-        float be[2];
-        float y[2];
-        const float vs[2] = {vv.x, vv.y};
-        const float rG = 1.0f / Gt;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float e = vs[c] - Gt * sk[c];   // e = v - S'k
-          y[c] = Gt * sq[c] + beta * kq * e;    // S_t q
-          be[c] = beta * e * rG;
-        }
-        s_y[wave][t][lane] = (rg & 1) ? y[1] : y[0];
-#pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-          const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_qk[t][1][row0 + i]);
-          const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            Hs[i + u].x = fmaf(kv[u], be[0], Hs[i + u].x);
-            Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
-          }
-        }
-        if (t + 1 == commit) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i)
-            st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2_t{Gam * Hs[i].x, Gam * Hs[i].y});
-        }
-      }
-    }
-
-    // ---- epilogue: RMS over the head's 128 columns (four waves), SiLU(z) gate ---------
-    const float nwv = norm_w ? norm_w[ocol] : 1.0f;
-    float zr[kMaxStepTokens];
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t)
-      zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
-    float yown[kMaxStepTokens];
-#pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) {
-      yown[t] = (t < n && head_on) ? s_y[wave][t][lane] : 0.f;  // this lane's own writes
-      if (t < n) {
-        // each column sits in one of the lanes with rg < 2: sum over those
-        const float ssum = wave_sum(out_lane ? yown[t] * yown[t] : 0.f);
-        if (lane == 0) s_ss[wave][t] = ssum;
-      }
-    }
-    __syncthreads();
-    if (out_lane && head_on) {
-      const float *ssh4 = &s_ss[4 * jp][0];
+    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token
 #pragma unroll
       for (int t = 0; t < kMaxStepTokens; ++t) {
         if (t < n) {
-          const float ssh = (ssh4[t] + ssh4[kMaxStepTokens + t]) +
-                            (ssh4[2 * kMaxStepTokens + t] + ssh4[3 * kMaxStepTokens + t]);
-          const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
-          const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
-          Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
+          const float ss = wave_sum(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
+          const float f = (slot == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
+          xv[t][0] *= f;
+          xv[t][1] *= f;
         }
       }
     }
-    if (MULTI && j0 + P < r) __syncthreads();  // s_v, s_ab, s_y, s_ss reused by the next round
+    if (slot < 3) {
+#pragma unroll
+      for (int t = 0; t < kMaxStepTokens; ++t)
+        if (t < n) {
+          s_x[t][slot][c0] = xv[t][0];
+          s_x[t][slot][c0 + 1] = xv[t][1];
+        }
+    }
+  }
+  // the state (the barriers below do not wait for these loads)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
+  if (tid < 8 && gt < n) {
+    s_ab[gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
+    s_ab[gt][1] = sigmoidf_(gb);
+  }
+  __syncthreads();
+  if (wave == 0) {  // k_t . q_t of each token
+    for (int t = 0; t < n; ++t) {
+      const float kq = wave_sum(s_x[t][0][2 * lane] * s_x[t][1][2 * lane] +
+                                s_x[t][0][2 * lane + 1] * s_x[t][1][2 * lane + 1]);
+      if (lane == 0) s_kq[t] = kq;
+    }
+  }
+  __syncthreads();
+
+  // ---- token loop: the state stays in registers, no barrier -----------------------------
+  // The registers hold the state divided by the running decay product of this call,
+  // S = Gam * Hs, so a token costs one FMA per state element for the update instead
+  // of a decay multiply and an FMA: with Gam_t = alpha_t Gam_{t-1},
+  //   alpha_t S_{t-1} k = Gam_t (Hs k),  S_t = Gam_t (Hs + (beta e / Gam_t) k^T).
+  // When Gam_t falls below 2^-60 it is folded into Hs (and taken as 1), which also
+  // covers alpha = 0.  Gam is uniform (one head per workgroup).
+  float Gam = 1.0f;
+#pragma unroll 1
+  for (int t = 0; t < n; ++t) {
+    {
+      const float alpha = s_ab[t][0];
+      const float beta = s_ab[t][1];
+      float Gt = Gam * alpha;
+      if (Gt < 0x1p-60f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          Hs[i].x *= Gt; Hs[i].y *= Gt;
+        }
+        Gt = 1.0f;
+      }
+      Gam = Gt;
+      // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
+      // within each 16-lane row); k again for the update, to keep registers low
+      float sk[2] = {0, 0}, sq[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
+        const f32x4 qq = *reinterpret_cast<const f32x4 *>(&s_x[t][0][row0 + i]);
+        const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x2_t hv = Hs[i + u];
+          sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
+          sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        sk[c] = rows4_sum(sk[c]);
+        sq[c] = rows4_sum(sq[c]);
+      }
+      const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_x[t][2][col0]);
+      const float kq = s_kq[t];
+      float be[2];
+      float y[2];
+      const float vs[2] = {vv.x, vv.y};
+      const float rG = 1.0f / Gt;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float e = vs[c] - Gt * sk[c];   // e = v - S'k
+        y[c] = Gt * sq[c] + beta * kq * e;    // S_t q
+        be[c] = beta * e * rG;
+      }
+      s_y[wave][t][lane] = (rg & 1) ? y[1] : y[0];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
+        const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Hs[i + u].x = fmaf(kv[u], be[0], Hs[i + u].x);
+          Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
+        }
+      }
+      if (t + 1 == commit) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2_t{Gam * Hs[i].x, Gam * Hs[i].y});
+      }
+    }
+  }
+
+  // ---- epilogue: RMS over the head's 128 columns (four waves), SiLU(z) gate -----------
+  const float nwv = norm_w ? norm_w[ocol] : 1.0f;
+  float zr[kMaxStepTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxStepTokens; ++t)
+    zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
+  float yown[kMaxStepTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxStepTokens; ++t) {
+    yown[t] = t < n ? s_y[wave][t][lane] : 0.f;  // this lane's own writes: no barrier
+    if (t < n) {
+      // each column sits in one of the lanes with rg < 2: sum over those
+      const float ssum = wave_sum(out_lane ? yown[t] * yown[t] : 0.f);
+      if (lane == 0) s_ss[wave][t] = ssum;
+    }
+  }
+  __syncthreads();
+  if (out_lane) {
+#pragma unroll
+    for (int t = 0; t < kMaxStepTokens; ++t) {
+      if (t < n) {
+        const float ssh = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
+        const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
+        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
+        Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
+      }
+    }
+  }
+}
+
+// The q/k conv-cache channels advance by commit = num_commit[b] tokens after the
+// n-token step has read them (same stream, so every read of the step precedes these
+// writes): rows commit .. commit + 2 of [cache rows, new tokens].  One thread per
+// (sequence, q/k channel); coalesced over channels.
+template <typename T>
+__global__ void __launch_bounds__(256)
+qk_cache_advance_kernel(const T *__restrict__ q, const T *__restrict__ k, T *__restrict__ conv_state,
+                        const int32_t *__restrict__ num_commit, int batch, int Hk, int Hv, int n) {
+  const int64_t Cqk = 2LL * Hk * kD;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)batch * Cqk) return;
+  const int bseq = (int)(i / Cqk);
+  const int64_t ch = i % Cqk;
+  const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
+  if (commit == 0) return;
+  const int64_t Cc = Cqk + (int64_t)Hv * kD;
+  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+  const int64_t qkD = (int64_t)Hk * kD;
+  const T *src = ch < qkD ? q + (int64_t)bseq * n * qkD + ch : k + (int64_t)bseq * n * qkD + (ch - qkD);
+  T raw[3 + kMaxStepTokens];
+  raw[0] = cs[ch];
+  raw[1] = cs[Cc + ch];
+  raw[2] = cs[2 * Cc + ch];
+#pragma unroll
+  for (int t = 0; t < kMaxStepTokens; ++t) raw[3 + t] = t < n ? src[t * qkD] : raw[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 3; ++s2) {
+    T x = raw[0];
+#pragma unroll
+    for (int j = 1; j < 3 + kMaxStepTokens; ++j)
+      if (j == commit + s2) x = raw[j];
+    cs[s2 * Cc + ch] = x;
   }
 }
 
@@ -596,17 +613,15 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 void *conv_state, const int32_t *num_commit, void *o, int batch,
                                 int n, int Hk, int Hv, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  dim3 grid((unsigned)batch * (unsigned)Hk);
-  const int r = Hv / Hk;
-  auto go = [&](auto kern, int threads) {
-    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, (const T *)q, (const T *)k,
-                       (const T *)v, a, b, (const T *)z, conv_w, A_log, dt_bias, norm_w,
-                       q_scale, l2_eps, rms_eps, state, (T *)conv_state, num_commit, (T *)o, Hk,
-                       Hv, n);
-  };
-  if (r == 1) go(decode_tokens_kernel<T, 1, false>, 256);
-  else if (r == 2) go(decode_tokens_kernel<T, 2, false>, 512);
-  else go(decode_tokens_kernel<T, 2, true>, 512);
+  dim3 grid((unsigned)batch * (unsigned)Hv);
+  hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kTokThreads), 0, stream,
+                     (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
+                     dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
+                     num_commit, (T *)o, Hk, Hv, n);
+  const int64_t nch = (int64_t)batch * 2 * Hk * kD;
+  hipLaunchKernelGGL((qk_cache_advance_kernel<T>), dim3((unsigned)((nch + 255) / 256)), dim3(256),
+                     0, stream, (const T *)q, (const T *)k, (T *)conv_state, num_commit, batch, Hk,
+                     Hv, n);
   return hipGetLastError();
 }
 

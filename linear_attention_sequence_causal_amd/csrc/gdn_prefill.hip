@@ -95,6 +95,9 @@ template <> struct BufIO<float> {
   }
 };
 
+// 2^e as a float, e in [-126, 127]
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 __device__ __forceinline__ u16x8 cat4(u16x4 x, u16x4 y) {
   return u16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
@@ -106,17 +109,16 @@ __device__ __forceinline__ u16x8 cat4(u16x4 x, u16x4 y) {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
 constexpr int kRowS = 136;     // bf16 row stride of [32 tok][128 d] tiles (272 B)
-constexpr int kTokS = 36;      // bf16 row stride of [128 d][32 tok] tiles (72 B)
+constexpr int kTokS = 36;      // 16-bit row stride of the [128 d][32 tok] K^T tile (72 B)
 constexpr int kSqS = 36;       // bf16 row stride of [32][32] tiles (M, -L)
 
 constexpr int OFF_QH = 0;
 constexpr int OFF_QF = OFF_QH + kChunk * kRowS * 2;  // fp16 unit-norm q (Q K^T)
 constexpr int OFF_KF = OFF_QF + kChunk * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
 constexpr int OFF_M = OFF_KF + kChunk * kRowS * 2;   // bf16 [32][36] M with zero diagonal
-constexpr int OFF_KTH = OFF_M + kChunk * kSqS * 2;
-constexpr int OFF_KTL = OFF_KTH + 128 * kTokS * 2;
+constexpr int OFF_KT = OFF_M + kChunk * kSqS * 2;   // fp16 K^T [128 dk][32 tok]
 constexpr int kVtS = 36;       // fp32 row stride of the [128 dv][32 tok] V^T tile (144 B)
-constexpr int OFF_VT = OFF_KTL + 128 * kTokS * 2;
+constexpr int OFF_VT = OFF_KT + 128 * kTokS * 2;
 constexpr int OFF_CONVW = OFF_VT + 128 * kVtS * 4;
 constexpr float kConvScale = -1.4426950408889634f;  // -log2(e), folded into the conv taps
 constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no bank conflicts)
@@ -372,8 +374,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   bf16_t *const sQh = reinterpret_cast<bf16_t *>(smem + OFF_QH);
   bf16_t *const sQf = reinterpret_cast<bf16_t *>(smem + OFF_QF);  // fp16 bits
   bf16_t *const sKf = reinterpret_cast<bf16_t *>(smem + OFF_KF);  // fp16 bits
-  bf16_t *const sKTh = reinterpret_cast<bf16_t *>(smem + OFF_KTH);
-  bf16_t *const sKTl = reinterpret_cast<bf16_t *>(smem + OFF_KTL);
+  bf16_t *const sKT = reinterpret_cast<bf16_t *>(smem + OFF_KT);  // fp16 bits
   float *const sVT = reinterpret_cast<float *>(smem + OFF_VT);
   float *const sConvW = reinterpret_cast<float *>(smem + OFF_CONVW);
   float *const sGates = reinterpret_cast<float *>(smem + OFF_GATES);
@@ -600,6 +601,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   }
   __syncthreads();  // conv weights, first gates
 
+  // The accumulators hold sigma H with sigma = 2^sexp, a power of two chosen per wave
+  // and chunk so that the fp16 operand of the state update stays in range (below).
+  // Everything on the value side (beta V, Utilde, U, O) carries the same factor; o
+  // and the stored state are divided by it.
+  int sexp = 0;
   for (int c = c_begin; c < nchunks; ++c) {
     refresh();
     const int t0 = seg.begin + c * kChunk;
@@ -656,8 +662,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
       }
-      // fp16 rows of q or k (the gram products); bf16 rows of q (Q H); bf16 hi/lo
-      // halves of k regrouped into K^T (right-hand side and state update)
+      // fp16 rows of q or k (the gram products); bf16 rows of q (Q H); the fp16 k
+      // rows regrouped into K^T (right-hand side and state update)
       if (role == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -672,7 +678,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
           *reinterpret_cast<uint4 *>(sQh + off) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
         }
       } else {
-        // K^T [dk][tok]: the halves regrouped by channel, 8 bytes (4 tokens) per row;
+        // K^T [dk][tok]: fp16 k regrouped by channel, 8 bytes (4 tokens) per row;
         // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1.  Tokens (2p, 2p+1) of
         // channel cc are half (cc & 1) of word cc/2 of tokens 2p, 2p+1.
         const int swz = (((tbase >> 2) ^ (cg >> 1)) & 7) << 2;
@@ -686,21 +692,15 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
                            __builtin_amdgcn_perm(w[3][e], w[2][e], sel));
           }
         };
-        uint32_t hw[4][4], lw[4][4];  // token r: channels (2e, 2e+1) in word e
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) split_pk(x[r][2 * e], x[r][2 * e + 1], hw[r][e], lw[r][e]);
-        put_kt(sKTl, lw);
-        put_kt(sKTh, hw);
+        uint32_t fw[4][4];  // token r: fp16 channels (2e, 2e+1) in word e
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          uint32_t fw[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
+          for (int e = 0; e < 4; ++e) fw[r][e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
           *reinterpret_cast<uint4 *>(sKf + (tbase + r) * kRowS + cg * 8) =
-              make_uint4(fw[0], fw[1], fw[2], fw[3]);
+              make_uint4(fw[r][0], fw[r][1], fw[r][2], fw[r][3]);
         }
+        put_kt(sKT, fw);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -821,8 +821,10 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
 
     // ================= right-hand sides and the triangular solves =================
-    // fp32 right-hand sides beta V and beta gamma K of this wave's columns
+    // fp32 right-hand sides sigma beta V (the value side carries the state's scale)
+    // and beta gamma K of this wave's columns
     f32x4 Uacc[2][2], Wacc[2][2];  // [row tile of 16 tokens][column tile]
+    const float sig = pow2f(sexp);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
@@ -831,14 +833,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       for (int ct = 0; ct < 2; ++ct) {
         const int dcol = 32 * wave + 16 * ct + ln;
         const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
-        const u16x4 kh = *reinterpret_cast<const u16x4 *>(sKTh + toff);
-        const u16x4 kl = *reinterpret_cast<const u16x4 *>(sKTl + toff);  // beta gamma K in fp32
+        const f16x4_t kh = *reinterpret_cast<const f16x4_t *>(sKT + toff);
         f32x4 vv = {0.f, 0.f, 0.f, 0.f};
         if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Uacc[rt][ct][i] = be[i] * vv[i];
-          Wacc[rt][ct][i] = bg[i] * (bf2f(kh[i]) + bf2f(kl[i]));
+          Uacc[rt][ct][i] = (be[i] * sig) * vv[i];
+          Wacc[rt][ct][i] = bg[i] * (float)kh[i];
         }
       }
     }
@@ -922,19 +923,36 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         }
       }
     }
-    // state update H = gamma_C H + K^T diag(e^{G_C - G}) U
+    // state update H = gamma_C H + K^T diag(e^{G_C - G}) U, one fp16 pass: K is unit-norm,
+    // and u = U e^{G_C - G} rho (|u| <= |U|) is scaled by the power of two rho that puts
+    // the wave's largest |U| in [2^12, 2^13), so every u sits in fp16's normal range (or
+    // is below 2^-26 of the largest and negligible).  The new scale is sigma rho, kept
+    // within 2^-60 .. 2^60 (rho = 1 when U is zero or not finite).
     {
-      float u[2][2][4];
+      float mu = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mu = fmaxf(mu, fabsf(Uacc[rt][ct][i]));
+      mu = wave_max(mu);
+      const int ebits = (int)((__builtin_amdgcn_readfirstlane(__float_as_int(mu)) >> 23) & 0xFF);
+      int snew = sexp;
+      if (ebits > 0 && ebits < 255) snew = min(max(sexp + 139 - ebits, -60), 60);
+      const float rho = pow2f(snew - sexp);
+      sexp = snew;
       uint32_t uh[2][4];  // [ct]: tokens 4lg.. of row tile 0, then of row tile 1
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * rt + 4 * lg);
+        f32x4 dr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dr[i] = dec[i] * rho;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) u[rt][ct][i] = Uacc[rt][ct][i] * dec[i];
-          uh[ct][2 * rt] = pk_bf16(u[rt][ct][0], u[rt][ct][1]);
-          uh[ct][2 * rt + 1] = pk_bf16(u[rt][ct][2], u[rt][ct][3]);
+          uh[ct][2 * rt] = pk_f16(Uacc[rt][ct][0] * dr[0], Uacc[rt][ct][1] * dr[1]);
+          uh[ct][2 * rt + 1] = pk_f16(Uacc[rt][ct][2] * dr[2], Uacc[rt][ct][3] * dr[3]);
         }
       }
       u16x8 Uh[2];
@@ -942,50 +960,31 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       for (int ct = 0; ct < 2; ++ct)
         Uh[ct] = __builtin_bit_cast(u16x8, make_uint4(uh[ct][0], uh[ct][1], uh[ct][2], uh[ct][3]));
       const TokLane tl(ln, lg);
+      const float gCr = gC * rho;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Hacc[dt][ct][i] *= gC;
-      {
-        // lo parts of U: u - bf16(u)
-        u16x8 Ul[2];
+          for (int i = 0; i < 4; ++i) Hacc[dt][ct][i] *= gCr;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          uint32_t ul[4];
+      for (int dt = 0; dt < 8; ++dt) {
+        const u16x8 ak = load_a_tok(sKT, tl, dt);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rt = q >> 1, i0 = 2 * (q & 1);
-            const uint32_t hw = uh[ct][q];
-            ul[q] = pk_bf16(u[rt][ct][i0] - __uint_as_float(hw << 16),
-                            u[rt][ct][i0 + 1] - __uint_as_float(hw & 0xFFFF0000u));
-          }
-          Ul[ct] = __builtin_bit_cast(u16x8, make_uint4(ul[0], ul[1], ul[2], ul[3]));
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const u16x8 akh = load_a_tok(sKTh, tl, dt);
-          const u16x8 akl = load_a_tok(sKTl, tl, dt);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            Hacc[dt][ct] = mfma16(akh, Uh[ct], Hacc[dt][ct]);
-            Hacc[dt][ct] = mfma16(akh, Ul[ct], Hacc[dt][ct]);
-            Hacc[dt][ct] = mfma16(akl, Uh[ct], Hacc[dt][ct]);
-          }
-        }
+        for (int ct = 0; ct < 2; ++ct) Hacc[dt][ct] = mfma16h(ak, Uh[ct], Hacc[dt][ct]);
       }
     }
 
     // ================= epilogue: RMSNorm over 128 columns, SiLU(z) gate ============
-    if (MODE == kFull) {  // this wave's 32 columns of o -> the fp32 o tile
+    if (MODE == kFull) {  // this wave's 32 columns of o -> the fp32 o tile (1/sigma)
+      const float rsig = 1.0f / sig;  // exact: a power of two
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sO[(16 * rt + 4 * lg + i) * kOS + 32 * wave + 16 * ct + ln] = Oacc[rt][ct][i];
+            sO[(16 * rt + 4 * lg + i) * kOS + 32 * wave + 16 * ct + ln] = Oacc[rt][ct][i] * rsig;
     }
     __syncthreads();  // (5) o tile ready; this chunk's other LDS tiles are consumed
     refresh();
@@ -1045,13 +1044,14 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     Hout = P.maps + (((int64_t)unit * Hv + h) * 2 + half) * kD * kD;
   }
   if (Hout) {
+    const float rsig = pow2f(-sexp);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          Hout[(16 * dt + 4 * lg + i) * kD + 32 * wave + 16 * ct + ln] = Hacc[dt][ct][i];
+          Hout[(16 * dt + 4 * lg + i) * kD + 32 * wave + 16 * ct + ln] = Hacc[dt][ct][i] * rsig;
   }
 }
 
