@@ -95,6 +95,13 @@ template <> struct BufIO<float> {
   }
 };
 
+// fp32 -> fp16 bits (round to nearest even)
+__device__ __forceinline__ bf16_t f2h(float x) { return __builtin_bit_cast(bf16_t, (_Float16)x); }
+// biased exponent field of |x| (0 for zero and denormals, 255 for Inf and NaN)
+__device__ __forceinline__ int exp_bits(float x) {
+  return (int)((__float_as_uint(x) >> 23) & 0xFF);
+}
+
 // 2^e as a float, e in [-126, 127]
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
@@ -112,8 +119,7 @@ constexpr int kRowS = 136;     // bf16 row stride of [32 tok][128 d] tiles (272 
 constexpr int kTokS = 36;      // 16-bit row stride of the [128 d][32 tok] K^T tile (72 B)
 constexpr int kSqS = 36;       // bf16 row stride of [32][32] tiles (M, -L)
 
-constexpr int OFF_QH = 0;
-constexpr int OFF_QF = OFF_QH + kChunk * kRowS * 2;  // fp16 unit-norm q (Q K^T)
+constexpr int OFF_QF = 0;                            // fp16 unit-norm q (Q K^T, Q H)
 constexpr int OFF_KF = OFF_QF + kChunk * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
 constexpr int OFF_M = OFF_KF + kChunk * kRowS * 2;   // bf16 [32][36] M with zero diagonal
 constexpr int OFF_KT = OFF_M + kChunk * kSqS * 2;   // fp16 K^T [128 dk][32 tok]
@@ -125,8 +131,8 @@ constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no b
 // Per-token gate vectors of a chunk, two buffers (chunk parity): the next chunk's
 // are written while this chunk's are in use.  Vector k of a buffer starts at float
 // k * kChunk: beta, G (cumsum of g), gamma = e^G, beta gamma, e^{G_C - G},
-// beta / kConvScale (multiplies scaled v), q_scale gamma (multiplies Q H).
-enum { GB_BETA = 0, GB_G, GB_GAM, GB_BG, GB_DEC, GB_BV, GB_GAMQ, GB_N };
+// beta / kConvScale (multiplies scaled v).
+enum { GB_BETA = 0, GB_G, GB_GAM, GB_BG, GB_DEC, GB_BV, GB_N };
 constexpr int kGateN = GB_N * kChunk;                // floats per buffer
 constexpr int OFF_GATES = OFF_CONVW + 48 * kConvGS * 4;
 constexpr int OFF_MDIAG = OFF_GATES + 2 * kGateN * 4;
@@ -240,16 +246,16 @@ __device__ __forceinline__ void conv_silu_rows(const uint32_t (&raw)[NT + 3][Raw
   }
 }
 
-// B operand (K = 32) from two 16x16 C-layout tiles: slot 8lg+j <-> row 4lg+j of
-// tile a (j < 4), row 4lg+j-4 of tile b (j >= 4).  Any A operand paired with it
-// reads its k index in the same order.
-__device__ __forceinline__ u16x8 pack_b(const f32x4 &a, const f32x4 &b) {
-  const uint32_t w0 = pk_bf16(a[0], a[1]), w1 = pk_bf16(a[2], a[3]);
-  const uint32_t w2 = pk_bf16(b[0], b[1]), w3 = pk_bf16(b[2], b[3]);
+// fp16 B operand (K = 32) from two 16x16 C-layout tiles, each scaled by f: slot
+// 8lg+j <-> row 4lg+j of tile a (j < 4), row 4lg+j-4 of tile b (j >= 4).  Any A
+// operand paired with it reads its k index in the same order.
+__device__ __forceinline__ u16x8 pack_h(const f32x4 &a, const f32x4 &b, float f = 1.0f) {
+  const uint32_t w0 = pk_f16(a[0] * f, a[1] * f), w1 = pk_f16(a[2] * f, a[3] * f);
+  const uint32_t w2 = pk_f16(b[0] * f, b[1] * f), w3 = pk_f16(b[2] * f, b[3] * f);
   return __builtin_bit_cast(u16x8, make_uint4(w0, w1, w2, w3));
 }
-__device__ __forceinline__ u16x8 pack_b_half(const f32x4 &a) {  // tile b = 0
-  return __builtin_bit_cast(u16x8, make_uint4(pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]), 0u, 0u));
+__device__ __forceinline__ u16x8 pack_h_half(const f32x4 &a) {  // tile b = 0
+  return __builtin_bit_cast(u16x8, make_uint4(pk_f16(a[0], a[1]), pk_f16(a[2], a[3]), 0u, 0u));
 }
 // A operand row fragment in the permuted k order: cols c0+4lg..+3 and c1+4lg..+3
 __device__ __forceinline__ u16x8 load_a_perm(const bf16_t *row, int c0, int c1, int lg) {
@@ -282,7 +288,7 @@ struct TokLane {
     return base[rt & 3] + 16 * rt * kTokS + 4 * (half ? 4 - (rt & 4) : (rt & 4));
   }
 };
-// A operand of K^T U: rows 16rt + ln, tokens in the permuted k order of pack_b
+// A operand of K^T U: rows 16rt + ln, tokens in the permuted k order of pack_h
 // (4lg .. +3, then 16 + 4lg .. +3)
 __device__ __forceinline__ u16x8 load_a_tok(const bf16_t *tile, const TokLane &tl, int rt) {
   return cat4(*reinterpret_cast<const u16x4 *>(tile + tl(rt, 0)),
@@ -371,7 +377,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   const int seq_begin = seg.seq_begin;
   const int seg_end = seg.begin + seg.len;
 
-  bf16_t *const sQh = reinterpret_cast<bf16_t *>(smem + OFF_QH);
   bf16_t *const sQf = reinterpret_cast<bf16_t *>(smem + OFF_QF);  // fp16 bits
   bf16_t *const sKf = reinterpret_cast<bf16_t *>(smem + OFF_KF);  // fp16 bits
   bf16_t *const sKT = reinterpret_cast<bf16_t *>(smem + OFF_KT);  // fp16 bits
@@ -515,6 +520,30 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
           Hacc[dt][ct][i] = x;
         }
   }
+  // The accumulators hold sigma H with sigma = 2^sexp, a power of two per wave, and
+  // hb bounds |sigma H| (both uniform).  The start puts max |H0| in [2^13, 2^14).
+  int sexp = 0;
+  float hb = 0.f;
+  {
+    float m = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Hacc[dt][ct][i]));
+    m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(m))));
+    const int eb = exp_bits(m);
+    if (eb > 0 && eb < 255) sexp = min(max(140 - eb, -60), 60);
+    const float s0 = pow2f(sexp);
+    hb = m * s0;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Hacc[dt][ct][i] *= s0;
+  }
 
   const float A_log_h = P.A_log[h], dt_bias_h = P.dt_bias[h];
   // Gates of one chunk, computed by wave 3 one chunk ahead (where it has slack):
@@ -541,7 +570,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       gbuf[GB_BG * kChunk + lane] = be * gam;
       gbuf[GB_DEC * kChunk + lane] = __expf(GC - g);
       gbuf[GB_BV * kChunk + lane] = be * (1.0f / kConvScale);
-      gbuf[GB_GAMQ * kChunk + lane] = gam * P.q_scale;
     }
   };
   if (MODE == kFull && tid < kD) sNW[tid] = P.norm_w ? P.norm_w[tid] : 1.0f;
@@ -601,11 +629,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   }
   __syncthreads();  // conv weights, first gates
 
-  // The accumulators hold sigma H with sigma = 2^sexp, a power of two chosen per wave
-  // and chunk so that the fp16 operand of the state update stays in range (below).
-  // Everything on the value side (beta V, Utilde, U, O) carries the same factor; o
-  // and the stored state are divided by it.
-  int sexp = 0;
   for (int c = c_begin; c < nchunks; ++c) {
     refresh();
     const int t0 = seg.begin + c * kChunk;
@@ -616,7 +639,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     const float *const sBeta = gcur + GB_BETA * kChunk, *const sG = gcur + GB_G * kChunk;
     const float *const sGam = gcur + GB_GAM * kChunk, *const sBG = gcur + GB_BG * kChunk;
     const float *const sDec = gcur + GB_DEC * kChunk, *const sBv = gcur + GB_BV * kChunk;
-    const float *const sGamQ = gcur + GB_GAMQ * kChunk;
     // gC = gamma_C, the chunk's decay (the same in every lane)
     const float gC = sGam[kChunk - 1];
     // the next chunk's gate inputs (wave 3), issued first and consumed in the gram
@@ -662,20 +684,16 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
       }
-      // fp16 rows of q or k (the gram products); bf16 rows of q (Q H); the fp16 k
-      // rows regrouped into K^T (right-hand side and state update)
+      // fp16 rows of q (the gram products and Q H) or k (the gram products), and the
+      // fp16 k rows regrouped into K^T (right-hand side and state update)
       if (role == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          uint32_t fw[4], bw[4];
+          uint32_t fw[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
-            bw[e] = pk_bf16(x[r][2 * e], x[r][2 * e + 1]);
-          }
-          const int off = (tbase + r) * kRowS + cg * 8;
-          *reinterpret_cast<uint4 *>(sQf + off) = make_uint4(fw[0], fw[1], fw[2], fw[3]);
-          *reinterpret_cast<uint4 *>(sQh + off) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+          for (int e = 0; e < 4; ++e) fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
+          *reinterpret_cast<uint4 *>(sQf + (tbase + r) * kRowS + cg * 8) =
+              make_uint4(fw[0], fw[1], fw[2], fw[3]);
         }
       } else {
         // K^T [dk][tok]: fp16 k regrouped by channel, 8 bytes (4 tokens) per row;
@@ -773,12 +791,12 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool low = cj < 16 * ti + 4 * lg + i;
-          sM[(16 * ti + 4 * lg + i) * kSqS + cj] = f2bf(low ? d[i] * (qk[i] * P.q_scale) : 0.f);
+          sM[(16 * ti + 4 * lg + i) * kSqS + cj] = f2h(low ? d[i] * qk[i] : 0.f);
         }
       }
       if (ti != tj) {  // wave 2: the off-diagonal block of -L
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sLo[(16 * ti + 4 * lg + i) * kSqS + cj] = f2bf(-l[i]);
+        for (int i = 0; i < 4; ++i) sLo[(16 * ti + 4 * lg + i) * kSqS + cj] = f2h(-l[i]);
       } else {
         // diagonal block: M's diagonal (fp32) and (I + L_bb)^-1 - I from the C-layout
         // tiles of -L^T (mc) and -L (mt)
@@ -786,7 +804,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
           const int di = ln - 4 * lg;  // the lane's diagonal element, if any
           if (di >= 0 && di < 4) {
             const float qd = di == 0 ? qk[0] : (di == 1 ? qk[1] : (di == 2 ? qk[2] : qk[3]));
-            sMdiag[cj] = qd * P.q_scale;
+            sMdiag[cj] = qd;
           }
         }
         const float Bj = sBeta[cj];
@@ -803,7 +821,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[i] = tt[i] - (4 * lg + i == ln ? 1.0f : 0.0f);
         *reinterpret_cast<uint2 *>(sTd + (16 * ti + ln) * kTdS + 4 * lg) =
-            make_uint2(pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]));
+            make_uint2(pk_f16(e[0], e[1]), pk_f16(e[2], e[3]));
       }
     }
     if (MODE == kFull && wave == 3) {  // zero the upper tile (0,1) of M read by M U
@@ -821,10 +839,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
 
     // ================= right-hand sides and the triangular solves =================
-    // fp32 right-hand sides sigma beta V (the value side carries the state's scale)
-    // and beta gamma K of this wave's columns
+    // fp32 right-hand sides s_V beta V and beta gamma K of this wave's columns.  The
+    // solve runs on fp16 operands: beta gamma K <= 1, and s_V = 2^vexp puts the wave's
+    // largest |beta V| in [2^3, 2^4); the solution Utilde (the chunk's values started
+    // from a zero state) is then at most 32 times that, and its intermediate rows of
+    // the blocked substitution at most 17 times more, all inside fp16's range.
     f32x4 Uacc[2][2], Wacc[2][2];  // [row tile of 16 tokens][column tile]
-    const float sig = pow2f(sexp);
+    int vexp = 0;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
@@ -838,10 +859,28 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Uacc[rt][ct][i] = (be[i] * sig) * vv[i];
+          Uacc[rt][ct][i] = be[i] * vv[i];
           Wacc[rt][ct][i] = bg[i] * (float)kh[i];
         }
       }
+    }
+    if (withV) {
+      float mv = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(Uacc[rt][ct][i]));
+      const int eb = exp_bits(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mv)))));
+      if (eb > 0 && eb < 255) vexp = min(max(130 - eb, -60), 60);
+      const float sv = pow2f(vexp);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= sv;
     }
     // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
     //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
@@ -849,20 +888,20 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       const u16x8 at0 = load_a_perm_half(sTd + ln * kTdS, 0, lg);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[0][ct] = mfma16(at0, pack_b_half(Wacc[0][ct]), Wacc[0][ct]);
-        if (withV) Uacc[0][ct] = mfma16(at0, pack_b_half(Uacc[0][ct]), Uacc[0][ct]);
+        Wacc[0][ct] = mfma16h(at0, pack_h_half(Wacc[0][ct]), Wacc[0][ct]);
+        if (withV) Uacc[0][ct] = mfma16h(at0, pack_h_half(Uacc[0][ct]), Uacc[0][ct]);
       }
       const u16x8 a10 = load_a_perm_half(sLo + (16 + ln) * kSqS, 0, lg);  // -L_10
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mfma16(a10, pack_b_half(Wacc[0][ct]), Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mfma16(a10, pack_b_half(Uacc[0][ct]), Uacc[1][ct]);
+        Wacc[1][ct] = mfma16h(a10, pack_h_half(Wacc[0][ct]), Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mfma16h(a10, pack_h_half(Uacc[0][ct]), Uacc[1][ct]);
       }
       const u16x8 at1 = load_a_perm_half(sTd + (16 + ln) * kTdS, 0, lg);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mfma16(at1, pack_b_half(Wacc[1][ct]), Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mfma16(at1, pack_b_half(Uacc[1][ct]), Uacc[1][ct]);
+        Wacc[1][ct] = mfma16h(at1, pack_h_half(Wacc[1][ct]), Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mfma16h(at1, pack_h_half(Uacc[1][ct]), Uacc[1][ct]);
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -870,22 +909,33 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sW[(16 * rt + 4 * lg + i) * kRowS + 32 * wave + 16 * ct + ln] = f2bf(-Wacc[rt][ct][i]);
+            sW[(16 * rt + 4 * lg + i) * kRowS + 32 * wave + 16 * ct + ln] = f2h(-Wacc[rt][ct][i]);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (4) -W ready
     refresh();
 
     // ================= Q H, U = Utilde - W H, O += M U, H update ==================
-    // H as bf16 B operands: Hb[kb][ct] slots 8lg+j <-> dk 32kb + 4lg + j (j<4),
-    // 32kb + 16 + 4lg + j - 4 (j >= 4)
+    // The accumulators hold sigma H (sigma = 2^sexp per wave) with |sigma H| below 2^14
+    // (hb bounds it, see the update), so H enters Q H and W H as fp16 B operands:
+    // Hb[kb][ct] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb + 16 + 4lg + j - 4 (j >= 4).
+    // |W| <= 1 (its rows are the initial state's read-out directions, products of the
+    // contractions alpha (I - beta k k^T)) and Q is unit-norm.  Utilde is brought from
+    // s_V to sigma first, so U = Utilde - W H comes out as sigma U.
     f32x4 Oacc[2][2];
     {
+      const float vs = pow2f(sexp - vexp);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= vs;
       u16x8 Hb[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Hb[kb][ct] = pack_b(Hacc[2 * kb][ct], Hacc[2 * kb + 1][ct]);
+        for (int ct = 0; ct < 2; ++ct) Hb[kb][ct] = pack_h(Hacc[2 * kb][ct], Hacc[2 * kb + 1][ct]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -897,37 +947,21 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         for (int rt = 0; rt < 2; ++rt) {
           const u16x8 aw = load_a_perm(sW + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Uacc[rt][ct] = mfma16(aw, Hb[kb][ct], Uacc[rt][ct]);
+          for (int ct = 0; ct < 2; ++ct) Uacc[rt][ct] = mfma16h(aw, Hb[kb][ct], Uacc[rt][ct]);
           if (MODE == kFull) {
-            const u16x8 aq = load_a_perm(sQh + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
+            const u16x8 aq = load_a_perm(sQf + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) Oacc[rt][ct] = mfma16(aq, Hb[kb][ct], Oacc[rt][ct]);
+            for (int ct = 0; ct < 2; ++ct) Oacc[rt][ct] = mfma16h(aq, Hb[kb][ct], Oacc[rt][ct]);
           }
         }
       }
     }
-    if (MODE == kFull) {
-      u16x8 Ub[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_b(Uacc[0][ct], Uacc[1][ct]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGamQ + 16 * rt + 4 * lg);
-        const f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
-        const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Oacc[rt][ct][i] = fmaf(md[i], Uacc[rt][ct][i], Oacc[rt][ct][i] * gm[i]);
-          Oacc[rt][ct] = mfma16(am, Ub[ct], Oacc[rt][ct]);
-        }
-      }
-    }
-    // state update H = gamma_C H + K^T diag(e^{G_C - G}) U, one fp16 pass: K is unit-norm,
-    // and u = U e^{G_C - G} rho (|u| <= |U|) is scaled by the power of two rho that puts
-    // the wave's largest |U| in [2^12, 2^13), so every u sits in fp16's normal range (or
-    // is below 2^-26 of the largest and negligible).  The new scale is sigma rho, kept
-    // within 2^-60 .. 2^60 (rho = 1 when U is zero or not finite).
+    // The chunk's scale step rho (a power of two): the new state rho (gamma_C sigma H +
+    // K^T sigma u) and the fp16 operands rho sigma U stay below 2^14 with the bound
+    // hb' = gamma_C hb + 32 max|sigma U| (|K^T u| <= 32 max|u| for unit keys, u = U
+    // e^{G_C - G}, |u| <= |U|) placed in [2^13, 2^14); hb tracks a bound on |sigma H|.
+    // sigma stays within 2^-60 .. 2^60; rho = 1 when the bound is zero or not finite.
+    float rho;
     {
       float mu = 0.f;
 #pragma unroll
@@ -936,12 +970,35 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mu = fmaxf(mu, fabsf(Uacc[rt][ct][i]));
-      mu = wave_max(mu);
-      const int ebits = (int)((__builtin_amdgcn_readfirstlane(__float_as_int(mu)) >> 23) & 0xFF);
+      mu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mu))));
+      const float bound = fmaf(32.0f, mu, gC * hb);
+      const int eb = exp_bits(bound);
       int snew = sexp;
-      if (ebits > 0 && ebits < 255) snew = min(max(sexp + 139 - ebits, -60), 60);
-      const float rho = pow2f(snew - sexp);
+      if (eb > 0 && eb < 255) snew = min(max(sexp + 140 - eb, -60), 60);
+      rho = pow2f(snew - sexp);
+      hb = bound * rho;
       sexp = snew;
+    }
+    if (MODE == kFull) {  // O = gamma Q H + diag(M) U + M_off U, scaled by rho sigma / q_scale
+      u16x8 Ub[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct], rho);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+        const f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
+        const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Oacc[rt][ct][i] = rho * fmaf(md[i], Uacc[rt][ct][i], Oacc[rt][ct][i] * gm[i]);
+          Oacc[rt][ct] = mfma16h(am, Ub[ct], Oacc[rt][ct]);
+        }
+      }
+    }
+    // state update H = gamma_C H + K^T diag(e^{G_C - G}) U, one fp16 pass (K unit-norm)
+    {
       uint32_t uh[2][4];  // [ct]: tokens 4lg.. of row tile 0, then of row tile 1
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -976,8 +1033,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     }
 
     // ================= epilogue: RMSNorm over 128 columns, SiLU(z) gate ============
-    if (MODE == kFull) {  // this wave's 32 columns of o -> the fp32 o tile (1/sigma)
-      const float rsig = 1.0f / sig;  // exact: a power of two
+    if (MODE == kFull) {  // this wave's 32 columns of o -> the fp32 o tile
+      const float rsig = P.q_scale * pow2f(-sexp);  // O was scaled by sigma (new) / q_scale
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll

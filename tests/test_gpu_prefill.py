@@ -188,9 +188,9 @@ def test_segment_maps_alternate_zero_and_nonzero():
     chains them, reloading the state from a B map after a zero one).  Two of the four
     heads take the pattern in opposite phase.
 
-    The weak segments are the no-decay stress regime (nothing damps the rounding of the
-    bf16 products, see the delta-rule test), so the state is held to that test's stress
-    bar, 1e-2; a wrong start state gives errors of order 0.1-1.  o meets the main bar."""
+    The weak segments are the no-decay regime (nothing damps the rounding of the MFMA
+    operands); both outputs are held to the main bars (a wrong start state gives errors
+    of order 0.1-1)."""
     T = 3000
     w = S.scaled(S.PREFILL_4K, lengths=(T,), num_qk_heads=2, num_v_heads=4, seed=22,
                  init_state_std=0.01)
@@ -209,7 +209,7 @@ def test_segment_maps_alternate_zero_and_nonzero():
     eo, es = rel_l2(S.to_f64(o)[:, vi], o_ref), rel_l2(S.to_f64(fs)[:, vi], fs_ref)
     print(f"alternating zero/non-zero segment maps: o rel-L2 {eo:.3e} final-state rel-L2 "
           f"{es:.3e}")
-    assert eo <= O_TOL and es <= 1e-2
+    assert eo <= O_TOL and es <= STATE_TOL
 
 
 @gpu
@@ -382,12 +382,11 @@ def test_decode_after_prefill_matches_longer_prefill():
 @gpu
 def test_delta_rule_write_reproduces_the_last_value():
     """beta = 1 (b = +inf), alpha = 1 (A_log = -inf): the last write makes the state map the
-    last key to the last value, S_T k_T = v_T with the post-prologue k and v.
-
-    No decay is a stress regime: nothing damps the rounding of the bf16 MFMA operands, so
-    o and the state land near 4e-3 (an fp64 emulation of the same rounded products gives
-    4.7e-3 and 4.0e-3; no single product dominates).  The bar here is the stress bar of
-    the slow-decay test, 1e-2; a wrong write gives errors of order 1."""
+    last key to the last value, S_T k_T = v_T with the post-prologue k and v ("Qwen3-Next
+    80B-A3B" field guide, cutaway 02: with beta = 1 the write replaces the value read
+    under k).  No decay damps the rounding of the MFMA operands here; o and the final
+    state are held to the main bars, and the delta-rule write to 1e-3 (a wrong write
+    gives errors of order 1)."""
     w = S.scaled(S.PREFILL_4K, lengths=(200,), num_qk_heads=1, num_v_heads=2, seed=13,
                  init_state_std=0.0)
     d = S.prefill_inputs(w, "cuda")
@@ -406,7 +405,7 @@ def test_delta_rule_write_reproduces_the_last_value():
         assert np.linalg.norm(fs_ref[0, h].T @ kk[-1] - vv[-1]) <= 1e-6 * np.linalg.norm(vv[-1])
     print(f"beta=1 alpha=1: o rel-L2 {eo:.3e} final-state rel-L2 {es:.3e}; "
           f"|S k - v|/|v| {max(wr):.3e}")
-    assert eo < 1e-2 and es < 1e-2 and max(wr) < 1e-2
+    assert eo <= O_TOL and es <= STATE_TOL and max(wr) <= 1e-3
 
 
 @gpu
