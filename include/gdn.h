@@ -115,6 +115,32 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v,
                        void *o, float *final_state, void *conv_state_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Largest workspace, in bytes, that gdn_prefill_noalloc can use. */
+#define GDN_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+/* gdn_prefill for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments, results
+ * and errors are those of gdn_prefill without the workspace: the library uses its own
+ * static device array of GDN_NOALLOC_WORKSPACE_BYTES per device, which is part of
+ * the library's code object and stays allocated until the process ends.
+ *   - Returns GDN_ERR_WORKSPACE, before anything is enqueued, when
+ *     gdn_prefill_workspace_bytes() for the problem exceeds that size (one sequence
+ *     of up to 131072 tokens at 32 v heads fits; large varlen batches may not).
+ *   - Performs no allocation (no hipMalloc, hipFree or host buffer) and no host
+ *     synchronisation after its first call on a device, which looks the array's
+ *     device address up; GDN_VALIDATE and GDN_KERNEL_TIMING are ignored.
+ *   - Every call on one device shares that device's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that may
+ *     overlap on one device (on streams not ordered with each other) race, and
+ *     must not be issued. */
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v,
+                               const float *a, const float *b, const void *z,
+                               const gdn_params *p, const float *init_state,
+                               const int32_t *cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, const void *conv_state_in,
+                               void *o, float *final_state, void *conv_state_out,
+                               void *stream);
+
 /* Reports, and clears, an error that a kernel of an earlier call on the current
  * device found in device-resident arguments: today an invalid cu_seqlens table
  * passed to gdn_prefill (GDN_ERR_INVALID_ARGUMENT).  Synchronises `stream` first

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_BF16, GDN_F32 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
-EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode_step",
+EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_noalloc",
+            "gdn_decode_step",
             "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times",
             "gdn_check_device_errors", "gdn_status_string", "gdn_last_error", "gdn_version")
 PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
             L.gdn_prefill.restype = ctypes.c_int
             L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, i32, i64, vp, vp, vp,
                                       vp, vp, sz, vp]
+            L.gdn_prefill_noalloc.restype = ctypes.c_int
+            L.gdn_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, i32, i64, vp, vp,
+                                              vp, vp, vp]
             L.gdn_decode_step.restype = ctypes.c_int
             L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, i32, vp]
             L.gdn_decode_step_bf16_state.restype = ctypes.c_int
@@ -166,6 +170,27 @@ def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *, init_state
     if return_conv_state:
         return o, fs, cso
     return o, fs
+
+
+NOALLOC_WORKSPACE_BYTES = 128 << 20
+
+
+def prefill_noalloc(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, *, init_state=None,
+                    cu_seqlens=None, conv_state=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
+                    out, final_state, conv_state_out=None):
+    """gdn_prefill_noalloc: the prefill with the library's static workspace, into
+    caller-provided outputs (nothing is allocated)."""
+    T, Hk, D = q.shape
+    Hv = v.shape[1]
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, init_state, cu_seqlens, conv_state,
+            out, final_state, conv_state_out)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    _check(lib().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
+                                     ctypes.byref(p), _ptr(init_state), _ptr(cu_seqlens), N, T,
+                                     _ptr(conv_state), _ptr(out), _ptr(final_state),
+                                     _ptr(conv_state_out), _stream()))
+    return out, final_state
 
 
 def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, *,

@@ -155,12 +155,18 @@ size_t gdn_prefill_workspace_bytes(const gdn_params *p, int32_t num_seqs, int64_
   return plan.workspace_bytes;
 }
 
-gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *a, const float *b,
-                       const void *z, const gdn_params *p, const float *init_state,
-                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                       const void *conv_state_in, void *o, float *final_state,
-                       void *conv_state_out, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+}  // extern "C"
+
+namespace {
+// noalloc: the workspace is the library's static device array (gdn_prefill_noalloc);
+// then nothing here allocates or synchronises (GDN_VALIDATE and GDN_KERNEL_TIMING,
+// which need host copies and events, are ignored).
+gdn_status prefill_impl(const void *q, const void *k, const void *v, const float *a,
+                        const float *b, const void *z, const gdn_params *p,
+                        const float *init_state, const int32_t *cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, const void *conv_state_in, void *o,
+                        float *final_state, void *conv_state_out, void *workspace,
+                        size_t workspace_bytes, void *stream, bool noalloc) {
   g_err[0] = 0;
   gdn_status st = check_params(p);
   if (st != GDN_OK) return st;
@@ -178,16 +184,30 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
   if (o && (o == q || o == k || o == v || o == z))
     return fail(GDN_ERR_INVALID_ARGUMENT, "o must not alias an input");
   gdn::PrefillPlan plan = gdn::make_plan(num_seqs, total_tokens, p->num_v_heads);
-  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
-    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
-                workspace ? workspace_bytes : (size_t)0);
-  if (workspace && ((uintptr_t)workspace & 255u))
-    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (plan.workspace_bytes > gdn::kStaticWorkspaceBytes)
+      return fail(GDN_ERR_WORKSPACE,
+                  "this problem needs %zu bytes of workspace; gdn_prefill_noalloc has %zu",
+                  plan.workspace_bytes, gdn::kStaticWorkspaceBytes);
+  } else {
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+      return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                  plan.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+    if (workspace && ((uintptr_t)workspace & 255u))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
   st = check_device();
   if (st != GDN_OK) return st;
+  if (noalloc) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (hipError_t e = gdn::static_workspace(dev, &workspace); e != hipSuccess)
+      return hip_fail(e, "address of the static workspace");
+  }
   if (num_seqs == 0) return GDN_OK;
 
-  if (const char *ev = getenv("GDN_VALIDATE"); ev && ev[0] == '1') {
+  const char *validate = noalloc ? nullptr : getenv("GDN_VALIDATE");
+  if (validate && validate[0] == '1') {
     // report an invalid table met by an earlier call first
     if (hipError_t e = hipStreamSynchronize((hipStream_t)stream); e != hipSuccess)
       return hip_fail(e, "GDN_VALIDATE stream synchronisation");
@@ -198,7 +218,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
       return fail(GDN_ERR_INVALID_ARGUMENT,
                   "an earlier gdn_prefill call on this device had invalid cu_seqlens");
   }
-  if (const char *ev = getenv("GDN_VALIDATE"); ev && ev[0] == '1' && cu_seqlens) {
+  if (validate && validate[0] == '1' && cu_seqlens) {
     std::vector<int32_t> cu(num_seqs + 1);
     hipError_t e = hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (num_seqs + 1),
                              hipMemcpyDeviceToHost);
@@ -212,7 +232,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                   cu[num_seqs], (long long)total_tokens);
   }
   gdn::PrefillTiming *tm = nullptr;
-  if (const char *tv = getenv("GDN_KERNEL_TIMING"); tv && tv[0] == '1') {
+  const char *tv = noalloc ? nullptr : getenv("GDN_KERNEL_TIMING");
+  if (tv && tv[0] == '1') {
     if (!g_timing.created) {
       for (int i = 0; i <= gdn::kTimedKernels; ++i) {
         hipError_t ce = hipEventCreate(&g_timing.ev[i]);
@@ -228,6 +249,29 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
   if (tm) tm->valid = (e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *a, const float *b,
+                       const void *z, const gdn_params *p, const float *init_state,
+                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       const void *conv_state_in, void *o, float *final_state,
+                       void *conv_state_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  return prefill_impl(q, k, v, a, b, z, p, init_state, cu_seqlens, num_seqs, total_tokens,
+                      conv_state_in, o, final_state, conv_state_out, workspace, workspace_bytes,
+                      stream, false);
+}
+
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *a,
+                               const float *b, const void *z, const gdn_params *p,
+                               const float *init_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_tokens, const void *conv_state_in,
+                               void *o, float *final_state, void *conv_state_out, void *stream) {
+  return prefill_impl(q, k, v, a, b, z, p, init_state, cu_seqlens, num_seqs, total_tokens,
+                      conv_state_in, o, final_state, conv_state_out, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

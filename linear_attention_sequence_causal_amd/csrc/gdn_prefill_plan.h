@@ -56,6 +56,13 @@ struct PrefillTiming {
   bool ran[kTimedKernels];
 };
 
+// The static workspace of gdn_prefill_noalloc: one array of this many bytes per
+// device (gdn_noalloc.hip), addressed through hipGetSymbolAddress on the device.
+constexpr size_t kStaticWorkspaceBytes = (size_t)128 << 20;
+// Device address of that array on device `dev` (the current device), looked up
+// once per device and cached.
+hipError_t static_workspace(int dev, void **out);
+
 // Reads and clears this device's flag for invalid cu_seqlens contents (set by the
 // segment table of an earlier gdn_prefill call).  Synchronous.
 hipError_t take_prefill_error(int *flag);

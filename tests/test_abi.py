@@ -178,3 +178,24 @@ def test_valid_calls_report_missing_device(monkeypatch):
     addr = (raw.ctypes.data + 255) // 256 * 256
     assert _prefill(p, ws=ctypes.c_void_p(addr), ws_bytes=n) == NO_DEVICE
     assert np.all(raw == 0)
+
+
+def test_noalloc_prefill_rejects_problems_above_its_workspace_without_a_device():
+    """gdn_prefill_noalloc checks the problem's workspace against its static array on
+    the host, before the device check: no output is touched."""
+    p, host = _params(Hk=16, Hv=32)
+    need = gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 64, 1 << 20)
+    assert need > gdn.NOALLOC_WORKSPACE_BYTES
+    bufs = {n: _host(1 << 10) for n in ("q", "k", "v", "a", "b", "z", "cu")}
+    o, fs = _host(1 << 10), _host(1 << 10)
+    ptr = lambda x: ctypes.c_void_p(x.ctypes.data)
+    st = gdn.lib().gdn_prefill_noalloc(ptr(bufs["q"]), ptr(bufs["k"]), ptr(bufs["v"]),
+                                       ptr(bufs["a"]), ptr(bufs["b"]), ptr(bufs["z"]),
+                                       ctypes.byref(p), None, ptr(bufs["cu"]), 64, 1 << 20, None,
+                                       ptr(o), ptr(fs), None, None)
+    assert st == 3  # GDN_ERR_WORKSPACE
+    assert "gdn_prefill_noalloc" in gdn.lib().gdn_last_error().decode()
+    assert np.all(o == 7.0) and np.all(fs == 7.0)
+    # the 65536-token single-sequence workload fits
+    assert gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 65536) <= \
+        gdn.NOALLOC_WORKSPACE_BYTES
