@@ -100,9 +100,17 @@ def rel_l2(x, ref):
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
 
 
-def bench_prefill(args, torch, gdn, S):
+def bench_prefill(args, torch, gdn, S, slow_decay=None, d=None):
+    """The 65,536-token prefill; slow_decay = exp(A_log) for every head (alpha ~
+    exp(-slow_decay * softplus(a + dt_bias)) per token), which makes the segment maps
+    non-negligible so that the map and combine passes walk every chunk."""
+    import math
     w = S.PREFILL_64K
-    d = S.prefill_inputs(w, "cuda")
+    if d is None:
+        d = S.prefill_inputs(w, "cuda")
+    if slow_decay is not None:
+        d = dict(d)
+        d["A_log"] = torch.full_like(d["A_log"], math.log(slow_decay))
     T = d["q"].shape[0]
     Hk, Hv, D = w.num_qk_heads, w.num_v_heads, w.head_dim
 
@@ -113,6 +121,12 @@ def bench_prefill(args, torch, gdn, S):
 
     out = torch.empty_like(d["v"])
     fs = torch.empty((1, Hv, D, D), dtype=torch.float32, device="cuda")
+    # Untimed settle calls first: on a fresh box the full pass shortens over its first
+    # ~25 back-to-back calls (1.1-1.35 ms down to ~0.95 ms) while the clocks ramp up;
+    # then the warm-up, the timed calls and the per-kernel attribution all see the
+    # steady state (the warm-only trace selection skips settle + warm-up dispatches).
+    for _ in range(args.settle):
+        step()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -131,7 +145,7 @@ def bench_prefill(args, torch, gdn, S):
     # per-kernel attribution: HIP events between the library's kernels, same stream
     os.environ["GDN_KERNEL_TIMING"] = "1"
     per = {}
-    n_attr = max(3, min(10, args.steps))
+    n_attr = max(3, args.steps)
     for _ in range(n_attr):
         step()
         t = gdn.last_kernel_times()
@@ -147,7 +161,7 @@ def bench_prefill(args, torch, gdn, S):
     dom_ms = per.get(dom, call_avg) if dom else call_avg
     res = dict(T=T, out=out, fs=fs, d=d, ms_per_step=ms_per_step, call_ms=call_avg,
                call_ms_min=min(call_ms), flops=flops, bytes=nbytes, per_kernel_ms=per,
-               dominant=dom, dominant_ms=dom_ms)
+               dominant=dom, dominant_ms=dom_ms, n_attr=n_attr)
     return res
 
 
@@ -278,58 +292,173 @@ def bench_decode_tokens(args, torch, gdn, S, dec=None):
                        "hbm_frac": nb_v / (res["verify"] * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_prefill(res, S, oracle):
-    """fp64 oracle on the first `n` tokens of the same workload, all heads."""
-    import numpy as np
+    """The fp64 oracle on the same 65,536-token workload, all heads, on the host's
+    cores (one thread per (sequence, v head) unit, at most 32); then one thread on the
+    first 2048 tokens.  Also returns the oracle's o and final state for parity."""
     d = res["d"]
-    n = int(os.environ.get("GDN_BENCH_ORACLE_TOKENS", "65536"))
-    f = lambda t: S.to_f64(t[:n]) if t is not None else None
-    threads = min(oracle.default_threads(), d["v"].shape[1])
-    t0 = time.perf_counter()
-    o_ref, _, _ = oracle.prefill(f(d["q"]), f(d["k"]), f(d["v"]), f(d["a"]), f(d["b"]),
-                                 f(d["z"]), S.to_f64(d["conv_w"]), S.to_f64(d["A_log"]),
-                                 S.to_f64(d["dt_bias"]), S.to_f64(d["norm_w"]),
-                                 init_state=S.to_f64(d["init_state"]), nthreads=threads)
-    dt = time.perf_counter() - t0
-    err = rel_l2(S.to_f64(res["out"][:n]), o_ref)
-    return dict(value=n / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"first {n} of the 65536 tokens of the workload, all 32 v heads, fp64, "
-                       f"{dt:.1f} s"), err
-
-
-def cpu_baseline_decode(dec, S, oracle):
-    import numpy as np
-    n = int(os.environ.get("GDN_BENCH_ORACLE_DECODE_STEPS", "32"))
-    w, setup, toks = dec["w"], dec["setup"], dec["toks"]
     f = S.to_f64
-    # fresh copies of the decode start state (the GPU run advanced its own)
-    s2 = S.decode_setup(w, "cuda")
-    st, cc = f(s2["state"]), f(s2["conv_cache"])
-    threads = min(oracle.default_threads(), w.decode_batch * w.num_v_heads)
+    threads = min(oracle.default_threads(), d["v"].shape[1])
+    args = lambda n: (f(d["q"][:n]), f(d["k"][:n]), f(d["v"][:n]), f(d["a"][:n]), f(d["b"][:n]),
+                      f(d["z"][:n]), f(d["conv_w"]), f(d["A_log"]), f(d["dt_bias"]),
+                      f(d["norm_w"]))
+    T = d["q"].shape[0]
+    a_full = args(T)
     t0 = time.perf_counter()
-    for s in range(n):
-        _, st, cc = oracle.decode_step(f(toks["q"][s]), f(toks["k"][s]), f(toks["v"][s]),
-                                       f(toks["a"][s]), f(toks["b"][s]), f(toks["z"][s]),
-                                       f(setup["conv_w"]), f(setup["A_log"]),
-                                       f(setup["dt_bias"]), f(setup["norm_w"]), st, cc,
-                                       nthreads=threads)
+    o_ref, fs_ref, _ = oracle.prefill(*a_full, init_state=f(d["init_state"]), nthreads=threads)
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
-                sample=f"{n} decode steps of the B=256 workload (all sequences and heads), "
-                       f"fp64, {dt:.1f} s")
+    del a_full
+    n1 = 2048
+    a_one = args(n1)
+    t1 = time.perf_counter()
+    oracle.prefill(*a_one, init_state=f(d["init_state"]), nthreads=1)
+    dt1 = time.perf_counter() - t1
+    cb = dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
+              sample=f"all {T} tokens of the workload, all 32 v heads, fp64, {dt:.1f} s",
+              cpu_model=cpu_model(),
+              single_thread={"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"first {n1} tokens, all 32 v heads, {dt1:.1f} s"})
+    return cb, o_ref, fs_ref
+
+
+def decode_parity_and_cpu(args, torch, gdn, S, oracle):
+    """n decode steps of the B=256 workload from its start, on the GPU (untimed) and
+    with the fp64 oracle (timed on the host cores: the CPU baseline); o of every step
+    and the state and cache after step n compared."""
+    import numpy as np
+    w = S.DECODE_B256
+    n = args.oracle_decode_steps
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, n, "cuda")
+    f = S.to_f64
+    st, cc = f(setup["state"]), f(setup["conv_cache"])
+    outs = []
+    for s_ in range(n):
+        outs.append(gdn.decode_step(toks["q"][s_], toks["k"][s_], toks["v"][s_], toks["a"][s_],
+                                    toks["b"][s_], toks["z"][s_], setup["conv_w"],
+                                    setup["A_log"], setup["dt_bias"], setup["norm_w"],
+                                    setup["state"], setup["conv_cache"]))
+    torch.cuda.synchronize()
+    threads = min(oracle.default_threads(), w.decode_batch * w.num_v_heads)
+    num = den = 0.0
+    t0 = time.perf_counter()
+    for s_ in range(n):
+        o_r, st, cc = oracle.decode_step(f(toks["q"][s_]), f(toks["k"][s_]), f(toks["v"][s_]),
+                                         f(toks["a"][s_]), f(toks["b"][s_]), f(toks["z"][s_]),
+                                         f(setup["conv_w"]), f(setup["A_log"]),
+                                         f(setup["dt_bias"]), f(setup["norm_w"]), st, cc,
+                                         nthreads=threads)
+        og = f(outs[s_])
+        num += float(np.sum((og - o_r) ** 2))
+        den += float(np.sum(o_r ** 2))
+    dt = time.perf_counter() - t0
+    parity = {"o": (num / den) ** 0.5, "state": rel_l2(f(setup["state"]), st),
+              "conv_cache_bitwise": bool(np.array_equal(f(setup["conv_cache"]), cc)),
+              "checked": f"{n} consecutive steps, all 256 sequences and heads"}
+    cb = dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
+              sample=f"{n} decode steps of the B=256 workload (all sequences and heads), "
+                     f"fp64, {dt:.1f} s (includes the host copies of each step's inputs)",
+              cpu_model=cpu_model())
+    return cb, parity
+
+
+def prefill_parity(torch, gdn, S, oracle, w, group):
+    """GPU prefill of workload w against the oracle over every head, `group` q/k heads
+    per oracle call: relative L2 of o and of the final states (whole tensors)."""
+    import numpy as np
+    d = S.prefill_inputs(w, "cuda")
+    o, fs = gdn.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["z"], d["conv_w"],
+                        d["A_log"], d["dt_bias"], d["norm_w"], init_state=d["init_state"],
+                        cu_seqlens=d["cu_seqlens"], conv_state=d["conv_in"])
+    torch.cuda.synchronize()
+    Hk, Hv, D = w.num_qk_heads, w.num_v_heads, w.head_dim
+    f = S.to_f64
+    cu = d["cu_seqlens"].cpu().numpy()
+    num = {"o": 0.0, "s": 0.0}
+    den = {"o": 0.0, "s": 0.0}
+    for g0 in range(0, Hk, group):
+        qi, vi, ch = oracle.select_heads(range(g0, min(Hk, g0 + group)), Hk, Hv, D)
+        ti = lambda x: torch.as_tensor(x, device="cuda")
+        sel = lambda t, idx, dim=1: f(t.index_select(dim, ti(idx)))
+        o_r, fs_r, _ = oracle.prefill(
+            sel(d["q"], qi), sel(d["k"], qi), sel(d["v"], vi), sel(d["a"], vi), sel(d["b"], vi),
+            sel(d["z"], vi), sel(d["conv_w"], ch, 0), sel(d["A_log"], vi, 0),
+            sel(d["dt_bias"], vi, 0), f(d["norm_w"]), cu_seqlens=cu,
+            init_state=None if d["init_state"] is None else sel(d["init_state"], vi),
+            conv_in=None if d["conv_in"] is None else sel(d["conv_in"], ch, 2))
+        og, fg = sel(o, vi), sel(fs, vi)
+        num["o"] += float(np.sum((og - o_r) ** 2))
+        den["o"] += float(np.sum(o_r ** 2))
+        num["s"] += float(np.sum((fg - fs_r) ** 2))
+        den["s"] += float(np.sum(fs_r ** 2))
+        del o_r, fs_r, og, fg
+    del d, o, fs
+    return {"o": (num["o"] / den["o"]) ** 0.5, "state": (num["s"] / den["s"]) ** 0.5,
+            "checked": "all tokens, heads and sequences"}
+
+
+def summarize_trace(db_path, skip, count=None):
+    """Per-kernel durations from a rocprofv3 kernel-trace database (its `kernels`
+    view), grouped by kernel name and grid size, in dispatch order: dispatches
+    skip .. skip + count - 1 of each group (skip = the warm-up calls; count = None for
+    all the rest).  Returns a list of dicts."""
+    import sqlite3
+    import statistics
+    con = sqlite3.connect(db_path)
+    cols = [r[1] for r in con.execute("PRAGMA table_info(kernels)")]
+    pick = lambda *names: next(c for c in names if c in cols)
+    name_c = pick("name", "kernel_name", "kernel")
+    grid_c = pick("grid_size", "grid_size_x", "grid_x", "grid")
+    rows = con.execute(f'SELECT "{name_c}", "{grid_c}", start, "end" FROM kernels '
+                       f'ORDER BY start').fetchall()
+    groups = {}
+    for name, grid, t0, t1 in rows:
+        groups.setdefault((name, grid), []).append((t1 - t0) / 1e3)  # ns -> us
+    out = []
+    for (name, grid), durs in groups.items():
+        warm = durs[skip:] if len(durs) > skip else durs
+        if count is not None:
+            warm = warm[:count]
+        out.append({"kernel": name, "grid": grid, "dispatches": len(durs), "used": len(warm),
+                    "min_us": min(warm), "median_us": statistics.median(warm),
+                    "mean_us": statistics.fmean(warm), "max_us": max(warm)})
+    return sorted(out, key=lambda r: -r["mean_us"] * r["used"])
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # python bench.py --summarize-trace <results.db> [skip [count]]
+        skip = int(sys.argv[3]) if len(sys.argv) > 3 else 0
+        count = int(sys.argv[4]) if len(sys.argv) > 4 else None
+        for r in summarize_trace(sys.argv[2], skip, count):
+            if r["kernel"].startswith(("gdn::", "void gdn::")):
+                print(json.dumps(r))
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed prefill calls")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=int, default=30,
+                    help="untimed prefill calls before the warm-up (clock ramp)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--only", choices=("all", "prefill", "decode", "tokens"), default="all")
     ap.add_argument("--tokens-n", type=int, default=4,
                     help="new tokens per sequence of the n-token step leg (1..8)")
     ap.add_argument("--tokens-calls", type=int, default=100)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-decode-steps", type=int, default=100,
+                    help="decode steps the oracle recomputes (CPU baseline and parity)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle legs (CPU baseline and parity)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a device copy of this many GiB (PMC scale factor)")
     args = ap.parse_args()
@@ -361,29 +490,37 @@ def main():
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic"}
+    oracle_on = not args.no_cpu_baseline
+    if oracle_on:
+        import oracle
+    parity = {}
 
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, S)
         t_dom = pre["dominant_ms"] * 1e-3
         t_call = pre["call_ms"] * 1e-3
         ach = pre["flops"] / t_dom / 1e12
+        c32 = prefill_alg_flops_per_token(16, 32, 128, C=KERNEL_CHUNK) * pre["T"]
         line.update({
             "value": pre["T"] / (pre["ms_per_step"] * 1e-3),
             "unit": "tokens/s",
             "ms_per_step": pre["ms_per_step"],
             "config": {"workload": "prefill_T65536_hk16_hv32_d128_bf16", "num_seqs": 1,
                        "seq_len": pre["T"], "num_qk_heads": 16, "num_v_heads": 32,
-                       "head_dim": 128, "chunk": KERNEL_CHUNK, "state": "fp32"},
+                       "head_dim": 128, "chunk": KERNEL_CHUNK, "state": "fp32",
+                       "mfma_operands": "fp16, fp32 accumulation"},
             "roofline": {
                 "bound": "mfma", "kernel": f"prefill {pre['dominant']} pass",
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS,
                 "traffic": stored_traffic("prefill_full_bytes_per_launch"),
                 "alg_flops_per_launch": pre["flops"],
-                # the same formula at the kernel's own chunk size (what its products amount to)
-                "chunk32_form_flops_per_launch":
-                    prefill_alg_flops_per_token(16, 32, 128, C=KERNEL_CHUNK) * pre["T"],
                 "launch_ms": pre["dominant_ms"],
+                "launch_ms_source": f"HIP events on the library's stream around the full "
+                                    f"pass, mean of {pre['n_attr']} warm calls",
+                # the same formula at the kernel's own chunk size (the products it issues)
+                "chunk32_form_flops_per_launch": c32,
+                "chunk32_form_frac": c32 / t_dom / 1e12 / PEAK_BF16_TFLOPS,
             },
             "prefill_path": {
                 "call_ms": pre["call_ms"], "call_ms_min": pre["call_ms_min"],
@@ -392,9 +529,28 @@ def main():
                 "alg_bytes": pre["bytes"], "per_kernel_ms": pre["per_kernel_ms"],
             },
         })
-        # the other prefill workloads (parity configs), tokens/s of the whole call
+        # the same workload with slow decay (exp(A_log) = 0.03): every segment map is
+        # non-negligible, so the map and combine passes walk every chunk
+        slow = bench_prefill(args, torch, gdn, S, slow_decay=0.03, d=pre["d"])
+        line["prefill_slow_decay"] = {
+            "value": slow["T"] / (slow["call_ms"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": slow["call_ms"], "per_kernel_ms": slow["per_kernel_ms"],
+            "config": {"workload": "prefill_T65536_hk16_hv32_bf16, exp(A_log) = 0.03"}}
+        del slow
+        # the other prefill workloads, tokens/s of the whole call
         line["prefill_configs"] = {w.name: bench_prefill_config(args, torch, gdn, S, w)
                                    for w in (S.PREFILL_4K, S.VARLEN_64)}
+        if oracle_on:
+            cb, o_ref, fs_ref = cpu_baseline_prefill(pre, S, oracle)
+            line["cpu_baseline"] = cb
+            parity[S.PREFILL_64K.name] = {"o": rel_l2(S.to_f64(pre["out"]), o_ref),
+                                          "state": rel_l2(S.to_f64(pre["fs"]), fs_ref),
+                                          "checked": "all tokens and heads"}
+            del o_ref, fs_ref
+            for w, grp in ((S.TINY, 1), (S.PREFILL_4K, 16), (S.VARLEN_64, 4)):
+                parity[w.name] = prefill_parity(torch, gdn, S, oracle, w, grp)
+        del pre
+        torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, S)
         t = dec["ms_per_step"] * 1e-3
@@ -417,10 +573,18 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "decode_step (bf16 state)", "achieved": g16,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g16 / PEAK_HBM_GBS,
                          "alg_bytes_per_launch": d16["bytes"], "launch_ms": d16["ms_per_step"]}}
+        del dec, d16
+        torch.cuda.empty_cache()
+        if oracle_on:
+            cbd, par = decode_parity_and_cpu(args, torch, gdn, S, oracle)
+            dline["cpu_baseline"] = cbd
+            parity[S.DECODE_B256.name] = par
         if args.only == "decode":
             line.update({"value": dline["value"], "unit": "steps/s",
                          "ms_per_step": dline["ms_per_step"], "config": dline["config"],
                          "roofline": dline["roofline"], "bf16_state": dline["bf16_state"]})
+            if "cpu_baseline" in dline:
+                line["cpu_baseline"] = dline.pop("cpu_baseline")
         else:
             line["decode"] = dline
     if args.only in ("all", "tokens"):
@@ -431,20 +595,9 @@ def main():
                          "roofline": tl["roofline"], "verify": tl["verify"]})
         else:
             line["decode_tokens"] = tl
-    if not args.no_cpu_baseline and args.only != "tokens":
-        import oracle
-        if args.only in ("all", "prefill"):
-            cb, err = cpu_baseline_prefill(pre, S, oracle)
-            line["cpu_baseline"] = cb
-            line["parity_sample_o_rel_l2"] = err
-        if args.only in ("all", "decode"):
-            cbd = cpu_baseline_decode(dec, S, oracle)
-            if args.only == "decode":
-                line["cpu_baseline"] = cbd
-            else:
-                line["decode"]["cpu_baseline"] = cbd
-    else:
-        line["cpu_baseline"] = None
+    if parity:
+        line["parity"] = parity
+    line.setdefault("cpu_baseline", None)
     print(json.dumps(line), flush=True)
 
 

@@ -203,7 +203,7 @@ gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v,
 /* Diagnostics: per-kernel device time of the last gdn_prefill call made on
  * this thread while the environment had GDN_KERNEL_TIMING=1.  The library then
  * records HIP events on the caller's stream between its kernels (segment table,
- * map pass A, map pass B, combine, full pass, conv-state copy).  Writes up to
+ * segment-map pass, combine, full pass, conv-state copy).  Writes up to
  * `max_kernels` milliseconds (0 for a kernel that did not run) and returns the
  * number of slots written, or -1 when there is no timed call.  Waits for the
  * timed call's last event (host synchronisation). */

@@ -28,7 +28,7 @@ EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_noalloc",
             "gdn_decode_step",
             "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times",
             "gdn_check_device_errors", "gdn_status_string", "gdn_last_error", "gdn_version")
-PREFILL_KERNELS = ("segment_table", "map_A", "map_B", "combine", "full", "conv_state_out")
+PREFILL_KERNELS = ("segment_table", "maps", "combine", "full", "conv_state_out")
 
 
 class GdnParams(ctypes.Structure):

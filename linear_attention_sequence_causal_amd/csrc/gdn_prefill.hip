@@ -1403,6 +1403,8 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
   auto mark = [&](int slot) {  // event after kernel slot-1 (slot 0 = start)
     if (tm) (void)hipEventRecord(tm->ev[slot], stream);
   };
+  // slots: 0 segment table, 1 segment maps (both halves, one launch), 2 combine,
+  // 3 full pass, 4 conv-state copy
   if (tm) for (int i = 0; i < kTimedKernels; ++i) tm->ran[i] = false;
   if (tm) tm->ran[0] = true;  // the segment table was launched by the caller
   mark(1);
@@ -1415,31 +1417,29 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     dim3 g1((unsigned)(ids(plan.max_maps) * 2));
     hipLaunchKernelGGL((chunk_kernel<T, kMap>), g1, dim3(kThreads), kLdsBytes, stream, args);
     mark(2);
-    mark(3);
     dim3 g2((unsigned)((int64_t)N * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
                        args.seq_first, N, args.init_state, (const float *)args.maps,
                        args.map_zero, args.starts, Hv);
-    mark(4);
-    if (tm) tm->ran[1] = tm->ran[3] = true;
+    mark(3);
+    if (tm) tm->ran[1] = tm->ran[2] = true;
   } else {
     mark(2);
     mark(3);
-    mark(4);
   }
   dim3 g3((unsigned)ids(plan.max_segments));
   hipLaunchKernelGGL((chunk_kernel<T, kFull>), g3, dim3(kThreads), kLdsBytes, stream, args);
-  mark(5);
-  if (tm) tm->ran[4] = true;
+  mark(4);
+  if (tm) tm->ran[3] = true;
   if (conv_out) {
     const int64_t n = (int64_t)N * args.Cc;
     hipLaunchKernelGGL((conv_out_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, cu, N, Ttot, (const T *)args.q, (const T *)args.k,
                        (const T *)args.v, (const T *)args.conv_in, (T *)conv_out, args.Hk,
                        args.Hv, args.Cc);
-    if (tm) tm->ran[5] = true;
+    if (tm) tm->ran[4] = true;
   }
-  mark(6);
+  mark(5);
   return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ struct PrefillPlan {
 PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_heads);
 
 // Optional events between the prefill kernels (GDN_KERNEL_TIMING=1).
-constexpr int kTimedKernels = 6;
+constexpr int kTimedKernels = 5;
 struct PrefillTiming {
   hipEvent_t ev[kTimedKernels + 1];
   bool created = false, valid = false;
