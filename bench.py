@@ -15,6 +15,7 @@ choose to do):
   decode bytes/step  = B*Hv*D*D*4*2 (state read + write) + B*33,024 (tokens)
                        + B*3*Cc*2*2 (conv cache read + write)
   bf16-state decode  = the same with 2-byte state elements
+  fp8-state decode   = the same with 1-byte state elements + B*Hv*D*4*2 (row scales)
   n-token step bytes = the same with n*B*33,024 token bytes (commit pass); a
                        verify pass (commit 0) reads the state and cache only
 Peaks: MI355X dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s.
@@ -165,22 +166,34 @@ def bench_prefill(args, torch, gdn, S, slow_decay=None, d=None):
     return res
 
 
-def bench_decode(args, torch, gdn, S, state_bf16=False, toks=None):
+def fp8_rows(torch, x):
+    """E4M3 values and per-row power-of-two scales of a state (the smallest 2^e with
+    max|row| <= 448 * 2^e), for the fp8-storage decode leg's start state."""
+    m = x.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.where(m > 0, m / 448.0, torch.ones_like(m))))
+    sc = torch.exp2(e)
+    return (x / sc[..., None]).to(torch.float8_e4m3fn), sc.float().contiguous()
+
+
+def bench_decode(args, torch, gdn, S, state_bf16=False, toks=None, state_fp8=False):
     w = S.DECODE_B256
     steps = args.decode_steps
     setup = S.decode_setup(w, "cuda")
     if toks is None:
         toks = S.decode_tokens(w, setup, steps, "cuda")
     state, cache = setup["state"], setup["conv_cache"]
+    scale = None
     if state_bf16:  # reduced-precision storage of the same start state
         state = state.to(torch.bfloat16)
+    if state_fp8:
+        state, scale = fp8_rows(torch, state)
     o = torch.empty((w.decode_batch, w.num_v_heads, w.head_dim), dtype=torch.bfloat16,
                     device="cuda")
 
     def one(s):
         gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s], toks["b"][s],
                         toks["z"][s], setup["conv_w"], setup["A_log"], setup["dt_bias"],
-                        setup["norm_w"], state, cache, out=o)
+                        setup["norm_w"], state, cache, out=o, state_scale=scale)
 
     for s in range(min(args.warmup, steps)):  # warm-up steps advance the state; fine
         one(s)
@@ -195,7 +208,9 @@ def bench_decode(args, torch, gdn, S, state_bf16=False, toks=None):
     wall = time.perf_counter() - t0
     ev_ms = e0.elapsed_time(e1)
     nbytes = decode_alg_bytes(w.decode_batch, w.num_qk_heads, w.num_v_heads, w.head_dim,
-                              state_bytes=2 if state_bf16 else 4)
+                              state_bytes=2 if state_bf16 else 1 if state_fp8 else 4)
+    if state_fp8:  # the per-row scales, read and written
+        nbytes += w.decode_batch * w.num_v_heads * w.head_dim * 4 * 2
     return dict(steps=steps, wall_s=wall, ms_per_step=ev_ms / steps, bytes=nbytes,
                 w=w, setup=setup, toks=toks)
 
@@ -573,7 +588,16 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "decode_step (bf16 state)", "achieved": g16,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g16 / PEAK_HBM_GBS,
                          "alg_bytes_per_launch": d16["bytes"], "launch_ms": d16["ms_per_step"]}}
-        del dec, d16
+        # ... and in fp8 (E4M3 values, one power-of-two scale per state row)
+        d8 = bench_decode(args, torch, gdn, S, state_fp8=True, toks=dec["toks"])
+        t8 = d8["ms_per_step"] * 1e-3
+        g8 = d8["bytes"] / t8 / 1e9
+        dline["fp8_state"] = {
+            "value": 1.0 / t8, "unit": "steps/s", "ms_per_step": d8["ms_per_step"],
+            "roofline": {"bound": "hbm", "kernel": "decode_step (fp8 state)", "achieved": g8,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g8 / PEAK_HBM_GBS,
+                         "alg_bytes_per_launch": d8["bytes"], "launch_ms": d8["ms_per_step"]}}
+        del dec, d16, d8
         torch.cuda.empty_cache()
         if oracle_on:
             cbd, par = decode_parity_and_cpu(args, torch, gdn, S, oracle)
@@ -582,7 +606,8 @@ def main():
         if args.only == "decode":
             line.update({"value": dline["value"], "unit": "steps/s",
                          "ms_per_step": dline["ms_per_step"], "config": dline["config"],
-                         "roofline": dline["roofline"], "bf16_state": dline["bf16_state"]})
+                         "roofline": dline["roofline"], "bf16_state": dline["bf16_state"],
+                         "fp8_state": dline["fp8_state"]})
             if "cpu_baseline" in dline:
                 line["cpu_baseline"] = dline.pop("cpu_baseline")
         else:

@@ -176,6 +176,22 @@ gdn_status gdn_decode_step_bf16_state(const void *q, const void *k, const void *
                                       const gdn_params *p, void *state, void *conv_state,
                                       void *o, int32_t batch, void *stream);
 
+/* gdn_decode_step with the state stored in fp8: state is [B, Hv, D, D] OCP E4M3
+ * bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite value
+ * 448) and state_scale [B, Hv, D] fp32 holds one power-of-two scale per state row
+ * (per dk index i of H = S^T): the stored state is H[i][j] = e4m3(state[i][j]) *
+ * state_scale[i].  Each step reads both once, does the step's arithmetic in fp32
+ * (identical to gdn_decode_step's), and writes back every row re-scaled by the
+ * smallest power of two 2^e with max_j |H[i][j]| <= 448 * 2^e (1 for a zero row)
+ * and rounded to nearest even.  A quarter of the fp32 state's bytes; a
+ * reduced-precision storage mode beside the pages' fp32 state (one fp8 rounding per
+ * step: its own tolerance, see the tests).  Other arguments and errors as
+ * gdn_decode_step; state_scale is required (GDN_ERR_INVALID_ARGUMENT). */
+gdn_status gdn_decode_step_fp8_state(const void *q, const void *k, const void *v,
+                                     const float *a, const float *b, const void *z,
+                                     const gdn_params *p, void *state, float *state_scale,
+                                     void *conv_state, void *o, int32_t batch, void *stream);
+
 /* n_tokens new tokens per sequence on a cached state (multi-token decode; the
  * verify and commit passes of speculative decoding).  The result is that of
  * n_tokens gdn_decode_step calls in order (the field guide's six update

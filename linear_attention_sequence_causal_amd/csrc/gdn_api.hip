@@ -20,8 +20,8 @@ template <typename T>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *a,
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
-                         float rms_eps, void *state, bool state_bf16, void *conv_state, void *o,
-                         int batch, int Hk, int Hv, hipStream_t stream);
+                         float rms_eps, void *state, int state_kind, float *state_scale,
+                         void *conv_state, void *o, int batch, int Hk, int Hv, hipStream_t stream);
 int decode_max_ratio();
 template <typename T>
 hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, const float *a,
@@ -277,10 +277,11 @@ gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, cons
 }  // extern "C"
 
 namespace {
+// state_kind: 0 fp32, 1 bf16, 2 fp8 (E4M3 values + per-row scales in state_scale)
 gdn_status decode_step_impl(const void *q, const void *k, const void *v, const float *a,
                             const float *b, const void *z, const gdn_params *p, void *state,
-                            bool state_bf16, void *conv_state, void *o, int32_t batch,
-                            void *stream) {
+                            int state_kind, float *state_scale, void *conv_state, void *o,
+                            int32_t batch, void *stream) {
   g_err[0] = 0;
   gdn_status st = check_params(p);
   if (st != GDN_OK) return st;
@@ -290,6 +291,8 @@ gdn_status decode_step_impl(const void *q, const void *k, const void *v, const f
                 gdn::decode_max_ratio());
   if (batch > 0 && (!q || !k || !v || !a || !b || !z || !state || !conv_state || !o))
     return fail(GDN_ERR_INVALID_ARGUMENT, "all tensor pointers are required");
+  if (batch > 0 && state_kind == 2 && !state_scale)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state_scale is required with fp8 state storage");
   if ((int64_t)batch * p->num_qk_heads > (int64_t)INT32_MAX)
     return fail(GDN_ERR_UNSUPPORTED, "batch * num_qk_heads too large");
   if (o && (o == q || o == k || o == v || o == z))
@@ -300,12 +303,12 @@ gdn_status decode_step_impl(const void *q, const void *k, const void *v, const f
   if (p->act_dtype == GDN_BF16)
     e = gdn::launch_decode<gdn::bf16_t>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                         p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
-                                        state_bf16, conv_state, o, batch, p->num_qk_heads,
-                                        p->num_v_heads, (hipStream_t)stream);
+                                        state_kind, state_scale, conv_state, o, batch,
+                                        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
   else
     e = gdn::launch_decode<float>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                   p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
-                                  state_bf16, conv_state, o, batch, p->num_qk_heads,
+                                  state_kind, state_scale, conv_state, o, batch, p->num_qk_heads,
                                   p->num_v_heads, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return GDN_OK;
@@ -317,14 +320,22 @@ extern "C" {
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *a,
                            const float *b, const void *z, const gdn_params *p, float *state,
                            void *conv_state, void *o, int32_t batch, void *stream) {
-  return decode_step_impl(q, k, v, a, b, z, p, state, false, conv_state, o, batch, stream);
+  return decode_step_impl(q, k, v, a, b, z, p, state, 0, nullptr, conv_state, o, batch, stream);
 }
 
 gdn_status gdn_decode_step_bf16_state(const void *q, const void *k, const void *v,
                                       const float *a, const float *b, const void *z,
                                       const gdn_params *p, void *state, void *conv_state,
                                       void *o, int32_t batch, void *stream) {
-  return decode_step_impl(q, k, v, a, b, z, p, state, true, conv_state, o, batch, stream);
+  return decode_step_impl(q, k, v, a, b, z, p, state, 1, nullptr, conv_state, o, batch, stream);
+}
+
+gdn_status gdn_decode_step_fp8_state(const void *q, const void *k, const void *v,
+                                     const float *a, const float *b, const void *z,
+                                     const gdn_params *p, void *state, float *state_scale,
+                                     void *conv_state, void *o, int32_t batch, void *stream) {
+  return decode_step_impl(q, k, v, a, b, z, p, state, 2, state_scale, conv_state, o, batch,
+                          stream);
 }
 
 gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v, const float *a,

@@ -23,6 +23,8 @@
 namespace gdn {
 
 constexpr int kDecThreads = 256;
+// stored state formats of the decode step
+constexpr int kStateF32 = 0, kStateBf16 = 1, kStateFp8 = 2;
 constexpr int kDecMaxRatio = 8;  // largest Hv / Hk the decode kernel accepts
 
 // Stored state: fp32, or bf16 (rounded to nearest even on every store) with the
@@ -54,6 +56,53 @@ template <> struct StateIO<bf16_t> {
   }
 };
 
+// fp8 storage: OCP E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// largest finite value 448) times one power-of-two scale per state row (dk index)
+// kept in fp32 beside the state; the step's arithmetic is fp32.
+struct fp8_t {
+  uint8_t bits;
+};
+template <> struct StateIO<fp8_t> {
+  typedef uint32_t Raw;  // four consecutive columns
+  static __device__ __forceinline__ Raw load_raw(const fp8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+  }
+  static __device__ __forceinline__ f32x4 widen(Raw w) {
+    return f32x4{__builtin_amdgcn_cvt_f32_fp8((int)w, 0), __builtin_amdgcn_cvt_f32_fp8((int)w, 1),
+                 __builtin_amdgcn_cvt_f32_fp8((int)w, 2), __builtin_amdgcn_cvt_f32_fp8((int)w, 3)};
+  }
+  // x already divided by the row scale (|x| <= 448); round to nearest even
+  static __device__ __forceinline__ void store(fp8_t *p, f32x4 x) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x.x, x.y, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x.z, x.w, w, true);
+    __builtin_nontemporal_store((uint32_t)w, reinterpret_cast<uint32_t *>(p));
+  }
+};
+
+// Maximum over each half of a wave (lanes 0..31 and 32..63), left in every lane of
+// the half: rotate-and-max inside each 16-lane row, then the two rows of each half
+// combined with a gfx950 row swap.
+__device__ __forceinline__ float half_wave_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+// Exponent e of the fp8 row scale 2^e: the smallest with m <= 448 * 2^e, for a finite
+// normal m > 0 (m = f 2^E, 1 <= f < 2: e = E - 8, or E - 7 when f > 1.75); 0 (scale 1)
+// for zero, subnormal or non-finite m.
+__device__ __forceinline__ int fp8_scale_exp(float m) {
+  const uint32_t b = __float_as_uint(m);
+  const int eb = (int)((b >> 23) & 0xFF);
+  if (eb == 0 || eb == 255) return 0;
+  const int e = eb - 127 - 8 + ((b & 0x7FFFFF) > 0x600000u ? 1 : 0);
+  return min(max(e, -126), 127);
+}
+
 template <typename T, typename S>
 __global__ void __launch_bounds__(kDecThreads)
 decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -61,8 +110,9 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
                    const T *__restrict__ z, const float *__restrict__ conv_w,
                    const float *__restrict__ A_log, const float *__restrict__ dt_bias,
                    const float *__restrict__ norm_w, float q_scale, float l2_eps, float rms_eps,
-                   S *__restrict__ state, T *__restrict__ conv_state, T *__restrict__ o,
-                   int Hk, int Hv) {
+                   S *__restrict__ state, float *__restrict__ state_scale,
+                   T *__restrict__ conv_state, T *__restrict__ o, int Hk, int Hv) {
+  constexpr bool kFp8 = __is_same(S, fp8_t);
   const int g = blockIdx.x % Hk;
   const int bseq = blockIdx.x / Hk;
   const int r = Hv / Hk;
@@ -92,10 +142,18 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   uint32_t zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + r * g) * kD + ztid);
   // Start streaming the first head's state before the prologue.
   typename StateIO<S>::Raw Hraw[16];
+  f32x4 Sraw[4];  // fp8 storage: the scales of this thread's 16 rows
+  auto scale_ptr = [&](int j) {
+    return state_scale + ((int64_t)bseq * Hv + r * g + j) * kD + row0;
+  };
   {
     const S *Hp = head_ptr(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) Hraw[i] = StateIO<S>::load_raw(Hp + i * kD);
+    if (kFp8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sraw[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(0) + 4 * i);
+    }
   }
 
   // ---- 1. prologue --------------------------------------------------------------
@@ -181,14 +239,25 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     // the next head's loads go out first (vector-memory waits are in issue order, so
     // waiting for this head's state does not wait for them)
     typename StateIO<S>::Raw Hnext[16];
+    f32x4 Snext[4];
     if (j + 1 < r) {
       const S *Hn = head_ptr(j + 1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) Hnext[i] = StateIO<S>::load_raw(Hn + i * kD);
+      if (kFp8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Snext[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(j + 1) + 4 * i);
+      }
     }
     f32x4 Hcur[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Hcur[i] = StateIO<S>::widen(Hraw[i]);
+    for (int i = 0; i < 16; ++i) {
+      Hcur[i] = StateIO<S>::widen(Hraw[i]);
+      if (kFp8) {
+        const float sc = Sraw[i >> 2][i & 3];
+        Hcur[i].x *= sc; Hcur[i].y *= sc; Hcur[i].z *= sc; Hcur[i].w *= sc;
+      }
+    }
     const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
     const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
     float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
@@ -228,6 +297,14 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       hn.y = alpha * Hcur[i].y + kr[i] * ec[1];
       hn.z = alpha * Hcur[i].z + kr[i] * ec[2];
       hn.w = alpha * Hcur[i].w + kr[i] * ec[3];
+      if (kFp8) {  // the row's scale: max over its 128 columns (this half-wave's 32 lanes)
+        const float m = half_wave_max(fmaxf(fmaxf(fabsf(hn.x), fabsf(hn.y)),
+                                            fmaxf(fabsf(hn.z), fabsf(hn.w))));
+        const int e = fp8_scale_exp(m);
+        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e (|e| <= 126)
+        hn.x *= inv; hn.y *= inv; hn.z *= inv; hn.w *= inv;
+        if ((tid & 31) == 0) scale_ptr(j)[i] = __uint_as_float((uint32_t)(127 + e) << 23);
+      }
       StateIO<S>::store(Hp + i * kD, hn);
     }
     if (tid < kD) {
@@ -238,6 +315,10 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     if (j + 1 < r) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) Hraw[i] = Hnext[i];
+      if (kFp8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sraw[i] = Snext[i];
+      }
     }
   }
 }
@@ -247,20 +328,18 @@ template <typename T>
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *a,
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
-                         float rms_eps, void *state, bool state_bf16, void *conv_state, void *o,
-                         int batch, int Hk, int Hv, hipStream_t stream) {
+                         float rms_eps, void *state, int state_kind, float *state_scale,
+                         void *conv_state, void *o, int batch, int Hk, int Hv, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   dim3 grid((unsigned)batch * (unsigned)Hk);
-  if (state_bf16)
-    hipLaunchKernelGGL((decode_step_kernel<T, bf16_t>), grid, dim3(kDecThreads), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
-                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, (bf16_t *)state,
-                       (T *)conv_state, (T *)o, Hk, Hv);
-  else
-    hipLaunchKernelGGL((decode_step_kernel<T, float>), grid, dim3(kDecThreads), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
-                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, (float *)state,
-                       (T *)conv_state, (T *)o, Hk, Hv);
+  auto go = [&](auto kern, auto *st) {
+    hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), 0, stream, (const T *)q, (const T *)k,
+                       (const T *)v, a, b, (const T *)z, conv_w, A_log, dt_bias, norm_w, q_scale,
+                       l2_eps, rms_eps, st, state_scale, (T *)conv_state, (T *)o, Hk, Hv);
+  };
+  if (state_kind == kStateBf16) go(decode_step_kernel<T, bf16_t>, (bf16_t *)state);
+  else if (state_kind == kStateFp8) go(decode_step_kernel<T, fp8_t>, (fp8_t *)state);
+  else go(decode_step_kernel<T, float>, (float *)state);
   return hipGetLastError();
 }
 
@@ -269,13 +348,13 @@ int decode_max_ratio() { return kDecMaxRatio; }
 template hipError_t launch_decode<float>(const void *, const void *, const void *, const float *,
                                          const float *, const void *, const float *,
                                          const float *, const float *, const float *, float,
-                                         float, float, void *, bool, void *, void *, int, int,
-                                         int, hipStream_t);
+                                         float, float, void *, int, float *, void *, void *, int,
+                                         int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(const void *, const void *, const void *,
                                           const float *, const float *, const void *,
                                           const float *, const float *, const float *,
-                                          const float *, float, float, float, void *, bool,
-                                          void *, void *, int, int, int, hipStream_t);
+                                          const float *, float, float, float, void *, int,
+                                          float *, void *, void *, int, int, int, hipStream_t);
 
 // ---------------------------------------------------------------------------------
 // Multi-token step: n (1..8) new tokens per sequence on a cached state.  It is the

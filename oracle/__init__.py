@@ -231,6 +231,50 @@ def decode_step_bf16_state(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, sta
     return o, round_bf16(st), cache
 
 
+FP8_MAX = 448.0  # largest finite OCP E4M3 value, 1.75 * 2^8
+
+
+def round_fp8_e4m3(x):
+    """Nearest OCP E4M3 value of each fp64 element (ties to even), as fp64, for
+    |x| <= 448.  E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; normal values
+    from 2^-6 carry 4 significant bits, smaller ones are multiples of 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                              # x = m 2^e, 0.5 <= |m| < 1
+    normal = np.ldexp(np.rint(np.ldexp(m, 4)), e - 4)
+    sub = np.rint(np.ldexp(x, 9)) / 512.0
+    return np.where(np.abs(x) >= 2.0 ** -6, normal, sub)
+
+
+def fp8_row_scales(x):
+    """Per-row power-of-two scales of the fp8 state storage: for each row (last axis)
+    the smallest 2^e with max|row| <= 448 * 2^e (1 for an all-zero row)."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(np.abs(x), axis=-1)
+    f, E = np.frexp(np.where(m > 0, m, 1.0))       # m = f 2^E, 0.5 <= f < 1
+    e = (E - 1) - 8 + (2.0 * f > 1.75)              # 448 = 1.75 * 2^8
+    return np.where(m > 0, np.ldexp(1.0, e), 1.0)
+
+
+def quantize_fp8_rows(x):
+    """(stored values, scales): each row divided by its scale and rounded to E4M3;
+    the stored state is values * scales[..., None]."""
+    s = fp8_row_scales(x)
+    return round_fp8_e4m3(np.asarray(x, dtype=np.float64) / s[..., None]), s
+
+
+def decode_step_fp8_state(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state_q,
+                          state_scale, conv_cache, **kw):
+    """One decode step with the state stored in fp8 (E4M3 values state_q [B, Hv, D, D]
+    times one power-of-two scale per state row, state_scale [B, Hv, D]): the step in
+    fp64 on the stored state, then the new state re-quantised row by row.
+    Returns (o, new_state_q, new_state_scale, new_conv_cache)."""
+    st = np.asarray(state_q, dtype=np.float64) * np.asarray(state_scale, np.float64)[..., None]
+    o, st, cache = decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, st,
+                               conv_cache, **kw)
+    qv, sc = quantize_fp8_rows(st)
+    return o, qv, sc, cache
+
+
 def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
                   num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
     """n new tokens per sequence on a cached state (multi-token decode / verify / commit).

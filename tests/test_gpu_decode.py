@@ -275,3 +275,101 @@ def test_decode_bf16_state_identity_gates_keep_state_bitwise():
                     setup["conv_cache"])
     torch.cuda.synchronize()
     assert torch.equal(st0, state)
+
+
+# ------------------------------------------- reduced-precision (fp8) state storage
+
+def _fp8_start(state):
+    """The fp32 start state quantised by the oracle's rule (E4M3 values and per-row
+    power-of-two scales), as device tensors (float8_e4m3fn codes hold the values
+    exactly)."""
+    qv, sc = oracle.quantize_fp8_rows(S.to_f64(state))
+    dev = state.device
+    return (torch.as_tensor(qv, dtype=torch.float32).to(dev).to(torch.float8_e4m3fn),
+            torch.as_tensor(sc, dtype=torch.float32).to(dev), qv, sc)
+
+
+def _deq(q8, sc):
+    return S.to_f64(q8.float()) * S.to_f64(sc)[..., None]
+
+
+def _run_decode_fp8_state(w, steps, seq_sample=None, b_override=None, alog_override=None):
+    import linear_attention_sequence_causal_amd as gdn
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, steps, "cuda")
+    if b_override is not None:
+        toks["b"] = torch.full_like(toks["b"], b_override)
+    if alog_override is not None:
+        setup["A_log"] = torch.full_like(setup["A_log"], alog_override)
+    q8, sc, qv, scv = _fp8_start(setup["state"])
+    cache = setup["conv_cache"]
+    cc0 = cache.clone()
+    outs = []
+    for s in range(steps):
+        outs.append(gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s],
+                                    toks["b"][s], toks["z"][s], setup["conv_w"], setup["A_log"],
+                                    setup["dt_bias"], setup["norm_w"], q8, cache, state_scale=sc))
+    torch.cuda.synchronize()
+    sel = slice(None) if seq_sample is None else seq_sample
+    f = S.to_f64
+    qb, sb, cb = qv[sel], scv[sel], f(cc0[sel])
+    sx, cx = qv[sel] * scv[sel][..., None], cb.copy()
+    ob, ox = [], []
+    for s in range(steps):
+        args = (f(toks["q"][s][sel]), f(toks["k"][s][sel]), f(toks["v"][s][sel]),
+                f(toks["a"][s][sel]), f(toks["b"][s][sel]), f(toks["z"][s][sel]),
+                f(setup["conv_w"]), f(setup["A_log"]), f(setup["dt_bias"]), f(setup["norm_w"]))
+        o_s, qb, sb, cb = oracle.decode_step_fp8_state(*args, qb, sb, cb)
+        ob.append(o_s)
+        o_s, sx, cx = oracle.decode_step(*args, sx, cx)
+        ox.append(o_s)
+    return (np.stack([f(o[sel]) for o in outs]), _deq(q8, sc)[sel], f(cache[sel]),
+            np.stack(ob), qb * sb[..., None], cb, np.stack(ox), sx, q8, sc)
+
+
+@gpu
+@pytest.mark.parametrize("hk,hv", [(16, 32), (2, 8)])
+def test_decode_fp8_state_matches_its_oracle(hk, hv):
+    """Against the oracle of the same storage (fp64 step on the stored state, then
+    per-row power-of-two scales and E4M3 rounding): only the fp32 arithmetic differs,
+    which moves a stored element by one E4M3 unit where fp32 and fp64 fall on two
+    sides of a rounding midpoint."""
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=hk, num_v_heads=hv, seed=110 + hv)
+    o, st, cc, o_b, st_b, cc_b, o_x, st_x, q8, sc = _run_decode_fp8_state(w, steps=8)
+    eo, es = rel_l2(o, o_b), rel_l2(st, st_b)
+    print(f"decode fp8 state Hk={hk} Hv={hv}: o rel-L2 {eo:.3e} state rel-L2 {es:.3e} "
+          f"(vs fp32 storage: o {rel_l2(o, o_x):.3e} state {rel_l2(st, st_x):.3e})")
+    assert eo < O_TOL and es < 1e-3
+    assert np.array_equal(cc, cc_b)
+    s = S.to_f64(sc)
+    assert np.all(np.exp2(np.round(np.log2(s))) == s)  # powers of two
+    assert float(q8.float().abs().max()) <= 448.0
+
+
+@gpu
+def test_decode_fp8_state_full_batch_precision_cost():
+    """B=256, 16/32 heads, 40 steps: parity with the fp8-storage oracle on 6 sampled
+    sequences, and the cost of the storage against fp32 storage (the mode's own
+    tolerance, 5e-2 on o and on the state: one E4M3 rounding, 2^-4 relative at most, per
+    step, damped by the decay)."""
+    w = S.DECODE_B256
+    sample = [0, 5, 99, 128, 201, 255]
+    o, st, cc, o_b, st_b, cc_b, o_x, st_x, _, _ = _run_decode_fp8_state(w, 40, seq_sample=sample)
+    eo, es, ex_o, ex_s = rel_l2(o, o_b), rel_l2(st, st_b), rel_l2(o, o_x), rel_l2(st, st_x)
+    print(f"decode fp8 state B=256 sampled: o rel-L2 {eo:.3e} state rel-L2 {es:.3e}; "
+          f"vs fp32 storage o {ex_o:.3e} state {ex_s:.3e}")
+    assert eo < O_TOL and es < 1e-3
+    assert ex_o < 5e-2 and ex_s < 5e-2
+    assert np.array_equal(cc, cc_b)
+
+
+@gpu
+def test_decode_fp8_state_identity_gates_keep_state_values():
+    """beta = 0 and alpha = 1: the stored values come back unchanged (re-quantising an
+    unchanged row gives the same values)."""
+    w = S.scaled(S.DECODE_B256, decode_batch=3, seed=112)
+    o, st, cc, o_b, st_b, cc_b, o_x, st_x, _, _ = _run_decode_fp8_state(
+        w, 2, b_override=-float("inf"), alog_override=-float("inf"))
+    setup = S.decode_setup(w, "cuda")
+    q8, sc, qv, scv = _fp8_start(setup["state"])
+    assert np.array_equal(st, qv * scv[..., None])

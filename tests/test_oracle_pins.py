@@ -13,6 +13,7 @@ import math
 import os
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -582,3 +583,65 @@ def test_bf16_state_step_is_the_exact_step_rounded():
     nz = s1 != 0
     assert np.all(np.abs(s2[nz] - s1[nz]) <= np.abs(s1[nz]) * 2.0 ** -8)
     assert not np.array_equal(s1, s2)  # the rounding is real
+
+
+# ------------------------------------------------- fp8 (E4M3) state storage
+
+
+def test_round_fp8_hand_values_and_ties():
+    r = oracle.round_fp8_e4m3
+    assert r(448.0) == 448.0 and r(-448.0) == -448.0          # largest finite value
+    assert r(1.0 + 2.0 ** -4) == 1.0                            # tie -> even mantissa 000
+    assert r(1.0 + 3 * 2.0 ** -4) == 1.25                       # tie -> even mantissa 010
+    assert r(1.0 + 2.0 ** -4 + 2.0 ** -20) == 1.125
+    assert r(0.1) == 0.1015625                                  # 1.625 * 2^-4
+    assert r(2.0 ** -6) == 2.0 ** -6                            # smallest normal
+    assert r(3 * 2.0 ** -10) == 2.0 ** -8                       # subnormal tie -> even (2/512)
+    assert r(2.0 ** -10) == 0.0                                 # half the smallest subnormal
+    assert r(0.0) == 0.0
+
+
+def test_round_fp8_matches_torchs_e4m3fn_cast():
+    """An independent implementation of the same format: torch's float8_e4m3fn."""
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(200000, generator=g, dtype=torch.float64) * torch.exp(
+        torch.randn(200000, generator=g, dtype=torch.float64) * 3.0)
+    x = x.clamp(-448.0, 448.0).to(torch.float32)
+    ref = x.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_fp8_e4m3(x.to(torch.float64).numpy()), ref)
+    # every code decodes to a value the rounding maps to itself
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    vals = codes[torch.isfinite(codes)].numpy()
+    assert np.array_equal(oracle.round_fp8_e4m3(vals), vals)
+
+
+def test_fp8_row_scales_are_the_smallest_power_of_two_that_fits():
+    x = np.array([[448.0, -1.0], [448.5, 0.0], [0.0, 0.0], [-3.5, 1.0], [1e-30, 0.0]])
+    s = oracle.fp8_row_scales(x)
+    assert list(s[:4]) == [1.0, 2.0, 1.0, 2.0 ** -7]
+    for row, sc in zip(x, s):
+        m = np.max(np.abs(row))
+        if m > 0:
+            assert m <= 448.0 * sc and m > 448.0 * sc / 2
+    q, sc = oracle.quantize_fp8_rows(x)
+    assert np.all(np.abs(q) <= 448.0)
+    assert np.allclose(q * sc[:, None], x, rtol=2.0 ** -4, atol=0.0)
+
+
+def test_fp8_state_step_keeps_a_frozen_state_bit_for_bit():
+    """beta = 0, alpha = 1: the state is unchanged, so re-quantising a stored state gives
+    back the same values (a row whose largest stored code rounded down to 224 moves to
+    half the scale and doubled codes, the same values)."""
+    rng = np.random.default_rng(3)
+    B, Hk, Hv, D = 2, 1, 2, 128
+    Cc = 2 * Hk * D + Hv * D
+    st = rng.normal(0, 0.01, (B, Hv, D, D))
+    sq, ss = oracle.quantize_fp8_rows(st)
+    q = rng.normal(size=(B, Hk, D)); k = rng.normal(size=(B, Hk, D))
+    v = rng.normal(size=(B, Hv, D)); z = rng.normal(size=(B, Hv, D))
+    a = rng.normal(size=(B, Hv)); b = np.full((B, Hv), -np.inf)
+    cw = rng.normal(0, 0.5, (Cc, 4)); cache = rng.normal(size=(B, 3, Cc))
+    _, q2, s2, _ = oracle.decode_step_fp8_state(q, k, v, a, b, z, cw, np.full(Hv, -np.inf),
+                                                np.zeros(Hv), np.ones(D), sq, ss, cache)
+    assert np.array_equal(q2 * s2[..., None], sq * ss[..., None])
+    assert np.all(np.abs(q2) <= 448.0)
