@@ -10,6 +10,7 @@
  *   beta_t = sigmoid(b_t)
  *   S'    = alpha_t S;  e = v_t - S' k_t;  S = S' + beta_t e k_t^T;  y_t = S q_t
  *   o_t   = y_t * rsqrt(mean(y_t^2) + rms_eps) * norm_weight * SiLU(z_t)
+ *           (or * sigmoid(z_t) with params->output_gate = GDN_GATE_SIGMOID)
  * with Hk q/k heads, Hv v heads (v head h reads q/k head h / (Hv/Hk)), head
  * dim D = 128, one D x D fp32 state per (sequence, v head).
  *
@@ -47,6 +48,10 @@ extern "C" {
 
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 
+/* Output gate of the epilogue: SiLU(z) (the field guide's, the default) or
+ * sigmoid(z) (the variant the tech report's Fig. 2 caption starts to name). */
+typedef enum { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
+
 typedef enum {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad layout */
@@ -70,6 +75,7 @@ typedef struct {
   const float *A_log;         /* [Hv] */
   const float *dt_bias;       /* [Hv] */
   const float *norm_weight;   /* [D], or NULL for all ones */
+  int32_t output_gate;        /* gdn_gate: o = RMSNorm(y) * norm_weight * gate(z) */
 } gdn_params;
 
 /* Bytes of device workspace gdn_prefill needs for this problem (0 is a valid

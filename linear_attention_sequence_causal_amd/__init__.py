@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16, GDN_F32 = 0, 1
+GATES = {"silu": 0, "sigmoid": 1}  # gdn_gate
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_NO_DEVICE", 5: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_noalloc",
@@ -37,7 +38,7 @@ class GdnParams(ctypes.Structure):
                 ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
                 ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
-                ("norm_weight", ctypes.c_void_p)]
+                ("norm_weight", ctypes.c_void_p), ("output_gate", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -109,11 +110,12 @@ def _stream():
 
 
 def make_params(num_qk_heads, num_v_heads, head_dim, act_dtype, conv_w, A_log, dt_bias,
-                norm_w=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6) -> GdnParams:
+                norm_w=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
+                output_gate="silu") -> GdnParams:
     dt = GDN_BF16 if act_dtype == torch.bfloat16 else GDN_F32 if act_dtype == torch.float32 else -1
     return GdnParams(int(num_qk_heads), int(num_v_heads), int(head_dim), dt, float(q_scale),
                      float(l2_eps), float(rms_eps), _ptr(conv_w), _ptr(A_log), _ptr(dt_bias),
-                     _ptr(norm_w))
+                     _ptr(norm_w), GATES[output_gate])
 
 
 def _contig(*ts):
@@ -145,7 +147,7 @@ def _workspace(nbytes: int, device):
 
 def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *, init_state=None,
             cu_seqlens=None, conv_state=None, return_conv_state=False, q_scale=1.0,
-            l2_eps=1e-6, rms_eps=1e-6, out=None, final_state=None):
+            l2_eps=1e-6, rms_eps=1e-6, out=None, final_state=None, output_gate="silu"):
     """Chunked prefill over packed sequences -> (o, final_state[, conv_state_out]).
 
     q, k [T, Hk, D]; v, z [T, Hv, D] (bf16 or fp32); a, b [T, Hv] fp32;
@@ -158,7 +160,8 @@ def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *, init_state
     Hv = v.shape[1]
     N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, init_state, cu_seqlens, conv_state)
-    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps,
+                    output_gate)
     o = torch.empty_like(v) if out is None else out
     fs = (torch.empty((N, Hv, D, D), dtype=torch.float32, device=q.device)
           if final_state is None else final_state)
@@ -180,7 +183,7 @@ NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 def prefill_noalloc(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, *, init_state=None,
                     cu_seqlens=None, conv_state=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6,
-                    out, final_state, conv_state_out=None):
+                    out, final_state, conv_state_out=None, output_gate="silu"):
     """gdn_prefill_noalloc: the prefill with the library's static workspace, into
     caller-provided outputs (nothing is allocated)."""
     T, Hk, D = q.shape
@@ -188,7 +191,8 @@ def prefill_noalloc(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, *, init_st
     N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, init_state, cu_seqlens, conv_state,
             out, final_state, conv_state_out)
-    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps,
+                    output_gate)
     _check(lib().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
                                      ctypes.byref(p), _ptr(init_state), _ptr(cu_seqlens), N, T,
                                      _ptr(conv_state), _ptr(out), _ptr(final_state),
@@ -197,7 +201,8 @@ def prefill_noalloc(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, *, init_st
 
 
 def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, *,
-                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None, state_scale=None):
+                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None, state_scale=None,
+                output_gate="silu"):
     """One decode step; updates `state` and `conv_state` in place, returns o.
 
     q, k [B, Hk, D]; v, z [B, Hv, D]; a, b [B, Hv]; state [B, Hv, D, D] fp32, or bf16 or
@@ -208,7 +213,8 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
     B, Hk, D = q.shape
     Hv = v.shape[1]
     _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state)
-    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps,
+                    output_gate)
     o = torch.empty_like(v) if out is None else out
     if state.dtype == torch.float8_e4m3fn:
         if state_scale is None or state_scale.dtype != torch.float32:
@@ -230,7 +236,8 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_st
 
 
 def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, *,
-                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None):
+                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, out=None,
+                  output_gate="silu"):
     """n new tokens per sequence on a cached state; returns o [B, n, Hv, D].
 
     q, k [B, n, Hk, D]; v, z [B, n, Hv, D]; a, b [B, n, Hv]; state [B, Hv, D, D] fp32 and
@@ -242,7 +249,8 @@ def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_
     _contig(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_state, num_commit)
     if num_commit is not None and (num_commit.dtype != torch.int32 or num_commit.numel() != B):
         raise ValueError("num_commit must be an int32 tensor of B elements")
-    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps)
+    p = make_params(Hk, Hv, D, q.dtype, conv_w, A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps,
+                    output_gate)
     o = torch.empty_like(v) if out is None else out
     _check(lib().gdn_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z),
                                    ctypes.byref(p), _ptr(state), _ptr(conv_state),

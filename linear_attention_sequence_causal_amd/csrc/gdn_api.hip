@@ -21,7 +21,8 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
                          float rms_eps, void *state, int state_kind, float *state_scale,
-                         void *conv_state, void *o, int batch, int Hk, int Hv, hipStream_t stream);
+                         void *conv_state, void *o, int batch, int Hk, int Hv, int gate,
+                         hipStream_t stream);
 int decode_max_ratio();
 template <typename T>
 hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, const float *a,
@@ -29,7 +30,7 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 const float *A_log, const float *dt_bias, const float *norm_w,
                                 float q_scale, float l2_eps, float rms_eps, float *state,
                                 void *conv_state, const int32_t *num_commit, void *o, int batch,
-                                int n, int Hk, int Hv, hipStream_t stream);
+                                int n, int Hk, int Hv, int gate, hipStream_t stream);
 int decode_max_tokens();
 }  // namespace gdn
 
@@ -97,6 +98,9 @@ gdn_status check_params(const gdn_params *p) {
     return fail(GDN_ERR_INVALID_ARGUMENT, "conv_weight, A_log and dt_bias are required");
   if (!(p->l2_eps >= 0.0f) || !(p->rms_eps >= 0.0f))
     return fail(GDN_ERR_INVALID_ARGUMENT, "eps values must be >= 0");
+  if (p->output_gate != GDN_GATE_SILU && p->output_gate != GDN_GATE_SIGMOID)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "output_gate %d is not GDN_GATE_SILU or GDN_GATE_SIGMOID",
+                p->output_gate);
   return GDN_OK;
 }
 
@@ -304,12 +308,13 @@ gdn_status decode_step_impl(const void *q, const void *k, const void *v, const f
     e = gdn::launch_decode<gdn::bf16_t>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                         p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
                                         state_kind, state_scale, conv_state, o, batch,
-                                        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
+                                        p->num_qk_heads, p->num_v_heads, p->output_gate,
+                                        (hipStream_t)stream);
   else
     e = gdn::launch_decode<float>(q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias,
                                   p->norm_weight, p->q_scale, p->l2_eps, p->rms_eps, state,
                                   state_kind, state_scale, conv_state, o, batch, p->num_qk_heads,
-                                  p->num_v_heads, (hipStream_t)stream);
+                                  p->num_v_heads, p->output_gate, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return GDN_OK;
 }
@@ -365,12 +370,12 @@ gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v, const 
     e = gdn::launch_decode_tokens<gdn::bf16_t>(
         q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias, p->norm_weight, p->q_scale,
         p->l2_eps, p->rms_eps, state, conv_state, num_commit, o, batch, n_tokens,
-        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
+        p->num_qk_heads, p->num_v_heads, p->output_gate, (hipStream_t)stream);
   else
     e = gdn::launch_decode_tokens<float>(
         q, k, v, a, b, z, p->conv_weight, p->A_log, p->dt_bias, p->norm_weight, p->q_scale,
         p->l2_eps, p->rms_eps, state, conv_state, num_commit, o, batch, n_tokens,
-        p->num_qk_heads, p->num_v_heads, (hipStream_t)stream);
+        p->num_qk_heads, p->num_v_heads, p->output_gate, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode_tokens launch");
   return GDN_OK;
 }

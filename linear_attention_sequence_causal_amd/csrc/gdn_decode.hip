@@ -111,7 +111,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
                    const float *__restrict__ A_log, const float *__restrict__ dt_bias,
                    const float *__restrict__ norm_w, float q_scale, float l2_eps, float rms_eps,
                    S *__restrict__ state, float *__restrict__ state_scale,
-                   T *__restrict__ conv_state, T *__restrict__ o, int Hk, int Hv) {
+                   T *__restrict__ conv_state, T *__restrict__ o, int Hk, int Hv, int gate) {
   constexpr bool kFp8 = __is_same(S, fp8_t);
   const int g = blockIdx.x % Hk;
   const int bseq = blockIdx.x / Hk;
@@ -234,7 +234,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   // ---- 3./4. per v head: state stream and epilogue ---------------------------------
   for (int j = 0; j < r; ++j) {
     const int h = r * g + j;
-    const float zg = siluf_(Act<T>::from_bits(zbits));
+    const float zg = out_gate(gate, Act<T>::from_bits(zbits));
     if (j + 1 < r) zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + h + 1) * kD + ztid);
     // the next head's loads go out first (vector-memory waits are in issue order, so
     // waiting for this head's state does not wait for them)
@@ -329,13 +329,15 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          const float *b, const void *z, const float *conv_w, const float *A_log,
                          const float *dt_bias, const float *norm_w, float q_scale, float l2_eps,
                          float rms_eps, void *state, int state_kind, float *state_scale,
-                         void *conv_state, void *o, int batch, int Hk, int Hv, hipStream_t stream) {
+                         void *conv_state, void *o, int batch, int Hk, int Hv, int gate,
+                         hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   dim3 grid((unsigned)batch * (unsigned)Hk);
   auto go = [&](auto kern, auto *st) {
     hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), 0, stream, (const T *)q, (const T *)k,
                        (const T *)v, a, b, (const T *)z, conv_w, A_log, dt_bias, norm_w, q_scale,
-                       l2_eps, rms_eps, st, state_scale, (T *)conv_state, (T *)o, Hk, Hv);
+                       l2_eps, rms_eps, st, state_scale, (T *)conv_state, (T *)o, Hk, Hv,
+                       gate);
   };
   if (state_kind == kStateBf16) go(decode_step_kernel<T, bf16_t>, (bf16_t *)state);
   else if (state_kind == kStateFp8) go(decode_step_kernel<T, fp8_t>, (fp8_t *)state);
@@ -349,12 +351,13 @@ template hipError_t launch_decode<float>(const void *, const void *, const void 
                                          const float *, const void *, const float *,
                                          const float *, const float *, const float *, float,
                                          float, float, void *, int, float *, void *, void *, int,
-                                         int, int, hipStream_t);
+                                         int, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(const void *, const void *, const void *,
                                           const float *, const float *, const void *,
                                           const float *, const float *, const float *,
                                           const float *, float, float, float, void *, int,
-                                          float *, void *, void *, int, int, int, hipStream_t);
+                                          float *, void *, void *, int, int, int, int,
+                                          hipStream_t);
 
 // ---------------------------------------------------------------------------------
 // Multi-token step: n (1..8) new tokens per sequence on a cached state.  It is the
@@ -419,7 +422,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
                      const float *__restrict__ norm_w, float q_scale, float l2_eps,
                      float rms_eps, float *__restrict__ state, T *__restrict__ conv_state,
                      const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
-                     int n) {
+                     int n, int gate) {
   const int r = Hv / Hk;
   const int jh = blockIdx.x % r;                  // v head within its q/k group
   const int g = (blockIdx.x / r) % Hk;            // q/k head
@@ -643,7 +646,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         const float ssh = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
         const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
         const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
-        Act<T>::store(o, oi, yown[t] * inv * nwv * siluf_(zr[t]));
+        Act<T>::store(o, oi, yown[t] * inv * nwv * out_gate(gate, zr[t]));
       }
     }
   }
@@ -690,13 +693,13 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 const float *A_log, const float *dt_bias, const float *norm_w,
                                 float q_scale, float l2_eps, float rms_eps, float *state,
                                 void *conv_state, const int32_t *num_commit, void *o, int batch,
-                                int n, int Hk, int Hv, hipStream_t stream) {
+                                int n, int Hk, int Hv, int gate, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   dim3 grid((unsigned)batch * (unsigned)Hv);
   hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kTokThreads), 0, stream,
                      (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
                      dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
-                     num_commit, (T *)o, Hk, Hv, n);
+                     num_commit, (T *)o, Hk, Hv, n, gate);
   const int64_t nch = (int64_t)batch * 2 * Hk * kD;
   hipLaunchKernelGGL((qk_cache_advance_kernel<T>), dim3((unsigned)((nch + 255) / 256)), dim3(256),
                      0, stream, (const T *)q, (const T *)k, (T *)conv_state, num_commit, batch, Hk,
@@ -711,12 +714,12 @@ template hipError_t launch_decode_tokens<float>(const void *, const void *, cons
                                                 const float *, const float *, const float *,
                                                 const float *, float, float, float, float *,
                                                 void *, const int32_t *, void *, int, int, int,
-                                                int, hipStream_t);
+                                                int, int, hipStream_t);
 template hipError_t launch_decode_tokens<bf16_t>(const void *, const void *, const void *,
                                                  const float *, const float *, const void *,
                                                  const float *, const float *, const float *,
                                                  const float *, float, float, float, float *,
                                                  void *, const int32_t *, void *, int, int, int,
-                                                 int, hipStream_t);
+                                                 int, int, hipStream_t);
 
 }  // namespace gdn

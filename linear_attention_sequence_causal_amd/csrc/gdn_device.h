@@ -67,6 +67,11 @@ __device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_
   lo = pk_bf16(a - ah, b - bh);
 }
 __device__ __forceinline__ float siluf_(float u) { return u * sigmoidf_(u); }
+// Output gate of the epilogue: 0 SiLU(z), 1 sigmoid(z) (gdn_params.output_gate).
+__device__ __forceinline__ float out_gate(int gate, float z) {
+  const float s = sigmoidf_(z);
+  return gate == 1 ? s : z * s;
+}
 // log(1 + e^u) without overflow: max(u, 0) + log1p(e^-|u|).
 __device__ __forceinline__ float softplusf_(float u) {
   return fmaxf(u, 0.0f) + log1pf(__expf(-fabsf(u)));

@@ -177,6 +177,7 @@ struct PrefillArgs {
   float *starts;           // [max_segments][Hv][D][D]
   int Hk, Hv;
   int64_t Cc;
+  int gate;                // output gate: 0 SiLU(z), 1 sigmoid(z)
 };
 
 // NC channels of one token as raw 32-bit words (bf16 pairs or fp32)
@@ -1080,8 +1081,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       float val[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float zj = RZ::get(zw[j >> 3], j & 7);
-        const float e = __expf(-zj);
+        const float zraw = RZ::get(zw[j >> 3], j & 7);
+        const float zj = P.gate == 1 ? 1.0f : zraw;  // z sigmoid(z) or sigmoid(z)
+        const float e = __expf(-zraw);
         val[j] = ov[j] * zj * nw[j] * __builtin_amdgcn_rcpf(fmaf(e, sd, sd));
       }
       // one buffer over this chunk's o rows: stores of tokens at or past nvalid are dropped
@@ -1468,6 +1470,7 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   A.starts = plan.max_maps > 0 ? (float *)(ws + plan.off_start) : nullptr;
   A.map_zero = plan.max_maps > 0 ? (int32_t *)(ws + plan.off_flags) : nullptr;
   A.Hk = p.num_qk_heads; A.Hv = p.num_v_heads;
+  A.gate = p.output_gate;
   A.Cc = 2LL * p.num_qk_heads * kD + (int64_t)p.num_v_heads * kD;
   if (p.act_dtype == GDN_BF16)
     return launch_typed<bf16_t>(plan, A, cu_seqlens, num_seqs, total_tokens, conv_state_out,

@@ -66,8 +66,17 @@ def _load():
             lib.oracle_decode_step.restype = i32
             lib.oracle_decode_step.argtypes = [i32, i32, i32, i32, pd, pd, pd, pd, pd, pd,
                                                pd, pd, pd, pd, d, d, d, pd, pd, pd, i32]
+            lib.oracle_epilogue_gated.restype = None
+            lib.oracle_epilogue_gated.argtypes = [i64, i32, pd, pd, i64, pd, d, pd, i64, i32]
+            lib.oracle_prefill_gated.restype = i32
+            lib.oracle_prefill_gated.argtypes = lib.oracle_prefill.argtypes + [i32]
+            lib.oracle_decode_step_gated.restype = i32
+            lib.oracle_decode_step_gated.argtypes = lib.oracle_decode_step.argtypes + [i32]
             _lib = lib
     return _lib
+
+
+GATES = {"silu": 0, "sigmoid": 1}  # output gate of the epilogue
 
 
 def _f64(x):
@@ -150,13 +159,14 @@ def recurrence(alpha, beta, q, k, v, S0=None):
     return y, S
 
 
-def epilogue(y, z, norm_w=None, rms_eps=1e-6):
-    """RMS-normalise y per token over D, scale by norm_w, gate with SiLU(z)."""
+def epilogue(y, z, norm_w=None, rms_eps=1e-6, output_gate="silu"):
+    """RMS-normalise y per token over D, scale by norm_w, gate with SiLU(z) (or
+    sigmoid(z) with output_gate="sigmoid")."""
     y, z, norm_w = map(_f64, (y, z, norm_w))
     T, D = y.shape
     o = np.empty((T, D))
-    _load().oracle_epilogue(T, D, _ptr(y), _ptr(z), D, _ptr(norm_w), float(rms_eps),
-                            _ptr(o), D)
+    _load().oracle_epilogue_gated(T, D, _ptr(y), _ptr(z), D, _ptr(norm_w), float(rms_eps),
+                                  _ptr(o), D, GATES[output_gate])
     return o
 
 
@@ -164,7 +174,7 @@ def epilogue(y, z, norm_w=None, rms_eps=1e-6):
 
 def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *,
             cu_seqlens=None, init_state=None, conv_in=None,
-            q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+            q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None, output_gate="silu"):
     """Whole mixer over packed sequences, fp64.
 
     Returns (o [T, Hv, D], final_state [N, Hv, D, D] as H = S^T, conv_out [N, 3, Cc]).
@@ -182,19 +192,19 @@ def prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w=None, *,
     o = np.empty((T, Hv, D))
     fs = np.empty((N, Hv, D, D))
     co = np.empty((N, 3, Cc))
-    rc = _load().oracle_prefill(
+    rc = _load().oracle_prefill_gated(
         N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), Hk, Hv, D,
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z), _ptr(conv_w), _ptr(A_log),
         _ptr(dt_bias), _ptr(norm_w), float(q_scale), float(l2_eps), float(rms_eps),
         _ptr(init_state), _ptr(conv_in), _ptr(o), _ptr(fs), _ptr(co),
-        int(nthreads or default_threads()))
+        int(nthreads or default_threads()), GATES[output_gate])
     if rc != 0:
         raise ValueError("oracle_prefill: invalid arguments")
     return o, fs, co
 
 
 def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
-                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+                q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None, output_gate="silu"):
     """One decode step for B sequences.  Returns (o, new_state, new_conv_cache)."""
     q, k, v, a, b, z = map(_f64, (q, k, v, a, b, z))
     conv_w, A_log, dt_bias, norm_w = map(_f64, (conv_w, A_log, dt_bias, norm_w))
@@ -203,10 +213,11 @@ def decode_step(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_ca
     B, Hk, D = q.shape
     Hv = v.shape[1]
     o = np.empty((B, Hv, D))
-    rc = _load().oracle_decode_step(
+    rc = _load().oracle_decode_step_gated(
         B, Hk, Hv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(z), _ptr(conv_w),
         _ptr(A_log), _ptr(dt_bias), _ptr(norm_w), float(q_scale), float(l2_eps),
-        float(rms_eps), _ptr(state), _ptr(cache), _ptr(o), int(nthreads or default_threads()))
+        float(rms_eps), _ptr(state), _ptr(cache), _ptr(o), int(nthreads or default_threads()),
+        GATES[output_gate])
     if rc != 0:
         raise ValueError("oracle_decode_step: invalid arguments")
     return o, state, cache
@@ -276,7 +287,8 @@ def decode_step_fp8_state(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, stat
 
 
 def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_cache, *,
-                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None):
+                  num_commit=None, q_scale=1.0, l2_eps=1e-6, rms_eps=1e-6, nthreads=None,
+                  output_gate="silu"):
     """n new tokens per sequence on a cached state (multi-token decode / verify / commit).
 
     q, k [B, n, Hk, D]; v, z [B, n, Hv, D]; a, b [B, n, Hv].  Returns
@@ -294,7 +306,8 @@ def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_
     Hv = v.shape[2]
     state, cache = _f64(state), _f64(conv_cache)
     flat = lambda x: x.reshape((B * n,) + x.shape[2:])
-    kw = dict(q_scale=q_scale, l2_eps=l2_eps, rms_eps=rms_eps, nthreads=nthreads)
+    kw = dict(q_scale=q_scale, l2_eps=l2_eps, rms_eps=rms_eps, nthreads=nthreads,
+              output_gate=output_gate)
     cu = np.arange(B + 1, dtype=np.int64) * n
     o, _, _ = prefill(flat(q), flat(k), flat(v), flat(a), flat(b), flat(z), conv_w, A_log,
                       dt_bias, norm_w, cu_seqlens=cu, init_state=state, conv_in=cache, **kw)

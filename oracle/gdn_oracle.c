@@ -169,21 +169,35 @@ void oracle_recurrence(int64_t T, int D, const double *alpha, const double *beta
 
 /* ------------------------------------------------------------- epilogue */
 
-/* Output of one head (field guide cutaway 02, last line): RMS-normalise y over
- * the head's D values, scale by the norm weight, gate with SiLU(z).
- * y, z, o are [T][D] with z and o strided by z_stride / o_stride per token. */
-void oracle_epilogue(int64_t T, int D, const double *y, const double *z,
-                     int64_t z_stride, const double *norm_w /* [D] or NULL */,
-                     double rms_eps, double *o, int64_t o_stride) {
+/* Output gate: 0 = SiLU(z) (field guide cutaway 02, last line), 1 = sigmoid(z)
+ * (the variant the tech report's Fig. 2 caption starts to name, "while a sigmoid
+ * ...", and the form of the model card's attention output gate). */
+static double output_gate(int gate, double z) {
+  return gate == 1 ? oracle_sigmoid(z) : oracle_silu(z);
+}
+
+/* Output of one head: RMS-normalise y over the head's D values, scale by the norm
+ * weight, multiply by the output gate of z.  y, z, o are [T][D] with z and o
+ * strided by z_stride / o_stride per token. */
+void oracle_epilogue_gated(int64_t T, int D, const double *y, const double *z,
+                           int64_t z_stride, const double *norm_w /* [D] or NULL */,
+                           double rms_eps, double *o, int64_t o_stride, int gate) {
   for (int64_t t = 0; t < T; ++t) {
     double ss = 0.0;
     for (int i = 0; i < D; ++i) ss += y[t * D + i] * y[t * D + i];
     double inv = 1.0 / sqrt(ss / D + rms_eps);
     for (int i = 0; i < D; ++i) {
       double w = norm_w ? norm_w[i] : 1.0;
-      o[t * o_stride + i] = y[t * D + i] * inv * w * oracle_silu(z[t * z_stride + i]);
+      o[t * o_stride + i] = y[t * D + i] * inv * w * output_gate(gate, z[t * z_stride + i]);
     }
   }
+}
+
+/* The field guide's epilogue: the SiLU(z) gate. */
+void oracle_epilogue(int64_t T, int D, const double *y, const double *z,
+                     int64_t z_stride, const double *norm_w, double rms_eps, double *o,
+                     int64_t o_stride) {
+  oracle_epilogue_gated(T, D, y, z, z_stride, norm_w, rms_eps, o, o_stride, 0);
 }
 
 /* ---------------------------------------------------------------- mixer */
@@ -193,6 +207,7 @@ typedef struct {
   const int64_t *cu;
   const double *q, *k, *v, *a, *b, *z, *conv_w, *A_log, *dt_bias, *norm_w;
   double q_scale, l2_eps, rms_eps;
+  int gate;
   const double *init_state, *conv_in;
   double *o, *final_state;
   int64_t next_unit; /* work counter, taken with an atomic add */
@@ -227,8 +242,8 @@ static void run_unit(mixer_job *J, int64_t unit) {
     }
     oracle_gates(T, at, bt, J->A_log[h], J->dt_bias[h], al, be);
     oracle_recurrence(T, D, al, be, qo, ko, vo, S, y);
-    oracle_epilogue(T, D, y, J->z + (t0 * Hv + h) * D, (int64_t)Hv * D, J->norm_w,
-                    J->rms_eps, J->o + (t0 * Hv + h) * D, (int64_t)Hv * D);
+    oracle_epilogue_gated(T, D, y, J->z + (t0 * Hv + h) * D, (int64_t)Hv * D, J->norm_w,
+                          J->rms_eps, J->o + (t0 * Hv + h) * D, (int64_t)Hv * D, J->gate);
     free(qo); free(ko); free(vo); free(y); free(al); free(be); free(at); free(bt);
   }
   double *Hf = J->final_state + ((int64_t)n * Hv + h) * D * D;
@@ -252,14 +267,17 @@ static void *worker(void *arg) {
  * init_state / conv_in may be NULL (zeros).  conv_out [N][3][Cc] (may be NULL)
  * receives the last three raw inputs of each sequence, taking rows from the
  * inherited history when the sequence is shorter than three.
+ * gate selects the output gate (0 SiLU(z), 1 sigmoid(z)).
  * Returns 0, or -1 on an invalid argument. */
-int oracle_prefill(int N, const int64_t *cu_seqlens, int Hk, int Hv, int D,
-                   const double *q, const double *k, const double *v,
-                   const double *a, const double *b, const double *z,
-                   const double *conv_w, const double *A_log, const double *dt_bias,
-                   const double *norm_w, double q_scale, double l2_eps, double rms_eps,
-                   const double *init_state, const double *conv_in,
-                   double *o, double *final_state, double *conv_out, int nthreads) {
+int oracle_prefill_gated(int N, const int64_t *cu_seqlens, int Hk, int Hv, int D,
+                         const double *q, const double *k, const double *v,
+                         const double *a, const double *b, const double *z,
+                         const double *conv_w, const double *A_log, const double *dt_bias,
+                         const double *norm_w, double q_scale, double l2_eps, double rms_eps,
+                         const double *init_state, const double *conv_in,
+                         double *o, double *final_state, double *conv_out, int nthreads,
+                         int gate) {
+  if (gate != 0 && gate != 1) return -1;
   if (N < 0 || Hk <= 0 || Hv <= 0 || D <= 0 || Hv % Hk != 0 || !cu_seqlens) return -1;
   if (cu_seqlens[0] != 0) return -1;
   for (int n = 0; n < N; ++n)
@@ -269,7 +287,7 @@ int oracle_prefill(int N, const int64_t *cu_seqlens, int Hk, int Hv, int D,
   J.N = N; J.Hk = Hk; J.Hv = Hv; J.D = D; J.cu = cu_seqlens;
   J.q = q; J.k = k; J.v = v; J.a = a; J.b = b; J.z = z; J.conv_w = conv_w;
   J.A_log = A_log; J.dt_bias = dt_bias; J.norm_w = norm_w;
-  J.q_scale = q_scale; J.l2_eps = l2_eps; J.rms_eps = rms_eps;
+  J.q_scale = q_scale; J.l2_eps = l2_eps; J.rms_eps = rms_eps; J.gate = gate;
   J.init_state = init_state; J.conv_in = conv_in; J.o = o; J.final_state = final_state;
   J.next_unit = 0;
   if (nthreads < 1) nthreads = 1;
@@ -306,25 +324,50 @@ int oracle_prefill(int N, const int64_t *cu_seqlens, int Hk, int Hv, int D,
   return 0;
 }
 
+/* The mixer with the field guide's SiLU(z) gate. */
+int oracle_prefill(int N, const int64_t *cu_seqlens, int Hk, int Hv, int D,
+                   const double *q, const double *k, const double *v,
+                   const double *a, const double *b, const double *z,
+                   const double *conv_w, const double *A_log, const double *dt_bias,
+                   const double *norm_w, double q_scale, double l2_eps, double rms_eps,
+                   const double *init_state, const double *conv_in,
+                   double *o, double *final_state, double *conv_out, int nthreads) {
+  return oracle_prefill_gated(N, cu_seqlens, Hk, Hv, D, q, k, v, a, b, z, conv_w, A_log,
+                              dt_bias, norm_w, q_scale, l2_eps, rms_eps, init_state, conv_in,
+                              o, final_state, conv_out, nthreads, 0);
+}
+
 /* One decode step for B independent sequences: exactly one token of the mixer
  * with the conv cache as history, the state updated in place, and the cache
  * shifted to [cache1, cache2, x_t].  Shapes as oracle_prefill with T = B. */
+int oracle_decode_step_gated(int B, int Hk, int Hv, int D,
+                             const double *q, const double *k, const double *v,
+                             const double *a, const double *b, const double *z,
+                             const double *conv_w, const double *A_log, const double *dt_bias,
+                             const double *norm_w, double q_scale, double l2_eps,
+                             double rms_eps, double *state, double *conv_cache, double *o,
+                             int nthreads, int gate) {
+  if (B < 0) return -1;
+  int64_t *cu = (int64_t *)malloc(sizeof(int64_t) * (B + 1));
+  for (int i = 0; i <= B; ++i) cu[i] = i;
+  int64_t Cc = 2LL * Hk * D + (int64_t)Hv * D;
+  double *new_cache = (double *)malloc(sizeof(double) * (size_t)B * 3 * Cc + 1);
+  int rc = oracle_prefill_gated(B, cu, Hk, Hv, D, q, k, v, a, b, z, conv_w, A_log, dt_bias,
+                                norm_w, q_scale, l2_eps, rms_eps, state, conv_cache, o, state,
+                                new_cache, nthreads, gate);
+  if (rc == 0) memcpy(conv_cache, new_cache, sizeof(double) * (size_t)B * 3 * Cc);
+  free(new_cache);
+  free(cu);
+  return rc;
+}
+
 int oracle_decode_step(int B, int Hk, int Hv, int D,
                        const double *q, const double *k, const double *v,
                        const double *a, const double *b, const double *z,
                        const double *conv_w, const double *A_log, const double *dt_bias,
                        const double *norm_w, double q_scale, double l2_eps, double rms_eps,
                        double *state, double *conv_cache, double *o, int nthreads) {
-  if (B < 0) return -1;
-  int64_t *cu = (int64_t *)malloc(sizeof(int64_t) * (B + 1));
-  for (int i = 0; i <= B; ++i) cu[i] = i;
-  int64_t Cc = 2LL * Hk * D + (int64_t)Hv * D;
-  double *new_cache = (double *)malloc(sizeof(double) * (size_t)B * 3 * Cc + 1);
-  int rc = oracle_prefill(B, cu, Hk, Hv, D, q, k, v, a, b, z, conv_w, A_log, dt_bias,
-                          norm_w, q_scale, l2_eps, rms_eps, state, conv_cache, o, state,
-                          new_cache, nthreads);
-  if (rc == 0) memcpy(conv_cache, new_cache, sizeof(double) * (size_t)B * 3 * Cc);
-  free(new_cache);
-  free(cu);
-  return rc;
+  return oracle_decode_step_gated(B, Hk, Hv, D, q, k, v, a, b, z, conv_w, A_log, dt_bias,
+                                  norm_w, q_scale, l2_eps, rms_eps, state, conv_cache, o,
+                                  nthreads, 0);
 }

@@ -199,3 +199,14 @@ def test_noalloc_prefill_rejects_problems_above_its_workspace_without_a_device()
     # the 65536-token single-sequence workload fits
     assert gdn.lib().gdn_prefill_workspace_bytes(ctypes.byref(p), 1, 65536) <= \
         gdn.NOALLOC_WORKSPACE_BYTES
+
+
+def test_output_gate_must_be_silu_or_sigmoid():
+    p, host = _params()
+    p.output_gate = 2
+    o = _host(1 << 16)
+    assert _decode(p, out=o) == 1  # GDN_ERR_INVALID_ARGUMENT
+    assert "output_gate" in gdn.lib().gdn_last_error().decode()
+    assert np.all(o == 7.0)
+    p.output_gate = 1
+    assert _decode(p, out=o) == 4  # valid: reaches the (missing) device

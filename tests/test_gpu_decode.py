@@ -373,3 +373,32 @@ def test_decode_fp8_state_identity_gates_keep_state_values():
     setup = S.decode_setup(w, "cuda")
     q8, sc, qv, scv = _fp8_start(setup["state"])
     assert np.array_equal(st, qv * scv[..., None])
+
+
+@gpu
+def test_decode_sigmoid_output_gate_variant():
+    """Decode steps with the sigmoid output gate against the oracle's."""
+    import linear_attention_sequence_causal_amd as gdn
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=2, num_v_heads=8, seed=113)
+    setup = S.decode_setup(w, "cuda")
+    toks = S.decode_tokens(w, setup, 3, "cuda")
+    f = S.to_f64
+    st, cc = f(setup["state"]), f(setup["conv_cache"])
+    num = den = 0.0
+    for s in range(3):
+        o = gdn.decode_step(toks["q"][s], toks["k"][s], toks["v"][s], toks["a"][s], toks["b"][s],
+                            toks["z"][s], setup["conv_w"], setup["A_log"], setup["dt_bias"],
+                            setup["norm_w"], setup["state"], setup["conv_cache"],
+                            output_gate="sigmoid")
+        o_r, st, cc = oracle.decode_step(f(toks["q"][s]), f(toks["k"][s]), f(toks["v"][s]),
+                                         f(toks["a"][s]), f(toks["b"][s]), f(toks["z"][s]),
+                                         f(setup["conv_w"]), f(setup["A_log"]),
+                                         f(setup["dt_bias"]), f(setup["norm_w"]), st, cc,
+                                         output_gate="sigmoid")
+        torch.cuda.synchronize()
+        num += float(np.sum((f(o) - o_r) ** 2))
+        den += float(np.sum(o_r ** 2))
+    eo = (num / den) ** 0.5
+    print(f"decode sigmoid output gate: o rel-L2 {eo:.3e}")
+    assert eo < O_TOL
+    assert rel_l2(f(setup["state"]), st) < 1e-5

@@ -215,3 +215,25 @@ def test_tokens_zero_batch_is_a_no_op():
     empty = {key: val[:0] for key, val in t.items()}
     o = _gpu(setup, empty, setup["state"][:0], setup["conv_cache"][:0])
     assert o.numel() == 0
+
+
+@gpu
+def test_tokens_sigmoid_output_gate_variant():
+    import linear_attention_sequence_causal_amd as gdn
+    n = 4
+    w = S.scaled(S.DECODE_B256, decode_batch=4, num_qk_heads=2, num_v_heads=4, seed=86)
+    setup, t = _case(w, n)
+    st0, cc0 = setup["state"].clone(), setup["conv_cache"].clone()
+    o = gdn.decode_tokens(t["q"], t["k"], t["v"], t["a"], t["b"], t["z"], setup["conv_w"],
+                          setup["A_log"], setup["dt_bias"], setup["norm_w"], setup["state"],
+                          setup["conv_cache"], output_gate="sigmoid")
+    torch.cuda.synchronize()
+    f = S.to_f64
+    o_ref, st_ref, _ = oracle.decode_tokens(f(t["q"]), f(t["k"]), f(t["v"]), f(t["a"]),
+                                            f(t["b"]), f(t["z"]), f(setup["conv_w"]),
+                                            f(setup["A_log"]), f(setup["dt_bias"]),
+                                            f(setup["norm_w"]), f(st0), f(cc0),
+                                            output_gate="sigmoid")
+    eo = rel_l2(f(o), o_ref)
+    print(f"decode_tokens sigmoid output gate: o rel-L2 {eo:.3e}")
+    assert eo < O_TOL and rel_l2(f(setup["state"]), st_ref) < 1e-5

@@ -447,3 +447,25 @@ def test_invalid_cu_seqlens_is_reported_and_runs_nothing():
     o_ref, fs_ref, _, _ = run_oracle(d)
     assert rel_l2(S.to_f64(o), o_ref) <= O_TOL and rel_l2(S.to_f64(fs), fs_ref) <= STATE_TOL
     gdn.check_device_errors()
+
+
+@gpu
+def test_sigmoid_output_gate_variant():
+    """The epilogue with the sigmoid output gate (gdn_params.output_gate =
+    GDN_GATE_SIGMOID) against the oracle's sigmoid-gated mixer, with a multi-segment
+    sequence and a short one; the final states equal the SiLU-gated run's bit for bit
+    (the gate touches o only)."""
+    w = S.scaled(S.PREFILL_4K, lengths=(2300, 70), num_qk_heads=2, num_v_heads=4, seed=23,
+                 init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o, fs, _ = run_gpu(d, output_gate="sigmoid")
+    _, fs_silu, _ = run_gpu(d)
+    f = S.to_f64
+    o_ref, fs_ref, _ = oracle.prefill(
+        f(d["q"]), f(d["k"]), f(d["v"]), f(d["a"]), f(d["b"]), f(d["z"]), f(d["conv_w"]),
+        f(d["A_log"]), f(d["dt_bias"]), f(d["norm_w"]), cu_seqlens=d["cu_seqlens"].cpu().numpy(),
+        init_state=f(d["init_state"]), conv_in=f(d["conv_in"]), output_gate="sigmoid")
+    eo, es = rel_l2(f(o), o_ref), rel_l2(f(fs), fs_ref)
+    print(f"sigmoid output gate: o rel-L2 {eo:.3e} final-state rel-L2 {es:.3e}")
+    assert eo <= O_TOL and es <= STATE_TOL
+    assert torch.equal(fs, fs_silu)

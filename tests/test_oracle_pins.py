@@ -645,3 +645,49 @@ def test_fp8_state_step_keeps_a_frozen_state_bit_for_bit():
                                                 np.zeros(Hv), np.ones(D), sq, ss, cache)
     assert np.array_equal(q2 * s2[..., None], sq * ss[..., None])
     assert np.all(np.abs(q2) <= 448.0)
+
+
+# ------------------------------------------------- sigmoid output-gate variant
+
+
+def test_sigmoid_gate_epilogue_closed_forms():
+    """o = RMSNorm(y) * w * sigmoid(z): z = 0 halves the normalised y; a constant y
+    normalises to its sign; and since SiLU(z) = z sigmoid(z), the SiLU-gated output
+    is the sigmoid-gated one times z."""
+    rng = np.random.default_rng(8)
+    y = rng.normal(size=(5, 16))
+    nw = rng.uniform(0.5, 1.5, 16)
+    o0 = oracle.epilogue(y, np.zeros_like(y), nw, rms_eps=0.0, output_gate="sigmoid")
+    rms = np.sqrt(np.mean(y * y, axis=1, keepdims=True))
+    assert np.allclose(o0, 0.5 * y / rms * nw, rtol=1e-14, atol=0)
+    c = np.full((1, 16), -2.5)
+    zc = np.linspace(-3, 3, 16)[None]
+    oc = oracle.epilogue(c, zc, None, rms_eps=0.0, output_gate="sigmoid")
+    assert np.allclose(oc, -1.0 / (1.0 + np.exp(-zc)), rtol=1e-14, atol=0)
+    z = rng.normal(size=y.shape) * 3
+    o_sig = oracle.epilogue(y, z, nw, output_gate="sigmoid")
+    o_silu = oracle.epilogue(y, z, nw)
+    assert np.allclose(o_silu, o_sig * z, rtol=1e-13, atol=1e-15)
+
+
+def test_sigmoid_gate_reaches_the_mixer_outputs_only():
+    """Through the whole mixer the gate changes o exactly as in the epilogue (o_silu =
+    o_sigmoid * z) and leaves the final state and conv state alone; decode agrees."""
+    rng = np.random.default_rng(9)
+    T, Hk, Hv, D = 40, 1, 2, 128
+    Cc = 2 * Hk * D + Hv * D
+    q = rng.normal(size=(T, Hk, D)); k = rng.normal(size=(T, Hk, D))
+    v = rng.normal(size=(T, Hv, D)); z = rng.normal(size=(T, Hv, D))
+    a = rng.normal(size=(T, Hv)); b = rng.normal(size=(T, Hv))
+    cw = rng.normal(0, 0.5, (Cc, 4)); A_log = rng.uniform(0, np.log(16), Hv)
+    dt = rng.uniform(-1, 1, Hv)
+    o1, f1, c1 = oracle.prefill(q, k, v, a, b, z, cw, A_log, dt)
+    o2, f2, c2 = oracle.prefill(q, k, v, a, b, z, cw, A_log, dt, output_gate="sigmoid")
+    assert np.array_equal(f1, f2) and np.array_equal(c1, c2)
+    assert np.allclose(o1, o2 * z, rtol=1e-12, atol=1e-15)
+    st = rng.normal(0, 0.01, (1, Hv, D, D)); cache = rng.normal(size=(1, 3, Cc))
+    od, _, _ = oracle.decode_step(q[:1], k[:1], v[:1], a[:1], b[:1], z[:1], cw, A_log, dt,
+                                  None, st, cache, output_gate="sigmoid")
+    od1, _, _ = oracle.decode_step(q[:1], k[:1], v[:1], a[:1], b[:1], z[:1], cw, A_log, dt,
+                                   None, st, cache)
+    assert np.allclose(od1, od * z[:1], rtol=1e-12, atol=1e-15)
