@@ -307,6 +307,65 @@ def bench_decode_tokens(args, torch, gdn, S, dec=None):
                        "hbm_frac": nb_v / (res["verify"] * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
 
+def bench_projections(args, torch, gdn, S):
+    """The projections around the mixer at the layer's size (T = 65536 tokens, d_model =
+    2048, 16/32 heads): the in-projection (N = 12,352 outputs into q, k, v, z, a, b), the
+    output projection (K = 4096, N = 2048), each against the 16-bit dense MFMA peak; and
+    torch.matmul (hipBLASLt) on the same shapes for comparison."""
+    w = S.LAYER_64K
+    d_model = 2048
+    d = S.layer_inputs(w, d_model, "cuda")
+    T, Hk, Hv, D = int(sum(w.lengths)), w.num_qk_heads, w.num_v_heads, w.head_dim
+    n_in = 2 * Hk * D + 2 * Hv * D + 2 * Hv
+    outs = gdn.in_projection(d["x"], d["w_in"], Hk, Hv, D)
+    o = torch.randn((T, Hv, D), device="cuda").to(torch.bfloat16)
+    y = torch.empty((T, d_model), dtype=torch.bfloat16, device="cuda")
+    p = gdn.GdnParams(Hk, Hv, D, gdn.GDN_BF16, 1.0, 1e-6, 1e-6, None, None, None, None, 0)
+    L = gdn.lib()
+    import ctypes
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def in_proj():
+        L.gdn_in_projection(ptr(d["x"]), ptr(d["w_in"]), ctypes.byref(p), T, d_model,
+                            *[ptr(t) for t in outs], gdn._stream())
+
+    def out_proj():
+        L.gdn_out_projection(ptr(o), ptr(d["w_out"]), ctypes.byref(p), T, d_model, ptr(y),
+                             gdn._stream())
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for name, fn, n, k in (("in_projection", in_proj, n_in, d_model),
+                           ("out_projection", out_proj, d_model, Hv * D)):
+        ms = timed(fn)
+        fl = 2.0 * T * n * k
+        a_ = torch.empty((T, k), dtype=torch.bfloat16, device="cuda")
+        b_ = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+        ms_t = timed(lambda: torch.matmul(a_, b_.t()))
+        del a_, b_
+        res[name] = {"ms": ms, "shape": {"M": T, "N": n, "K": k},
+                     "alg_flops_per_launch": fl,
+                     "roofline": {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12,
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                     "torch_matmul_ms": ms_t,
+                     "torch_matmul_frac": fl / (ms_t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del d, outs, o, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -555,6 +614,11 @@ def main():
         # the other prefill workloads, tokens/s of the whole call
         line["prefill_configs"] = {w.name: bench_prefill_config(args, torch, gdn, S, w)
                                    for w in (S.PREFILL_4K, S.VARLEN_64)}
+        # the projections on either side of the mixer at the same T
+        pj = bench_projections(args, torch, gdn, S)
+        line["projections"] = pj
+        line["layer_ms"] = (pj["in_projection"]["ms"] + pre["call_ms"] +
+                            pj["out_projection"]["ms"])
         if oracle_on:
             cb, o_ref, fs_ref = cpu_baseline_prefill(pre, S, oracle)
             line["cpu_baseline"] = cb

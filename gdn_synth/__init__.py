@@ -117,6 +117,34 @@ def prefill_inputs(w: Workload, device="cpu") -> dict:
                 lengths=lengths)
 
 
+LAYER_64K = Workload("layer_T65536_d2048_hk16_hv32_bf16", seed=5, lengths=(65536,),
+                     init_state_std=0.01)
+
+
+def layer_inputs(w: Workload, d_model: int, device="cpu") -> dict:
+    """Inputs of a whole layer (in-projection, mixer, output projection): the mixer's
+    parameters and initial state as prefill_inputs draws them (steps 1-5), then hidden
+    states x [T, d_model] ~ N(0, 1), w_in [2HkD + 2HvD + 2Hv, d_model] ~ N(0, 1/d_model)
+    (so the projected q, k, v, z, a, b are ~ N(0, 1) as in the other workloads) and
+    w_out [d_model, Hv*D] ~ N(0, 1/(Hv*D)), all rounded to bf16."""
+    g = _gen(w.seed, device)
+    T = int(sum(w.lengths))
+    Hk, Hv, D = w.num_qk_heads, w.num_v_heads, w.head_dim
+    Cc = w.conv_channels
+    conv_w = _normal((Cc, 4), g, device, std=0.5)
+    A_log = _uniform((Hv,), 0.0, math.log(16.0), g, device)
+    dt_bias = _uniform((Hv,), -1.0, 1.0, g, device)
+    init_state = (_normal((1, Hv, D, D), g, device, std=w.init_state_std)
+                  if w.init_state_std > 0 else None)
+    n_in = 2 * Hk * D + 2 * Hv * D + 2 * Hv
+    x = _normal((T, d_model), g, device).to(torch.bfloat16)
+    w_in = _normal((n_in, d_model), g, device, std=d_model ** -0.5).to(torch.bfloat16)
+    w_out = _normal((d_model, Hv * D), g, device, std=(Hv * D) ** -0.5).to(torch.bfloat16)
+    return dict(x=x, w_in=w_in, w_out=w_out, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
+                norm_w=torch.ones(D, device=device, dtype=torch.float32),
+                init_state=init_state, d_model=d_model)
+
+
 def decode_setup(w: Workload, device="cpu") -> dict:
     """Parameters, initial per-sequence state and conv cache of a decode workload."""
     g = _gen(w.seed, device)

@@ -222,6 +222,34 @@ gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v,
                              const int32_t *num_commit, void *o, int32_t batch,
                              int32_t n_tokens, void *stream);
 
+/* ---- Projections around the mixer (token-parallel linear layers) ----------------
+ * The mixer's q, k, v, z, a, b are projections of the hidden states, and its gated
+ * output is projected back ("Qwen3.8-Flash-Next" tech report, Fig. 2 caption: the
+ * projected query, key and value streams; "Qwen3-Next 80B-A3B" field guide, cutaway
+ * 02: the output is gated and projected).  All three run one bf16 MFMA GEMM kernel,
+ * y = x w^T with fp32 accumulation: x [M, K] bf16 row-major (one token per row), w
+ * [N, K] bf16 row-major (one row of weights per output feature, the layout of a
+ * linear layer's weight matrix), K a multiple of 64 (GDN_ERR_UNSUPPORTED otherwise).
+ * Outputs are rounded to nearest even where they are bf16. */
+
+/* y [M, N] bf16 = x w^T. */
+gdn_status gdn_linear(const void *x, const void *w, int64_t M, int32_t N, int32_t K, void *y,
+                      void *stream);
+
+/* The mixer's input projection, written straight into the tensors gdn_prefill reads:
+ * x [T, d_model] bf16, w_in [N_in, d_model] bf16 with N_in = 2*Hk*D + 2*Hv*D + 2*Hv, its
+ * rows in the order q (Hk*D rows, head-major), k (Hk*D), v (Hv*D), z (Hv*D), a (Hv),
+ * b (Hv).  q, k [T, Hk, D] and v, z [T, Hv, D] in p->act_dtype; a, b [T, Hv] fp32.
+ * (Only the head counts, head_dim and act_dtype of p are used.) */
+gdn_status gdn_in_projection(const void *x, const void *w_in, const gdn_params *p, int64_t T,
+                             int32_t d_model, void *q, void *k, void *v, void *z, float *a,
+                             float *b, void *stream);
+
+/* The output projection: y [T, d_model] bf16 = o w_out^T with o [T, Hv, D] bf16 read as
+ * [T, Hv*D] and w_out [d_model, Hv*D] bf16.  p->act_dtype must be GDN_BF16. */
+gdn_status gdn_out_projection(const void *o, const void *w_out, const gdn_params *p, int64_t T,
+                              int32_t d_model, void *y, void *stream);
+
 /* Diagnostics: per-kernel device time of the last gdn_prefill call made on
  * this thread while the environment had GDN_KERNEL_TIMING=1.  The library then
  * records HIP events on the caller's stream between its kernels (segment table,

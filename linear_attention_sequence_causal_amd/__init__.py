@@ -28,6 +28,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED",
 EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_noalloc",
             "gdn_decode_step", "gdn_decode_step_fp8_state",
             "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times",
+            "gdn_linear", "gdn_in_projection", "gdn_out_projection",
             "gdn_check_device_errors", "gdn_status_string", "gdn_last_error", "gdn_version")
 PREFILL_KERNELS = ("segment_table", "maps", "combine", "full", "conv_state_out")
 
@@ -87,6 +88,12 @@ def lib() -> ctypes.CDLL:
             L.gdn_last_error.argtypes = []
             L.gdn_version.restype = ctypes.c_char_p
             L.gdn_version.argtypes = []
+            L.gdn_linear.restype = ctypes.c_int
+            L.gdn_linear.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+            L.gdn_in_projection.restype = ctypes.c_int
+            L.gdn_in_projection.argtypes = [vp, vp, pp, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+            L.gdn_out_projection.restype = ctypes.c_int
+            L.gdn_out_projection.argtypes = [vp, vp, pp, i64, i32, vp, vp]
             L.gdn_check_device_errors.restype = ctypes.c_int
             L.gdn_check_device_errors.argtypes = [vp]
             L.gdn_prefill_last_kernel_times.restype = ctypes.c_int
@@ -256,6 +263,48 @@ def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_
                                    ctypes.byref(p), _ptr(state), _ptr(conv_state),
                                    _ptr(num_commit), _ptr(o), B, n, _stream()))
     return o
+
+
+def linear(x, w, out=None):
+    """y = x w^T on bf16 MFMA (fp32 accumulation, bf16 out): x [M, K], w [N, K]."""
+    M, K = x.shape
+    N = w.shape[0]
+    _contig(x, w)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _check(lib().gdn_linear(_ptr(x), _ptr(w), M, N, K, _ptr(y), _stream()))
+    return y
+
+
+def in_projection(x, w_in, num_qk_heads, num_v_heads, head_dim=128, act_dtype=torch.bfloat16):
+    """(q, k, v, z, a, b) of the mixer from hidden states x [T, d_model] bf16 and
+    w_in [2*Hk*D + 2*Hv*D + 2*Hv, d_model] bf16 (rows q | k | v | z | a | b)."""
+    T, d_model = x.shape
+    Hk, Hv, D = num_qk_heads, num_v_heads, head_dim
+    _contig(x, w_in)
+    dev = x.device
+    q = torch.empty((T, Hk, D), dtype=act_dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((T, Hv, D), dtype=act_dtype, device=dev)
+    z = torch.empty_like(v)
+    a = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    p = GdnParams(Hk, Hv, D, GDN_BF16 if act_dtype == torch.bfloat16 else GDN_F32, 1.0, 1e-6,
+                  1e-6, None, None, None, None, 0)
+    _check(lib().gdn_in_projection(_ptr(x), _ptr(w_in), ctypes.byref(p), T, d_model, _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(z), _ptr(a), _ptr(b), _stream()))
+    return q, k, v, z, a, b
+
+
+def out_projection(o, w_out, out=None):
+    """y [T, d_model] bf16 = o w_out^T for o [T, Hv, D] bf16, w_out [d_model, Hv*D]."""
+    T, Hv, D = o.shape
+    d_model = w_out.shape[0]
+    _contig(o, w_out)
+    y = torch.empty((T, d_model), dtype=torch.bfloat16, device=o.device) if out is None else out
+    p = GdnParams(1, Hv, D, GDN_BF16, 1.0, 1e-6, 1e-6, None, None, None, None, 0)
+    _check(lib().gdn_out_projection(_ptr(o), _ptr(w_out), ctypes.byref(p), T, d_model, _ptr(y),
+                                    _stream()))
+    return y
 
 
 def check_device_errors():

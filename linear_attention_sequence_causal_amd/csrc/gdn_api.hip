@@ -13,6 +13,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_device.h"
+#include "gdn_linear.h"
 #include "gdn_prefill_plan.h"
 
 namespace gdn {
@@ -378,6 +379,98 @@ gdn_status gdn_decode_tokens(const void *q, const void *k, const void *v, const 
         p->num_qk_heads, p->num_v_heads, p->output_gate, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode_tokens launch");
   return GDN_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ projections
+namespace {
+gdn_status linear_checks(const void *x, const void *w, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be M >= 0, N > 0, K > 0");
+  if (M > 0 && (!x || !w)) return fail(GDN_ERR_INVALID_ARGUMENT, "x and w are required");
+  if (K % gdn::kLinearKStep != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "K (%lld) must be a multiple of %d", (long long)K,
+                gdn::kLinearKStep);
+  if (N > (int64_t)INT32_MAX || K > (int64_t)INT32_MAX / 256)
+    return fail(GDN_ERR_UNSUPPORTED, "N or K too large");
+  return GDN_OK;
+}
+// The projections read only the head layout and the activation dtype of p.
+gdn_status check_layout(const gdn_params *p) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_qk_heads <= 0 || p->num_v_heads <= 0 || p->num_v_heads % p->num_qk_heads != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "head counts must be positive, Hv a multiple of Hk");
+  if (p->head_dim <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "head_dim must be positive");
+  if (p->act_dtype != GDN_BF16 && p->act_dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "act_dtype %d is not GDN_BF16 or GDN_F32", p->act_dtype);
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_linear(const void *x, const void *w, int64_t M, int32_t N, int32_t K, void *y,
+                      void *stream) {
+  g_err[0] = 0;
+  gdn_status st = linear_checks(x, w, M, N, K);
+  if (st != GDN_OK) return st;
+  if (M > 0 && !y) return fail(GDN_ERR_INVALID_ARGUMENT, "y is required");
+  if (M == 0) return GDN_OK;
+  st = check_device();
+  if (st != GDN_OK) return st;
+  gdn::LinearOut out{};
+  out.nseg = 1;
+  out.ptr[0] = y;
+  out.row_stride[0] = N;
+  out.dtype[0] = gdn::kLinBf16;
+  hipError_t e = gdn::launch_linear_bf16(x, w, M, N, K, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_in_projection(const void *x, const void *w_in, const gdn_params *p, int64_t T,
+                             int32_t d_model, void *q, void *k, void *v, void *z, float *a,
+                             float *b, void *stream) {
+  g_err[0] = 0;
+  gdn_status st = check_layout(p);
+  if (st != GDN_OK) return st;
+  const int64_t qk = (int64_t)p->num_qk_heads * p->head_dim, vd = (int64_t)p->num_v_heads * p->head_dim;
+  const int64_t N = 2 * qk + 2 * vd + 2 * (int64_t)p->num_v_heads;
+  st = linear_checks(x, w_in, T, N, d_model);
+  if (st != GDN_OK) return st;
+  if (T > 0 && (!q || !k || !v || !z || !a || !b))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, z, a and b are required");
+  if (T == 0) return GDN_OK;
+  st = check_device();
+  if (st != GDN_OK) return st;
+  const int act = p->act_dtype == GDN_BF16 ? gdn::kLinBf16 : gdn::kLinF32;
+  gdn::LinearOut out{};
+  out.nseg = 6;
+  const int64_t begin[6] = {0, qk, 2 * qk, 2 * qk + vd, 2 * qk + 2 * vd,
+                            2 * qk + 2 * vd + p->num_v_heads};
+  void *ptrs[6] = {q, k, v, z, a, b};
+  const int64_t strides[6] = {qk, qk, vd, vd, p->num_v_heads, p->num_v_heads};
+  const int types[6] = {act, act, act, act, gdn::kLinF32, gdn::kLinF32};
+  for (int i = 0; i < 6; ++i) {
+    out.col_begin[i] = (int)begin[i];
+    out.ptr[i] = ptrs[i];
+    out.row_stride[i] = strides[i];
+    out.dtype[i] = types[i];
+  }
+  hipError_t e = gdn::launch_linear_bf16(x, w_in, T, (int)N, d_model, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "in-projection launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_out_projection(const void *o, const void *w_out, const gdn_params *p, int64_t T,
+                              int32_t d_model, void *y, void *stream) {
+  g_err[0] = 0;
+  gdn_status st = check_layout(p);
+  if (st != GDN_OK) return st;
+  if (p->act_dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "the output projection takes bf16 o (act_dtype GDN_BF16)");
+  return gdn_linear(o, w_out, T, d_model, p->num_v_heads * p->head_dim, y, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,173 @@
+// gdn_linear.hip -- token-parallel linear layers around the mixer, on bf16 MFMA.
+//
+// The mixer's inputs are projections of the hidden states and its output is
+// projected back ("Qwen3.8-Flash-Next" tech report, Fig. 2 caption: the projected
+// query, key and value streams; "Qwen3-Next 80B-A3B" field guide, cutaway 02: the
+// gated output is projected).  Both are plain GEMMs C = A W^T with A [M, K] (tokens x
+// features) and W [N, K] (one row of weights per output feature), bf16 operands and
+// fp32 accumulation.  The epilogue scatters column ranges of C into separate output
+// tensors, so the in-projection writes q, k, v, z (bf16) and a, b (fp32) in exactly
+// the layouts the mixer reads, with no intermediate buffer.
+//
+// Tiling: one workgroup of 8 waves computes a 256 x 256 block of C, K in steps of
+// 64 through double-buffered LDS tiles (one barrier per step; the next step's tiles
+// are loaded into registers while the current one is multiplied).  Wave (wm, wn) owns
+// rows 64 wm .. + 63 and columns 128 wn .. + 127: 2 x 4 products
+// v_mfma_f32_32x32x16_bf16 per 16-wide k slice (128 accumulators per lane).
+#include "gdn_device.h"
+#include "gdn_linear.h"
+
+namespace gdn {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kLinThreads = 512;
+constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (144 B: 16-byte reads spread over banks)
+constexpr int kTileElems = kBM * kLdsRow;
+constexpr size_t kLinLds = 2 * 2 * (size_t)kTileElems * sizeof(bf16_t);  // A and B, 2 buffers
+static_assert(kLinLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__global__ void __launch_bounds__(kLinThreads, 1)
+linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, int64_t M, int N,
+                   int K, LinearOut out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16_t *const sA = reinterpret_cast<bf16_t *>(smem);
+  bf16_t *const sB = sA + 2 * kTileElems;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  // column blocks fastest: consecutive workgroups share their rows of A (in L2)
+  const int nblk = (N + kBN - 1) / kBN;
+  const int64_t m0 = (int64_t)(blockIdx.x / nblk) * kBM;
+  const int n0 = (int)(blockIdx.x % nblk) * kBN;
+
+  // one buffer per operand over this block's rows: rows past M or N read as zero
+  const int64_t rowsA = M - m0 < kBM ? M - m0 : kBM;
+  const int rowsB = N - n0 < kBN ? N - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * K, (uint32_t)(rowsA * K * 2));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(W + (int64_t)n0 * K, (uint32_t)((int64_t)rowsB * K * 2));
+
+  // this thread's four 16-byte chunks of each 256 x 64 tile: chunk c = tid + 512 i,
+  // row c / 8, k offset 8 (c % 8)
+  i32x4 ga[4], gb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kLinThreads * i;
+      const uint32_t off = (uint32_t)(((c >> 3) * K + k0 + 8 * (c & 7)) * 2);
+      ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kLinThreads * i;
+      const int o = buf * kTileElems + (c >> 3) * kLdsRow + 8 * (c & 7);
+      *reinterpret_cast<i32x4 *>(sA + o) = ga[i];
+      *reinterpret_cast<i32x4 *>(sB + o) = gb[i];
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int nk = K / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  // operand rows of this lane: A rows 64 wm + 32 mt + (lane % 32), W rows 128 wn + 32 nt +
+  // (lane % 32); k = 16 kk + 8 (lane / 32) .. + 7 of the step
+  const int arow = 64 * wm + (lane & 31), brow = 128 * wn + (lane & 31);
+  const int kl = 8 * (lane >> 5);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const bf16_t *a0 = sA + buf * kTileElems + arow * kLdsRow + kl;
+    const bf16_t *b0 = sB + buf * kTileElems + brow * kLdsRow + kl;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8_t af[2], bfr[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8_t *>(a0 + 32 * mt * kLdsRow + 16 * kk);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bfr[nt] = *reinterpret_cast<const bf16x8_t *>(b0 + 32 * nt * kLdsRow + 16 * kk);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0,
+                                                                 0, 0);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);  // the other buffer was last read before the barrier
+    __syncthreads();
+  }
+
+  // epilogue: lane holds column (lane % 32) and rows 8 (r / 4) + 4 (lane / 32) + (r % 4) of
+  // each 32 x 32 tile
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int nbase = n0 + 128 * wn + 32 * nt;
+    if (nbase >= N) continue;
+    const int col = nbase + (lane & 31);
+    if (col >= N) continue;
+    int s = 0;  // the lane's column's segment
+#pragma unroll
+    for (int i = 1; i < kMaxLinearSegs; ++i)
+      if (i < out.nseg && col >= out.col_begin[i]) s = i;
+    const int64_t cs = col - out.col_begin[s];
+    const int64_t stride = out.row_stride[s];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= M) continue;
+        const float x = acc[mt][nt][r];
+        if (out.dtype[s] == kLinF32)
+          reinterpret_cast<float *>(out.ptr[s])[row * stride + cs] = x;
+        else
+          reinterpret_cast<bf16_t *>(out.ptr[s])[row * stride + cs] = f2bf(x);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t linear_lds_bytes() { return kLinLds; }
+
+hipError_t launch_linear_bf16(const void *A, const void *W, int64_t M, int N, int K,
+                              const LinearOut &out, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)linear_bf16_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t blocks = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  hipLaunchKernelGGL(linear_bf16_kernel, dim3((unsigned)blocks), dim3(kLinThreads), kLinLds,
+                     stream, (const bf16_t *)A, (const bf16_t *)W, M, N, K, out);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

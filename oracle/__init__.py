@@ -321,6 +321,39 @@ def decode_tokens(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, state, conv_
     return o.reshape(B, n, Hv, D), fs, co
 
 
+# --------------------------------------------------------- projections
+
+def linear(x, w):
+    """y = x w^T in fp64: x [M, K] (one token per row), w [N, K] (one row of weights per
+    output feature).  A plain matrix product (the projections on either side of the
+    mixer: tech report Fig. 2 caption, the projected q/k/v streams; field guide
+    cutaway 02, the gated output is projected)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def in_projection(x, w_in, Hk: int, Hv: int, D: int):
+    """The mixer's inputs from hidden states x [T, d_model]: y = x w_in^T, split by
+    columns into q, k [T, Hk, D], v, z [T, Hv, D], a, b [T, Hv] (rows of w_in in the
+    order q | k | v | z | a | b)."""
+    y = linear(x, w_in)
+    T = y.shape[0]
+    cuts = np.cumsum([0, Hk * D, Hk * D, Hv * D, Hv * D, Hv, Hv])
+    if cuts[-1] != y.shape[1]:
+        raise ValueError("w_in must have 2*Hk*D + 2*Hv*D + 2*Hv rows")
+    part = [y[:, cuts[i]:cuts[i + 1]] for i in range(6)]
+    return (part[0].reshape(T, Hk, D), part[1].reshape(T, Hk, D), part[2].reshape(T, Hv, D),
+            part[3].reshape(T, Hv, D), part[4], part[5])
+
+
+def gdn_layer(x, w_in, w_out, conv_w, A_log, dt_bias, norm_w, Hk: int, Hv: int, D: int,
+              **kw):
+    """The whole layer: in-projection, mixer (prefill), output projection of o read as
+    [T, Hv*D].  Returns (y [T, d_model], final_state, conv_out)."""
+    q, k, v, z, a, b = in_projection(x, w_in, Hk, Hv, D)
+    o, fs, co = prefill(q, k, v, a, b, z, conv_w, A_log, dt_bias, norm_w, **kw)
+    return linear(o.reshape(o.shape[0], Hv * D), w_out), fs, co
+
+
 def select_heads(qk_heads, Hk: int, Hv: int, D: int):
     """Index helpers to run the oracle on a subset of q/k heads (and their v heads).
 

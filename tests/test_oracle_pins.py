@@ -691,3 +691,46 @@ def test_sigmoid_gate_reaches_the_mixer_outputs_only():
     od1, _, _ = oracle.decode_step(q[:1], k[:1], v[:1], a[:1], b[:1], z[:1], cw, A_log, dt,
                                    None, st, cache)
     assert np.allclose(od1, od * z[:1], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------- projections around the mixer
+
+
+def test_linear_is_the_matrix_product_by_brute_force():
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(5, 7))
+    w = rng.normal(size=(3, 7))
+    y = oracle.linear(x, w)
+    for m in range(5):
+        for n in range(3):
+            acc = 0.0
+            for kk in range(7):
+                acc += x[m, kk] * w[n, kk]
+            assert abs(y[m, n] - acc) <= 1e-13 * (1 + abs(acc))
+
+
+def test_one_hot_projections_reduce_the_layer_to_the_mixer():
+    """w_in with one-hot rows picks hidden features as q, k, v, z, a, b, and w_out = I
+    returns o: the layer equals the mixer on the picked features, bit for bit."""
+    rng = np.random.default_rng(12)
+    T, Hk, Hv, D = 37, 1, 2, 128
+    n_in = 2 * Hk * D + 2 * Hv * D + 2 * Hv
+    d_model = n_in + 5
+    x = rng.normal(size=(T, d_model))
+    perm = rng.permutation(d_model)[:n_in]
+    w_in = np.zeros((n_in, d_model))
+    w_in[np.arange(n_in), perm] = 1.0
+    w_out = np.eye(Hv * D)
+    Cc = 2 * Hk * D + Hv * D
+    cw = rng.normal(0, 0.5, (Cc, 4))
+    A_log = rng.uniform(0, np.log(16), Hv)
+    dt = rng.uniform(-1, 1, Hv)
+    y, fs, co = oracle.gdn_layer(x, w_in, w_out, cw, A_log, dt, None, Hk, Hv, D)
+    sel = x[:, perm]
+    c = np.cumsum([0, Hk * D, Hk * D, Hv * D, Hv * D, Hv, Hv])
+    q, k = sel[:, c[0]:c[1]].reshape(T, Hk, D), sel[:, c[1]:c[2]].reshape(T, Hk, D)
+    v, z = sel[:, c[2]:c[3]].reshape(T, Hv, D), sel[:, c[3]:c[4]].reshape(T, Hv, D)
+    a, b = sel[:, c[4]:c[5]], sel[:, c[5]:c[6]]
+    o, fs2, co2 = oracle.prefill(q, k, v, a, b, z, cw, A_log, dt, None)
+    assert np.array_equal(y, o.reshape(T, Hv * D))
+    assert np.array_equal(fs, fs2) and np.array_equal(co, co2)
