@@ -354,6 +354,69 @@ def gdn_layer(x, w_in, w_out, conv_w, A_log, dt_bias, norm_w, Hk: int, Hv: int, 
     return linear(o.reshape(o.shape[0], Hv * D), w_out), fs, co
 
 
+# ------------------------------------------------- gated full attention
+
+def attn_rms_norm(x, w, eps):
+    """QK-Norm: RMSNorm over the head dimension (last axis) times the weight w
+    ("Qwen3.8-Flash-Next" model card, attention entry: per-head RMSNorm of queries and
+    keys before RoPE; "Qwen3-Next 80B-A3B" field guide, cutaway 03)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * (1.0 if w is None else np.asarray(w, np.float64))
+
+
+def partial_rope(x, pos, rotary_dim, theta):
+    """RoPE on the first rotary_dim dims of each head (model card: partial_rotary_factor
+    0.25, the rotate/nope split q[..., :rotary_dim], q[..., rotary_dim:]; field guide
+    cutaway 03: 64 of 256 dims).  Rotate-half pairing: dim i and i + rotary_dim/2
+    rotate by the angle pos * theta^(-2i/rotary_dim), i < rotary_dim/2.
+    x [T, H, D], pos [T]."""
+    x = np.asarray(x, dtype=np.float64)
+    half = rotary_dim // 2
+    inv = theta ** (-2.0 * np.arange(half) / rotary_dim)
+    ang = np.asarray(pos, np.float64)[:, None] * inv[None, :]       # [T, half]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:rotary_dim]
+    out = x.copy()
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:rotary_dim] = x2 * c + x1 * s
+    return out
+
+
+def gated_attention(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens=None, *, rotary_dim=64,
+                    theta=10000.0, norm_eps=1e-6, scale=None):
+    """The hybrid's gated full-attention mixer (field guide cutaway 03; model card
+    attention entries), fp64:
+        q^ = RoPE(RMSNorm(q) w_q),  k^ = RoPE(RMSNorm(k) w_k)      (positions from 0 in
+                                                                    each sequence)
+        o  = softmax_causal(q^ k^T * scale) v  *  sigmoid(gate)
+    with grouped queries: q head h reads kv head h / (Hq / Hkv).
+    q, gate [T, Hq, D]; k, v [T, Hkv, D]; returns o [T, Hq, D]."""
+    q, k, v, gate = (np.asarray(x, dtype=np.float64) for x in (q, k, v, gate))
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = D ** -0.5 if scale is None else scale
+    cu = np.asarray([0, T] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    o = np.zeros_like(q)
+    for n in range(cu.size - 1):
+        b, e = int(cu[n]), int(cu[n + 1])
+        if e == b:
+            continue
+        pos = np.arange(e - b)
+        qh = partial_rope(attn_rms_norm(q[b:e], q_norm_w, norm_eps), pos, rotary_dim, theta)
+        kh = partial_rope(attn_rms_norm(k[b:e], k_norm_w, norm_eps), pos, rotary_dim, theta)
+        mask = np.tril(np.ones((e - b, e - b), dtype=bool))
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            sc = qh[:, h, :] @ kh[:, g, :].T * scale
+            sc = np.where(mask, sc, -np.inf)
+            sc -= sc.max(axis=1, keepdims=True)
+            p = np.exp(sc)
+            p /= p.sum(axis=1, keepdims=True)
+            o[b:e, h, :] = (p @ v[b:e, g, :]) / (1.0 + np.exp(-gate[b:e, h, :]))
+    return o
+
+
 def select_heads(qk_heads, Hk: int, Hv: int, D: int):
     """Index helpers to run the oracle on a subset of q/k heads (and their v heads).
 

@@ -734,3 +734,82 @@ def test_one_hot_projections_reduce_the_layer_to_the_mixer():
     o, fs2, co2 = oracle.prefill(q, k, v, a, b, z, cw, A_log, dt, None)
     assert np.array_equal(y, o.reshape(T, Hv * D))
     assert np.array_equal(fs, fs2) and np.array_equal(co, co2)
+
+
+# ------------------------------------------------- gated full attention
+
+
+def _attn_case(T, Hq=4, Hkv=2, D=16, seed=0):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(T, Hq, D)), rng.normal(size=(T, Hkv, D)),
+            rng.normal(size=(T, Hkv, D)), rng.normal(size=(T, Hq, D)),
+            rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D))
+
+
+def test_attention_first_token_returns_its_gated_value():
+    """Softmax over a single (causal) key is 1: o_0 = v_0 * sigmoid(gate_0)."""
+    q, k, v, g, wq, wk = _attn_case(5)
+    o = oracle.gated_attention(q, k, v, g, wq, wk, rotary_dim=8)
+    for h in range(4):
+        assert np.allclose(o[0, h], v[0, h // 2] / (1 + np.exp(-g[0, h])), rtol=1e-14)
+
+
+def test_attention_equal_keys_average_the_values():
+    """All keys equal (same raw k at every position and no rotation): every causal
+    score of a query is the same, so o_t = mean(v_0..t) * sigmoid(gate_t)."""
+    q, k, v, g, wq, wk = _attn_case(9, seed=1)
+    k[:] = k[0]
+    o = oracle.gated_attention(q, k, v, g, wq, wk, rotary_dim=0)
+    for t in range(9):
+        for h in range(4):
+            ref = v[:t + 1, h // 2].mean(axis=0) / (1 + np.exp(-g[t, h]))
+            assert np.allclose(o[t, h], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_grouped_query_mapping():
+    """Negating the values of kv head 1 negates exactly the outputs of q heads 2, 3
+    (Hq = 4, Hkv = 2: q head h reads kv head h // 2)."""
+    q, k, v, g, wq, wk = _attn_case(7, seed=2)
+    o1 = oracle.gated_attention(q, k, v, g, wq, wk, rotary_dim=8)
+    v2 = v.copy()
+    v2[:, 1] *= -1
+    o2 = oracle.gated_attention(q, k, v2, g, wq, wk, rotary_dim=8)
+    assert np.array_equal(o2[:, :2], o1[:, :2]) and np.allclose(o2[:, 2:], -o1[:, 2:], rtol=0)
+
+
+def test_partial_rope_rotates_pairs_and_keeps_the_rest():
+    """Dims i and i + r/2 (i < r/2) rotate by pos * theta^(-2i/r); dims >= r are
+    untouched; a rotation keeps each pair's norm and q.k depends on the position
+    difference only."""
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(3, 1, 16))
+    pos = np.array([0.0, 1.0, 5.0])
+    y = oracle.partial_rope(x, pos, 8, 100.0)
+    assert np.array_equal(y[0], x[0])                  # position 0: no rotation
+    assert np.array_equal(y[:, :, 8:], x[:, :, 8:])
+    i, p = 2, 5.0
+    a = p * 100.0 ** (-2 * i / 8)
+    x1, x2 = x[2, 0, i], x[2, 0, i + 4]
+    assert np.isclose(y[2, 0, i], x1 * np.cos(a) - x2 * np.sin(a), rtol=1e-14)
+    assert np.isclose(y[2, 0, i + 4], x2 * np.cos(a) + x1 * np.sin(a), rtol=1e-14)
+    qv, kv = rng.normal(size=(1, 1, 16)), rng.normal(size=(1, 1, 16))
+    d1 = np.sum(oracle.partial_rope(qv, [7.0], 8, 100.0) * oracle.partial_rope(kv, [3.0], 8, 100.0))
+    d2 = np.sum(oracle.partial_rope(qv, [14.0], 8, 100.0) * oracle.partial_rope(kv, [10.0], 8, 100.0))
+    assert np.isclose(d1, d2, rtol=1e-12)
+
+
+def test_qk_norm_is_rms_normalisation_with_weight():
+    x = np.array([[[3.0, 4.0]]])
+    y = oracle.attn_rms_norm(x, np.array([2.0, 1.0]), 0.0)
+    r = np.sqrt((9 + 16) / 2)
+    assert np.allclose(y, [[[6.0 / r, 4.0 / r]]], rtol=1e-15)
+
+
+def test_attention_sequences_do_not_see_each_other():
+    """Packed sequences equal separate runs (positions restart at each sequence)."""
+    q, k, v, g, wq, wk = _attn_case(12, seed=4)
+    cu = [0, 5, 5, 12]
+    o = oracle.gated_attention(q, k, v, g, wq, wk, cu, rotary_dim=8)
+    for b, e in ((0, 5), (5, 12)):
+        oe = oracle.gated_attention(q[b:e], k[b:e], v[b:e], g[b:e], wq, wk, rotary_dim=8)
+        assert np.array_equal(o[b:e], oe)
