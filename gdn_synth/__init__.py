@@ -145,6 +145,48 @@ def layer_inputs(w: Workload, d_model: int, device="cpu") -> dict:
                 init_state=init_state, d_model=d_model)
 
 
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Inputs of the hybrid's gated full-attention layer: 16 query heads over 2 key/value
+    heads of dim 256, RoPE on 64 dims."""
+    name: str
+    seed: int
+    lengths: tuple = ()
+    varlen: int = 0               # >0: number of log-uniform sequences to draw
+    num_q_heads: int = 16
+    num_kv_heads: int = 2
+    head_dim: int = 256
+    rotary_dim: int = 64
+
+
+ATTN_64K = AttnWorkload("attn_T65536_hq16_hkv2_d256_bf16", seed=6, lengths=(65536,))
+ATTN_4K = AttnWorkload("attn_T4096_hq16_hkv2_d256_bf16", seed=7, lengths=(4096,))
+ATTN_VARLEN = AttnWorkload("attn_varlen_N64_len128to32768_hq16_hkv2_d256_bf16", seed=8,
+                           varlen=64)
+
+
+def attention_inputs(w: AttnWorkload, device="cpu") -> dict:
+    """Inputs of one attention workload.  Draws, in this order: sequence lengths (varlen
+    only, as draw_lengths), the QK-Norm weights [D] ~ 1 + N(0, 0.1^2) (q, then k), then
+    q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D], gate [T, Hq, D] ~ N(0, 1) rounded to bf16."""
+    g = _gen(w.seed, device)
+    lengths = draw_lengths(w.varlen, g, device) if w.varlen else list(w.lengths)
+    T = int(sum(lengths))
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    q_norm_w = 1.0 + _normal((D,), g, device, std=0.1)
+    k_norm_w = 1.0 + _normal((D,), g, device, std=0.1)
+    q = _normal((T, Hq, D), g, device).to(torch.bfloat16)
+    k = _normal((T, Hkv, D), g, device).to(torch.bfloat16)
+    v = _normal((T, Hkv, D), g, device).to(torch.bfloat16)
+    gate = _normal((T, Hq, D), g, device).to(torch.bfloat16)
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    return dict(q=q, k=k, v=v, gate=gate, q_norm_w=q_norm_w, k_norm_w=k_norm_w,
+                cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device),
+                lengths=lengths, rotary_dim=w.rotary_dim)
+
+
 def decode_setup(w: Workload, device="cpu") -> dict:
     """Parameters, initial per-sequence state and conv cache of a decode workload."""
     g = _gen(w.seed, device)

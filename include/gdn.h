@@ -149,7 +149,7 @@ gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v,
 
 /* Reports, and clears, an error that a kernel of an earlier call on the current
  * device found in device-resident arguments: today an invalid cu_seqlens table
- * passed to gdn_prefill (GDN_ERR_INVALID_ARGUMENT).  Synchronises `stream` first
+ * passed to gdn_prefill or gdn_gated_attention (GDN_ERR_INVALID_ARGUMENT).  Synchronises `stream` first
  * (host synchronisation).  GDN_OK when no such error is pending. */
 gdn_status gdn_check_device_errors(void *stream);
 
@@ -249,6 +249,53 @@ gdn_status gdn_in_projection(const void *x, const void *w_in, const gdn_params *
  * [T, Hv*D] and w_out [d_model, Hv*D] bf16.  p->act_dtype must be GDN_BF16. */
 gdn_status gdn_out_projection(const void *o, const void *w_out, const gdn_params *p, int64_t T,
                               int32_t d_model, void *y, void *stream);
+
+/* ---- The hybrid's gated full-attention layer ------------------------------------
+ * Every fourth mixer of the hybrid is softmax attention ("Qwen3-Next 80B-A3B" field
+ * guide, cutaway 03: grouped queries, 16 query heads over 2 key/value heads, head dim
+ * 256, rotary embedding on the first 64 dims, QK-Norm, a sigmoid output gate;
+ * "Qwen3.8-Flash-Next" model card, attention entries: per-head RMSNorm of q and k
+ * before the rotation, the rotate/nope split, the output times sigmoid of the gate):
+ *   q^ = RoPE(RMSNorm(q) * q_norm_weight),  k^ = RoPE(RMSNorm(k) * k_norm_weight)
+ *   o  = softmax(causal(q^ k^T * scale)) v * sigmoid(gate)
+ * RMSNorm(x) = x / sqrt(mean(x^2) + norm_eps) over the head dim.  RoPE rotates the
+ * pair (i, i + rotary_dim/2), i < rotary_dim/2, by pos * rope_theta^(-2i/rotary_dim),
+ * pos counted from 0 at each sequence's first token; dims >= rotary_dim pass through.
+ * Query head h reads key/value head h / (Hq / Hkv).  Queries attend to the keys of
+ * their own sequence up to and including their own position. */
+typedef struct {
+  int32_t num_q_heads;           /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;          /* Hkv >= 1 */
+  int32_t head_dim;              /* the kernels are built for 256 */
+  int32_t rotary_dim;            /* 0 <= rotary_dim <= head_dim, a multiple of 16 (64) */
+  float rope_theta;              /* > 0 (10000) */
+  float norm_eps;                /* >= 0 (1e-6) */
+  float scale;                   /* softmax scale; <= 0 selects head_dim^-1/2 */
+  const float *q_norm_weight;    /* [head_dim] device fp32, or NULL for all ones */
+  const float *k_norm_weight;    /* [head_dim] device fp32, or NULL for all ones */
+} gdn_attn_params;
+
+/* Bytes of device workspace gdn_gated_attention needs (2 * T * (Hq + Hkv) * head_dim
+ * plus 512 at most); (size_t)-1 for invalid arguments. */
+size_t gdn_gated_attention_workspace_bytes(const gdn_attn_params *p, int64_t total_tokens);
+
+/* Causal gated attention over num_seqs packed sequences, bf16 in and out:
+ *   q, gate      [T, Hq, head_dim] bf16          T = total_tokens
+ *   k, v         [T, Hkv, head_dim] bf16
+ *   cu_seqlens   [N+1] int32 device, as for gdn_prefill (NULL allowed when N = 1).  The
+ *                first kernel checks the table on the device; for an invalid one no
+ *                output is written and gdn_check_device_errors() reports the error.
+ *                GDN_VALIDATE=1 makes the call check it on the host first
+ *                (synchronising), as gdn_prefill does.
+ *   o            [T, Hq, head_dim] bf16 (out); must not alias an input
+ *   workspace    at least gdn_gated_attention_workspace_bytes() bytes, 256-byte
+ *                aligned (holds the normalised, rotated q^ and k^ in fp16).
+ * Errors: GDN_ERR_UNSUPPORTED for head_dim != 256 or T * (Hq + Hkv) >= 2^27;
+ * GDN_ERR_INVALID_ARGUMENT for bad sizes, rotary_dim, theta or pointers. */
+gdn_status gdn_gated_attention(const void *q, const void *k, const void *v, const void *gate,
+                               const gdn_attn_params *p, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_tokens, void *o,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Diagnostics: per-kernel device time of the last gdn_prefill call made on
  * this thread while the environment had GDN_KERNEL_TIMING=1.  The library then

@@ -29,6 +29,7 @@ EXPORTED = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_noalloc",
             "gdn_decode_step", "gdn_decode_step_fp8_state",
             "gdn_decode_step_bf16_state", "gdn_decode_tokens", "gdn_prefill_last_kernel_times",
             "gdn_linear", "gdn_in_projection", "gdn_out_projection",
+            "gdn_gated_attention_workspace_bytes", "gdn_gated_attention",
             "gdn_check_device_errors", "gdn_status_string", "gdn_last_error", "gdn_version")
 PREFILL_KERNELS = ("segment_table", "maps", "combine", "full", "conv_state_out")
 
@@ -40,6 +41,14 @@ class GdnParams(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
                 ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
                 ("norm_weight", ctypes.c_void_p), ("output_gate", ctypes.c_int32)]
+
+
+class GdnAttnParams(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("scale", ctypes.c_float), ("q_norm_weight", ctypes.c_void_p),
+                ("k_norm_weight", ctypes.c_void_p)]
 
 
 class GdnError(RuntimeError):
@@ -94,6 +103,11 @@ def lib() -> ctypes.CDLL:
             L.gdn_in_projection.argtypes = [vp, vp, pp, i64, i32, vp, vp, vp, vp, vp, vp, vp]
             L.gdn_out_projection.restype = ctypes.c_int
             L.gdn_out_projection.argtypes = [vp, vp, pp, i64, i32, vp, vp]
+            ap = ctypes.POINTER(GdnAttnParams)
+            L.gdn_gated_attention_workspace_bytes.restype = sz
+            L.gdn_gated_attention_workspace_bytes.argtypes = [ap, i64]
+            L.gdn_gated_attention.restype = ctypes.c_int
+            L.gdn_gated_attention.argtypes = [vp, vp, vp, vp, ap, vp, i32, i64, vp, vp, sz, vp]
             L.gdn_check_device_errors.restype = ctypes.c_int
             L.gdn_check_device_errors.argtypes = [vp]
             L.gdn_prefill_last_kernel_times.restype = ctypes.c_int
@@ -305,6 +319,29 @@ def out_projection(o, w_out, out=None):
     _check(lib().gdn_out_projection(_ptr(o), _ptr(w_out), ctypes.byref(p), T, d_model, _ptr(y),
                                     _stream()))
     return y
+
+
+def gated_attention(q, k, v, gate, q_norm_w=None, k_norm_w=None, cu_seqlens=None, *,
+                    rotary_dim=64, theta=10000.0, norm_eps=1e-6, scale=None, out=None):
+    """The hybrid's gated full-attention mixer (QK-Norm, partial RoPE, causal GQA softmax,
+    sigmoid output gate) -> o [T, Hq, D] bf16.  q, gate [T, Hq, D] and k, v [T, Hkv, D]
+    bf16, D = 256; norm weights [D] fp32 or None; cu_seqlens [N+1] int32 or None."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _contig(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens)
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    p = GdnAttnParams(Hq, Hkv, D, int(rotary_dim), float(theta), float(norm_eps),
+                      0.0 if scale is None else float(scale), _ptr(q_norm_w), _ptr(k_norm_w))
+    nbytes = lib().gdn_gated_attention_workspace_bytes(ctypes.byref(p), T)
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise GdnError(1, lib().gdn_last_error().decode())
+    ws = _workspace(nbytes, q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().gdn_gated_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), ctypes.byref(p),
+                                     _ptr(cu_seqlens), N, T, _ptr(o), _ptr(ws),
+                                     0 if ws is None else ws.numel(),
+                                     _stream()))
+    return o
 
 
 def check_device_errors():

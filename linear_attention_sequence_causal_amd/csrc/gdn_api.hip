@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/gdn.h"
+#include "gdn_attention.h"
 #include "gdn_device.h"
 #include "gdn_linear.h"
 #include "gdn_prefill_plan.h"
@@ -144,13 +145,19 @@ gdn_status gdn_check_device_errors(void *stream) {
   if (st != GDN_OK) return st;
   if (hipError_t e = hipStreamSynchronize((hipStream_t)stream); e != hipSuccess)
     return hip_fail(e, "stream synchronisation");
-  int flag = 0;
+  int flag = 0, aflag = 0;
   if (hipError_t e = gdn::take_prefill_error(&flag); e != hipSuccess)
     return hip_fail(e, "reading the device error flag");
+  if (hipError_t e = gdn::take_attention_error(&aflag); e != hipSuccess)
+    return hip_fail(e, "reading the attention error flag");
   if (flag)
     return fail(GDN_ERR_INVALID_ARGUMENT,
                 "a gdn_prefill call on this device had invalid cu_seqlens contents (its o and "
                 "final states were not written)");
+  if (aflag)
+    return fail(GDN_ERR_INVALID_ARGUMENT,
+                "a gdn_gated_attention call on this device had invalid cu_seqlens contents "
+                "(its o was not written)");
   return GDN_OK;
 }
 
@@ -471,6 +478,88 @@ gdn_status gdn_out_projection(const void *o, const void *w_out, const gdn_params
   if (p->act_dtype != GDN_BF16)
     return fail(GDN_ERR_UNSUPPORTED, "the output projection takes bf16 o (act_dtype GDN_BF16)");
   return gdn_linear(o, w_out, T, d_model, p->num_v_heads * p->head_dim, y, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ gated attention
+namespace {
+gdn_status check_attn(const gdn_attn_params *p, int64_t T) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_kv_heads <= 0 || p->num_q_heads <= 0 || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT,
+                "head counts must be positive, num_q_heads (%d) a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->head_dim <= 0) return fail(GDN_ERR_INVALID_ARGUMENT, "head_dim must be positive");
+  if (p->head_dim != gdn::kAttnHeadDim)
+    return fail(GDN_ERR_UNSUPPORTED, "head_dim %d: the attention kernels are built for %d",
+                p->head_dim, gdn::kAttnHeadDim);
+  if (p->rotary_dim < 0 || p->rotary_dim > p->head_dim || p->rotary_dim % 16 != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "rotary_dim %d must be a multiple of 16 in [0, %d]",
+                p->rotary_dim, p->head_dim);
+  if (!(p->rope_theta > 0.f) || !(p->norm_eps >= 0.f))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "rope_theta must be > 0 and norm_eps >= 0");
+  if (T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "total_tokens must be >= 0");
+  if (T * (int64_t)(p->num_q_heads + p->num_kv_heads) >= ((int64_t)1 << 27))
+    return fail(GDN_ERR_UNSUPPORTED, "total_tokens * (Hq + Hkv) must be below 2^27");
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t gdn_gated_attention_workspace_bytes(const gdn_attn_params *p, int64_t total_tokens) {
+  if (check_attn(p, total_tokens) != GDN_OK) return (size_t)-1;
+  return gdn::attention_workspace_bytes(total_tokens, p->num_q_heads, p->num_kv_heads);
+}
+
+gdn_status gdn_gated_attention(const void *q, const void *k, const void *v, const void *gate,
+                               const gdn_attn_params *p, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_tokens, void *o,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  gdn_status st = check_attn(p, total_tokens);
+  if (st != GDN_OK) return st;
+  const int64_t T = total_tokens;
+  if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if (num_seqs == 0 && T != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "total_tokens must be 0 when num_seqs is 0");
+  if (!cu_seqlens && num_seqs != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens may be NULL only when num_seqs == 1");
+  if (T > 0 && (!q || !k || !v || !gate || !o))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, gate and o are required when T > 0");
+  if (o && (o == q || o == k || o == v || o == gate))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "o must not alias an input");
+  const size_t need = gdn::attention_workspace_bytes(T, p->num_q_heads, p->num_kv_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (workspace && ((uintptr_t)workspace & 255u))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  if (T == 0) return GDN_OK;
+  const char *validate = getenv("GDN_VALIDATE");
+  if (validate && validate[0] == '1' && cu_seqlens) {
+    std::vector<int32_t> cu(num_seqs + 1);
+    hipError_t e = hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (num_seqs + 1),
+                             hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "GDN_VALIDATE copy of cu_seqlens");
+    if (cu[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int i = 0; i < num_seqs; ++i)
+      if (cu[i + 1] < cu[i])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d", i);
+    if (cu[num_seqs] != T)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d, expected total_tokens %lld",
+                  cu[num_seqs], (long long)T);
+  }
+  const float scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  hipError_t e = gdn::launch_attention(q, k, v, gate, cu_seqlens, num_seqs, T, p->num_q_heads,
+                                       p->num_kv_heads, p->q_norm_weight, p->k_norm_weight,
+                                       p->rotary_dim, p->rope_theta, p->norm_eps, scale,
+                                       workspace, o, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gated attention launch");
+  return GDN_OK;
 }
 
 }  // extern "C"

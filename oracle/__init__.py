@@ -417,6 +417,34 @@ def gated_attention(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens=None, *, rotar
     return o
 
 
+def gated_attention_rows(q_rows, k, v, gate_rows, q_norm_w, k_norm_w, rows, cu_seqlens=None,
+                         *, rotary_dim=64, theta=10000.0, norm_eps=1e-6, scale=None):
+    """gated_attention at the query tokens `rows` only (for sizes where the whole output
+    is too costly): q_rows, gate_rows [len(rows), Hq, D] are q and gate at those tokens;
+    each row attends to the keys of its sequence up to itself, exactly as in
+    gated_attention.  Returns o [len(rows), Hq, D]."""
+    q, k, v, gate = (np.asarray(x, dtype=np.float64) for x in (q_rows, k, v, gate_rows))
+    T, Hkv, D = k.shape
+    Hq = q.shape[1]
+    scale = D ** -0.5 if scale is None else scale
+    cu = np.asarray([0, T] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    out = np.zeros((len(rows), Hq, D))
+    for j, t in enumerate(rows):
+        n = int(np.searchsorted(cu, t, side="right")) - 1
+        b = int(cu[n])
+        pos = np.arange(t + 1 - b)
+        kh = partial_rope(attn_rms_norm(k[b:t + 1], k_norm_w, norm_eps), pos, rotary_dim, theta)
+        qh = partial_rope(attn_rms_norm(q[j:j + 1], q_norm_w, norm_eps), pos[-1:], rotary_dim,
+                          theta)[0]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            sc = kh[:, g, :] @ qh[h] * scale
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            out[j, h] = (p @ v[b:t + 1, g, :]) / (1.0 + np.exp(-gate[j, h]))
+    return out
+
+
 def select_heads(qk_heads, Hk: int, Hv: int, D: int):
     """Index helpers to run the oracle on a subset of q/k heads (and their v heads).
 

@@ -210,3 +210,56 @@ def test_output_gate_must_be_silu_or_sigmoid():
     assert np.all(o == 7.0)
     p.output_gate = 1
     assert _decode(p, out=o) == 4  # valid: reaches the (missing) device
+
+
+def _attn_params(Hq=16, Hkv=2, D=256, rot=64, theta=1e4, eps=1e-6):
+    return gdn.GdnAttnParams(Hq, Hkv, D, rot, theta, eps, 0.0, None, None)
+
+
+def test_gated_attention_argument_errors_leave_outputs_untouched():
+    L = gdn.lib()
+    T = 8
+    q = _host(T * 16 * 256)
+    kv = _host(T * 2 * 256)
+    o = _host(T * 16 * 256)
+    ptr = lambda x: ctypes.c_void_p(x.ctypes.data)
+
+    def call(p, N=1, cu=None, out=o, ws=None, ws_bytes=0):
+        return L.gdn_gated_attention(ptr(q), ptr(kv), ptr(kv), ptr(q), ctypes.byref(p), cu, N,
+                                     T, ptr(out), ws, ws_bytes, None)
+
+    cases = [(_attn_params(Hq=3, Hkv=2), 1, "multiple"),
+             (_attn_params(D=128), 2, "256"),
+             (_attn_params(rot=24), 1, "rotary_dim"),
+             (_attn_params(rot=272), 1, "rotary_dim"),
+             (_attn_params(theta=0.0), 1, "rope_theta"),
+             (_attn_params(eps=-1.0), 1, "norm_eps")]
+    for p, code, word in cases:
+        assert call(p) == code, word
+        assert word in L.gdn_last_error().decode()
+    assert call(_attn_params(), N=2) == 1             # cu_seqlens required for N > 1
+    assert call(_attn_params(), out=q) == 1           # o aliases q
+    assert call(_attn_params()) == 3                  # workspace missing
+    assert np.all(o == 7.0)
+
+
+def test_gated_attention_workspace_and_missing_device():
+    import torch
+    L = gdn.lib()
+    p = _attn_params()
+    assert L.gdn_gated_attention_workspace_bytes(ctypes.byref(p), 0) == 0
+    n = L.gdn_gated_attention_workspace_bytes(ctypes.byref(p), 100)
+    assert 2 * 100 * 18 * 256 <= n <= 2 * 100 * 18 * 256 + 512
+    assert L.gdn_gated_attention_workspace_bytes(ctypes.byref(_attn_params(D=64)), 1) == \
+        ctypes.c_size_t(-1).value
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    T = 100
+    q, kv, o = _host(T * 16 * 256), _host(T * 2 * 256), _host(T * 16 * 256)
+    raw = np.zeros(n + 512, dtype=np.uint8)
+    addr = (raw.ctypes.data + 255) // 256 * 256
+    ptr = lambda x: ctypes.c_void_p(x.ctypes.data)
+    st = L.gdn_gated_attention(ptr(q), ptr(kv), ptr(kv), ptr(q), ctypes.byref(p), None, 1, T,
+                               ptr(o), ctypes.c_void_p(addr), n, None)
+    assert st == NO_DEVICE
+    assert np.all(o == 7.0) and np.all(raw == 0)

@@ -813,3 +813,34 @@ def test_attention_sequences_do_not_see_each_other():
     for b, e in ((0, 5), (5, 12)):
         oe = oracle.gated_attention(q[b:e], k[b:e], v[b:e], g[b:e], wq, wk, rotary_dim=8)
         assert np.array_equal(o[b:e], oe)
+
+
+def test_attention_without_rotation_and_gate_is_causal_sdpa():
+    """With unit-RMS q and k (QK-Norm then the identity: weights None, eps 0), no rotated
+    dims and a gate of 40 (sigmoid = 1 to 4e-18), the mixer is plain causal softmax
+    attention: it must equal torch's scaled_dot_product_attention (CPU, fp64) with the
+    kv heads repeated for the grouped queries."""
+    rng = np.random.default_rng(5)
+    T, Hq, Hkv, D = 23, 4, 2, 16
+    q, k, v = (rng.normal(size=(T, H, D)) for H in (Hq, Hkv, Hkv))
+    q /= np.sqrt(np.mean(q * q, axis=-1, keepdims=True))
+    k /= np.sqrt(np.mean(k * k, axis=-1, keepdims=True))
+    g = np.full((T, Hq, D), 40.0)
+    o = oracle.gated_attention(q, k, v, g, None, None, rotary_dim=0, norm_eps=0.0, scale=0.3)
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                           scale=0.3)
+    assert np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_rows_match_the_whole_output():
+    """The sampled form gives the rows of the whole output (first, middle and last
+    tokens of packed sequences, a sequence of length 1 included)."""
+    q, k, v, g, wq, wk = _attn_case(20, seed=6)
+    cu = [0, 7, 8, 20]
+    o = oracle.gated_attention(q, k, v, g, wq, wk, cu, rotary_dim=8)
+    rows = [0, 3, 6, 7, 8, 13, 19]
+    orows = oracle.gated_attention_rows(q[rows], k, v, g[rows], wq, wk, rows, cu, rotary_dim=8)
+    assert np.allclose(orows, o[rows], rtol=1e-12, atol=1e-14)
