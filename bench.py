@@ -366,6 +366,51 @@ def bench_projections(args, torch, gdn, S):
     return res
 
 
+def attention_alg_flops(lengths, Hq, D):
+    """Causal attention: query t of a sequence meets t + 1 keys (positions from 0), each
+    costing D multiply-adds for q.k and D for p.v, per query head."""
+    return sum(4.0 * D * Hq * L * (L + 1) / 2 for L in lengths)
+
+
+def bench_attention(args, torch, gdn, S, w, reps=None):
+    """The hybrid's gated full-attention layer on one workload (QK-Norm + RoPE prologue and
+    the causal GQA kernel, the whole call timed with HIP events)."""
+    d = S.attention_inputs(w, "cuda")
+    T = int(sum(d["lengths"]))
+    cu = d["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    o = torch.empty_like(d["q"])
+
+    def call():
+        gdn.gated_attention(d["q"], d["k"], d["v"], d["gate"], d["q_norm_w"], d["k_norm_w"],
+                            cu, rotary_dim=d["rotary_dim"], out=o)
+
+    reps = reps or max(3, min(args.steps, 10))
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = attention_alg_flops(d["lengths"], w.num_q_heads, w.head_dim)
+    ach = fl / (ms * 1e-3) / 1e12
+    res = {"value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "calls": reps,
+           "config": {"workload": w.name, "num_seqs": len(d["lengths"]), "tokens": T,
+                      "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                      "head_dim": w.head_dim, "rotary_dim": w.rotary_dim},
+           "roofline": {"bound": "mfma", "kernel": "gated attention call (prologue + "
+                                                   "attention kernel)",
+                        "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_BF16_TFLOPS, "alg_flops_per_launch": fl,
+                        "launch_ms": ms}}
+    del d, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -525,7 +570,8 @@ def main():
     ap.add_argument("--settle", type=int, default=30,
                     help="untimed prefill calls before the warm-up (clock ramp)")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "tokens"), default="all")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "tokens", "attention"),
+                    default="all")
     ap.add_argument("--tokens-n", type=int, default=4,
                     help="new tokens per sequence of the n-token step leg (1..8)")
     ap.add_argument("--tokens-calls", type=int, default=100)
@@ -684,6 +730,16 @@ def main():
                          "roofline": tl["roofline"], "verify": tl["verify"]})
         else:
             line["decode_tokens"] = tl
+    if args.only in ("all", "attention"):
+        al = {w.name: bench_attention(args, torch, gdn, S, w)
+              for w in (S.ATTN_64K, S.ATTN_4K, S.ATTN_VARLEN)}
+        if args.only == "attention":
+            a0 = al[S.ATTN_64K.name]
+            line.update({"value": a0["value"], "unit": "tokens/s",
+                         "ms_per_step": a0["ms_per_call"], "config": a0["config"],
+                         "roofline": a0["roofline"], "attention": al})
+        else:
+            line["gated_attention"] = al
     if parity:
         line["parity"] = parity
     line.setdefault("cpu_baseline", None)

@@ -11,25 +11,59 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed-fp32 instructions are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions.  The attention kernel keeps its MFMA accumulators in VGPRs: its
+# O accumulators are rescaled by VALU code inside the key loop, and in AGPRs the
+# compiler copies all of them to VGPRs and back on every tile.
+EXTRA_FLAGS = {
+    "gdn_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libgdn.so")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source of csrc/ to an object (in parallel), then link libgdn.so."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    for src in srcs:
+        obj = os.path.join(CSRC, os.path.basename(src)[:-4] + ".o.tmp" + tag)
+        cmd = ([hipcc] + HIPCC_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) +
+               ["-c", src, "-o", obj])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                       text=True), obj))
+    failed = False
+    for p, obj in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            failed = True
+        objs.append(obj)
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed building libgdn.so")
+        tmp = LIB + ".tmp" + tag
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB
 
 

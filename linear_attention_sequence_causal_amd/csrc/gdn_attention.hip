@@ -12,12 +12,13 @@
 //   qk_prep_kernel   one pass over q and k: RMSNorm, weight, rotate-half RoPE of the
 //                    first rotary_dim dims (angles in fp64, reduced mod 2 pi before the
 //                    fp32 sine and cosine) -> fp16 q^, k^ in the workspace;
-//   attention_kernel one workgroup = 64 queries of one q head (4 waves x 16 queries),
-//                    keys in tiles of 32 through LDS.  It computes S^T = K^ Q^T and
-//                    O^T = V^T P^T on MFMA, so a query is a column of both: its lane
-//                    holds its softmax statistics, and P^T (C layout of S^T) is already
-//                    the B operand of the second product (k slots in the permuted
-//                    order the A operand V^T reads).  Online softmax in base 2.
+//   attention_kernel one workgroup = 4 waves of 32 queries each (up to four q heads of
+//                    one kv head share it), keys in tiles of 64 through double-buffered
+//                    LDS.  It computes S^T = K^ Q^T and O^T = V^T P^T on 32x32x16 MFMA,
+//                    so a query is a column of both: its lane holds its softmax
+//                    statistics, and P^T (C layout of S^T) is already the B operand of
+//                    the second product (k slots in the permuted order the A operand V^T
+//                    reads).  Online softmax in base 2.
 #include "gdn_attention.h"
 #include "gdn_device.h"
 
@@ -34,20 +35,14 @@ namespace {
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAD = 256;          // head dim the kernels are built for
-constexpr int kQB = 64;           // queries per workgroup
-constexpr int kKT = 32;           // keys per tile
-constexpr int kKsS = kAD + 8;     // fp16 row stride of the K^ tile [32 keys][256]
-constexpr int kVtS = kKT + 8;     // bf16 row stride of the V^T tile [256][32 keys]
 
-__device__ __forceinline__ f32x4 mfma_h(u16x8 a, u16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_b(u16x8 a, u16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+// Raw buffer over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > INT32_MAX ? INT32_MAX : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
 // First token of the sequence holding token t (cu may be NULL: one sequence).
@@ -62,19 +57,11 @@ __device__ __forceinline__ int seq_begin(const int32_t *cu, int N, int t) {
   return cu[lo];
 }
 
-// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes of one query).
-__device__ __forceinline__ float rows4_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows4_add(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+// RoPE frequencies in revolutions per position: rev[i] = theta^(-2i/rotary_dim) / (2 pi),
+// formed on the host in fp64 (passed by value with the kernel arguments).
+struct RopeTable {
+  double rev[kAD / 2];
+};
 
 // 256 threads = 8 rows of 256 (32 threads x 8 dims each); rows ordered token-major,
 // q heads then kv heads.
@@ -82,7 +69,7 @@ __global__ void __launch_bounds__(256)
 qk_prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                const int32_t *__restrict__ cu, int N, int T, int Hq, int Hkv,
                const float *__restrict__ wq, const float *__restrict__ wk, int rot,
-               double log2_theta, float eps, int *__restrict__ bad_word,
+               RopeTable tab, float eps, int *__restrict__ bad_word,
                _Float16 *__restrict__ qh, _Float16 *__restrict__ kh) {
   if (blockIdx.x == 0 && bad_word) {
     // cu_seqlens check for this call: cu[0] = 0, non-decreasing, cu[N] = T
@@ -138,10 +125,11 @@ qk_prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     for (int e = 0; e < 8; ++e) {
       const int i = (lo ? 8 * j : 8 * j - half) + e;  // frequency index
       // angle pos * theta^(-2i/rot) in fp64, reduced to [-pi, pi] before sin/cos
-      double ang = (double)pos * exp2(-2.0 * i / rot * log2_theta);
-      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-      float s, c;
-      sincosf((float)ang, &s, &c);
+      // angle in revolutions, pos * theta^(-2i/rot) / (2 pi), reduced to [-1/2, 1/2] in
+      // fp64; the hardware sine and cosine take revolutions
+      double rv = (double)pos * tab.rev[i];
+      rv -= rint(rv);
+      const float s = __builtin_amdgcn_sinf((float)rv), c = __builtin_amdgcn_cosf((float)rv);
       y[e] = lo ? y[e] * c - pr[e] * s : y[e] * c + pr[e] * s;
     }
   }
@@ -153,156 +141,259 @@ qk_prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   *reinterpret_cast<h8 *>(dst + 8 * j) = out;
 }
 
-__global__ void __launch_bounds__(256)
+// Key tiles of 32 through double-buffered LDS: K^ [32 keys][264] fp16 and V^T [256 dims][36
+// keys] bf16 (the pads spread the MFMA operand reads over all banks).
+constexpr int kKT = 32;
+constexpr int kKsS = kAD + 8;
+constexpr int kVtS = kKT + 4;
+constexpr int kKBuf = kKT * kKsS;          // fp16 elements per K^ buffer
+constexpr int kVBuf = kAD * kVtS;          // bf16 elements per V^T buffer
+constexpr size_t kAttnLds = 2 * (size_t)kKBuf * 2 + 2 * (size_t)kVBuf * 2;
+static_assert(kAttnLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ f32x16 mfma32h(u16x8 a, u16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32b(u16x8 a, u16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// One workgroup = 4 waves = hpb query heads of one kv head x qpb blocks of 32 queries
+// (hpb * qpb <= 4; waves past that only help load the tiles).  Each wave owns 32 queries
+// of one head: S^T [keys][32 queries] = K^ Q^T and O^T [256 dims][32 queries] += V^T P^T
+// on 32x32x16 MFMA, so a lane holds one query's column (its softmax statistics) and P^T
+// in C layout is already the B operand of the second product.  The running max m is
+// only raised when a tile's max exceeds it by more than 8 (base 2), so O is rescaled
+// rarely and p <= 2^8.
+__global__ void __launch_bounds__(256, 1)
 attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ kh,
                  const bf16_t *__restrict__ v, const bf16_t *__restrict__ gate,
-                 const int32_t *__restrict__ cu, int N, int T, int Hq, int Hkv, float scale2,
-                 const int *__restrict__ bad_word, bf16_t *__restrict__ o) {
-  __shared__ __attribute__((aligned(16))) _Float16 sK[kKT * kKsS];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[kAD * kVtS];
+                 const int32_t *__restrict__ cu, int N, int T, int Hq, int Hkv, int hpb,
+                 int qpb, float scale2, const int *__restrict__ bad_word,
+                 bf16_t *__restrict__ o) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16 *const sK = reinterpret_cast<_Float16 *>(smem);
+  bf16_t *const sVt = reinterpret_cast<bf16_t *>(smem + 2 * (size_t)kKBuf * 2);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 15, lg = lane >> 4;
-  // ids 8 apart go to the same XCD: the r = Hq/Hkv q heads of a kv head and query block
+  const int ln = lane & 31, lh = lane >> 5;
+  const int r = Hq / Hkv, ng = r / hpb;
+  // ids 8 apart go to the same XCD: the ng head groups of one (kv head, query block)
   // get ids 8 apart, so their shared K^ and V tiles are fetched into one L2
-  const int r = Hq / Hkv;
   const int bid = blockIdx.x, x = bid & 7, yb = bid >> 3;
-  const int member = yb % r, rest = (yb / r) * 8 + x;
-  const int nqb = (T + kQB - 1) / kQB;
+  const int member = yb % ng, rest = (yb / ng) * 8 + x;
+  const int span = 32 * qpb;
+  const int nqb = (T + span - 1) / span;
   if (rest >= nqb * Hkv) return;
   if (bad_word && *bad_word) return;  // invalid cu_seqlens: o is left unwritten
   // the last query blocks see the most keys: they are dispatched first
   const int qb = nqb - 1 - rest / Hkv, kvh = rest % Hkv;
-  const int h = kvh * r + member;
-  const int t0 = qb * kQB;
-  const int tq = t0 + 16 * wave + ln;          // this lane's query
-  const bool qvalid = tq < T;
-  const int tqc = qvalid ? tq : T - 1;
-  // its sequence's first token, and the first key any query of the block sees (both
-  // clamped, so that no table can send an access out of bounds)
+  const int t0 = qb * span;
+  const bool active = wave < hpb * qpb;
+  const int h = kvh * r + member * hpb + (active ? wave % hpb : 0);
+  const int t0w = t0 + 32 * (active ? wave / hpb : 0);   // the wave's first query
+  const int tq = t0w + ln;                               // this lane's query
+  const bool qvalid = active && tq < T;
+  const int tqc = min(tq, T - 1);
+  // sequence starts (clamped, so that no table can send an access out of bounds)
   const int sb = min(max(seq_begin(cu, N, tqc), 0), tqc);
   const int kstart = min(max(seq_begin(cu, N, t0), 0), t0);
-  const int kend = min(t0 + kQB - 1, T - 1);   // last one
+  const int kend = min(t0 + span - 1, T - 1);
+  // wave-uniform key range that needs no mask: [sb_hi, t0w]
+  const int tlast = min(t0w + 31, T - 1);
+  const int sb_hi = min(max(seq_begin(cu, N, tlast), 0), tlast);
+  const int wave_kend = active && t0w < T ? tlast : -1;
 
-  // Q^ fragments (B operand of S^T = K^ Q^T): lane holds dims 32c + 8lg .. + 7 of its query
-  u16x8 qf[8];
+  // Q^ fragments (B operand): lane holds dims 16c + 8lh .. + 7 of its query
+  u16x8 qf[16];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    qf[c] = *reinterpret_cast<const u16x8 *>(qh + ((int64_t)tqc * Hq + h) * kAD + 32 * c + 8 * lg);
+  for (int c = 0; c < 16; ++c)
+    qf[c] = *reinterpret_cast<const u16x8 *>(qh + ((int64_t)tqc * Hq + h) * kAD + 16 * c + 8 * lh);
 
-  f32x4 oacc[16];
+  f32x16 oacc[8];
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  for (int k0 = kstart; k0 <= kend; k0 += kKT) {
-    __syncthreads();  // the previous tile is consumed
-    {  // K^ tile [32 keys][256]: thread = key tid / 8, dims 32 (tid % 8) .. + 31
-      const int key = k0 + (tid >> 3), d0 = 32 * (tid & 7);
-      uint4 w4[4] = {};
-      if (key < T) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(kh + ((int64_t)key * Hkv + kvh) * kAD + d0);
+  // tile staging: K^ chunk c = tid + 256 i (key c / 32, dims 8 (c % 32)); V keys
+  // 4 kq .. + 3 (kq = tid % 8) at dims 8 dc .. + 7 (dc = tid / 8).  Buffers start at
+  // the tile's first key, so keys past T read as zero.
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 gk[4], gv[4];
+  const int64_t key_bytes = (int64_t)Hkv * kAD * 2;
+  auto gload = [&](int k0) {
+    const int64_t left = (int64_t)(T - k0) * key_bytes;
+    const auto rk = rsrc(kh + ((int64_t)k0 * Hkv + kvh) * kAD, left);
+    const auto rv = rsrc(v + ((int64_t)k0 * Hkv + kvh) * kAD, left);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w4[i] = src[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4 *>(sK + (tid >> 3) * kKsS + d0 + 8 * i) = w4[i];
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      gk[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, (uint32_t)((c >> 5) * key_bytes + 16 * (c & 31)), 0, 0);
     }
-    {  // V^T tile [256][32 keys]: thread = keys 2 (tid % 16), + 1 and dims 16 (tid / 16) .. + 15
-      const int kp = tid & 15, d0 = 16 * (tid >> 4);
-      uint32_t a[8] = {}, b[8] = {};
-      const int ka = k0 + 2 * kp, kb = ka + 1;
-      if (ka < T) {
-        const uint4 *s = reinterpret_cast<const uint4 *>(v + ((int64_t)ka * Hkv + kvh) * kAD + d0);
-        const uint4 u0 = s[0], u1 = s[1];
-        a[0] = u0.x; a[1] = u0.y; a[2] = u0.z; a[3] = u0.w; a[4] = u1.x; a[5] = u1.y; a[6] = u1.z; a[7] = u1.w;
-      }
-      if (kb < T) {
-        const uint4 *s = reinterpret_cast<const uint4 *>(v + ((int64_t)kb * Hkv + kvh) * kAD + d0);
-        const uint4 u0 = s[0], u1 = s[1];
-        b[0] = u0.x; b[1] = u0.y; b[2] = u0.z; b[3] = u0.w; b[4] = u1.x; b[5] = u1.y; b[6] = u1.z; b[7] = u1.w;
-      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // dims d0 + 2e (low halves) and d0 + 2e + 1 (high)
-        *reinterpret_cast<uint32_t *>(sVt + (d0 + 2 * e) * kVtS + 2 * kp) =
-            __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
-        *reinterpret_cast<uint32_t *>(sVt + (d0 + 2 * e + 1) * kVtS + 2 * kp) =
-            __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
-      }
+    for (int e = 0; e < 4; ++e)
+      gv[e] = __builtin_amdgcn_raw_buffer_load_b128(
+          rv, (uint32_t)((4 * (tid & 7) + e) * key_bytes + 16 * (tid >> 3)), 0, 0);
+  };
+  auto lstore = [&](int buf) {
+    _Float16 *k_ = sK + buf * kKBuf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<i32x4 *>(k_ + (c >> 5) * kKsS + 8 * (c & 31)) = gk[i];
     }
-    __syncthreads();
+    bf16_t *v_ = sVt + buf * kVBuf;
+    const int dc = tid >> 3, kq = tid & 7;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {  // dim 8 dc + e of keys 4 kq .. + 3
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int w = e >> 1;
+      const uint32_t lo = __builtin_amdgcn_perm((uint32_t)gv[1][w], (uint32_t)gv[0][w], sel);
+      const uint32_t hi = __builtin_amdgcn_perm((uint32_t)gv[3][w], (uint32_t)gv[2][w], sel);
+      *reinterpret_cast<uint2 *>(v_ + (8 * dc + e) * kVtS + 4 * kq) = make_uint2(lo, hi);
+    }
+  };
 
-    // S^T [32 keys][16 queries] of this wave: two 16-key tiles
-    f32x4 st[2];
+  // One key tile of the wave's own range: S^T, masked online softmax, O^T += V^T P^T.
+  auto compute = [&](int k0, int buf) {
+    const _Float16 *k_ = sK + buf * kKBuf;
+    const bf16_t *v_ = sVt + buf * kVBuf;
+    // two independent accumulation chains over the 16 dim slices, added at the end
+    f32x16 st, s2;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) st[i] = s2[i] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u16x8 a = *reinterpret_cast<const u16x8 *>(sK + (16 * kt + ln) * kKsS + 32 * c + 8 * lg);
-        st[kt] = mfma_h(a, qf[c], st[kt]);
+    for (int c = 0; c < 16; c += 2) {
+      const u16x8 a0 = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 8 * lh);
+      const u16x8 a1 = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 16 + 8 * lh);
+      st = mfma32h(a0, qf[c], st);
+      s2 = mfma32h(a1, qf[c + 1], s2);
+    }
+    // lane holds the raw scores of keys k0 + 8 (i / 4) + 4 lh + i % 4 of its query; the
+    // logits are scale2 * s (base 2)
+    const bool full = k0 >= sb_hi && k0 + kKT - 1 <= t0w;
+    float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        st[i] += s2[i];
+        mx = fmaxf(mx, st[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        const bool ok = qvalid && key >= sb && key <= tq;
+        st[i] = ok ? st[i] + s2[i] : -INFINITY;
+        mx = fmaxf(mx, st[i]);
       }
     }
-    // causal and sequence mask, base-2 logits, online softmax per query (lane column)
-    float mx = -INFINITY;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
+    }
+    // raise the reference max only when this tile exceeds it by more than 8
+    const bool raise = mx > m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float al = raise ? exp2f(m - mx) : 1.0f;  // m = -inf: al = 0 (O, l are 0)
+      if (raise) m = mx;
+      l *= al;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * kt + 4 * lg + i;
-        const bool ok = qvalid && key >= sb && key <= tq;
-        st[kt][i] = ok ? st[kt][i] * scale2 : -INFINITY;
-        mx = fmaxf(mx, st[kt][i]);
-      }
-    mx = rows4_max(mx);
-    const float mn = fmaxf(m, mx);
-    const float mu = mn == -INFINITY ? 0.f : mn;  // no key yet: every p is 0
-    const float al = exp2f(m - mu);
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= al;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;  // no key yet: every p is 0
+    // p = 2^(scale2 s - mu) <= 2^8; masked scores are -inf and give 0
     float ps = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st[kt][i] = exp2f(st[kt][i] - mu);
-        ps += st[kt][i];
-      }
-    l = l * al + rows4_add(ps);
-    m = mn;
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] *= al;
-    // P^T as the B operand: slot 8lg + j <-> key 4lg + j (tile 0, j < 4), 16 + 4lg + j - 4
-    const u16x8 pb = __builtin_bit_cast(
-        u16x8, make_uint4(pk_bf16(st[0][0], st[0][1]), pk_bf16(st[0][2], st[0][3]),
-                          pk_bf16(st[1][0], st[1][1]), pk_bf16(st[1][2], st[1][3])));
-    // O^T += V^T P^T; V^T rows 16 dt + ln, keys in the same permuted order
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const bf16_t *row = sVt + (16 * dt + ln) * kVtS;
-      const uint2 lo = *reinterpret_cast<const uint2 *>(row + 4 * lg);
-      const uint2 hi = *reinterpret_cast<const uint2 *>(row + 16 + 4 * lg);
-      const u16x8 a = __builtin_bit_cast(u16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      oacc[dt] = mfma_b(a, pb, oacc[dt]);
+    for (int i = 0; i < 16; ++i) {
+      st[i] = __builtin_amdgcn_exp2f(fmaf(st[i], scale2, -mu));
+      ps += st[i];
     }
+    l += ps;  // this lane's half of the keys; the halves are added at the end
+    // O^T += V^T P^T over two 16-key chunks: slot 8 lh + j <-> key 16 kc + 4 lh + j
+    // (j < 4) and 16 kc + 8 + 4 lh + j - 4 (j >= 4), the lane's C-layout values
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int i0 = 8 * kc;
+      const u16x8 pb = __builtin_bit_cast(
+          u16x8, make_uint4(pk_bf16(st[i0], st[i0 + 1]), pk_bf16(st[i0 + 2], st[i0 + 3]),
+                            pk_bf16(st[i0 + 4], st[i0 + 5]), pk_bf16(st[i0 + 6], st[i0 + 7])));
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16_t *row = v_ + (32 * db + ln) * kVtS + 16 * kc + 4 * lh;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(row);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(row + 8);
+        const u16x8 a = __builtin_bit_cast(u16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[db] = mfma32b(a, pb, oacc[db]);
+      }
+    }
+  };
+
+  // Every wave takes part in loading all of the block's tiles; it computes only those
+  // holding a key in [its first query's sequence start, its last query].  The three
+  // loops keep the tile-skip decision out of the loop that carries O.
+  const int ntiles = (kend - kstart) / kKT + 1;
+  const int sb_lo = min(max(seq_begin(cu, N, min(t0w, T - 1)), 0), t0w);
+  int it_lo = __builtin_amdgcn_readfirstlane(wave_kend >= 0 ? (sb_lo - kstart) / kKT : ntiles);
+  const int it_hi = __builtin_amdgcn_readfirstlane(wave_kend >= 0 ? (wave_kend - kstart) / kKT : -1);
+  it_lo = min(it_lo, ntiles);
+  gload(kstart);
+  lstore(0);
+  __syncthreads();
+  int it = 0;
+  for (; it < it_lo; ++it) {
+    if (it + 1 < ntiles) {
+      gload(kstart + (it + 1) * kKT);
+      lstore((it & 1) ^ 1);
+    }
+    __syncthreads();
+  }
+  for (; it <= it_hi; ++it) {
+    const int k0 = kstart + it * kKT, buf = it & 1;
+    if (it + 1 < ntiles) gload(k0 + kKT);
+    compute(k0, buf);
+    if (it + 1 < ntiles) lstore(buf ^ 1);  // the other buffer was last read before the barrier
+    __syncthreads();
+  }
+  for (; it < ntiles; ++it) {
+    if (it + 1 < ntiles) {
+      gload(kstart + (it + 1) * kKT);
+      lstore((it & 1) ^ 1);
+    }
+    __syncthreads();
   }
 
-  // epilogue: lane holds dims 16 dt + 4 lg .. + 3 of its query; o / l * sigmoid(gate)
+  // epilogue: lane holds dims 32 db + 8 (i / 4) + 4 lh + i % 4 of its query; o / l * sigmoid(gate)
   if (!qvalid) return;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false,
+                                                     false);
+    l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   const float il = l > 0.f ? 1.0f / l : 0.f;
   const int64_t base = ((int64_t)tq * Hq + h) * kAD;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) {
-    const int d = 16 * dt + 4 * lg;
-    const uint2 gw = *reinterpret_cast<const uint2 *>(gate + base + d);
-    const float g[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xFFFF0000u),
-                        __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xFFFF0000u)};
-    float val[4];
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) val[i] = oacc[dt][i] * il * sigmoidf_(g[i]);
-    *reinterpret_cast<uint2 *>(o + base + d) = make_uint2(pk_bf16(val[0], val[1]), pk_bf16(val[2], val[3]));
-  }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * db + 8 * g4 + 4 * lh;
+      const uint2 gw = *reinterpret_cast<const uint2 *>(gate + base + d);
+      const float g[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xFFFF0000u),
+                          __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xFFFF0000u)};
+      float val[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) val[i] = oacc[db][4 * g4 + i] * il * sigmoidf_(g[i]);
+      *reinterpret_cast<uint2 *>(o + base + d) = make_uint2(pk_bf16(val[0], val[1]),
+                                                            pk_bf16(val[2], val[3]));
+    }
 }
 
 }  // namespace
@@ -332,16 +423,34 @@ hipError_t launch_attention(const void *q, const void *k, const void *v, const v
   _Float16 *qh = (_Float16 *)(ws + 256);
   _Float16 *kh = (_Float16 *)(ws + 256 + (((size_t)T * Hq * kAD * 2 + 255) & ~(size_t)255));
   const int64_t rows = T * (Hq + Hkv);
+  RopeTable tab{};
+  for (int i = 0; i < rotary_dim / 2; ++i)
+    tab.rev[i] = std::pow((double)theta, -2.0 * i / rotary_dim) / 6.283185307179586;
   hipLaunchKernelGGL(qk_prep_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream,
                      (const bf16_t *)q, (const bf16_t *)k, cu, N, (int)T, Hq, Hkv, wq, wk,
-                     rotary_dim, std::log2((double)theta), eps, bad_word, qh, kh);
-  const int64_t nqb = (T + kQB - 1) / kQB;
+                     rotary_dim, tab, eps, bad_word, qh, kh);
+  // heads per workgroup: the largest divisor of Hq / Hkv up to 4; the rest of the four
+  // waves take further 32-query blocks of the same heads
+  const int r = Hq / Hkv;
+  int hpb = 1;
+  for (int d = 4; d >= 1; --d)
+    if (r % d == 0) { hpb = d; break; }
+  const int qpb = 4 / hpb;
+  const int64_t span = 32 * qpb;
+  const int64_t nqb = (T + span - 1) / span;
   const int64_t pairs = nqb * Hkv;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * (Hq / Hkv);
-  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+  const int64_t blocks = (pairs + 7) / 8 * 8 * (r / hpb);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)attention_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAttnLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)blocks), dim3(256), kAttnLds, stream,
                      (const _Float16 *)qh, (const _Float16 *)kh, (const bf16_t *)v,
-                     (const bf16_t *)gate, cu, N, (int)T, Hq, Hkv, scale * 1.4426950408889634f,
-                     (const int *)bad_word, (bf16_t *)o);
+                     (const bf16_t *)gate, cu, N, (int)T, Hq, Hkv, hpb, qpb,
+                     scale * 1.4426950408889634f, (const int *)bad_word, (bf16_t *)o);
   return hipGetLastError();
 }
 
