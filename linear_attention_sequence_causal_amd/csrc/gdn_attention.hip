@@ -211,6 +211,10 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
 #pragma unroll
   for (int c = 0; c < 16; ++c)
     qf[c] = *reinterpret_cast<const u16x8 *>(qh + ((int64_t)tqc * Hq + h) * kAD + 16 * c + 8 * lh);
+  // Q^ lives in AGPRs (the MFMA reads its B operand from there), which leaves the
+  // VGPRs to O, the scores and the operand reads in flight
+#pragma unroll
+  for (int c = 0; c < 16; ++c) asm volatile("" : "+a"(qf[c]));
 
   f32x16 oacc[8];
 #pragma unroll
@@ -219,34 +223,43 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // tile staging: K^ chunk c = tid + 256 i (key c / 32, dims 8 (c % 32)); V keys
+  // Tile staging: K^ chunk c = tid + 256 i (key c / 32, dims 8 (c % 32)); V keys
   // 4 kq .. + 3 (kq = tid % 8) at dims 8 dc .. + 7 (dc = tid / 8).  Buffers start at
   // the tile's first key, so keys past T read as zero.
+  //
+  // Software pipeline: in iteration it a wave forms the scores of tile it + 1 on MFMA
+  // while its VALU runs the softmax of tile it, then O^T += V^T P^T of tile it.  So K^
+  // runs two tiles ahead of V: at the start of iteration it, K^ buffers hold tiles it and
+  // it + 1 and V^T buffer it & 1 holds tile it; during it the block stores K^(it + 2)
+  // (over K^(it), last read in iteration it - 1) and V(it + 1) (over V(it - 1)).
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   i32x4 gk[4], gv[4];
   const int64_t key_bytes = (int64_t)Hkv * kAD * 2;
-  auto gload = [&](int k0) {
-    const int64_t left = (int64_t)(T - k0) * key_bytes;
-    const auto rk = rsrc(kh + ((int64_t)k0 * Hkv + kvh) * kAD, left);
-    const auto rv = rsrc(v + ((int64_t)k0 * Hkv + kvh) * kAD, left);
+  auto gload_k = [&](int k0) {
+    const auto rk = rsrc(kh + ((int64_t)k0 * Hkv + kvh) * kAD, (int64_t)(T - k0) * key_bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       gk[i] = __builtin_amdgcn_raw_buffer_load_b128(
           rk, (uint32_t)((c >> 5) * key_bytes + 16 * (c & 31)), 0, 0);
     }
+  };
+  auto gload_v = [&](int k0) {
+    const auto rv = rsrc(v + ((int64_t)k0 * Hkv + kvh) * kAD, (int64_t)(T - k0) * key_bytes);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       gv[e] = __builtin_amdgcn_raw_buffer_load_b128(
           rv, (uint32_t)((4 * (tid & 7) + e) * key_bytes + 16 * (tid >> 3)), 0, 0);
   };
-  auto lstore = [&](int buf) {
+  auto lstore_k = [&](int buf) {
     _Float16 *k_ = sK + buf * kKBuf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       *reinterpret_cast<i32x4 *>(k_ + (c >> 5) * kKsS + 8 * (c & 31)) = gk[i];
     }
+  };
+  auto lstore_v = [&](int buf) {
     bf16_t *v_ = sVt + buf * kVBuf;
     const int dc = tid >> 3, kq = tid & 7;
 #pragma unroll
@@ -258,41 +271,46 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
       *reinterpret_cast<uint2 *>(v_ + (8 * dc + e) * kVtS + 4 * kq) = make_uint2(lo, hi);
     }
   };
+  const int ntiles = (kend - kstart) / kKT + 1;
+  // loads issued at the top of iteration it and stored at its bottom
+  auto loads = [&](int it) {
+    if (it + 2 < ntiles) gload_k(kstart + (it + 2) * kKT);
+    if (it + 1 < ntiles) gload_v(kstart + (it + 1) * kKT);
+  };
+  auto stores = [&](int it) {
+    if (it + 2 < ntiles) lstore_k(it & 1);
+    if (it + 1 < ntiles) lstore_v((it + 1) & 1);
+  };
 
-  // One key tile of the wave's own range: S^T, masked online softmax, O^T += V^T P^T.
-  auto compute = [&](int k0, int buf) {
+  // raw scores S^T of the tile in K^ buffer buf (lane: keys 8 (i / 4) + 4 lh + i % 4)
+  auto scores = [&](int buf) {
     const _Float16 *k_ = sK + buf * kKBuf;
-    const bf16_t *v_ = sVt + buf * kVBuf;
-    // two independent accumulation chains over the 16 dim slices, added at the end
-    f32x16 st, s2;
+    f32x16 st;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = s2[i] = 0.f;
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; c += 2) {
-      const u16x8 a0 = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 8 * lh);
-      const u16x8 a1 = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 16 + 8 * lh);
-      st = mfma32h(a0, qf[c], st);
-      s2 = mfma32h(a1, qf[c + 1], s2);
+    for (int c = 0; c < 16; ++c) {
+      const u16x8 a = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 8 * lh);
+      st = mfma32h(a, qf[c], st);
     }
-    // lane holds the raw scores of keys k0 + 8 (i / 4) + 4 lh + i % 4 of its query; the
-    // logits are scale2 * s (base 2)
+    return st;
+  };
+  // Online softmax of the tile at k0 with raw scores st, in two parts: `limit` masks
+  // the scores and updates the reference max (its branches stay ahead of the next
+  // tile's score products), `accumulate` forms p and O^T += V^T P^T.
+  auto limit = [&](f32x16 &st, int k0) {
     const bool full = k0 >= sb_hi && k0 + kKT - 1 <= t0w;
-    float mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        st[i] += s2[i];
-        mx = fmaxf(mx, st[i]);
-      }
-    } else {
+    if (!full) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + 8 * (i >> 2) + 4 * lh + (i & 3);
         const bool ok = qvalid && key >= sb && key <= tq;
-        st[i] = ok ? st[i] + s2[i] : -INFINITY;
-        mx = fmaxf(mx, st[i]);
+        st[i] = ok ? st[i] : -INFINITY;
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
@@ -309,6 +327,9 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= al;
     }
+  };
+  auto accumulate = [&](f32x16 st, int buf) {
+    const bf16_t *v_ = sVt + buf * kVBuf;
     const float mu = m == -INFINITY ? 0.f : m;  // no key yet: every p is 0
     // p = 2^(scale2 s - mu) <= 2^8; masked scores are -inf and give 0
     float ps = 0.f;
@@ -338,36 +359,58 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
   };
 
   // Every wave takes part in loading all of the block's tiles; it computes only those
-  // holding a key in [its first query's sequence start, its last query].  The three
-  // loops keep the tile-skip decision out of the loop that carries O.
-  const int ntiles = (kend - kstart) / kKT + 1;
+  // holding a key in [its first query's sequence start, its last query]: tiles
+  // it_lo .. it_hi.  Separate loops keep the tile-skip decisions out of the loop that
+  // carries O.
   const int sb_lo = min(max(seq_begin(cu, N, min(t0w, T - 1)), 0), t0w);
   int it_lo = __builtin_amdgcn_readfirstlane(wave_kend >= 0 ? (sb_lo - kstart) / kKT : ntiles);
   const int it_hi = __builtin_amdgcn_readfirstlane(wave_kend >= 0 ? (wave_kend - kstart) / kKT : -1);
-  it_lo = min(it_lo, ntiles);
-  gload(kstart);
-  lstore(0);
+  it_lo = min(max(it_lo, 0), ntiles);
+  gload_k(kstart);
+  gload_v(kstart);
+  lstore_k(0);
+  lstore_v(0);
+  if (ntiles > 1) {
+    gload_k(kstart + kKT);
+    lstore_k(1);
+  }
   __syncthreads();
+  f32x16 scur;
+  if (it_lo == 0 && it_hi >= 0) scur = scores(0);
+  __syncthreads();  // K^(0) is read before iteration 0 stores K^(2) over it
   int it = 0;
-  for (; it < it_lo; ++it) {
-    if (it + 1 < ntiles) {
-      gload(kstart + (it + 1) * kKT);
-      lstore((it & 1) ^ 1);
-    }
+  for (; it + 1 < it_lo; ++it) {  // tiles before the wave's range
+    loads(it);
+    stores(it);
     __syncthreads();
   }
-  for (; it <= it_hi; ++it) {
-    const int k0 = kstart + it * kKT, buf = it & 1;
-    if (it + 1 < ntiles) gload(k0 + kKT);
-    compute(k0, buf);
-    if (it + 1 < ntiles) lstore(buf ^ 1);  // the other buffer was last read before the barrier
+  if (it + 1 == it_lo && it_lo <= it_hi) {  // the wave's first scores
+    loads(it);
+    scur = scores((it + 1) & 1);
+    stores(it);
+    __syncthreads();
+    ++it;
+  }
+  for (; it < it_hi; ++it) {  // scores of it + 1 on MFMA beside the softmax of it
+    loads(it);
+    limit(scur, kstart + it * kKT);
+    const f32x16 snext = scores((it + 1) & 1);
+    accumulate(scur, it & 1);
+    scur = snext;
+    stores(it);
     __syncthreads();
   }
-  for (; it < ntiles; ++it) {
-    if (it + 1 < ntiles) {
-      gload(kstart + (it + 1) * kKT);
-      lstore((it & 1) ^ 1);
-    }
+  if (it == it_hi) {  // the wave's last tile
+    loads(it);
+    limit(scur, kstart + it * kKT);
+    accumulate(scur, it & 1);
+    stores(it);
+    __syncthreads();
+    ++it;
+  }
+  for (; it < ntiles; ++it) {  // tiles after the wave's range
+    loads(it);
+    stores(it);
     __syncthreads();
   }
 
