@@ -16,11 +16,14 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source additions.  The attention kernel keeps its MFMA accumulators in VGPRs: its
+# Per-source additions.  The attention kernel keeps its MFMA accumulators in VGPRs (its
 # O accumulators are rescaled by VALU code inside the key loop, and in AGPRs the
-# compiler copies all of them to VGPRs and back on every tile.
+# compiler copies all of them to VGPRs and back on every tile), and is scheduled with
+# the iterative ILP strategy, which keeps more LDS operand reads in flight ahead of the
+# products (measured 40.6 against 44.6 ms with the default strategy at T = 65536).
 EXTRA_FLAGS = {
-    "gdn_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gdn_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                          "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 

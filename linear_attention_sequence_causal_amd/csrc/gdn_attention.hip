@@ -288,10 +288,15 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
     f32x16 st;
 #pragma unroll
     for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    // operand reads in batches of 8 ahead of their products
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const u16x8 a = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * c + 8 * lh);
-      st = mfma32h(a, qf[c], st);
+    for (int c0 = 0; c0 < 16; c0 += 8) {
+      u16x8 a[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        a[c] = *reinterpret_cast<const u16x8 *>(k_ + ln * kKsS + 16 * (c0 + c) + 8 * lh);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st = mfma32h(a[c], qf[c0 + c], st);
     }
     return st;
   };
@@ -347,14 +352,16 @@ attention_kernel(const _Float16 *__restrict__ qh, const _Float16 *__restrict__ k
       const u16x8 pb = __builtin_bit_cast(
           u16x8, make_uint4(pk_bf16(st[i0], st[i0 + 1]), pk_bf16(st[i0 + 2], st[i0 + 3]),
                             pk_bf16(st[i0 + 4], st[i0 + 5]), pk_bf16(st[i0 + 6], st[i0 + 7])));
+      u16x8 a[8];
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const bf16_t *row = v_ + (32 * db + ln) * kVtS + 16 * kc + 4 * lh;
         const uint2 lo = *reinterpret_cast<const uint2 *>(row);
         const uint2 hi = *reinterpret_cast<const uint2 *>(row + 8);
-        const u16x8 a = __builtin_bit_cast(u16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[db] = mfma32b(a, pb, oacc[db]);
+        a[db] = __builtin_bit_cast(u16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] = mfma32b(a[db], pb, oacc[db]);
     }
   };
 
