@@ -63,10 +63,20 @@ def decode_alg_bytes(B, Hk, Hv, D, act_bytes=2, state_bytes=4):
     return state + tokens + cache
 
 
-def source_hash():
+# The kernel sources each stored traffic figure depends on (gdn_device.h is shared).
+TRAFFIC_SOURCES = {
+    "prefill_full_bytes_per_launch": ("gdn_prefill.hip", "gdn_prefill_plan.h", "gdn_device.h"),
+    "decode_bytes_per_launch": ("gdn_decode.hip", "gdn_device.h"),
+    "decode_tokens_bytes_per_launch": ("gdn_decode.hip", "gdn_device.h"),
+    "attention_bytes_per_launch": ("gdn_attention.hip", "gdn_attention.h", "gdn_device.h"),
+}
+
+
+def source_hash(kernel_key):
+    """Hash of the sources of one kernel (the files its stored traffic depends on)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_sequence_causal_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in TRAFFIC_SOURCES[kernel_key]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -74,24 +84,32 @@ def source_hash():
 
 
 def stored_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel sources (else None)."""
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on
+    the current sources of that kernel (else None).  profiles/traffic.txt holds one line
+    per kernel: `<key> = <bytes> <source hash>`."""
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
-    vals = {}
     for line in open(path):
         line = line.strip()
         if not line or line.startswith("#") or "=" not in line:
             continue
-        k, v = line.split("=", 1)
-        vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
-        return None
-    try:
-        return int(float(vals[kernel_key]))
-    except (KeyError, ValueError):
-        return None
+        k, v = (x.strip() for x in line.split("=", 1))
+        if k != kernel_key:
+            continue
+        parts = v.split()
+        if len(parts) != 2 or parts[1] != source_hash(kernel_key):
+            return None
+        try:
+            return int(float(parts[0]))
+        except ValueError:
+            return None
+    return None
+
+
+def progress(msg):
+    """One line on stderr as each leg finishes (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def rel_l2(x, ref):
@@ -405,7 +423,9 @@ def bench_attention(args, torch, gdn, S, w, reps=None):
                                                    "attention kernel)",
                         "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": ach / PEAK_BF16_TFLOPS, "alg_flops_per_launch": fl,
-                        "launch_ms": ms}}
+                        "launch_ms": ms,
+                        "traffic": stored_traffic("attention_bytes_per_launch")
+                        if w.name == S.ATTN_64K.name else None}}
     del d, o
     torch.cuda.empty_cache()
     return res
@@ -617,6 +637,7 @@ def main():
 
     if args.only in ("all", "prefill"):
         pre = bench_prefill(args, torch, gdn, S)
+        progress(f"prefill T=65536: {pre['call_ms']:.3f} ms per call")
         t_dom = pre["dominant_ms"] * 1e-3
         t_call = pre["call_ms"] * 1e-3
         ach = pre["flops"] / t_dom / 1e12
@@ -652,6 +673,7 @@ def main():
         # the same workload with slow decay (exp(A_log) = 0.03): every segment map is
         # non-negligible, so the map and combine passes walk every chunk
         slow = bench_prefill(args, torch, gdn, S, slow_decay=0.03, d=pre["d"])
+        progress(f"prefill slow decay: {slow['call_ms']:.3f} ms per call")
         line["prefill_slow_decay"] = {
             "value": slow["T"] / (slow["call_ms"] * 1e-3), "unit": "tokens/s",
             "ms_per_step": slow["call_ms"], "per_kernel_ms": slow["per_kernel_ms"],
@@ -661,12 +683,15 @@ def main():
         line["prefill_configs"] = {w.name: bench_prefill_config(args, torch, gdn, S, w)
                                    for w in (S.PREFILL_4K, S.VARLEN_64)}
         # the projections on either side of the mixer at the same T
+        progress("prefill T=4096 and varlen done")
         pj = bench_projections(args, torch, gdn, S)
+        progress("projections done")
         line["projections"] = pj
         line["layer_ms"] = (pj["in_projection"]["ms"] + pre["call_ms"] +
                             pj["out_projection"]["ms"])
         if oracle_on:
             cb, o_ref, fs_ref = cpu_baseline_prefill(pre, S, oracle)
+            progress("oracle prefill (CPU baseline) done")
             line["cpu_baseline"] = cb
             parity[S.PREFILL_64K.name] = {"o": rel_l2(S.to_f64(pre["out"]), o_ref),
                                           "state": rel_l2(S.to_f64(pre["fs"]), fs_ref),
@@ -678,6 +703,7 @@ def main():
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         dec = bench_decode(args, torch, gdn, S)
+        progress(f"decode: {dec['ms_per_step']:.4f} ms per step")
         t = dec["ms_per_step"] * 1e-3
         gbs = dec["bytes"] / t / 1e9
         dline = {"value": 1.0 / t, "unit": "steps/s", "ms_per_step": dec["ms_per_step"],
@@ -711,6 +737,7 @@ def main():
         torch.cuda.empty_cache()
         if oracle_on:
             cbd, par = decode_parity_and_cpu(args, torch, gdn, S, oracle)
+            progress("oracle decode done")
             dline["cpu_baseline"] = cbd
             parity[S.DECODE_B256.name] = par
         if args.only == "decode":
@@ -724,6 +751,7 @@ def main():
             line["decode"] = dline
     if args.only in ("all", "tokens"):
         tl = bench_decode_tokens(args, torch, gdn, S)
+        progress("n-token step done")
         if args.only == "tokens":
             line.update({"value": tl["value"], "unit": "tokens/s",
                          "ms_per_step": tl["ms_per_step"], "config": tl["config"],
@@ -731,8 +759,10 @@ def main():
         else:
             line["decode_tokens"] = tl
     if args.only in ("all", "attention"):
-        al = {w.name: bench_attention(args, torch, gdn, S, w)
-              for w in (S.ATTN_64K, S.ATTN_4K, S.ATTN_VARLEN)}
+        al = {}
+        for w in (S.ATTN_64K, S.ATTN_4K, S.ATTN_VARLEN):
+            al[w.name] = bench_attention(args, torch, gdn, S, w)
+            progress(f"attention {w.name}: {al[w.name]['ms_per_call']:.3f} ms per call")
         if args.only == "attention":
             a0 = al[S.ATTN_64K.name]
             line.update({"value": a0["value"], "unit": "tokens/s",

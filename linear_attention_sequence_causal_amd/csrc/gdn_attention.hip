@@ -4,21 +4,24 @@
 // ("Qwen3-Next 80B-A3B" field guide, cutaway 03: 16 query heads share 2 key/value
 // heads, head dim 256; RoPE on the first 64 dims; QK-Norm; a learned sigmoid output
 // gate.  "Qwen3.8-Flash-Next" model card, attention entries: per-head RMSNorm of q and
-// k before RoPE, the rotate/nope split, attn_output * sigmoid(gate)):
+// k before RoPE, a rotated and a position-free part of each head, the output times the
+// sigmoid of a gate):
 //   q^ = RoPE(RMSNorm(q) w_q),  k^ = RoPE(RMSNorm(k) w_k)   (positions from 0 per sequence)
 //   o  = softmax_causal(q^ k^T * scale) v * sigmoid(gate),  q head h -> kv head h / (Hq/Hkv)
 //
 // Two kernels:
 //   qk_prep_kernel   one pass over q and k: RMSNorm, weight, rotate-half RoPE of the
-//                    first rotary_dim dims (angles in fp64, reduced mod 2 pi before the
-//                    fp32 sine and cosine) -> fp16 q^, k^ in the workspace;
+//                    first rotary_dim dims (angle in revolutions from an fp64 frequency
+//                    table, reduced to [-1/2, 1/2] in fp64 before the hardware sine and
+//                    cosine) -> fp16 q^, k^ in the workspace;
 //   attention_kernel one workgroup = 4 waves of 32 queries each (up to four q heads of
-//                    one kv head share it), keys in tiles of 64 through double-buffered
+//                    one kv head share it), keys in tiles of 32 through double-buffered
 //                    LDS.  It computes S^T = K^ Q^T and O^T = V^T P^T on 32x32x16 MFMA,
 //                    so a query is a column of both: its lane holds its softmax
 //                    statistics, and P^T (C layout of S^T) is already the B operand of
 //                    the second product (k slots in the permuted order the A operand V^T
-//                    reads).  Online softmax in base 2.
+//                    reads).  Online softmax in base 2; the next tile's scores are formed
+//                    while the current tile's softmax runs.
 #include "gdn_attention.h"
 #include "gdn_device.h"
 

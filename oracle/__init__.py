@@ -367,7 +367,7 @@ def attn_rms_norm(x, w, eps):
 
 def partial_rope(x, pos, rotary_dim, theta):
     """RoPE on the first rotary_dim dims of each head (model card: partial_rotary_factor
-    0.25, the rotate/nope split q[..., :rotary_dim], q[..., rotary_dim:]; field guide
+    0.25, each head split into a rotated part and a position-free part; field guide
     cutaway 03: 64 of 256 dims).  Rotate-half pairing: dim i and i + rotary_dim/2
     rotate by the angle pos * theta^(-2i/rotary_dim), i < rotary_dim/2.
     x [T, H, D], pos [T]."""

@@ -31,15 +31,39 @@ def test_algorithmic_counts():
 
 
 def test_stored_traffic_follows_the_sources():
-    # the committed PMC figures are reported only for the kernel sources they were taken on
+    # each committed PMC figure is reported only for the sources of its own kernel
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return
-    vals = dict(l.split("=", 1) for l in open(path).read().splitlines()
-                if "=" in l and not l.startswith("#"))
-    vals = {k.strip(): v.strip() for k, v in vals.items()}
-    t = bench.stored_traffic("decode_bytes_per_launch")
-    if vals.get("source_hash") == bench.source_hash():
-        assert t == int(vals["decode_bytes_per_launch"])
-    else:
-        assert t is None
+    for line in open(path).read().splitlines():
+        if "=" not in line or line.startswith("#"):
+            continue
+        key, val = (x.strip() for x in line.split("=", 1))
+        if key not in bench.TRAFFIC_SOURCES:
+            continue
+        nbytes, h = val.split()
+        t = bench.stored_traffic(key)
+        if h == bench.source_hash(key):
+            assert t == int(float(nbytes))
+        else:
+            assert t is None
+
+
+def test_stored_traffic_is_dropped_when_its_kernel_changes(tmp_path, monkeypatch):
+    # a figure whose hash does not match its kernel's sources reads as None; another
+    # kernel's figure is unaffected
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    good = bench.source_hash("decode_bytes_per_launch")
+    (prof / "traffic.txt").write_text(
+        f"decode_bytes_per_launch = 123 {good}\n"
+        "prefill_full_bytes_per_launch = 456 0000000000000000\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    csrc = tmp_path / "linear_attention_sequence_causal_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    import shutil
+    for name in os.listdir(os.path.join(ROOT, "linear_attention_sequence_causal_amd", "csrc")):
+        shutil.copy(os.path.join(ROOT, "linear_attention_sequence_causal_amd", "csrc", name), csrc)
+    assert bench.stored_traffic("decode_bytes_per_launch") == 123
+    assert bench.stored_traffic("prefill_full_bytes_per_launch") is None
+    assert bench.stored_traffic("attention_bytes_per_launch") is None

@@ -70,10 +70,11 @@ def test_packed_sequences_match_oracle():
 
 
 @gpu
-@pytest.mark.parametrize("Hq,Hkv,rot", [(4, 4, 0), (8, 1, 256), (6, 2, 16)])
+@pytest.mark.parametrize("Hq,Hkv,rot", [(4, 4, 0), (8, 1, 256), (6, 2, 16), (24, 2, 64)])
 def test_head_layouts_and_rotary_widths(Hq, Hkv, rot):
-    """Plain multi-head (ratio 1), one kv head for 8 q heads, ratio 3; no rotation, all
-    dims rotated and the narrowest rotary block."""
+    """Plain multi-head (ratio 1), one kv head for 8 q heads, ratio 3 and ratio 12 (the
+    model card's 24 query heads over 2 kv heads); no rotation, all dims rotated and the
+    narrowest rotary block."""
     _run_and_compare(_inputs([150], seed=300 + Hq, Hq=Hq, Hkv=Hkv, rotary_dim=rot),
                      cu=False, label=f"heads {Hq}/{Hkv} rot {rot}")
 
