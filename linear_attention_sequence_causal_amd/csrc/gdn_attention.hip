@@ -25,6 +25,7 @@
 #include "gdn_attention.h"
 #include "gdn_device.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace gdn {
@@ -66,14 +67,23 @@ struct RopeTable {
   double rev[kAD / 2];
 };
 
-// 256 threads = 8 rows of 256 (32 threads x 8 dims each); rows ordered token-major,
-// q heads then kv heads.
+// cu_seqlens tables up to this many entries are searched in LDS
+constexpr int kCuLds = 1024;
+
+// 256 threads = 8 rows of 256 at a time (32 threads x 8 dims each), over a grid-stride
+// loop; rows are ordered token-major, q heads then kv heads.  The next row's input is
+// loaded before the current one is processed, the norm weights once per thread, and a
+// short cu_seqlens table is searched in LDS.
 __global__ void __launch_bounds__(256)
 qk_prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                const int32_t *__restrict__ cu, int N, int T, int Hq, int Hkv,
                const float *__restrict__ wq, const float *__restrict__ wk, int rot,
                RopeTable tab, float eps, int *__restrict__ bad_word,
                _Float16 *__restrict__ qh, _Float16 *__restrict__ kh) {
+  __shared__ int s_cu[kCuLds];
+  const bool cu_lds = cu && N < kCuLds;
+  if (cu_lds)
+    for (int i = threadIdx.x; i <= N; i += blockDim.x) s_cu[i] = cu[i];
   if (blockIdx.x == 0 && bad_word) {
     // cu_seqlens check for this call: cu[0] = 0, non-decreasing, cu[N] = T
     int bad = 0;
@@ -87,61 +97,85 @@ qk_prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       if (bad) g_attn_bad_cu = 1;
     }
   }
+  __syncthreads();
   const int H = Hq + Hkv;
-  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int rows = T * H;  // below 2^27 (checked on the host)
   const int j = threadIdx.x & 31;  // dims 8j .. 8j + 7
-  if (row >= (int64_t)T * H) return;  // uniform per 32-lane row group
-  const int t = (int)(row / H), hh = (int)(row % H);
-  const bool isq = hh < Hq;
-  const bf16_t *src = isq ? q + ((int64_t)t * Hq + hh) * kAD : k + ((int64_t)t * Hkv + hh - Hq) * kAD;
-  const float *w = isq ? wq : wk;
-  const uint4 raw = *reinterpret_cast<const uint4 *>(src + 8 * j);
-  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(rw[e] << 16);
-    x[2 * e + 1] = __uint_as_float(rw[e] & 0xFFFF0000u);
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 32);
-  const float inv = rsqrtf(ss * (1.0f / kAD) + eps);
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * (w ? w[8 * j + e] : 1.0f);
-  // rotate-half RoPE on dims < rot: dim d < rot/2 pairs with d + rot/2 (8-dim groups
-  // rot/16 apart); every lane takes part in the exchange, only rotary lanes use it
-  const int half = rot >> 1, sh = half >> 3;
-  float pr[8];
+  float wqj[8], wkj[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int partner = (8 * j < half) ? j + sh : j - sh;
-    pr[e] = __shfl(y[e], (int)(threadIdx.x & 32) + (partner & 31), 64);
+    wqj[e] = wq ? wq[8 * j + e] : 1.0f;
+    wkj[e] = wk ? wk[8 * j + e] : 1.0f;
   }
-  if (8 * j < rot) {
-    const int pos = t - seq_begin(cu, N, t);
-    const bool lo = 8 * j < half;
+  const int half = rot >> 1, sh = half >> 3;
+  const bool rot_lane = 8 * j < rot, lo = 8 * j < half;
+  const int partner = lo ? j + sh : j - sh;  // the lane holding this lane's RoPE pair
+  auto src_of = [&](int row) {
+    const int t = row / H, hh = row - t * H;
+    return hh < Hq ? q + ((int64_t)t * Hq + hh) * kAD : k + ((int64_t)t * Hkv + hh - Hq) * kAD;
+  };
+  const int stride = gridDim.x * 8;
+  int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;  // uniform per 32-lane row group
+  uint4 raw = *reinterpret_cast<const uint4 *>(src_of(row) + 8 * j);
+  for (; row < rows; row += stride) {
+    const uint4 cur = raw;
+    if (row + stride < rows) raw = *reinterpret_cast<const uint4 *>(src_of(row + stride) + 8 * j);
+    const int t = row / H, hh = row - t * H;
+    const bool isq = hh < Hq;
+    const uint32_t rw[4] = {cur.x, cur.y, cur.z, cur.w};
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = (lo ? 8 * j : 8 * j - half) + e;  // frequency index
-      // angle pos * theta^(-2i/rot) in fp64, reduced to [-pi, pi] before sin/cos
-      // angle in revolutions, pos * theta^(-2i/rot) / (2 pi), reduced to [-1/2, 1/2] in
-      // fp64; the hardware sine and cosine take revolutions
-      double rv = (double)pos * tab.rev[i];
-      rv -= rint(rv);
-      const float s = __builtin_amdgcn_sinf((float)rv), c = __builtin_amdgcn_cosf((float)rv);
-      y[e] = lo ? y[e] * c - pr[e] * s : y[e] * c + pr[e] * s;
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(rw[e] << 16);
+      x[2 * e + 1] = __uint_as_float(rw[e] & 0xFFFF0000u);
     }
-  }
-  _Float16 *dst = isq ? qh + ((int64_t)t * Hq + hh) * kAD : kh + ((int64_t)t * Hkv + hh - Hq) * kAD;
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  h8 out;
+    float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (_Float16)y[e];
-  *reinterpret_cast<h8 *>(dst + 8 * j) = out;
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 32);
+    const float inv = rsqrtf(ss * (1.0f / kAD) + eps);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * (isq ? wqj[e] : wkj[e]);
+    // rotate-half RoPE on dims < rot: dim d < rot/2 pairs with d + rot/2 (8-dim groups
+    // rot/16 apart); every lane takes part in the exchange, only rotary lanes use it
+    float pr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = __shfl(y[e], (int)(threadIdx.x & 32) + (partner & 31), 64);
+    if (rot_lane) {
+      int sbeg = 0;
+      if (cu_lds) {
+        int a = 0, b = N;  // s_cu[a] <= t < s_cu[b]
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (s_cu[mid] <= t) a = mid;
+          else b = mid;
+        }
+        sbeg = s_cu[a];
+      } else {
+        sbeg = seq_begin(cu, N, t);
+      }
+      const int pos = t - sbeg;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = (lo ? 8 * j : 8 * j - half) + e;  // frequency index
+        // angle in revolutions, pos * theta^(-2i/rot) / (2 pi), reduced to [-1/2, 1/2]
+        // in fp64; the hardware sine and cosine take revolutions
+        double rv = (double)pos * tab.rev[i];
+        rv -= rint(rv);
+        const float sn = __builtin_amdgcn_sinf((float)rv), cs = __builtin_amdgcn_cosf((float)rv);
+        y[e] = lo ? y[e] * cs - pr[e] * sn : y[e] * cs + pr[e] * sn;
+      }
+    }
+    _Float16 *dst = isq ? qh + ((int64_t)t * Hq + hh) * kAD : kh + ((int64_t)t * Hkv + hh - Hq) * kAD;
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (_Float16)y[e];
+    *reinterpret_cast<h8 *>(dst + 8 * j) = out;
+  }
 }
 
 // Key tiles of 32 through double-buffered LDS: K^ [32 keys][264] fp16 and V^T [256 dims][36
@@ -479,7 +513,9 @@ hipError_t launch_attention(const void *q, const void *k, const void *v, const v
   RopeTable tab{};
   for (int i = 0; i < rotary_dim / 2; ++i)
     tab.rev[i] = std::pow((double)theta, -2.0 * i / rotary_dim) / 6.283185307179586;
-  hipLaunchKernelGGL(qk_prep_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream,
+  // a few resident workgroups per CU, each looping over rows
+  const int64_t prep_blocks = std::min<int64_t>((rows + 7) / 8, 256 * 5);
+  hipLaunchKernelGGL(qk_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream,
                      (const bf16_t *)q, (const bf16_t *)k, cu, N, (int)T, Hq, Hkv, wq, wk,
                      rotary_dim, tab, eps, bad_word, qh, kh);
   // heads per workgroup: the largest divisor of Hq / Hkv up to 4; the rest of the four
