@@ -263,3 +263,16 @@ def test_gated_attention_workspace_and_missing_device():
                                ptr(o), ctypes.c_void_p(addr), n, None)
     assert st == NO_DEVICE
     assert np.all(o == 7.0) and np.all(raw == 0)
+
+
+def test_gated_attention_size_limit_is_reported_before_anything_else():
+    """T * (Hq + Hkv) >= 2^27 is refused on the host (GDN_ERR_UNSUPPORTED), by the call and
+    by the workspace query, before any pointer or device is looked at."""
+    L = gdn.lib()
+    p = _attn_params()
+    T = (1 << 27) // 18 + 1
+    assert L.gdn_gated_attention_workspace_bytes(ctypes.byref(p), T) == ctypes.c_size_t(-1).value
+    assert L.gdn_gated_attention(None, None, None, None, ctypes.byref(p), None, 1, T, None, None,
+                                 0, None) == 2
+    assert "2^27" in L.gdn_last_error().decode()
+    assert L.gdn_gated_attention_workspace_bytes(ctypes.byref(p), T - 1) != ctypes.c_size_t(-1).value

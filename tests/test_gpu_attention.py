@@ -153,3 +153,18 @@ def test_argument_errors_are_reported_before_launch():
     k128 = torch.zeros((16, 2, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(gdn.GdnError):  # head_dim 128 is not built
         gdn.gated_attention(q128, k128, k128, q128)
+
+
+@gpu
+def test_empty_inputs():
+    """T = 0 (one empty sequence), and packed sequences that are all empty but one token
+    long: nothing to attend to is not an error, and the one token returns its gated value
+    divided by nothing else (softmax over itself)."""
+    gdn = _gdn()
+    inp = _inputs([16], seed=800)
+    z = inp["q"][:0]
+    o = gdn.gated_attention(z, inp["k"][:0], inp["v"][:0], inp["gate"][:0], rotary_dim=64)
+    assert o.shape == (0, 16, 256)
+    inp = _inputs([0, 0, 1, 0], seed=801)
+    _run_and_compare(inp, label="empty sequences around one token")
+
