@@ -37,6 +37,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                            0x00020000);
 }
 
+// kTileSeg: every segment boundary is a multiple of 32, so each 32-column MFMA tile lies in
+// one segment (a scalar lookup) and its stores are raw buffer stores: a per-lane column
+// offset, a scalar row offset, and the buffer's bound dropping rows past M.
+template <bool kTileSeg>
 __global__ void __launch_bounds__(kLinThreads, 1)
 linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, int64_t M, int N,
                    int K, LinearOut out) {
@@ -122,29 +126,64 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
 
   // epilogue: lane holds column (lane % 32) and rows 8 (r / 4) + 4 (lane / 32) + (r % 4) of
   // each 32 x 32 tile
+  if constexpr (kTileSeg) {
+    const int64_t r0 = m0 + 64 * wm;  // this wave's first row
+    const int64_t rows = M - r0 < 64 ? M - r0 : 64;
+    const int ln = lane & 31, lh = lane >> 5;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int nbase = n0 + 128 * wn + 32 * nt;
-    if (nbase >= N) continue;
-    const int col = nbase + (lane & 31);
-    if (col >= N) continue;
-    int s = 0;  // the lane's column's segment
+    for (int nt = 0; nt < 4; ++nt) {
+      const int nbase = n0 + 128 * wn + 32 * nt;  // uniform
+      if (nbase >= N || rows <= 0) continue;
+      int s = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxLinearSegs; ++i)
-      if (i < out.nseg && col >= out.col_begin[i]) s = i;
-    const int64_t cs = col - out.col_begin[s];
-    const int64_t stride = out.row_stride[s];
+      for (int i = 1; i < kMaxLinearSegs; ++i)
+        if (i < out.nseg && nbase >= out.col_begin[i]) s = i;
+      const int ncol = N - nbase < 32 ? N - nbase : 32;
+      if (ln >= ncol) continue;
+      const int64_t stride = out.row_stride[s];
+      const bool f32 = out.dtype[s] == kLinF32;
+      const int esz = f32 ? 4 : 2;
+      const __amdgpu_buffer_rsrc_t ro = rsrc(
+          (char *)out.ptr[s] + (r0 * stride + (nbase - out.col_begin[s])) * esz,
+          (uint32_t)(((rows - 1) * stride + ncol) * esz));
+      const uint32_t vo = (uint32_t)((4 * lh * stride + ln) * esz);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= M) continue;
-        const float x = acc[mt][nt][r];
-        if (out.dtype[s] == kLinF32)
-          reinterpret_cast<float *>(out.ptr[s])[row * stride + cs] = x;
-        else
-          reinterpret_cast<bf16_t *>(out.ptr[s])[row * stride + cs] = f2bf(x);
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t so = (uint32_t)((32 * mt + 8 * (r >> 2) + (r & 3)) * stride * esz);
+          const float x = acc[mt][nt][r];
+          if (f32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ro, vo, so, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), ro, vo, so, 0);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int nbase = n0 + 128 * wn + 32 * nt;
+      if (nbase >= N) continue;
+      const int col = nbase + (lane & 31);
+      if (col >= N) continue;
+      int s = 0;  // the lane's column's segment
+#pragma unroll
+      for (int i = 1; i < kMaxLinearSegs; ++i)
+        if (i < out.nseg && col >= out.col_begin[i]) s = i;
+      const int64_t cs = col - out.col_begin[s];
+      const int64_t stride = out.row_stride[s];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= M) continue;
+          const float x = acc[mt][nt][r];
+          if (out.dtype[s] == kLinF32)
+            reinterpret_cast<float *>(out.ptr[s])[row * stride + cs] = x;
+          else
+            reinterpret_cast<bf16_t *>(out.ptr[s])[row * stride + cs] = f2bf(x);
+        }
       }
     }
   }
@@ -157,16 +196,27 @@ size_t linear_lds_bytes() { return kLinLds; }
 hipError_t launch_linear_bf16(const void *A, const void *W, int64_t M, int N, int K,
                               const LinearOut &out, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)linear_bf16_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinLds);
+  bool tile_seg = true;
+  for (int i = 0; i < out.nseg; ++i) {
+    if (out.col_begin[i] % 32 != 0) tile_seg = false;
+    // the buffer-store epilogue also needs the row strides to fit its 32-bit offsets
+    if (out.row_stride[i] > (int64_t)1 << 22) tile_seg = false;
+  }
+  static bool attr[2] = {false, false};
+  const void *fn = tile_seg ? (const void *)linear_bf16_kernel<true>
+                            : (const void *)linear_bf16_kernel<false>;
+  if (!attr[tile_seg]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinLds);
     if (e != hipSuccess) return e;
-    attr = true;
+    attr[tile_seg] = true;
   }
   const int64_t blocks = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(linear_bf16_kernel, dim3((unsigned)blocks), dim3(kLinThreads), kLinLds,
-                     stream, (const bf16_t *)A, (const bf16_t *)W, M, N, K, out);
+  if (tile_seg)
+    hipLaunchKernelGGL(linear_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kLinThreads), kLinLds,
+                       stream, (const bf16_t *)A, (const bf16_t *)W, M, N, K, out);
+  else
+    hipLaunchKernelGGL(linear_bf16_kernel<false>, dim3((unsigned)blocks), dim3(kLinThreads),
+                       kLinLds, stream, (const bf16_t *)A, (const bf16_t *)W, M, N, K, out);
   return hipGetLastError();
 }
 

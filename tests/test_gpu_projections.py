@@ -73,11 +73,14 @@ def test_linear_integer_inputs_are_bitwise(M, N, K):
 
 
 @gpu
-def test_in_projection_scatters_into_the_mixer_inputs():
-    """All six outputs against the oracle's split (bitwise with integer inputs, with
-    column ranges that are not multiples of the 32-column tile), then random inputs."""
+@pytest.mark.parametrize("Hk,Hv", [(2, 4), (2, 32)])
+def test_in_projection_scatters_into_the_mixer_inputs(Hk, Hv):
+    """All six outputs against the oracle's split (bitwise with integer inputs), then
+    random inputs.  With Hv = 4 the a and b column ranges are not multiples of the
+    32-column tile (the per-lane epilogue); with Hv = 32 every range is, and the epilogue
+    stores each tile through one buffer (bf16 q, k, v, z and fp32 a, b)."""
     gdn = _gdn()
-    T, d_model, Hk, Hv, D = 333, 192, 2, 4, 128
+    T, d_model, D = 333, 192, 128
     n_in = 2 * Hk * D + 2 * Hv * D + 2 * Hv
     x, w = _ints((T, d_model), 5000, -1, 1), _ints((n_in, d_model), 5001, -1, 1)
     outs = gdn.in_projection(x, w, Hk, Hv, D)
