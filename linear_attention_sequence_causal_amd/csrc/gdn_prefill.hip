@@ -408,7 +408,9 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   int vbase = (tid >> 5) * 4;          // v tokens vbase .. vbase+3
   // Re-derive the lane coordinates behind an optimisation barrier after every
   // workgroup barrier, so that LDS addresses are formed next to their use
-  // instead of being hoisted out of the chunk loop (and spilled).
+  // instead of being hoisted out of the chunk loop (and spilled).  The v-conv
+  // coordinates (cv, vbase) are left to the compiler: it keeps their addresses in
+  // registers without spilling (221 VGPRs), which measured ~1 % faster.
   auto refresh = [&]() {
     tid = opaque(tid);
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,8 +419,6 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     lg = lane >> 4;
     cg = opaque(cg);
     tbase = opaque(tbase);
-    cv = opaque(cv);
-    vbase = opaque(vbase);
   };
   const bool qk_on = MODE == kFull || role == 1;
   const bool v_on = withV;
