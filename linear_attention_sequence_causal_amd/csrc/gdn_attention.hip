@@ -24,6 +24,7 @@
 //                    while the current tile's softmax runs.
 #include "gdn_attention.h"
 #include "gdn_device.h"
+#include "gdn_launch.h"
 
 #include <algorithm>
 #include <cmath>
@@ -529,13 +530,10 @@ hipError_t launch_attention(const void *q, const void *k, const void *v, const v
   const int64_t nqb = (T + span - 1) / span;
   const int64_t pairs = nqb * Hkv;
   const int64_t blocks = (pairs + 7) / 8 * 8 * (r / hpb);
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)attention_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAttnLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void *)attention_kernel, (int)kAttnLds, lds_set);
+      e != hipSuccess)
+    return e;
   hipLaunchKernelGGL(attention_kernel, dim3((unsigned)blocks), dim3(256), kAttnLds, stream,
                      (const _Float16 *)qh, (const _Float16 *)kh, (const bf16_t *)v,
                      (const bf16_t *)gate, cu, N, (int)T, Hq, Hkv, hpb, qpb,

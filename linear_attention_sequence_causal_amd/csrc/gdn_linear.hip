@@ -16,6 +16,7 @@
 // v_mfma_f32_32x32x16_bf16 per 16-wide k slice (128 accumulators per lane).
 #include "gdn_device.h"
 #include "gdn_linear.h"
+#include "gdn_launch.h"
 
 namespace gdn {
 
@@ -202,14 +203,11 @@ hipError_t launch_linear_bf16(const void *A, const void *W, int64_t M, int N, in
     // the buffer-store epilogue also needs the row strides to fit its 32-bit offsets
     if (out.row_stride[i] > (int64_t)1 << 22) tile_seg = false;
   }
-  static bool attr[2] = {false, false};
+  static std::atomic<uint64_t> lds_set[2];
   const void *fn = tile_seg ? (const void *)linear_bf16_kernel<true>
                             : (const void *)linear_bf16_kernel<false>;
-  if (!attr[tile_seg]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinLds);
-    if (e != hipSuccess) return e;
-    attr[tile_seg] = true;
-  }
+  if (hipError_t e = ensure_lds_limit(fn, (int)kLinLds, lds_set[tile_seg]); e != hipSuccess)
+    return e;
   const int64_t blocks = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   if (tile_seg)
     hipLaunchKernelGGL(linear_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kLinThreads), kLinLds,

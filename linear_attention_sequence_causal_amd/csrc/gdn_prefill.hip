@@ -35,6 +35,7 @@
 // runs the full chunk loop of every segment from its start state.
 #include "gdn_device.h"
 #include "gdn_prefill_plan.h"
+#include "gdn_launch.h"
 
 namespace gdn {
 
@@ -1391,17 +1392,13 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
                                int N, int64_t Ttot, void *conv_out, hipStream_t stream,
                                PrefillTiming *tm) {
   const int Hv = args.Hv;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e;
-    e = hipFuncSetAttribute((const void *)chunk_kernel<T, kFull>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)chunk_kernel<T, kMap>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set[2];
+  if (hipError_t e = ensure_lds_limit((const void *)chunk_kernel<T, kFull>, kLdsBytes, lds_set[0]);
+      e != hipSuccess)
+    return e;
+  if (hipError_t e = ensure_lds_limit((const void *)chunk_kernel<T, kMap>, kLdsBytes, lds_set[1]);
+      e != hipSuccess)
+    return e;
   auto mark = [&](int slot) {  // event after kernel slot-1 (slot 0 = start)
     if (tm) (void)hipEventRecord(tm->ev[slot], stream);
   };
