@@ -111,22 +111,17 @@ __device__ __forceinline__ u16x8 cat4(u16x4 x, u16x4 y) {
 }
 
 // --------------------------------------------------------------------- LDS
-// One workgroup = 4 waves; two workgroups share a compute unit (LDS <= 80 KB and
-// <= 256 VGPRs each), so one's VALU-heavy prologue/epilogue overlaps the other's
-// LDS- and MFMA-heavy chain.
-constexpr int kThreads = 256;  // 4 waves
+// A workgroup runs NH v heads of one q/k head with 4 waves per v head.  NH = 1: two
+// workgroups share a compute unit (LDS <= 80 KB and <= 256 VGPRs each), so one's
+// VALU-heavy prologue/epilogue overlaps the other's LDS- and MFMA-heavy chain.
+// NH = 2: one 8-wave workgroup per compute unit; the q/k prologue (conv, SiLU, L2
+// norm, the fp16 tiles) is computed once for both v heads.
+constexpr int kThreads = 256;  // 4 waves per v head
 constexpr int kWaves = 4;
 constexpr int kRowS = 136;     // bf16 row stride of [32 tok][128 d] tiles (272 B)
 constexpr int kTokS = 36;      // 16-bit row stride of the [128 d][32 tok] K^T tile (72 B)
 constexpr int kSqS = 36;       // bf16 row stride of [32][32] tiles (M, -L)
-
-constexpr int OFF_QF = 0;                            // fp16 unit-norm q (Q K^T, Q H)
-constexpr int OFF_KF = OFF_QF + kChunk * kRowS * 2;  // fp16 unit-norm k (K K^T, Q K^T)
-constexpr int OFF_M = OFF_KF + kChunk * kRowS * 2;   // bf16 [32][36] M with zero diagonal
-constexpr int OFF_KT = OFF_M + kChunk * kSqS * 2;   // fp16 K^T [128 dk][32 tok]
 constexpr int kVtS = 36;       // fp32 row stride of the [128 dv][32 tok] V^T tile (144 B)
-constexpr int OFF_VT = OFF_KT + 128 * kTokS * 2;
-constexpr int OFF_CONVW = OFF_VT + 128 * kVtS * 4;
 constexpr float kConvScale = -1.4426950408889634f;  // -log2(e), folded into the conv taps
 constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no bank conflicts)
 // Per-token gate vectors of a chunk, two buffers (chunk parity): the next chunk's
@@ -134,28 +129,40 @@ constexpr int kConvGS = 36;  // fp32 stride of 8 channels x 4 taps (padded: no b
 // k * kChunk: beta, G (cumsum of g), gamma = e^G, beta gamma, e^{G_C - G},
 // beta / kConvScale (multiplies scaled v).
 enum { GB_BETA = 0, GB_G, GB_GAM, GB_BG, GB_DEC, GB_BV, GB_N };
-constexpr int kGateN = GB_N * kChunk;                // floats per buffer
-constexpr int OFF_GATES = OFF_CONVW + 48 * kConvGS * 4;
-constexpr int OFF_MDIAG = OFF_GATES + 2 * kGateN * 4;
-constexpr int OFF_NW = OFF_MDIAG + kChunk * 4;       // fp32 [128] RMSNorm weight (1 if none)
-// -L and the diagonal blocks of T have their own regions, so the waves that form
-// them need not wait for the gram products of the others
-constexpr int kTdS = 24;                             // bf16 row stride of (T_bb - I) blocks
-constexpr int OFF_LO = OFF_NW + kD * 4;              // bf16 [32][36]  -L (strictly lower)
-constexpr int OFF_TD = OFF_LO + kChunk * kSqS * 2;   // bf16 [2][16][24] T_bb - I
-static_assert(OFF_TD % 16 == 0, "T_bb blocks must be 16-byte aligned");
-constexpr int kLdsBytes = OFF_TD + 2 * 16 * kTdS * 2;
-// fp32 [32 tok][132] o tile for the epilogue, in the V^T region (dead after the
-// right-hand side; the next chunk writes V^T only after its first barrier)
-constexpr int kOS = 132;
-constexpr int OFF_O = OFF_VT;
-static_assert(kChunk * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
-// map mode's per-chunk log-decays (before the chunk loop), also in the V^T region
-constexpr int OFF_CHG = OFF_VT;
-constexpr int kMaxSegChunks = 256;                   // segments hold at most 8192 tokens
-static_assert(kMaxSegChunks * 4 <= 128 * kVtS * 4, "chunk sums overflow the V^T region");
-constexpr int OFF_W = OFF_KF;                        // bf16 [32][136] -W (K tile dead then)
-static_assert(2 * kLdsBytes <= 160 * 1024, "LDS budget of two workgroups per compute unit");
+constexpr int kGateN = GB_N * kChunk;  // floats per buffer
+constexpr int kTdS = 24;               // bf16 row stride of (T_bb - I) blocks
+constexpr int kOS = 132;               // fp32 row stride of the [32 tok][128] o tile
+constexpr int kMaxSegChunks = 256;     // segments hold at most 8192 tokens
+
+// Byte offsets.  Shared by the workgroup's v heads: the fp16 unit-norm q and k rows,
+// the fp16 K^T tile, the conv taps of q, k and every v head, the RMSNorm weight.  One
+// block per v head: V^T (fp32; the o tile of the epilogue and map mode's chunk sums
+// reuse it), M, the gate buffers, M's diagonal, -L and T_bb - I (regions of their
+// own, so the waves that form them need not wait for the others' gram products).
+// -W of head slot 0 reuses the k rows (dead after the gram products); slot 1 has its
+// own.
+template <int NH> struct Lds {
+  static constexpr int QF = 0;                           // fp16 q [32][136] (Q K^T, Q H)
+  static constexpr int KF = QF + kChunk * kRowS * 2;     // fp16 k [32][136] (K K^T, Q K^T)
+  static constexpr int KT = KF + kChunk * kRowS * 2;     // fp16 K^T [128 dk][32 tok]
+  static constexpr int CONVW = KT + 128 * kTokS * 2;     // taps: q, k, then each v head
+  static constexpr int NW = CONVW + (32 + 16 * NH) * kConvGS * 4;  // fp32 [128]
+  static constexpr int HEAD = NW + kD * 4;               // first per-head block
+  static constexpr int H_VT = 0;                         // fp32 V^T [128 dv][36]
+  static constexpr int H_M = H_VT + 128 * kVtS * 4;      // fp16 [32][36] M, zero diagonal
+  static constexpr int H_GATES = H_M + kChunk * kSqS * 2;
+  static constexpr int H_MDIAG = H_GATES + 2 * kGateN * 4;
+  static constexpr int H_LO = H_MDIAG + kChunk * 4;      // fp16 [32][36] -L (strictly lower)
+  static constexpr int H_TD = H_LO + kChunk * kSqS * 2;  // fp16 [2][16][24] T_bb - I
+  static constexpr int H_BYTES = H_TD + 2 * 16 * kTdS * 2;
+  static constexpr int W1 = HEAD + NH * H_BYTES;         // fp16 [32][136] -W of slot 1
+  static constexpr int BYTES = W1 + (NH == 2 ? kChunk * kRowS * 2 : 0);
+  static_assert(HEAD % 16 == 0 && H_BYTES % 16 == 0 && H_TD % 16 == 0, "16-byte tiles");
+  static_assert(kChunk * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
+  static_assert(kMaxSegChunks * 4 <= 128 * kVtS * 4, "chunk sums overflow the V^T region");
+  static_assert(NH == 2 ? BYTES <= 160 * 1024 : 2 * BYTES <= 160 * 1024,
+                "LDS budget: two 4-wave or one 8-wave workgroup per compute unit");
+};
 static_assert(kChunk == 32, "the tile code below is written for 32-token chunks");
 
 enum Mode { kFull = 0, kMap = 1 };
@@ -337,15 +344,28 @@ __device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4 &mc, const f32
 // MODE kFull: the whole mixer for one (segment, v head).  MODE kMap: the
 // segment's affine map; blockIdx selects the A half (state columns of the
 // identity) or the B half (columns of zero with the values written in).
-template <typename T, int MODE>
-__global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
+template <typename T, int MODE, int NH>
+__global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArgs P) {
+  static_assert(NH == 1 || (NH == 2 && MODE == kFull), "two v heads per workgroup: full pass");
+  typedef Lds<NH> L;
+  constexpr int kTh = kThreads * NH;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // Physical wave pw = tid / 64; head slot hh = pw / 4; wave = the role within the head
+  // (state columns 32 wave.., gram tile, gates).  The second head's roles are rotated by
+  // two, so that each SIMD (waves pw and pw + 4) holds one of the diagonal-tile waves
+  // (roles 0, 1) and one of the others.
   int tid = threadIdx.x;
-  int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  int hh = 0, wave, lane = tid & 63;
+  auto roles = [&]() {
+    const int pw = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hh = NH == 2 ? pw >> 2 : 0;
+    wave = NH == 2 ? (pw + 2 * hh) & 3 : pw;
+  };
+  roles();
   int ln = lane & 15, lg = lane >> 4;  // MFMA lane coordinates
   const int Hv = P.Hv, Hk = P.Hk;
   // Workgroup ids go round-robin over the 8 XCDs (each with its own L2).  The
-  // r = Hv/Hk v heads that read the same q/k head get ids 8 apart, i.e. the same
+  // r / NH workgroups that read the same q/k head get ids 8 apart, i.e. the same
   // XCD at nearly the same time, so their shared q/k rows are fetched once.
   int h, unit, half = 0;
   {
@@ -357,11 +377,11 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       half = bid < hgrid ? 1 : 0;  // 0: A columns, 1: B columns
       bid -= half ? 0 : hgrid;
     }
-    const int r = Hv / Hk;
+    const int r = Hv / Hk, rw = r / NH;
     const int x = bid & 7, y = bid >> 3;
-    const int member = y % r;
-    const int pair = (y / r) * 8 + x;  // (unit, q/k head) index
-    h = (pair % Hk) * r + member;
+    const int member = y % rw;
+    const int pair = (y / rw) * 8 + x;  // (unit, q/k head) index
+    h = (pair % Hk) * r + member * NH + hh;
     unit = pair / Hk;
   }
   const int gq = h / (Hv / Hk);
@@ -379,42 +399,47 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   const int seq_begin = seg.seq_begin;
   const int seg_end = seg.begin + seg.len;
 
-  bf16_t *const sQf = reinterpret_cast<bf16_t *>(smem + OFF_QF);  // fp16 bits
-  bf16_t *const sKf = reinterpret_cast<bf16_t *>(smem + OFF_KF);  // fp16 bits
-  bf16_t *const sKT = reinterpret_cast<bf16_t *>(smem + OFF_KT);  // fp16 bits
-  float *const sVT = reinterpret_cast<float *>(smem + OFF_VT);
-  float *const sConvW = reinterpret_cast<float *>(smem + OFF_CONVW);
-  float *const sGates = reinterpret_cast<float *>(smem + OFF_GATES);
-  float *const sMdiag = reinterpret_cast<float *>(smem + OFF_MDIAG);
-  float *const sNW = reinterpret_cast<float *>(smem + OFF_NW);
-  float *const sO = reinterpret_cast<float *>(smem + OFF_O);
-  bf16_t *const sLo = reinterpret_cast<bf16_t *>(smem + OFF_LO);
-  bf16_t *const sTd = reinterpret_cast<bf16_t *>(smem + OFF_TD);
-  bf16_t *const sM = reinterpret_cast<bf16_t *>(smem + OFF_M);
-  bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + OFF_W);
+  unsigned char *const hblk = smem + L::HEAD + hh * L::H_BYTES;  // this head's block
+  bf16_t *const sQf = reinterpret_cast<bf16_t *>(smem + L::QF);  // fp16 bits
+  bf16_t *const sKf = reinterpret_cast<bf16_t *>(smem + L::KF);  // fp16 bits
+  bf16_t *const sKT = reinterpret_cast<bf16_t *>(smem + L::KT);  // fp16 bits
+  float *const sConvW = reinterpret_cast<float *>(smem + L::CONVW);
+  float *const sNW = reinterpret_cast<float *>(smem + L::NW);
+  float *const sVT = reinterpret_cast<float *>(hblk + L::H_VT);
+  float *const sO = sVT;  // the o tile (V^T is dead after the right-hand sides)
+  float *const sGates = reinterpret_cast<float *>(hblk + L::H_GATES);
+  float *const sMdiag = reinterpret_cast<float *>(hblk + L::H_MDIAG);
+  bf16_t *const sLo = reinterpret_cast<bf16_t *>(hblk + L::H_LO);
+  bf16_t *const sTd = reinterpret_cast<bf16_t *>(hblk + L::H_TD);
+  bf16_t *const sM = reinterpret_cast<bf16_t *>(hblk + L::H_M);
+  bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + (hh ? L::W1 : L::KF));
 
   // ---- roles of the prologue ----------------------------------------------------
-  // Before the first barrier every wave convolves q (waves 0-1) or k (waves 2-3):
-  // 4 tokens x 8 channels per thread, the 16 lanes of a token row spanning its
-  // 128 channels (for the L2 norm).  After it every thread convolves 4 tokens x
-  // 4 channels of v, which only the right-hand side (after barrier 3) reads.
-  // Map mode needs no q (and no v for the A half).
+  // Before the first barrier every wave convolves q (roles 0-1) or k (roles 2-3):
+  // TPT tokens x 8 channels per thread, the 16 lanes of a token row spanning its 128
+  // channels (for the L2 norm); the q/k wave qi of a kind takes tokens 16 qi / NH ..
+  // After it every thread convolves 4 tokens x 4 channels of its head's v, which only
+  // the right-hand side (after barrier 3) reads.  Map mode needs no q (and no v for
+  // the A half).
+  constexpr int TPT = 4 / NH;          // q/k tokens per thread
   const int role = wave < 2 ? 0 : 1;   // uniform per wave
-  int cg = tid & 15;                   // q/k channels 8cg .. 8cg+7
-  int tbase = ((tid & 127) >> 4) * 4;  // q/k tokens tbase .. tbase+3
-  // v channels 4cv .. 4cv+3; cv rotates the 5 lane bits so that the 8 lanes of one
-  // 16-byte LDS write cycle take cv values 4 apart: their V^T rows 4cv + cc lie in
-  // 8 different 16-row blocks, which the tile's swizzle spreads over all banks
-  int cv = ((tid & 7) << 2) | ((tid >> 3) & 3);
-  int vbase = (tid >> 5) * 4;          // v tokens vbase .. vbase+3
+  int cg = lane & 15;                  // q/k channels 8cg .. 8cg+7
+  int tbase = TPT * (4 * (NH == 2 ? 2 * hh + (wave & 1) : (wave & 1)) + (lane >> 4));
+  // v channels 4cv .. 4cv+3 of the head, ht = the thread's index among its head's 256;
+  // cv rotates the 5 lane bits so that the 8 lanes of one 16-byte LDS write cycle take
+  // cv values 4 apart: their V^T rows 4cv + cc lie in 8 different 16-row blocks, which
+  // the tile's swizzle spreads over all banks
+  const int ht = wave * 64 + lane;
+  int cv = ((ht & 7) << 2) | ((ht >> 3) & 3);
+  int vbase = (ht >> 5) * 4;           // v tokens vbase .. vbase+3
   // Re-derive the lane coordinates behind an optimisation barrier after every
   // workgroup barrier, so that LDS addresses are formed next to their use
   // instead of being hoisted out of the chunk loop (and spilled).  The v-conv
   // coordinates (cv, vbase) are left to the compiler: it keeps their addresses in
-  // registers without spilling (221 VGPRs), which measured ~1 % faster.
+  // registers without spilling, which measured ~1 % faster.
   auto refresh = [&]() {
     tid = opaque(tid);
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    roles();
     lane = tid & 63;
     ln = lane & 15;
     lg = lane >> 4;
@@ -424,13 +449,13 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
   const bool qk_on = MODE == kFull || role == 1;
   const bool v_on = withV;
 
-  // conv weights of this head's 384 channels -> LDS (q 0..127, k 128..255, v 256..383)
-  for (int i = tid; i < 384 * 4; i += kThreads) {
+  // conv taps -> LDS: q channels 0..127, k 128..255, then 128 per v head of the workgroup
+  for (int i = tid; i < (256 + 128 * NH) * 4; i += kTh) {
     const int ch = i >> 2, tap = i & 3;
     int64_t c;
     if (ch < 128) c = (int64_t)gq * kD + ch;
     else if (ch < 256) c = (int64_t)Hk * kD + (int64_t)gq * kD + (ch - 128);
-    else c = 2LL * Hk * kD + (int64_t)h * kD + (ch - 256);
+    else c = 2LL * Hk * kD + (int64_t)(h - hh) * kD + (ch - 256);
     sConvW[(ch >> 3) * kConvGS + (ch & 7) * 4 + tap] = P.conv_w[c * 4 + tap] * kConvScale;
   }
 
@@ -445,10 +470,12 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     vhist = hs + 2LL * Hk * kD + (int64_t)h * kD + cv * 4;
   }
 
-  // raw rows for one chunk: rows base-3 .. base+3 relative to the chunk start
+  // raw rows for one chunk: rows base-3 .. base+TPT-1 (q/k), base-3 .. base+3 (v)
+  // relative to the chunk start
   typedef RawN<T, 8> RQ;
   typedef RawN<T, 4> RV;
-  uint32_t raw[7][RQ::W], vraw[7][RV::W];
+  constexpr int kQR = TPT + 3;
+  uint32_t raw[kQR][RQ::W], vraw[7][RV::W];
   // Interior chunks use one buffer per stream (rows at or past the segment end
   // read as zero); chunks that start within 3 rows of the sequence start take
   // rows before it from the conv history (or zero them at use) and clamp rows
@@ -461,7 +488,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         const rsrc_t rs = buf(src + (int64_t)(t0 - 3) * qk_stride, nrows * rowb);
         const uint32_t lo = (uint32_t)(tbase * rowb + cg * 8 * (int)sizeof(T));
 #pragma unroll
-        for (int rr = 0; rr < 7; ++rr) RQ::load_buf(raw[rr], rs, lo + rr * rowb);
+        for (int rr = 0; rr < kQR; ++rr) RQ::load_buf(raw[rr], rs, lo + rr * rowb);
       }
       if (v_on) {
         const int rowb = v_stride * (int)sizeof(T);
@@ -471,15 +498,18 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
         for (int rr = 0; rr < 7; ++rr) RV::load_buf(vraw[rr], rs, lo + rr * rowb);
       }
     } else {
+      if (qk_on) {
 #pragma unroll
-      for (int rr = 0; rr < 7; ++rr) {
-        if (qk_on) {
+        for (int rr = 0; rr < kQR; ++rr) {
           const int tau = t0 + tbase - 3 + rr;
           const int tc = min(max(tau, seq_begin), seg_end - 1);
           RQ::load(raw[rr], (tau < seq_begin && hist) ? hist + (3 + tau - seq_begin) * P.Cc
                                                       : src + (int64_t)tc * qk_stride + cg * 8);
         }
-        if (v_on) {
+      }
+      if (v_on) {
+#pragma unroll
+        for (int rr = 0; rr < 7; ++rr) {
           const int tau = t0 + vbase - 3 + rr;
           const int tc = min(max(tau, seq_begin), seg_end - 1);
           RV::load(vraw[rr], (tau < seq_begin && vhist) ? vhist + (3 + tau - seq_begin) * P.Cc
@@ -591,7 +621,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     // where it does is the truncation point of the B map, and then the whole
     // segment's sum is below the threshold too: the A map is zero.  Only if no
     // suffix reaches it does the scan cover every chunk (A and B need them all).
-    float *sChG = reinterpret_cast<float *>(smem + OFF_CHG);
+    float *sChG = sVT;  // V^T is not in use before the chunk loop
     const float thr = -69.31471805599453f;  // ln 2^-100
     float S = 0.f;
     bool reached = false;
@@ -658,18 +688,19 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     if (MODE == kFull && wave >= 2) __builtin_amdgcn_s_setprio(1);
     if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
-      for (int rr = 0; rr < 7; ++rr) {
+      for (int rr = 0; rr < kQR; ++rr)
         if (t0 + tbase - 3 + rr < seq_begin)
 #pragma unroll
           for (int w = 0; w < RQ::W; ++w) raw[rr][w] = 0u;
+#pragma unroll
+      for (int rr = 0; rr < 7; ++rr)
         if (t0 + vbase - 3 + rr < seq_begin)
 #pragma unroll
           for (int w = 0; w < RV::W; ++w) vraw[rr][w] = 0u;
-      }
     }
-    if (qk_on) {  // q or k: 4 tokens x 8 channels, L2 over the head's 128 channels
-      float x[4][8];
-      conv_silu_rows<T, 4, 8>(raw, sConvW + (role * 16 + cg) * kConvGS, x);
+    if (qk_on) {  // q or k: TPT tokens x 8 channels, L2 over the head's 128 channels
+      float x[TPT][8];
+      conv_silu_rows<T, TPT, 8>(raw, sConvW + (role * 16 + cg) * kConvGS, x);
       // x = kConvScale SiLU(u): dividing by the norm of x takes out |kConvScale|,
       // the sign is applied here and eps scales with kConvScale^2.  q and k stay
       // unit-norm (q_scale multiplies the products that use q instead), so their
@@ -677,7 +708,7 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       const float scale0 = -1.0f;
       const float eps = P.l2_eps * (kConvScale * kConvScale);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < TPT; ++r) {
         float ss = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
@@ -688,39 +719,31 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
       }
       // fp16 rows of q (the gram products and Q H) or k (the gram products), and the
       // fp16 k rows regrouped into K^T (right-hand side and state update)
-      if (role == 0) {
+      uint32_t fw[TPT][4];  // token r: fp16 channels (2e, 2e+1) in word e
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t fw[4];
+      for (int r = 0; r < TPT; ++r) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fw[e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
-          *reinterpret_cast<uint4 *>(sQf + (tbase + r) * kRowS + cg * 8) =
-              make_uint4(fw[0], fw[1], fw[2], fw[3]);
+        for (int e = 0; e < 4; ++e) fw[r][e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
+        *reinterpret_cast<uint4 *>((role == 0 ? sQf : sKf) + (tbase + r) * kRowS + cg * 8) =
+            make_uint4(fw[r][0], fw[r][1], fw[r][2], fw[r][3]);
+      }
+      if (role == 1) {
+        // K^T [dk][tok]: fp16 k regrouped by channel, 2 bytes per token; rows 8cg + cc
+        // (cc < 8) share row >> 4 = cg >> 1.  Tokens (2p, 2p+1) of channel cc are half
+        // (cc & 1) of word cc/2 of tokens 2p, 2p+1.  The 4-token group tbase >> 2 is
+        // swizzled; TPT = 2 fills half of it (4 bytes), TPT = 4 all of it (8 bytes).
+        const int swz = ((((tbase >> 2) ^ (cg >> 1)) & 7) << 2) + (tbase & 2);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+          const int e = cc >> 1;
+          bf16_t *const dst = sKT + (cg * 8 + cc) * kTokS + swz;
+          if constexpr (TPT == 4)
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(__builtin_amdgcn_perm(fw[1][e], fw[0][e], sel),
+                                                         __builtin_amdgcn_perm(fw[3][e], fw[2][e], sel));
+          else
+            *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(fw[1][e], fw[0][e], sel);
         }
-      } else {
-        // K^T [dk][tok]: fp16 k regrouped by channel, 8 bytes (4 tokens) per row;
-        // rows 8cg + cc (cc < 8) share row >> 4 = cg >> 1.  Tokens (2p, 2p+1) of
-        // channel cc are half (cc & 1) of word cc/2 of tokens 2p, 2p+1.
-        const int swz = (((tbase >> 2) ^ (cg >> 1)) & 7) << 2;
-        auto put_kt = [&](bf16_t *tile, const uint32_t (&w)[4][4]) {
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-            const int e = cc >> 1;
-            *reinterpret_cast<uint2 *>(tile + (cg * 8 + cc) * kTokS + swz) =
-                make_uint2(__builtin_amdgcn_perm(w[1][e], w[0][e], sel),
-                           __builtin_amdgcn_perm(w[3][e], w[2][e], sel));
-          }
-        };
-        uint32_t fw[4][4];  // token r: fp16 channels (2e, 2e+1) in word e
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fw[r][e] = pk_f16(x[r][2 * e], x[r][2 * e + 1]);
-          *reinterpret_cast<uint4 *>(sKf + (tbase + r) * kRowS + cg * 8) =
-              make_uint4(fw[r][0], fw[r][1], fw[r][2], fw[r][3]);
-        }
-        put_kt(sKT, fw);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -730,7 +753,8 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
 
     if (v_on) {  // v: 4 tokens x 4 channels -> fp32 V^T [dv][tok], 16 bytes per channel
       float x[4][4];
-      conv_silu_rows<T, 4, 4>(vraw, sConvW + (32 + (cv >> 1)) * kConvGS + (cv & 1) * 16, x);
+      conv_silu_rows<T, 4, 4>(vraw, sConvW + (32 + 16 * hh + (cv >> 1)) * kConvGS + (cv & 1) * 16,
+                              x);
       // rows 4cv + cc share row >> 4 = cv >> 2; vbase = 4 * (4-token group)
       const int swz = ((vbase >> 2) ^ ((cv >> 2) & 7)) << 2;
 #pragma unroll
@@ -742,15 +766,16 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     // this chunk's gate z (raw bits, consumed by the epilogue) and the next chunk's
     // raw rows (consumed by the next prologue) stay in flight during the math; z is
     // issued first so that waiting for it never waits for the prefetch
-    // epilogue layout: token tid >> 3, columns 8e..8e+7 and 64+8e..64+8e+7 with
-    // e = tid & 7 (two 16-byte bf16 blocks per thread for z and o)
+    // epilogue layout: token ht >> 3, columns 8e..8e+7 and 64+8e..64+8e+7 with
+    // e = ht & 7 (two 16-byte bf16 blocks per thread for z and o)
     typedef RawN<T, 8> RZ;
     uint32_t zw[2][RZ::W];
     if (MODE == kFull) {
       // one buffer over this chunk's rows (uniform); tokens at or past nvalid read as zero
       const int rowb = Hv * kD * (int)sizeof(T);
       const rsrc_t zs = buf((const T *)P.z + ((int64_t)t0 * Hv + h) * kD, nvalid * rowb);
-      const uint32_t zo = (uint32_t)((tid >> 3) * rowb + 8 * (tid & 7) * (int)sizeof(T));
+      const int zt = wave * 64 + lane;
+      const uint32_t zo = (uint32_t)((zt >> 3) * rowb + 8 * (zt & 7) * (int)sizeof(T));
       RZ::load_buf(zw[0], zs, zo);
       RZ::load_buf(zw[1], zs, zo + 64 * (int)sizeof(T));
     }
@@ -1048,9 +1073,10 @@ __global__ void __launch_bounds__(kThreads, 2) chunk_kernel(PrefillArgs P) {
     __syncthreads();  // (5) o tile ready; this chunk's other LDS tiles are consumed
     refresh();
     if (MODE == kFull) {
-      // token tid >> 3 (8 lanes per token), columns 8e.. and 64+8e.. with e = tid & 7;
+      // token ht >> 3 (8 lanes per token), columns 8e.. and 64+8e.. with e = ht & 7;
       // the four 16-byte reads of a row are bank-conflict free with kOS = 132
-      const int etok = tid >> 3, e8 = 8 * (tid & 7);
+      const int et = wave * 64 + lane;
+      const int etok = et >> 3, e8 = 8 * (et & 7);
       const float *orow = sO + etok * kOS;
       float ov[16], nw[16];
       {
@@ -1392,11 +1418,17 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
                                int N, int64_t Ttot, void *conv_out, hipStream_t stream,
                                PrefillTiming *tm) {
   const int Hv = args.Hv;
-  static std::atomic<uint64_t> lds_set[2];
-  if (hipError_t e = ensure_lds_limit((const void *)chunk_kernel<T, kFull>, kLdsBytes, lds_set[0]);
-      e != hipSuccess)
+  // the full pass runs two v heads per workgroup (one shared q/k prologue) when the
+  // v heads of a q/k head pair up
+  const bool pairs = (Hv / args.Hk) % 2 == 0;
+  static std::atomic<uint64_t> lds_set[3];
+  const void *full_fn = pairs ? (const void *)chunk_kernel<T, kFull, 2>
+                              : (const void *)chunk_kernel<T, kFull, 1>;
+  const int full_lds = pairs ? Lds<2>::BYTES : Lds<1>::BYTES;
+  if (hipError_t e = ensure_lds_limit(full_fn, full_lds, lds_set[pairs ? 2 : 0]); e != hipSuccess)
     return e;
-  if (hipError_t e = ensure_lds_limit((const void *)chunk_kernel<T, kMap>, kLdsBytes, lds_set[1]);
+  if (hipError_t e = ensure_lds_limit((const void *)chunk_kernel<T, kMap, 1>, Lds<1>::BYTES,
+                                      lds_set[1]);
       e != hipSuccess)
     return e;
   auto mark = [&](int slot) {  // event after kernel slot-1 (slot 0 = start)
@@ -1407,14 +1439,14 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
   if (tm) for (int i = 0; i < kTimedKernels; ++i) tm->ran[i] = false;
   if (tm) tm->ran[0] = true;  // the segment table was launched by the caller
   mark(1);
-  // grids cover ceil(units * Hk / 8) * 8 * r ids (see the id mapping in chunk_kernel)
-  auto ids = [&](int64_t units) {
-    const int64_t pairs = units * args.Hk;
-    return ((pairs + 7) / 8) * 8 * (Hv / args.Hk);
+  // grids cover ceil(units * Hk / 8) * 8 * r / NH ids (see the id mapping in chunk_kernel)
+  auto ids = [&](int64_t units, int nh) {
+    const int64_t n = units * args.Hk;
+    return ((n + 7) / 8) * 8 * (Hv / args.Hk / nh);
   };
   if (plan.max_maps > 0) {
-    dim3 g1((unsigned)(ids(plan.max_maps) * 2));
-    hipLaunchKernelGGL((chunk_kernel<T, kMap>), g1, dim3(kThreads), kLdsBytes, stream, args);
+    dim3 g1((unsigned)(ids(plan.max_maps, 1) * 2));
+    hipLaunchKernelGGL((chunk_kernel<T, kMap, 1>), g1, dim3(kThreads), Lds<1>::BYTES, stream, args);
     mark(2);
     dim3 g2((unsigned)((int64_t)N * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
@@ -1426,8 +1458,12 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     mark(2);
     mark(3);
   }
-  dim3 g3((unsigned)ids(plan.max_segments));
-  hipLaunchKernelGGL((chunk_kernel<T, kFull>), g3, dim3(kThreads), kLdsBytes, stream, args);
+  if (pairs)
+    hipLaunchKernelGGL((chunk_kernel<T, kFull, 2>), dim3((unsigned)ids(plan.max_segments, 2)),
+                       dim3(2 * kThreads), Lds<2>::BYTES, stream, args);
+  else
+    hipLaunchKernelGGL((chunk_kernel<T, kFull, 1>), dim3((unsigned)ids(plan.max_segments, 1)),
+                       dim3(kThreads), Lds<1>::BYTES, stream, args);
   mark(4);
   if (tm) tm->ran[3] = true;
   if (conv_out) {

@@ -106,9 +106,10 @@ def test_prefill_4k_full_parity():
 
 
 @gpu
-@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 3)])
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 3), (2, 6)])
 def test_head_layouts(hk, hv):
-    """One v head per q/k head (r = 1), four (r = 4), and a head count that is not a
+    """One v head per q/k head (r = 1), four (r = 4: two workgroups of two v heads per
+    q/k head), three (r = 3: one v head per workgroup), and a head count that is not a
     multiple of the workgroup id groups of 8; multi-segment (T = 2000)."""
     w = S.scaled(S.PREFILL_4K, lengths=(2000, 300), num_qk_heads=hk, num_v_heads=hv,
                  seed=30 + hv, init_state_std=0.01, conv_history=True)
