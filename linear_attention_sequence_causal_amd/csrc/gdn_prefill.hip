@@ -15,24 +15,26 @@
 // beta = sigmoid(b)) and the gated RMSNorm epilogue are fused into the chunk
 // loop, so q/k/v/z/a/b are read once and o is written once.
 //
-// Precision plan (fp32 accumulation, fp32 state):
-//   K K^T and Q K^T take one fp16 pass on the unit-norm q and k (q_scale is
-//   applied to the products); W, T V, W H, Q H and M U take one bf16 pass; the
-//   state update K^T U takes split bf16 operands x = hi + lo (hi*hi + hi*lo +
-//   lo*hi) over the last 128 tokens of a sequence and on chunks whose decay keeps
-//   more than 2^-4 of the state (2^-8 per 64 tokens), one pass elsewhere;
-//   the identity part of T V (beta V, beta gamma K) and the diagonal of M U
-//   are applied in fp32.  The triangular inverse is formed per 16x16 diagonal
-//   block from fp16 products and merged with bf16 products.
+// Precision plan (fp32 accumulation, fp32 state): every product takes fp16
+// operands.  q and k are unit-norm (q_scale multiplies o at the end), |L| <= 1 and
+// the entries of each (I + L_bb)^-1 stay below 2^15, |W| <= 1; beta V is scaled by a
+// power of two per wave before the triangular solve, and the state by another one
+// (sigma, with a tracked bound that keeps |sigma H| below 2^14), so every fp16
+// operand is in range.  The identity part of T V (beta V, beta gamma K) and the
+// diagonal of M U are applied in fp32.  Powers of two are exact: o and the final
+// state are divided by them at the end.
 //
-// Work decomposition: one workgroup = 4 waves = one (segment, v head); wave w
-// owns value columns 32w..32w+31 of the state in MFMA accumulators, and two
-// workgroups share a compute unit (75-80 KB of LDS and <= 256 VGPRs each), so
-// one's VALU-bound prologue and epilogue overlap the other's LDS- and MFMA-bound
-// chain.  Long sequences are cut into segments: pass 1 computes each non-final
-// segment's affine map H -> A H + B (the same chunk loop run on the columns of
-// A = I and B = 0), pass 2 chains the maps into segment start states, pass 3
-// runs the full chunk loop of every segment from its start state.
+// Work decomposition: a workgroup runs NH v heads of one q/k head and one segment,
+// 4 waves per v head; wave role w owns value columns 32w..32w+31 of its head's state
+// in MFMA accumulators.  NH = 2 (the v heads of a q/k head pair up): 8 waves, one
+// workgroup per compute unit, and the q/k prologue (conv, SiLU, L2 norm, the fp16 q,
+// k and K^T tiles) is computed once for both heads.  NH = 1: 4 waves, two
+// workgroups per compute unit (~60 KB of LDS and <= 256 VGPRs each), so that one's
+// VALU-bound prologue and epilogue overlap the other's LDS- and MFMA-bound chain.
+// Long sequences are cut into segments: pass 1 computes each non-final segment's
+// affine map H -> A H + B (the same chunk loop run on the columns of A = I and
+// B = 0, NH = 1), pass 2 chains the maps into segment start states, pass 3 runs the
+// full chunk loop of every segment from its start state.
 #include "gdn_device.h"
 #include "gdn_prefill_plan.h"
 #include "gdn_launch.h"
@@ -341,7 +343,7 @@ __device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4 &mc, const f32
 }
 
 // ------------------------------------------------------------ chunk kernel
-// MODE kFull: the whole mixer for one (segment, v head).  MODE kMap: the
+// MODE kFull: the whole mixer for one segment and NH v heads.  MODE kMap: the
 // segment's affine map; blockIdx selects the A half (state columns of the
 // identity) or the B half (columns of zero with the values written in).
 template <typename T, int MODE, int NH>
@@ -682,9 +684,12 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 
     // ================= prologue: conv + SiLU (+ L2) -> LDS ========================
     // Issue priority follows each phase's longest waves: here the k waves (K^T
-    // regrouping, the lo halves), from barrier 1 to barrier 4 waves 0 and 1 (their
-    // diagonal gram tiles, L/M, the 16x16 inverses, then the q waves' prefetch).
-    // Between them the two workgroups on a compute unit fill the SIMDs.
+    // regrouping), from barrier 1 to barrier 4 roles 0 and 1 (their diagonal gram
+    // tiles, L/M, the 16x16 inverses, then the q waves' prefetch), and after barrier 4
+    // the second head's waves (NH = 2), which the SIMDs otherwise serve after the older
+    // first-head waves, so that they do not arrive last at barrier 1.  With NH = 1 the
+    // two workgroups on a compute unit fill the SIMDs between these phases.
+    __builtin_amdgcn_s_setprio(0);
     if (MODE == kFull && wave >= 2) __builtin_amdgcn_s_setprio(1);
     if (t0 - 3 < seq_begin && !hist) {  // rows before the sequence read as zero
 #pragma unroll
@@ -941,6 +946,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // (4) -W ready
     refresh();
+    if (NH == 2 && hh == 1) __builtin_amdgcn_s_setprio(1);
 
     // ================= Q H, U = Utilde - W H, O += M U, H update ==================
     // The accumulators hold sigma H (sigma = 2^sexp per wave) with |sigma H| below 2^14
