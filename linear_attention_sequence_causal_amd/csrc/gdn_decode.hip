@@ -27,69 +27,85 @@ constexpr int kDecThreads = 256;
 constexpr int kStateF32 = 0, kStateBf16 = 1, kStateFp8 = 2;
 constexpr int kDecMaxRatio = 8;  // largest Hv / Hk the decode kernel accepts
 
-// Stored state: fp32, or bf16 (rounded to nearest even on every store) with the
-// step itself computed in fp32.  Four consecutive columns per access, streamed
-// once (non-temporal).  A prefetched head is kept in its stored form (Raw) until
-// it is used, so bf16 storage needs half the registers for it.
+// Stored state: fp32, or bf16 (rounded to nearest even on every store), or fp8 with
+// one scale per row; the step itself is computed in fp32.  C consecutive columns of a
+// row per access (16 bytes for fp32 and fp8, 8 for bf16), streamed once (non-temporal).
+// A prefetched head is kept in its stored form (Raw) until it is used, so the narrow
+// formats need fewer registers for it.
 template <typename S> struct StateIO;
 template <> struct StateIO<float> {
+  static constexpr int C = 4;
   typedef f32x4 Raw;
   static __device__ __forceinline__ Raw load_raw(const float *p) { return ld_nt4(p); }
-  static __device__ __forceinline__ f32x4 widen(Raw x) { return x; }
-  static __device__ __forceinline__ f32x4 load(const float *p) { return ld_nt4(p); }
-  static __device__ __forceinline__ void store(float *p, f32x4 x) { st_nt4(p, x); }
+  static __device__ __forceinline__ void widen(Raw x, float (&o)[C]) {
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+  }
+  static __device__ __forceinline__ void store(float *p, const float (&x)[C]) {
+    st_nt4(p, f32x4{x[0], x[1], x[2], x[3]});
+  }
 };
 template <> struct StateIO<bf16_t> {
+  static constexpr int C = 4;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef u32x2 Raw;
   static __device__ __forceinline__ Raw load_raw(const bf16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
   }
-  static __device__ __forceinline__ f32x4 widen(Raw w) {
-    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  static __device__ __forceinline__ void widen(Raw w, float (&o)[C]) {
+    o[0] = __uint_as_float(w.x << 16); o[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(w.y << 16); o[3] = __uint_as_float(w.y & 0xFFFF0000u);
   }
-  static __device__ __forceinline__ f32x4 load(const bf16_t *p) { return widen(load_raw(p)); }
-  static __device__ __forceinline__ void store(bf16_t *p, f32x4 x) {
-    const u32x2 w = {pk_bf16(x.x, x.y), pk_bf16(x.z, x.w)};
+  static __device__ __forceinline__ void store(bf16_t *p, const float (&x)[C]) {
+    const u32x2 w = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
   }
 };
 
 // fp8 storage: OCP E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
 // largest finite value 448) times one power-of-two scale per state row (dk index)
-// kept in fp32 beside the state; the step's arithmetic is fp32.
+// kept in fp32 beside the state; the step's arithmetic is fp32.  16 columns per access.
 struct fp8_t {
   uint8_t bits;
 };
 template <> struct StateIO<fp8_t> {
-  typedef uint32_t Raw;  // four consecutive columns
+  static constexpr int C = 16;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef u32x4 Raw;
   static __device__ __forceinline__ Raw load_raw(const fp8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   }
-  static __device__ __forceinline__ f32x4 widen(Raw w) {
-    return f32x4{__builtin_amdgcn_cvt_f32_fp8((int)w, 0), __builtin_amdgcn_cvt_f32_fp8((int)w, 1),
-                 __builtin_amdgcn_cvt_f32_fp8((int)w, 2), __builtin_amdgcn_cvt_f32_fp8((int)w, 3)};
+  // codes times the row scale sc (a power of two): one scaled conversion per 2 values
+  static __device__ __forceinline__ void widen(Raw w, float sc, float (&o)[C]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[q], sc, false);  // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[q], sc, true);   // bytes 2, 3
+      o[4 * q] = lo[0]; o[4 * q + 1] = lo[1]; o[4 * q + 2] = hi[0]; o[4 * q + 3] = hi[1];
+    }
   }
-  // x already divided by the row scale (|x| <= 448); round to nearest even
-  static __device__ __forceinline__ void store(fp8_t *p, f32x4 x) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x.x, x.y, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(x.z, x.w, w, true);
-    __builtin_nontemporal_store((uint32_t)w, reinterpret_cast<uint32_t *>(p));
+  // codes of x / sc for the row scale sc (a power of two, so the division is exact and
+  // |x / sc| <= 448), rounded to nearest even
+  static __device__ __forceinline__ void store(fp8_t *p, const float (&x)[C], float sc) {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s16x2 t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, x[4 * q], x[4 * q + 1], sc,
+                                                         false);
+      t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, x[4 * q + 2], x[4 * q + 3], sc, true);
+      w[q] = __builtin_bit_cast(uint32_t, t);
+    }
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
   }
 };
 
-// Maximum over each half of a wave (lanes 0..31 and 32..63), left in every lane of
-// the half: rotate-and-max inside each 16-lane row, then the two rows of each half
-// combined with a gfx950 row swap.
-__device__ __forceinline__ float half_wave_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+// Maximum over each group of 8 lanes (8g .. 8g+7), left in every lane of the group:
+// swaps of neighbours and of pairs inside each quad, then the two quads of the group
+// (row_half_mirror pairs lane i with 7 - i).
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm 2,3,0,1
+  return fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
 }
 
 // Exponent e of the fp8 row scale 2^e: the smallest with m <= 448 * 2^e, for a finite
@@ -119,16 +135,24 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   const int tid = threadIdx.x;
   const int64_t Cc = 2LL * Hk * kD + (int64_t)Hv * kD;
 
+  // thread t of the state stream: columns CPT*(t%NCG)..+CPT-1 of rows RPT*(t/NCG)..+RPT-1
+  // (fp32 and bf16: 4 columns of 16 rows; fp8: 16 columns of 4 rows, i.e. 16-byte
+  // accesses and a row's scale from a max over 8 lanes)
+  constexpr int CPT = StateIO<S>::C;
+  constexpr int NCG = kD / CPT;            // threads per state row
+  constexpr int NRG = kDecThreads / NCG;   // row groups
+  constexpr int RPT = kD / NRG;            // rows per thread
+  static_assert(RPT % 4 == 0 && (!kFp8 || NCG == 8), "state stream layout");
+
   __shared__ float s_x[2 + kDecMaxRatio][kD];  // post-prologue q, k, then v of each v head
-  __shared__ float s_red[8][2][kD];            // partial column sums per row group
+  __shared__ float s_red[NRG][2][kD];          // partial column sums per row group
   __shared__ float s_e[kD];
   __shared__ float s_y[kD];
   __shared__ float s_misc[4];
 
-  // thread t of the state stream: columns 4*(t%32)..+3, rows 16*(t/32)..+15
-  const int col = (tid & 31) * 4;
-  const int rg = tid >> 5;
-  const int row0 = rg * 16;
+  const int col = (tid % NCG) * CPT;
+  const int rg = tid / NCG;
+  const int row0 = rg * RPT;
   auto head_ptr = [&](int j) {
     return state + (((int64_t)bseq * Hv + r * g + j) * kD + row0) * kD + col;
   };
@@ -141,18 +165,18 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   const float nwv = norm_w ? norm_w[ztid] : 1.0f;
   uint32_t zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + r * g) * kD + ztid);
   // Start streaming the first head's state before the prologue.
-  typename StateIO<S>::Raw Hraw[16];
-  f32x4 Sraw[4];  // fp8 storage: the scales of this thread's 16 rows
+  typename StateIO<S>::Raw Hraw[RPT];
+  f32x4 Sraw[RPT / 4];  // fp8 storage: the scales of this thread's rows
   auto scale_ptr = [&](int j) {
     return state_scale + ((int64_t)bseq * Hv + r * g + j) * kD + row0;
   };
   {
     const S *Hp = head_ptr(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Hraw[i] = StateIO<S>::load_raw(Hp + i * kD);
+    for (int i = 0; i < RPT; ++i) Hraw[i] = StateIO<S>::load_raw(Hp + i * kD);
     if (kFp8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sraw[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(0) + 4 * i);
+      for (int i = 0; i < RPT / 4; ++i) Sraw[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(0) + 4 * i);
     }
   }
 
@@ -224,9 +248,9 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   __syncthreads();
   const float kq = s_misc[0];
 
-  float kr[16], qr[16];
+  float kr[RPT], qr[RPT];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < RPT; ++i) {
     kr[i] = s_x[1][row0 + i];
     qr[i] = s_x[0][row0 + i];
   }
@@ -238,43 +262,59 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     if (j + 1 < r) zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + h + 1) * kD + ztid);
     // the next head's loads go out first (vector-memory waits are in issue order, so
     // waiting for this head's state does not wait for them)
-    typename StateIO<S>::Raw Hnext[16];
-    f32x4 Snext[4];
+    typename StateIO<S>::Raw Hnext[RPT];
+    f32x4 Snext[RPT / 4];
     if (j + 1 < r) {
       const S *Hn = head_ptr(j + 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hnext[i] = StateIO<S>::load_raw(Hn + i * kD);
+      for (int i = 0; i < RPT; ++i) Hnext[i] = StateIO<S>::load_raw(Hn + i * kD);
       if (kFp8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Snext[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(j + 1) + 4 * i);
+        for (int i = 0; i < RPT / 4; ++i)
+          Snext[i] = *reinterpret_cast<const f32x4 *>(scale_ptr(j + 1) + 4 * i);
       }
     }
-    f32x4 Hcur[16];
+    // fp32 / bf16: the head widened once (64 fp32 registers).  fp8: each row widened where
+    // it is used (twice), which keeps the workgroup under 128 VGPRs (four per compute
+    // unit, more state bytes in flight); the raw words pass an optimisation barrier
+    // before the second widening so that it is not merged with the first.
+    float Hcur[kFp8 ? 1 : RPT][CPT];
+    if constexpr (!kFp8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      Hcur[i] = StateIO<S>::widen(Hraw[i]);
-      if (kFp8) {
-        const float sc = Sraw[i >> 2][i & 3];
-        Hcur[i].x *= sc; Hcur[i].y *= sc; Hcur[i].z *= sc; Hcur[i].w *= sc;
-      }
+      for (int i = 0; i < RPT; ++i) StateIO<S>::widen(Hraw[i], Hcur[i]);
     }
+    auto row = [&](int i, float (&t)[CPT]) __attribute__((always_inline)) {
+      if constexpr (kFp8) StateIO<S>::widen(Hraw[i], Sraw[i >> 2][i & 3], t);
+      else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) t[c] = Hcur[i][c];
+      }
+    };
     const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
     const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
-    float sk[4] = {0, 0, 0, 0}, sq[4] = {0, 0, 0, 0};
+    float sk[CPT], sq[CPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sk[0] += Hcur[i].x * kr[i]; sk[1] += Hcur[i].y * kr[i];
-      sk[2] += Hcur[i].z * kr[i]; sk[3] += Hcur[i].w * kr[i];
-      sq[0] += Hcur[i].x * qr[i]; sq[1] += Hcur[i].y * qr[i];
-      sq[2] += Hcur[i].z * qr[i]; sq[3] += Hcur[i].w * qr[i];
+    for (int c = 0; c < CPT; ++c) sk[c] = sq[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float t[CPT];
+      row(i, t);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        sk[c] += t[c] * kr[i];
+        sq[c] += t[c] * qr[i];
+      }
     }
-    *reinterpret_cast<f32x4 *>(&s_red[rg][0][col]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
-    *reinterpret_cast<f32x4 *>(&s_red[rg][1][col]) = f32x4{sq[0], sq[1], sq[2], sq[3]};
+#pragma unroll
+    for (int c = 0; c < CPT; c += 4) {
+      *reinterpret_cast<f32x4 *>(&s_red[rg][0][col + c]) = f32x4{sk[c], sk[c + 1], sk[c + 2], sk[c + 3]};
+      *reinterpret_cast<f32x4 *>(&s_red[rg][1][col + c]) = f32x4{sq[c], sq[c + 1], sq[c + 2], sq[c + 3]};
+    }
     __syncthreads();
     if (tid < kD) {
       float vk = 0.f, vq = 0.f;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < NRG; ++p) {
         vk += s_red[p][0][tid];
         vq += s_red[p][1][tid];
       }
@@ -286,26 +326,38 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       if ((tid & 63) == 0) s_misc[1 + (tid >> 6)] = ssum;
     }
     __syncthreads();
-    float ec[4];
+    float ec[CPT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ec[c] = beta * s_e[col + c];
+    for (int c = 0; c < CPT; ++c) ec[c] = beta * s_e[col + c];
     S *Hp = head_ptr(j);
+    float snew[RPT];  // fp8 storage: the new row scales
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      f32x4 hn;
-      hn.x = alpha * Hcur[i].x + kr[i] * ec[0];
-      hn.y = alpha * Hcur[i].y + kr[i] * ec[1];
-      hn.z = alpha * Hcur[i].z + kr[i] * ec[2];
-      hn.w = alpha * Hcur[i].w + kr[i] * ec[3];
-      if (kFp8) {  // the row's scale: max over its 128 columns (this half-wave's 32 lanes)
-        const float m = half_wave_max(fmaxf(fmaxf(fabsf(hn.x), fabsf(hn.y)),
-                                            fmaxf(fabsf(hn.z), fabsf(hn.w))));
-        const int e = fp8_scale_exp(m);
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e (|e| <= 126)
-        hn.x *= inv; hn.y *= inv; hn.z *= inv; hn.w *= inv;
-        if ((tid & 31) == 0) scale_ptr(j)[i] = __uint_as_float((uint32_t)(127 + e) << 23);
+      for (int i = 0; i < RPT; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) asm volatile("" : "+v"(Hraw[i][w]));
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float hn[CPT];
+      row(i, hn);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) hn[c] = alpha * hn[c] + kr[i] * ec[c];
+      if constexpr (kFp8) {  // the row's scale: max over its 128 columns (8 lanes x 16)
+        float m = fabsf(hn[0]);
+#pragma unroll
+        for (int c = 1; c < CPT; ++c) m = fmaxf(m, fabsf(hn[c]));
+        const int e = fp8_scale_exp(max8(m));
+        snew[i] = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e, e in [-126, 127]
+        StateIO<S>::store(Hp + i * kD, hn, snew[i]);
+      } else {
+        StateIO<S>::store(Hp + i * kD, hn);
       }
-      StateIO<S>::store(Hp + i * kD, hn);
+    }
+    if (kFp8 && (tid % NCG) == 0) {
+#pragma unroll
+      for (int i = 0; i < RPT; i += 4)
+        *reinterpret_cast<f32x4 *>(scale_ptr(j) + i) = f32x4{snew[i], snew[i + 1], snew[i + 2], snew[i + 3]};
     }
     if (tid < kD) {
       const float inv = rsqrtf((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
@@ -314,10 +366,10 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
     __syncthreads();  // s_red, s_e, s_y, s_misc are reused by the next head
     if (j + 1 < r) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Hraw[i] = Hnext[i];
+      for (int i = 0; i < RPT; ++i) Hraw[i] = Hnext[i];
       if (kFp8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sraw[i] = Snext[i];
+        for (int i = 0; i < RPT / 4; ++i) Sraw[i] = Snext[i];
       }
     }
   }
