@@ -10,8 +10,9 @@
 // the layouts the mixer reads, with no intermediate buffer.
 //
 // Tiling: one workgroup of 8 waves computes a 256 x 256 block of C, K in steps of
-// 64 through double-buffered LDS tiles (one barrier per step; the next step's tiles
-// are loaded into registers while the current one is multiplied).  Wave (wm, wn) owns
+// 64 through double-buffered LDS tiles (one barrier per step): the next step's tiles
+// go from global memory straight into the other LDS buffer (buffer loads with the LDS
+// destination, no register staging) while the current one is multiplied.  Wave (wm, wn) owns
 // rows 64 wm .. + 63 and columns 128 wn .. + 127: 2 x 4 products
 // v_mfma_f32_32x32x16_bf16 per 16-wide k slice (128 accumulators per lane).
 #include "gdn_device.h"
@@ -28,15 +29,19 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kLinThreads = 512;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (144 B: 16-byte reads spread over banks)
-constexpr int kTileElems = kBM * kLdsRow;
-constexpr size_t kLinLds = 2 * 2 * (size_t)kTileElems * sizeof(bf16_t);  // A and B, 2 buffers
+// LDS tiles [256 rows][64 k] bf16, unpadded (128-byte rows), filled straight from global
+// memory: a wave's 16-byte load writes 64 consecutive 16-byte slots (8 rows).  The k
+// chunk g (8 bf16) of row r sits in slot g ^ (r & 7) ^ ((r >> 3) & 1) of its row, so the
+// 16-byte operand reads of 16 consecutive rows at one g hit distinct banks.
+constexpr int kTileBytes = kBM * kBK * 2;                  // 32 KB
+constexpr size_t kLinLds = 2 * 2 * (size_t)kTileBytes;   // A and B, 2 buffers: 128 KB
 static_assert(kLinLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+__device__ __forceinline__ int swz_slot(int row, int g) { return g ^ (row & 7) ^ ((row >> 3) & 1); }
 
 // kTileSeg: every segment boundary is a multiple of 32, so each 32-column MFMA tile lies in
 // one segment (a scalar lookup) and its stores are raw buffer stores: a per-lane column
@@ -46,8 +51,6 @@ __global__ void __launch_bounds__(kLinThreads, 1)
 linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, int64_t M, int N,
                    int K, LinearOut out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16_t *const sA = reinterpret_cast<bf16_t *>(smem);
-  bf16_t *const sB = sA + 2 * kTileElems;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;
@@ -62,25 +65,22 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
   const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * K, (uint32_t)(rowsA * K * 2));
   const __amdgpu_buffer_rsrc_t rb = rsrc(W + (int64_t)n0 * K, (uint32_t)((int64_t)rowsB * K * 2));
 
-  // this thread's four 16-byte chunks of each 256 x 64 tile: chunk c = tid + 512 i,
-  // row c / 8, k offset 8 (c % 8)
-  i32x4 ga[4], gb[4];
-  auto gload = [&](int k0) {
+  // loads of one K step: wave w fills 8-row blocks 4w .. 4w+3 of each tile; lane l takes
+  // row 8b + l/8 and slot l%8, i.e. the global chunk swz_slot(row, l%8) of that row
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
+    voff[i] = (uint32_t)(row * K * 2 + swz_slot(row, lane & 7) * 16);
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto gload = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + kLinThreads * i;
-      const uint32_t off = (uint32_t)(((c >> 3) * K + k0 + 8 * (c & 7)) * 2);
-      ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-      gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kLinThreads * i;
-      const int o = buf * kTileElems + (c >> 3) * kLdsRow + 8 * (c & 7);
-      *reinterpret_cast<i32x4 *>(sA + o) = ga[i];
-      *reinterpret_cast<i32x4 *>(sB + o) = gb[i];
+      const int blk = (buf * 2 * kTileBytes) + (4 * wave + i) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(smem + blk), 16, voff[i], k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(smem + blk + kTileBytes), 16, voff[i],
+                                               k0 * 2, 0, 0);
     }
   };
 
@@ -93,27 +93,31 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
   const int nk = K / kBK;
-  gload(0);
-  lstore(0);
+  gload(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
   // operand rows of this lane: A rows 64 wm + 32 mt + (lane % 32), W rows 128 wn + 32 nt +
-  // (lane % 32); k = 16 kk + 8 (lane / 32) .. + 7 of the step
-  const int arow = 64 * wm + (lane & 31), brow = 128 * wn + (lane & 31);
-  const int kl = 8 * (lane >> 5);
+  // (lane % 32); k chunk 2 kk + lane / 32 of the step
+  const int lr = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const bf16_t *a0 = sA + buf * kTileElems + arow * kLdsRow + kl;
-    const bf16_t *b0 = sB + buf * kTileElems + brow * kLdsRow + kl;
+    if (kt + 1 < nk) gload((kt + 1) * kBK, buf ^ 1);  // the other buffer was last read before the barrier
+    const unsigned char *tA = smem + buf * 2 * kTileBytes;
+    const unsigned char *tB = tA + kTileBytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int g = 2 * kk + kh;
       bf16x8_t af[2], bfr[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        af[mt] = *reinterpret_cast<const bf16x8_t *>(a0 + 32 * mt * kLdsRow + 16 * kk);
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = 64 * wm + 32 * mt + lr;
+        af[mt] = *reinterpret_cast<const bf16x8_t *>(tA + row * 128 + swz_slot(row, g) * 16);
+      }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bfr[nt] = *reinterpret_cast<const bf16x8_t *>(b0 + 32 * nt * kLdsRow + 16 * kk);
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 128 * wn + 32 * nt + lr;
+        bfr[nt] = *reinterpret_cast<const bf16x8_t *>(tB + row * 128 + swz_slot(row, g) * 16);
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -121,7 +125,7 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0,
                                                                  0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);  // the other buffer was last read before the barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next step's tiles are in LDS
     __syncthreads();
   }
 
