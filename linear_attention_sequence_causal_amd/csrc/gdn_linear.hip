@@ -28,7 +28,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kLinThreads = 512;
+// waves along M and N; a wave computes a kWaveRows x kWaveCols block of C from
+// MT x NT 32 x 32 MFMA tiles
+constexpr int kWavesM = 4, kWavesN = 2;
+constexpr int kLinWaves = kWavesM * kWavesN, kLinThreads = 64 * kLinWaves;
+constexpr int kWaveRows = kBM / kWavesM, kWaveCols = kBN / kWavesN;
+constexpr int MT = kWaveRows / 32, NT = kWaveCols / 32;
+constexpr int kLoadsPerWave = 32 / kLinWaves;  // 1 KB blocks of each 32 KB tile
 // LDS tiles [256 rows][64 k] bf16, unpadded (128-byte rows), filled straight from global
 // memory: a wave's 16-byte load writes 64 consecutive 16-byte slots (8 rows).  The k
 // chunk g (8 bf16) of row r sits in slot g ^ (r & 7) ^ ((r >> 3) & 1) of its row, so the
@@ -53,7 +59,7 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % kWavesM, wn = wave / kWavesM;
   // column blocks fastest: consecutive workgroups share their rows of A (in L2)
   const int nblk = (N + kBN - 1) / kBN;
   const int64_t m0 = (int64_t)(blockIdx.x / nblk) * kBM;
@@ -65,30 +71,30 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
   const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * K, (uint32_t)(rowsA * K * 2));
   const __amdgpu_buffer_rsrc_t rb = rsrc(W + (int64_t)n0 * K, (uint32_t)((int64_t)rowsB * K * 2));
 
-  // loads of one K step: wave w fills 8-row blocks 4w .. 4w+3 of each tile; lane l takes
-  // row 8b + l/8 and slot l%8, i.e. the global chunk swz_slot(row, l%8) of that row
-  uint32_t voff[4];
+  // loads of one K step: wave w fills 8-row blocks kLoadsPerWave w .. of each tile; lane l
+  // takes row 8b + l/8 and slot l%8, i.e. the global chunk swz_slot(row, l%8) of that row
+  uint32_t voff[kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (4 * wave + i) + (lane >> 3);
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = 8 * (kLoadsPerWave * wave + i) + (lane >> 3);
     voff[i] = (uint32_t)(row * K * 2 + swz_slot(row, lane & 7) * 16);
   }
   typedef __attribute__((address_space(3))) void lds_void;
   auto gload = [&](int k0, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = (buf * 2 * kTileBytes) + (4 * wave + i) * 1024;
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int blk = (buf * 2 * kTileBytes) + (kLoadsPerWave * wave + i) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(smem + blk), 16, voff[i], k0 * 2, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(smem + blk + kTileBytes), 16, voff[i],
                                                k0 * 2, 0, 0);
     }
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
@@ -96,8 +102,8 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
   gload(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
-  // operand rows of this lane: A rows 64 wm + 32 mt + (lane % 32), W rows 128 wn + 32 nt +
-  // (lane % 32); k chunk 2 kk + lane / 32 of the step
+  // operand rows of this lane: A rows kWaveRows wm + 32 mt + (lane % 32), W rows
+  // kWaveCols wn + 32 nt + (lane % 32); k chunk 2 kk + lane / 32 of the step
   const int lr = lane & 31, kh = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
@@ -107,21 +113,21 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int g = 2 * kk + kh;
-      bf16x8_t af[2], bfr[4];
+      bf16x8_t af[MT], bfr[NT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int row = 64 * wm + 32 * mt + lr;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = kWaveRows * wm + 32 * mt + lr;
         af[mt] = *reinterpret_cast<const bf16x8_t *>(tA + row * 128 + swz_slot(row, g) * 16);
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int row = 128 * wn + 32 * nt + lr;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int row = kWaveCols * wn + 32 * nt + lr;
         bfr[nt] = *reinterpret_cast<const bf16x8_t *>(tB + row * 128 + swz_slot(row, g) * 16);
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0,
                                                                  0, 0);
     }
@@ -132,12 +138,12 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
   // epilogue: lane holds column (lane % 32) and rows 8 (r / 4) + 4 (lane / 32) + (r % 4) of
   // each 32 x 32 tile
   if constexpr (kTileSeg) {
-    const int64_t r0 = m0 + 64 * wm;  // this wave's first row
-    const int64_t rows = M - r0 < 64 ? M - r0 : 64;
+    const int64_t r0 = m0 + kWaveRows * wm;  // this wave's first row
+    const int64_t rows = M - r0 < kWaveRows ? M - r0 : kWaveRows;
     const int ln = lane & 31, lh = lane >> 5;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int nbase = n0 + 128 * wn + 32 * nt;  // uniform
+    for (int nt = 0; nt < NT; ++nt) {
+      const int nbase = n0 + kWaveCols * wn + 32 * nt;  // uniform
       if (nbase >= N || rows <= 0) continue;
       int s = 0;
 #pragma unroll
@@ -153,7 +159,7 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
           (uint32_t)(((rows - 1) * stride + ncol) * esz));
       const uint32_t vo = (uint32_t)((4 * lh * stride + ln) * esz);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t so = (uint32_t)((32 * mt + 8 * (r >> 2) + (r & 3)) * stride * esz);
@@ -166,8 +172,8 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
     }
   } else {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int nbase = n0 + 128 * wn + 32 * nt;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int nbase = n0 + kWaveCols * wn + 32 * nt;
       if (nbase >= N) continue;
       const int col = nbase + (lane & 31);
       if (col >= N) continue;
@@ -178,10 +184,10 @@ linear_bf16_kernel(const bf16_t *__restrict__ A, const bf16_t *__restrict__ W, i
       const int64_t cs = col - out.col_begin[s];
       const int64_t stride = out.row_stride[s];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + 64 * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t row = m0 + kWaveRows * wm + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row >= M) continue;
           const float x = acc[mt][nt][r];
           if (out.dtype[s] == kLinF32)
