@@ -1382,12 +1382,17 @@ __global__ void conv_out_kernel(const int32_t *cu, int N, int64_t T_total, const
 // ------------------------------------------------------------ host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Segment length: the smallest power of two >= 256 (at most 8192 tokens)
-// that still gives about two workgroups per compute unit over all v heads.
-static int32_t pick_seg_len(int64_t T, int32_t Hv) {
-  int64_t target = T * (int64_t)Hv / 512;
+// Segment length: the smallest power of two >= 256 that still gives about one
+// round of workgroups over all v heads (512 v-head segments: 256 workgroups of two
+// heads, or two of one per compute unit), at most 8192 tokens for one sequence.  Packed
+// sequences of different lengths leave a tail of partial segments after the last full
+// round, so their segments stop at 2048 tokens (a 64-sequence batch of 368,804 tokens:
+// 6.35 ms with 8192, 5.92 with 4096, 5.80 with 2048, 6.43 with 1024).
+static int32_t pick_seg_len(int64_t T, int32_t Hv, int32_t N) {
+  const int64_t target = T * (int64_t)Hv / 512;
+  const int32_t cap = N > 1 ? 2048 : 8192;
   int32_t s = 256;
-  while (s < 8192 && s < target) s *= 2;
+  while (s < cap && s < target) s *= 2;
   return s;
 }
 
@@ -1397,7 +1402,7 @@ PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_head
   p.total_tokens = total_tokens;
   p.num_v_heads = num_v_heads;
   if (num_seqs <= 0) return p;
-  p.seg_len = pick_seg_len(total_tokens, num_v_heads);
+  p.seg_len = pick_seg_len(total_tokens, num_v_heads, num_seqs);
   // sum_i max(1, ceil(L_i / s)) <= N + T / s; segments that are not the last of
   // their sequence are full, so there are at most T / s of them.
   p.max_segments = num_seqs + total_tokens / p.seg_len;
