@@ -182,6 +182,7 @@ struct PrefillArgs {
   const int32_t *hdr;      // [0] segments, [1] maps
   const int32_t *map_seg;  // map slot -> segment index
   const int32_t *seq_first;  // sequence -> index of its first segment
+  const int32_t *order;      // full-pass unit -> segment index (longest segments first)
   float *maps;             // [max_maps][Hv][2][D][D]
   int32_t *map_zero;       // [max_maps][Hv]: 1 if the A map is zero (not stored)
   float *starts;           // [max_segments][Hv][D][D]
@@ -392,7 +393,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
   int segi;
   if (MODE == kFull) {
     if (unit >= P.hdr[0]) return;
-    segi = unit;
+    segi = P.order[unit];
   } else {
     if (unit >= P.hdr[1]) return;
     segi = P.map_seg[unit];
@@ -1158,7 +1159,7 @@ __device__ int g_prefill_bad_cu = 0;
 // and g_prefill_bad_cu is set.
 __global__ void __launch_bounds__(1024) segment_table_kernel(
     const int32_t *cu, int N, int64_t T, int seg_len, int64_t max_segments, int64_t max_maps,
-    SegInfo *segs, int32_t *hdr, int32_t *map_seg, int32_t *seq_first) {
+    SegInfo *segs, int32_t *hdr, int32_t *map_seg, int32_t *seq_first, int32_t *order) {
   __shared__ int s_nseg[1024], s_nmap[1024];
   __shared__ int s_base_seg, s_base_map, s_bad;
   const int tid = threadIdx.x;
@@ -1236,6 +1237,41 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
       s_base_map += s_nmap[1023];
     }
     __syncthreads();
+  }
+  // The full pass's order: segments by chunk count, longest first, so that the shortest
+  // ones run last and the final round of workgroups leaves little idle time (packed
+  // sequences of different lengths).  A counting sort over the <= 256 + 1 chunk counts;
+  // the order inside a count is whatever the atomics give, which changes no result
+  // (every segment is computed the same way by whichever workgroup takes it).
+  const int nseg_all = (int)min((int64_t)s_base_seg, max_segments);
+  if (N == 1) {  // one sequence: equal segments, in order
+    for (int i = tid; i < nseg_all; i += 1024) order[i] = i;
+  } else {
+    __threadfence_block();
+    __syncthreads();  // the segment records are written
+    constexpr int kBins = kMaxSegChunks + 1;
+    static_assert(kBins <= 512, "bins of the order scan");
+    // bin j (j < 512) counts the segments of kMaxSegChunks - j chunks (longest first)
+    int *cnt = s_nseg;  // reused
+    if (tid < 512) cnt[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < nseg_all; i += 1024)
+      atomicAdd(&cnt[kMaxSegChunks - min((segs[i].len + kChunk - 1) / kChunk, kMaxSegChunks)], 1);
+    __syncthreads();
+    int *scan = s_nmap;  // exclusive prefix sums of the bins
+    const int own = tid < 512 ? cnt[tid] : 0;
+    if (tid < 512) scan[tid] = own;
+    __syncthreads();
+    for (int o = 1; o < 512; o <<= 1) {
+      const int add = (tid < 512 && tid >= o) ? scan[tid - o] : 0;
+      __syncthreads();
+      if (tid < 512) scan[tid] += add;
+      __syncthreads();
+    }
+    if (tid < 512) cnt[tid] = scan[tid] - own;
+    __syncthreads();
+    for (int i = tid; i < nseg_all; i += 1024)
+      order[atomicAdd(&cnt[kMaxSegChunks - min((segs[i].len + kChunk - 1) / kChunk, kMaxSegChunks)], 1)] = i;
   }
   if (tid == 0) {
     // (cannot happen for a valid table; kept so that no segment index ever passes
@@ -1411,7 +1447,8 @@ PrefillPlan make_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_v_head
   size_t off = 0;
   p.off_table = off;
   off = align256(off + sizeof(int32_t) * 16 + sizeof(SegInfo) * (size_t)p.max_segments +
-                 sizeof(int32_t) * (size_t)(p.max_maps + 1) + sizeof(int32_t) * (size_t)num_seqs);
+                 sizeof(int32_t) * (size_t)(p.max_maps + 1) + sizeof(int32_t) * (size_t)num_seqs +
+                 sizeof(int32_t) * (size_t)p.max_segments);
   if (p.max_maps > 0) {
     p.off_maps = off;
     off = align256(off + 2 * DD * (size_t)p.max_maps * num_v_heads);
@@ -1501,15 +1538,16 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   SegInfo *segs = (SegInfo *)(ws + plan.off_table + 16 * sizeof(int32_t));
   int32_t *map_seg = (int32_t *)(segs + plan.max_segments);
   int32_t *seq_first = map_seg + plan.max_maps + 1;
+  int32_t *order = seq_first + num_seqs;
   hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, num_seqs,
                      total_tokens, plan.seg_len, plan.max_segments, plan.max_maps, segs, hdr,
-                     map_seg, seq_first);
+                     map_seg, seq_first, order);
   PrefillArgs A;
   A.q = q; A.k = k; A.v = v; A.z = z; A.a = a; A.b = b;
   A.conv_w = p.conv_weight; A.A_log = p.A_log; A.dt_bias = p.dt_bias; A.norm_w = p.norm_weight;
   A.q_scale = p.q_scale; A.l2_eps = p.l2_eps; A.rms_eps = p.rms_eps;
   A.init_state = init_state; A.conv_in = conv_state_in; A.o = o; A.final_state = final_state;
-  A.segs = segs; A.hdr = hdr; A.map_seg = map_seg; A.seq_first = seq_first;
+  A.segs = segs; A.hdr = hdr; A.map_seg = map_seg; A.seq_first = seq_first; A.order = order;
   A.maps = plan.max_maps > 0 ? (float *)(ws + plan.off_maps) : nullptr;
   A.starts = plan.max_maps > 0 ? (float *)(ws + plan.off_start) : nullptr;
   A.map_zero = plan.max_maps > 0 ? (int32_t *)(ws + plan.off_flags) : nullptr;
