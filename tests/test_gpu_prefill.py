@@ -226,6 +226,21 @@ def test_varlen_with_empty_and_short_sequences():
 
 
 @gpu
+def test_many_packed_sequences():
+    """More sequences than the segment table's 1024 threads take in one pass (1,502: short
+    ones of 0..80 tokens around two long ones that split into several segments of at most
+    2048 tokens), so the table's scan runs in several passes and the full pass's
+    longest-first order sorts segments of many different lengths."""
+    lengths = [int(x) for x in np.random.default_rng(11).integers(0, 81, 1500)]
+    lengths.insert(700, 5000)
+    lengths.insert(1200, 9001)
+    w = S.scaled(S.PREFILL_4K, lengths=tuple(lengths), num_qk_heads=1, num_v_heads=2, seed=12,
+                 init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    check_parity(d, tag=f"{len(lengths)} packed sequences")
+
+
+@gpu
 def test_packing_is_bit_exact():
     """Each packed sequence's o rows and final state equal its standalone run."""
     w = S.scaled(S.PREFILL_4K, lengths=(300, 77, 1024, 5, 2000), seed=9, init_state_std=0.01,
