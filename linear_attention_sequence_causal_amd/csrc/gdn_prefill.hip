@@ -1418,17 +1418,19 @@ __global__ void conv_out_kernel(const int32_t *cu, int N, int64_t T_total, const
 // ------------------------------------------------------------ host side
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Segment length: the smallest power of two >= 256 that still gives about one
-// round of workgroups over all v heads (512 v-head segments: 256 workgroups of two
-// heads, or two of one per compute unit), at most 8192 tokens for one sequence.  Packed
-// sequences of different lengths leave a tail of partial segments after the last full
-// round, so their segments stop at 2048 tokens (a 64-sequence batch of 368,804 tokens:
-// 6.35 ms with 8192, 5.92 with 4096, 5.80 with 2048, 6.43 with 1024).
+// Segment length: a power of two >= 256 (at most 8192 tokens).  One sequence: the
+// smallest that still gives about one round of workgroups over all v heads (512 v-head
+// segments: 256 workgroups of two heads, or two of one per compute unit); its segments
+// are equal.  Packed sequences of unknown, different lengths: the smallest that gives
+// about three rounds, so that the longest-first order of the full pass can fill the last
+// round with short segments (the host knows only N and T).  Measured with 16/32 heads:
+// 64 sequences of 128-32768 tokens 5.33 ms (one-round rule 5.33, 2048-token cap 5.66);
+// five sequences of 500-45000 tokens 1.41 ms (one-round rule 1.65); equal-length
+// batches of 2-16 sequences 0.95-0.98 ms (one-round rule 0.92-0.96).
 static int32_t pick_seg_len(int64_t T, int32_t Hv, int32_t N) {
-  const int64_t target = T * (int64_t)Hv / 512;
-  const int32_t cap = N > 1 ? 2048 : 8192;
+  const int64_t target = T * (int64_t)Hv / (N > 1 ? 1536 : 512);
   int32_t s = 256;
-  while (s < cap && s < target) s *= 2;
+  while (s < 8192 && s < target) s *= 2;
   return s;
 }
 
