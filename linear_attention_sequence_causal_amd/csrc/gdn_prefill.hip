@@ -420,14 +420,16 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
   // ---- roles of the prologue ----------------------------------------------------
   // Before the first barrier every wave convolves q (roles 0-1) or k (roles 2-3):
   // TPT tokens x 8 channels per thread, the 16 lanes of a token row spanning its 128
-  // channels (for the L2 norm); the q/k wave qi of a kind takes tokens 16 qi / NH ..
-  // After it every thread convolves 4 tokens x 4 channels of its head's v, which only
-  // the right-hand side (after barrier 3) reads.  Map mode needs no q (and no v for
-  // the A half).
-  constexpr int TPT = 4 / NH;          // q/k tokens per thread
-  const int role = wave < 2 ? 0 : 1;   // uniform per wave
+  // channels (for the L2 norm); wave qi of its kind takes tokens 4 TPT qi .. + 4 TPT - 1.
+  // Map mode needs no q: all four waves convolve k (and the A half needs no v).  After
+  // the barrier every thread convolves 4 tokens x 4 channels of its head's v, which
+  // only the right-hand side (after barrier 3) reads.
+  constexpr int TPT = (NH == 2 || MODE == kMap) ? 2 : 4;  // q/k tokens per thread
+  const int role = (MODE == kMap || wave >= 2) ? 1 : 0;   // uniform per wave
   int cg = lane & 15;                  // q/k channels 8cg .. 8cg+7
-  int tbase = TPT * (4 * (NH == 2 ? 2 * hh + (wave & 1) : (wave & 1)) + (lane >> 4));
+  // the wave's index among the waves of its kind (q or k), 16 / TPT tokens each
+  const int qi = MODE == kMap ? wave : NH == 2 ? 2 * hh + (wave & 1) : (wave & 1);
+  int tbase = TPT * (4 * qi + (lane >> 4));
   // v channels 4cv .. 4cv+3 of the head, ht = the thread's index among its head's 256;
   // cv rotates the 5 lane bits so that the 8 lanes of one 16-byte LDS write cycle take
   // cv values 4 apart: their V^T rows 4cv + cc lie in 8 different 16-row blocks, which
