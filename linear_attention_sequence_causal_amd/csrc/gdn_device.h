@@ -138,6 +138,29 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// The same for x >= 0 (or NaN with the sign bit clear), returned uniform: such
+// floats order like their bit patterns as unsigned integers, so the butterfly is
+// an integer max that fuses with its DPP move, and the four row results are
+// combined on the scalar unit.  A NaN comes out as a NaN.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
+// 1/sqrt(x) for x >= 0 as the bare v_rsq_f32: x is raised to the smallest normal
+// float first (v_rsq_f32 takes no denormal input), so 0 gives 2^63, not infinity.
+__device__ __forceinline__ float rsq_normal(float x) {
+  return __builtin_amdgcn_rsqf(fmaxf(x, 1.17549435e-38f));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));

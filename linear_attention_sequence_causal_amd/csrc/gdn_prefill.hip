@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Hacc[dt][ct][i]));
-    m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(m))));
+    m = wave_max_nonneg(m);
     const int eb = exp_bits(m);
     if (eb > 0 && eb < 255) sexp = min(max(140 - eb, -60), 60);
     const float s0 = pow2f(sexp);
@@ -721,7 +721,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) ss += x[r][cc] * x[r][cc];
         ss = row16_sum(ss);
-        const float f = scale0 * rsqrtf(ss + eps);
+        const float f = scale0 * rsq_normal(ss + eps);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) x[r][cc] *= f;
       }
@@ -907,7 +907,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(Uacc[rt][ct][i]));
-      const int eb = exp_bits(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mv)))));
+      const int eb = exp_bits(wave_max_nonneg(mv));
       if (eb > 0 && eb < 255) vexp = min(max(130 - eb, -60), 60);
       const float sv = pow2f(vexp);
 #pragma unroll
@@ -1006,7 +1006,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mu = fmaxf(mu, fabsf(Uacc[rt][ct][i]));
-      mu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mu))));
+      mu = wave_max_nonneg(mu);
       const float bound = fmaf(32.0f, mu, gC * hb);
       const int eb = exp_bits(bound);
       int snew = sexp;
@@ -1021,14 +1021,20 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
       for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct], rho);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
-        const f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
+        // rho is a power of two: folding it into the row factors changes no rounding
+        f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+        f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gm[i] *= rho;
+          md[i] *= rho;
+        }
         const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            Oacc[rt][ct][i] = rho * fmaf(md[i], Uacc[rt][ct][i], Oacc[rt][ct][i] * gm[i]);
+            Oacc[rt][ct][i] = fmaf(md[i], Uacc[rt][ct][i], Oacc[rt][ct][i] * gm[i]);
           Oacc[rt][ct] = mfma16h(am, Ub[ct], Oacc[rt][ct]);
         }
       }
@@ -1113,14 +1119,17 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
       // o * rsqrt(ms) * w * z * sigmoid(z) with the RMS folded into the sigmoid's
       // denominator: 1 / (sd (1 + e^-z)), sd = sqrt(ms + eps)
       const float ms = ss * (1.0f / kD) + P.rms_eps;
-      const float sd = ms * rsqrtf(ms);
-      float val[16];
+      const float sd = ms * rsq_normal(ms);
+      float val[16], zv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float zraw = RZ::get(zw[j >> 3], j & 7);
-        const float zj = P.gate == 1 ? 1.0f : zraw;  // z sigmoid(z) or sigmoid(z)
-        const float e = __expf(-zraw);
-        val[j] = ov[j] * zj * nw[j] * __builtin_amdgcn_rcpf(fmaf(e, sd, sd));
+        zv[j] = RZ::get(zw[j >> 3], j & 7);
+        const float e = __expf(-zv[j]);
+        val[j] = ov[j] * nw[j] * __builtin_amdgcn_rcpf(fmaf(e, sd, sd));
+      }
+      if (P.gate == 0) {  // SiLU gate z sigmoid(z); the sigmoid gate stops at sigmoid(z)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) val[j] *= zv[j];
       }
       // one buffer over this chunk's o rows: stores of tokens at or past nvalid are dropped
       const int rowb = Hv * kD * (int)sizeof(T);
