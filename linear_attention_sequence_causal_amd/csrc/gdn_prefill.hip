@@ -105,6 +105,19 @@ __device__ __forceinline__ int exp_bits(float x) {
   return (int)((__float_as_uint(x) >> 23) & 0xFF);
 }
 
+// (fp16 in the low / high half of w) * b in one v_fma_mix_f32 (the fp16 value is
+// widened exactly, the product rounded once, as (float)h * b)
+__device__ __forceinline__ float mul_lo_h(uint32_t w, float b) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(b));
+  return d;
+}
+__device__ __forceinline__ float mul_hi_h(uint32_t w, float b) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(b));
+  return d;
+}
+
 // 2^e as a float, e in [-126, 127]
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
@@ -876,29 +889,21 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
     // ================= right-hand sides and the triangular solves =================
     // fp32 right-hand sides s_V beta V and beta gamma K of this wave's columns.  The
     // solve runs on fp16 operands: beta gamma K <= 1, and s_V = 2^vexp puts the wave's
-    // largest |beta V| in [2^3, 2^4); the solution Utilde (the chunk's values started
-    // from a zero state) is then at most 32 times that, and its intermediate rows of
-    // the blocked substitution at most 17 times more, all inside fp16's range.
+    // largest |V| in [2^3, 2^4), so |s_V beta V| < 2^4 (the beta vector here also holds
+    // 1 / |kConvScale| < 1); the solution Utilde (the chunk's values started from a
+    // zero state) is then at most 32 times that, and its intermediate rows of the
+    // blocked substitution at most 17 times more, all inside fp16's range.
     f32x4 Uacc[2][2], Wacc[2][2];  // [row tile of 16 tokens][column tile]
+    f32x4 vv[2][2];
     int vexp = 0;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
-      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * rt + 4 * lg);
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int dcol = 32 * wave + 16 * ct + ln;
-        const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
-        const f16x4_t kh = *reinterpret_cast<const f16x4_t *>(sKT + toff);
-        f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-        if (withV) vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Uacc[rt][ct][i] = be[i] * vv[i];
-          Wacc[rt][ct][i] = bg[i] * (float)kh[i];
-        }
+        vv[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (withV) vv[rt][ct] = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
       }
-    }
     if (withV) {
       float mv = 0.f;
 #pragma unroll
@@ -906,16 +911,29 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(Uacc[rt][ct][i]));
+          for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
       const int eb = exp_bits(wave_max_nonneg(mv));
       if (eb > 0 && eb < 255) vexp = min(max(130 - eb, -60), 60);
-      const float sv = pow2f(vexp);
+    }
+    const float sv = pow2f(vexp);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
+      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * rt + 4 * lg);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+      for (int i = 0; i < 4; ++i) be[i] *= sv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= sv;
+      for (int ct = 0; ct < 2; ++ct) {
+        const int dcol = 32 * wave + 16 * ct + ln;
+        const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
+        const uint2 kh = *reinterpret_cast<const uint2 *>(sKT + toff);  // 4 fp16 values
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] = be[i] * vv[rt][ct][i];
+        Wacc[rt][ct][0] = mul_lo_h(kh.x, bg[0]);
+        Wacc[rt][ct][1] = mul_hi_h(kh.x, bg[1]);
+        Wacc[rt][ct][2] = mul_lo_h(kh.y, bg[2]);
+        Wacc[rt][ct][3] = mul_hi_h(kh.y, bg[3]);
+      }
     }
     // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
     //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
