@@ -279,17 +279,10 @@ __device__ __forceinline__ u16x8 pack_h(const f32x4 &a, const f32x4 &b, float f 
   const uint32_t w2 = pk_f16(b[0] * f, b[1] * f), w3 = pk_f16(b[2] * f, b[3] * f);
   return __builtin_bit_cast(u16x8, make_uint4(w0, w1, w2, w3));
 }
-__device__ __forceinline__ u16x8 pack_h_half(const f32x4 &a) {  // tile b = 0
-  return __builtin_bit_cast(u16x8, make_uint4(pk_f16(a[0], a[1]), pk_f16(a[2], a[3]), 0u, 0u));
-}
 // A operand row fragment in the permuted k order: cols c0+4lg..+3 and c1+4lg..+3
 __device__ __forceinline__ u16x8 load_a_perm(const bf16_t *row, int c0, int c1, int lg) {
   return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg),
               *reinterpret_cast<const u16x4 *>(row + c1 + 4 * lg));
-}
-__device__ __forceinline__ u16x8 load_a_perm_half(const bf16_t *row, int c0, int lg) {
-  const u16x4 z = {0, 0, 0, 0};
-  return cat4(*reinterpret_cast<const u16x4 *>(row + c0 + 4 * lg), z);
 }
 
 // [row][tok] tiles over the chunk's 32 tokens (bf16 K^T hi/lo, fp32 V^T): the
@@ -938,23 +931,30 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
     // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
     //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
     {
-      const u16x8 at0 = load_a_perm_half(sTd + ln * kTdS, 0, lg);
+      // 16 x 16 blocks (K = 16): the A operand is row ln of the block, columns 4lg..4lg+3,
+      // the B operand the C-layout tile itself
+      const f16x4_t at0 = *reinterpret_cast<const f16x4_t *>(sTd + ln * kTdS + 4 * lg);
+      f16x4_t w0h[2], u0h[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[0][ct] = mfma16h(at0, pack_h_half(Wacc[0][ct]), Wacc[0][ct]);
-        if (withV) Uacc[0][ct] = mfma16h(at0, pack_h_half(Uacc[0][ct]), Uacc[0][ct]);
+        Wacc[0][ct] = mm16(at0, h4(Wacc[0][ct]), Wacc[0][ct]);
+        w0h[ct] = h4(Wacc[0][ct]);
+        if (withV) {
+          Uacc[0][ct] = mm16(at0, h4(Uacc[0][ct]), Uacc[0][ct]);
+          u0h[ct] = h4(Uacc[0][ct]);
+        }
       }
-      const u16x8 a10 = load_a_perm_half(sLo + (16 + ln) * kSqS, 0, lg);  // -L_10
+      const f16x4_t a10 = *reinterpret_cast<const f16x4_t *>(sLo + (16 + ln) * kSqS + 4 * lg);  // -L_10
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mfma16h(a10, pack_h_half(Wacc[0][ct]), Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mfma16h(a10, pack_h_half(Uacc[0][ct]), Uacc[1][ct]);
+        Wacc[1][ct] = mm16(a10, w0h[ct], Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mm16(a10, u0h[ct], Uacc[1][ct]);
       }
-      const u16x8 at1 = load_a_perm_half(sTd + (16 + ln) * kTdS, 0, lg);
+      const f16x4_t at1 = *reinterpret_cast<const f16x4_t *>(sTd + (16 + ln) * kTdS + 4 * lg);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mfma16h(at1, pack_h_half(Wacc[1][ct]), Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mfma16h(at1, pack_h_half(Uacc[1][ct]), Uacc[1][ct]);
+        Wacc[1][ct] = mm16(at1, h4(Wacc[1][ct]), Wacc[1][ct]);
+        if (withV) Uacc[1][ct] = mm16(at1, h4(Uacc[1][ct]), Uacc[1][ct]);
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
