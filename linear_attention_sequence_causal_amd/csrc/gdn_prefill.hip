@@ -5,6 +5,7 @@
 //   L[i][j] = beta_i e^{G_i-G_j} (k_i . k_j)  (j < i)      T = (I + L)^-1
 //   W       = T diag(beta gamma) K                         Utilde = T diag(beta) V
 //   U       = Utilde - W H                                 ("v_new")
+//           = T (diag(beta) V - diag(beta gamma) K H)      (the form computed: one solve)
 //   M[i][j] = e^{G_i-G_j} (q_i . k_j)  (j <= i)
 //   O       = diag(gamma) Q H + M U                        (y of every token)
 //   H      <- gamma_C H + K^T diag(e^{G_C-G}) U            (state * chunk_decay + key^T v_new)
@@ -17,10 +18,10 @@
 //
 // Precision plan (fp32 accumulation, fp32 state): every product takes fp16
 // operands.  q and k are unit-norm (q_scale multiplies o at the end), |L| <= 1 and
-// the entries of each (I + L_bb)^-1 stay below 2^15, |W| <= 1; beta V is scaled by a
-// power of two per wave before the triangular solve, and the state by another one
-// (sigma, with a tracked bound that keeps |sigma H| below 2^14), so every fp16
-// operand is in range.  The identity part of T V (beta V, beta gamma K) and the
+// the entries of each (I + L_bb)^-1 stay below 2^15; the right-hand side of the
+// triangular solve is scaled by a power of two per wave, and the state by another
+// one (sigma, with a tracked bound that keeps |sigma H| below 2^14), so every fp16
+// operand is in range.  The identity part of the solve (its right-hand side) and the
 // diagonal of M U are applied in fp32.  Powers of two are exact: o and the final
 // state are divided by them at the end.
 //
@@ -151,11 +152,9 @@ constexpr int kMaxSegChunks = 256;     // segments hold at most 8192 tokens
 
 // Byte offsets.  Shared by the workgroup's v heads: the fp16 unit-norm q and k rows,
 // the fp16 K^T tile, the conv taps of q, k and every v head, the RMSNorm weight.  One
-// block per v head: V^T (fp32; the o tile of the epilogue and map mode's chunk sums
-// reuse it), M, the gate buffers, M's diagonal, -L and T_bb - I (regions of their
-// own, so the waves that form them need not wait for the others' gram products).
-// -W of head slot 0 reuses the k rows (dead after the gram products); slot 1 has its
-// own.
+// block per v head: V^T (fp32; map mode's chunk sums reuse it before the chunk loop),
+// M, the gate buffers, M's diagonal, -L and T_bb - I (regions of their own, so the
+// waves that form them need not wait for the others' gram products), the o tile.
 template <int NH> struct Lds {
   static constexpr int QF = 0;                           // fp16 q [32][136] (Q K^T, Q H)
   static constexpr int KF = QF + kChunk * kRowS * 2;     // fp16 k [32][136] (K K^T, Q K^T)
@@ -169,11 +168,10 @@ template <int NH> struct Lds {
   static constexpr int H_MDIAG = H_GATES + 2 * kGateN * 4;
   static constexpr int H_LO = H_MDIAG + kChunk * 4;      // fp16 [32][36] -L (strictly lower)
   static constexpr int H_TD = H_LO + kChunk * kSqS * 2;  // fp16 [2][16][24] T_bb - I
-  static constexpr int H_BYTES = H_TD + 2 * 16 * kTdS * 2;
-  static constexpr int W1 = HEAD + NH * H_BYTES;         // fp16 [32][136] -W of slot 1
-  static constexpr int BYTES = W1 + (NH == 2 ? kChunk * kRowS * 2 : 0);
+  static constexpr int H_O = H_TD + 2 * 16 * kTdS * 2;   // fp32 [32 tok][132] o tile
+  static constexpr int H_BYTES = H_O + kChunk * kOS * 4;
+  static constexpr int BYTES = HEAD + NH * H_BYTES;
   static_assert(HEAD % 16 == 0 && H_BYTES % 16 == 0 && H_TD % 16 == 0, "16-byte tiles");
-  static_assert(kChunk * kOS * 4 <= 128 * kVtS * 4, "o tile overflows the V^T region");
   static_assert(kMaxSegChunks * 4 <= 128 * kVtS * 4, "chunk sums overflow the V^T region");
   static_assert(NH == 2 ? BYTES <= 160 * 1024 : 2 * BYTES <= 160 * 1024,
                 "LDS budget: two 4-wave or one 8-wave workgroup per compute unit");
@@ -415,13 +413,14 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
   float *const sConvW = reinterpret_cast<float *>(smem + L::CONVW);
   float *const sNW = reinterpret_cast<float *>(smem + L::NW);
   float *const sVT = reinterpret_cast<float *>(hblk + L::H_VT);
-  float *const sO = sVT;  // the o tile (V^T is dead after the right-hand sides)
+  // the o tile has a region of its own: a wave writes it while the head's other waves
+  // may still read their V^T rows
+  float *const sO = reinterpret_cast<float *>(hblk + L::H_O);
   float *const sGates = reinterpret_cast<float *>(hblk + L::H_GATES);
   float *const sMdiag = reinterpret_cast<float *>(hblk + L::H_MDIAG);
   bf16_t *const sLo = reinterpret_cast<bf16_t *>(hblk + L::H_LO);
   bf16_t *const sTd = reinterpret_cast<bf16_t *>(hblk + L::H_TD);
   bf16_t *const sM = reinterpret_cast<bf16_t *>(hblk + L::H_M);
-  bf16_t *const sW = reinterpret_cast<bf16_t *>(smem + (hh ? L::W1 : L::KF));
 
   // ---- roles of the prologue ----------------------------------------------------
   // Before the first barrier every wave convolves q (roles 0-1) or k (roles 2-3):
@@ -429,7 +428,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
   // channels (for the L2 norm); wave qi of its kind takes tokens 4 TPT qi .. + 4 TPT - 1.
   // Map mode needs no q: all four waves convolve k (and the A half needs no v).  After
   // the barrier every thread convolves 4 tokens x 4 channels of its head's v, which
-  // only the right-hand side (after barrier 3) reads.
+  // only the right-hand side (after barrier 2) reads.
   constexpr int TPT = (NH == 2 || MODE == kMap) ? 2 : 4;  // q/k tokens per thread
   const int role = (MODE == kMap || wave >= 2) ? 1 : 0;   // uniform per wave
   int cg = lane & 15;                  // q/k channels 8cg .. 8cg+7
@@ -693,8 +692,8 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 
     // ================= prologue: conv + SiLU (+ L2) -> LDS ========================
     // Issue priority follows each phase's longest waves: here the k waves (K^T
-    // regrouping), from barrier 1 to barrier 4 roles 0 and 1 (their diagonal gram
-    // tiles, L/M, the 16x16 inverses, then the q waves' prefetch), and after barrier 4
+    // regrouping), from barrier 1 to barrier 2 roles 0 and 1 (their diagonal gram
+    // tiles, L/M, the 16x16 inverses, then the q waves' prefetch), and after that
     // the second head's waves (NH = 2), which the SIMDs otherwise serve after the older
     // first-head waves, so that they do not arrive last at barrier 1.  With NH = 1 the
     // two workgroups on a compute unit fill the SIMDs between these phases.
@@ -875,116 +874,24 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
     // next chunk's raw rows: the k waves (off the diagonal tiles) go first so that
     // the q waves' loads after the barrier do not queue behind theirs
     if (role == 1 && c + 1 < nchunks) load_chunk(t0 + kChunk);
-    __syncthreads();  // (3) -L, M, T_bb - I and the next gates ready; Q and K consumed
+    __syncthreads();  // (2) -L, M, T_bb - I, V^T and the next gates ready
     refresh();
     if (role == 0 && c + 1 < nchunks) load_chunk(t0 + kChunk);  // next chunk's raw rows
 
-    // ================= right-hand sides and the triangular solves =================
-    // fp32 right-hand sides s_V beta V and beta gamma K of this wave's columns.  The
-    // solve runs on fp16 operands: beta gamma K <= 1, and s_V = 2^vexp puts the wave's
-    // largest |V| in [2^3, 2^4), so |s_V beta V| < 2^4 (the beta vector here also holds
-    // 1 / |kConvScale| < 1); the solution Utilde (the chunk's values started from a
-    // zero state) is then at most 32 times that, and its intermediate rows of the
-    // blocked substitution at most 17 times more, all inside fp16's range.
-    f32x4 Uacc[2][2], Wacc[2][2];  // [row tile of 16 tokens][column tile]
-    f32x4 vv[2][2];
-    int vexp = 0;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int dcol = 32 * wave + 16 * ct + ln;
-        vv[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (withV) vv[rt][ct] = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
-      }
-    if (withV) {
-      float mv = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
-      const int eb = exp_bits(wave_max_nonneg(mv));
-      if (eb > 0 && eb < 255) vexp = min(max(130 - eb, -60), 60);
-    }
-    const float sv = pow2f(vexp);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
-      const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * rt + 4 * lg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) be[i] *= sv;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int dcol = 32 * wave + 16 * ct + ln;
-        const int toff = tok_swz(dcol, 16 * rt + 4 * lg, kTokS);
-        const uint2 kh = *reinterpret_cast<const uint2 *>(sKT + toff);  // 4 fp16 values
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] = be[i] * vv[rt][ct][i];
-        Wacc[rt][ct][0] = mul_lo_h(kh.x, bg[0]);
-        Wacc[rt][ct][1] = mul_hi_h(kh.x, bg[1]);
-        Wacc[rt][ct][2] = mul_lo_h(kh.y, bg[2]);
-        Wacc[rt][ct][3] = mul_hi_h(kh.y, bg[3]);
-      }
-    }
-    // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
-    //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
-    {
-      // 16 x 16 blocks (K = 16): the A operand is row ln of the block, columns 4lg..4lg+3,
-      // the B operand the C-layout tile itself
-      const f16x4_t at0 = *reinterpret_cast<const f16x4_t *>(sTd + ln * kTdS + 4 * lg);
-      f16x4_t w0h[2], u0h[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        Wacc[0][ct] = mm16(at0, h4(Wacc[0][ct]), Wacc[0][ct]);
-        w0h[ct] = h4(Wacc[0][ct]);
-        if (withV) {
-          Uacc[0][ct] = mm16(at0, h4(Uacc[0][ct]), Uacc[0][ct]);
-          u0h[ct] = h4(Uacc[0][ct]);
-        }
-      }
-      const f16x4_t a10 = *reinterpret_cast<const f16x4_t *>(sLo + (16 + ln) * kSqS + 4 * lg);  // -L_10
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mm16(a10, w0h[ct], Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mm16(a10, u0h[ct], Uacc[1][ct]);
-      }
-      const f16x4_t at1 = *reinterpret_cast<const f16x4_t *>(sTd + (16 + ln) * kTdS + 4 * lg);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        Wacc[1][ct] = mm16(at1, h4(Wacc[1][ct]), Wacc[1][ct]);
-        if (withV) Uacc[1][ct] = mm16(at1, h4(Uacc[1][ct]), Uacc[1][ct]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sW[(16 * rt + 4 * lg + i) * kRowS + 32 * wave + 16 * ct + ln] = f2h(-Wacc[rt][ct][i]);
-    }
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // (4) -W ready
-    refresh();
     if (NH == 2 && hh == 1) __builtin_amdgcn_s_setprio(1);
 
-    // ================= Q H, U = Utilde - W H, O += M U, H update ==================
+    // ================= K H and Q H, U by one triangular solve, O, H update ==========
+    // With W = T diag(beta gamma) K and Utilde = T diag(beta) V, the new values are
+    //   U = Utilde - W H = T (diag(beta) V - diag(beta gamma) K H),
+    // so the chunk needs K H (the same products as W H) and one solve of this wave's
+    // 32 columns, with no W tile shared between the waves.
     // The accumulators hold sigma H (sigma = 2^sexp per wave) with |sigma H| below 2^14
-    // (hb bounds it, see the update), so H enters Q H and W H as fp16 B operands:
+    // (hb bounds it, see the update), so H enters K H and Q H as fp16 B operands:
     // Hb[kb][ct] slots 8lg+j <-> dk 32kb + 4lg + j (j<4), 32kb + 16 + 4lg + j - 4 (j >= 4).
-    // |W| <= 1 (its rows are the initial state's read-out directions, products of the
-    // contractions alpha (I - beta k k^T)) and Q is unit-norm.  Utilde is brought from
-    // s_V to sigma first, so U = Utilde - W H comes out as sigma U.
-    f32x4 Oacc[2][2];
+    // K and Q are unit-norm.
+    f32x4 Uacc[2][2], Oacc[2][2];  // [row tile of 16 tokens][column tile]
     {
-      const float vs = pow2f(sexp - vexp);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= vs;
       u16x8 Hb[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -993,15 +900,18 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Oacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < 2; ++ct) {
+          Uacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+          Oacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       // k-block outer: four independent accumulators per product and block
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const u16x8 aw = load_a_perm(sW + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
+          const u16x8 ak = load_a_perm(sKf + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Uacc[rt][ct] = mfma16h(aw, Hb[kb][ct], Uacc[rt][ct]);
+          for (int ct = 0; ct < 2; ++ct) Uacc[rt][ct] = mfma16h(ak, Hb[kb][ct], Uacc[rt][ct]);
           if (MODE == kFull) {
             const u16x8 aq = load_a_perm(sQf + (16 * rt + ln) * kRowS, 32 * kb, 32 * kb + 16, lg);
 #pragma unroll
@@ -1010,42 +920,101 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
         }
       }
     }
-    // The chunk's scale step rho (a power of two): the new state rho (gamma_C sigma H +
-    // K^T sigma u) and the fp16 operands rho sigma U stay below 2^14 with the bound
-    // hb' = gamma_C hb + 32 max|sigma U| (|K^T u| <= 32 max|u| for unit keys, u = U
-    // e^{G_C - G}, |u| <= |U|) placed in [2^13, 2^14); hb tracks a bound on |sigma H|.
-    // sigma stays within 2^-60 .. 2^60; rho = 1 when the bound is zero or not finite.
-    float rho;
+    // Right-hand side R = sigma beta V - beta gamma (K sigma H) in fp32 (the beta vector of
+    // V also holds 1 / kConvScale), then scaled by s = 2^rexp, which puts the wave's
+    // largest |R| in [2^3, 2^4): the solution X = s sigma U is then at most 32 times
+    // that, and the intermediate rows of the blocked substitution at most 17 times
+    // more, all inside fp16's range.
+    int rexp = 0;
     {
-      float mu = 0.f;
+      const float sg = pow2f(sexp);
+      float mr = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const f32x4 be = *reinterpret_cast<const f32x4 *>(sBv + 16 * rt + 4 * lg);
+        const f32x4 bg = *reinterpret_cast<const f32x4 *>(sBG + 16 * rt + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+          if (withV) {
+            const int dcol = 32 * wave + 16 * ct + ln;
+            vv = *reinterpret_cast<const f32x4 *>(sVT + tok_swz(dcol, 16 * rt + 4 * lg, kVtS));
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Uacc[rt][ct][i] = fmaf(-bg[i], Uacc[rt][ct][i], (be[i] * sg) * vv[i]);
+            mr = fmaxf(mr, fabsf(Uacc[rt][ct][i]));
+          }
+        }
+      }
+      const int eb = exp_bits(wave_max_nonneg(mr));
+      if (eb > 0 && eb < 255) rexp = min(max(130 - eb, -120), 120);
+      const float sr = pow2f(rexp);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mu = fmaxf(mu, fabsf(Uacc[rt][ct][i]));
-      mu = wave_max_nonneg(mu);
+          for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= sr;
+    }
+    // block forward substitution (I + L) X = R over two row blocks of 16 tokens:
+    //   X_0 = (I + (T_00 - I)) R_0,   X_1 = (I + (T_11 - I)) (R_1 - L_10 X_0)
+    // on 16 x 16 blocks (K = 16): the A operand is row ln of the block, columns
+    // 4lg..4lg+3, the B operand the C-layout tile itself; the identity part in fp32
+    {
+      const f16x4_t at0 = *reinterpret_cast<const f16x4_t *>(sTd + ln * kTdS + 4 * lg);
+      f16x4_t x0h[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        Uacc[0][ct] = mm16(at0, h4(Uacc[0][ct]), Uacc[0][ct]);
+        x0h[ct] = h4(Uacc[0][ct]);
+      }
+      const f16x4_t a10 = *reinterpret_cast<const f16x4_t *>(sLo + (16 + ln) * kSqS + 4 * lg);  // -L_10
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) Uacc[1][ct] = mm16(a10, x0h[ct], Uacc[1][ct]);
+      const f16x4_t at1 = *reinterpret_cast<const f16x4_t *>(sTd + (16 + ln) * kTdS + 4 * lg);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) Uacc[1][ct] = mm16(at1, h4(Uacc[1][ct]), Uacc[1][ct]);
+    }
+    // The chunk's scale step rho (a power of two): the new state rho (gamma_C sigma H +
+    // K^T sigma u) and the fp16 operands rho sigma U stay below 2^14 with the bound
+    // hb' = gamma_C hb + 32 max|sigma U| (|K^T u| <= 32 max|u| for unit keys, u = U
+    // e^{G_C - G}, |u| <= |U|) placed in [2^13, 2^14); hb tracks a bound on |sigma H|.
+    // sigma stays within 2^-60 .. 2^60; rho = 1 when the bound is zero or not finite.
+    // Uacc holds X = s sigma U, so every consumer takes it times f = rho / s.
+    float rho, f;
+    {
+      float mx = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Uacc[rt][ct][i]));
+      const float mu = wave_max_nonneg(mx) * pow2f(-rexp);
       const float bound = fmaf(32.0f, mu, gC * hb);
       const int eb = exp_bits(bound);
       int snew = sexp;
       if (eb > 0 && eb < 255) snew = min(max(sexp + 140 - eb, -60), 60);
       rho = pow2f(snew - sexp);
+      // below 2^-126 the U terms are far under fp32 resolution of the state
+      f = pow2f(min(max(snew - sexp - rexp, -126), 127));
       hb = bound * rho;
       sexp = snew;
     }
     if (MODE == kFull) {  // O = gamma Q H + diag(M) U + M_off U, scaled by rho sigma / q_scale
       u16x8 Ub[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct], rho);
+      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct], f);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        // rho is a power of two: folding it into the row factors changes no rounding
+        // rho and f are powers of two: folding them into the row factors changes no rounding
         f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
         f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           gm[i] *= rho;
-          md[i] *= rho;
+          md[i] *= f;
         }
         const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
 #pragma unroll
@@ -1065,7 +1034,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
         const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * rt + 4 * lg);
         f32x4 dr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dr[i] = dec[i] * rho;
+        for (int i = 0; i < 4; ++i) dr[i] = dec[i] * f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           uh[ct][2 * rt] = pk_f16(Uacc[rt][ct][0] * dr[0], Uacc[rt][ct][1] * dr[1]);
@@ -1103,7 +1072,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
           for (int i = 0; i < 4; ++i)
             sO[(16 * rt + 4 * lg + i) * kOS + 32 * wave + 16 * ct + ln] = Oacc[rt][ct][i] * rsig;
     }
-    __syncthreads();  // (5) o tile ready; this chunk's other LDS tiles are consumed
+    __syncthreads();  // (3) o tile ready; this chunk's other LDS tiles are consumed
     refresh();
     if (MODE == kFull) {
       // token ht >> 3 (8 lanes per token), columns 8e.. and 64+8e.. with e = ht & 7;
