@@ -180,6 +180,36 @@ static_assert(kChunk == 32, "the tile code below is written for 32-token chunks"
 
 enum Mode { kFull = 0, kMap = 1 };
 
+// Set (to 1) by the segment table (or, for one sequence, by the kernels) when
+// cu_seqlens is invalid; read and cleared by the host (gdn_check_device_errors).  One
+// copy per device.
+__device__ int g_prefill_bad_cu = 0;
+
+// Segments of a sequence of len tokens: max(1, ceil(len / seg_len)).
+__host__ __device__ __forceinline__ int seg_count(int len, int seg_len) {
+  return len == 0 ? 1 : (len + seg_len - 1) / seg_len;
+}
+// Record of segment s of sequence seq = tokens [b, e): the chunks are spread evenly
+// over the segments (the first nch % ns get one more), so every segment of a split
+// sequence holds >= 4 full chunks.  first / firstmap: the global index of the
+// sequence's first segment / map slot (the non-final segments take map slots in order).
+__device__ __forceinline__ SegInfo seg_record(int seq, int b, int e, int s, int seg_len, int first,
+                                              int firstmap) {
+  const int len = e - b;
+  const int ns = seg_count(len, seg_len), nch = (len + kChunk - 1) / kChunk;
+  const int q = nch / ns, rem = nch % ns;
+  SegInfo si;
+  si.seq = seq;
+  si.begin = b + kChunk * (s * q + min(s, rem));
+  si.len = max(0, min(kChunk * (q + (s < rem ? 1 : 0)), e - si.begin));
+  si.idx = s;
+  si.nseg = ns;
+  si.first = first;
+  si.map = s < ns - 1 ? firstmap + s : -1;
+  si.seq_begin = b;
+  return si;
+}
+
 struct PrefillArgs {
   const void *q, *k, *v, *z;
   const float *a, *b;
@@ -200,7 +230,20 @@ struct PrefillArgs {
   int Hk, Hv;
   int64_t Cc;
   int gate;                // output gate: 0 SiLU(z), 1 sigmoid(z)
+  // one sequence: no table is built, the kernels form each segment's record from
+  // (seg_len, T) with seg_record; cu (cu_seqlens or NULL) is checked by every workgroup
+  int one_seq, seg_len, T;
+  const int32_t *cu;
 };
+
+// One sequence with a cu_seqlens table: it must read {0, T}.  A workgroup that finds
+// otherwise flags the call (as the segment table does for longer tables) and exits.
+__device__ __forceinline__ bool one_seq_table_bad(const int32_t *cu, int T) {
+  if (!cu) return false;
+  const bool bad = cu[0] != 0 || cu[1] != T;
+  if (bad) g_prefill_bad_cu = 1;
+  return bad;
+}
 
 // NC channels of one token as raw 32-bit words (bf16 pairs or fp32)
 template <typename T, int NC>
@@ -395,14 +438,16 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
   const bool withV = MODE == kFull || half == 1;
 
   int segi;
+  if (P.one_seq && one_seq_table_bad(P.cu, P.T)) return;
+  const int nseg1 = P.one_seq ? seg_count(P.T, P.seg_len) : 0;  // one sequence: its segments
   if (MODE == kFull) {
-    if (unit >= P.hdr[0]) return;
-    segi = P.order[unit];
+    if (unit >= (P.one_seq ? nseg1 : P.hdr[0])) return;
+    segi = P.one_seq ? unit : P.order[unit];
   } else {
-    if (unit >= P.hdr[1]) return;
-    segi = P.map_seg[unit];
+    if (unit >= (P.one_seq ? nseg1 - 1 : P.hdr[1])) return;
+    segi = P.one_seq ? unit : P.map_seg[unit];
   }
-  const SegInfo seg = P.segs[segi];
+  const SegInfo seg = P.one_seq ? seg_record(0, 0, P.T, segi, P.seg_len, 0, 0) : P.segs[segi];
   const int seq_begin = seg.seq_begin;
   const int seg_end = seg.begin + seg.len;
 
@@ -538,7 +583,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
       if (seg.idx > 0) {
         // start state after the previous segment: its B map itself when that
         // segment's A map is zero, else what the combine pass wrote
-        const int64_t m = P.segs[segi - 1].map;
+        const int64_t m = P.one_seq ? segi - 1 : P.segs[segi - 1].map;
         H0 = P.map_zero[m * Hv + h] ? P.maps + ((m * Hv + h) * 2 + 1) * kD * kD
                                     : P.starts + ((int64_t)segi * Hv + h) * kD * kD;
       } else if (P.init_state) {
@@ -1147,9 +1192,6 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 }
 
 // ------------------------------------------------------------ segment table
-// Set (to 1) by the segment table when cu_seqlens is invalid; read and cleared by
-// the host (gdn_check_device_errors).  One copy per device.
-__device__ int g_prefill_bad_cu = 0;
 
 // One workgroup: sequence lengths -> segments (prefix sums over sequences).
 // cu_seqlens must have cu[0] = 0, cu[i] <= cu[i+1] and cu[N] = T; otherwise the
@@ -1184,16 +1226,14 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
   }
   for (int n0 = 0; n0 < N; n0 += 1024) {
     const int n = n0 + tid;
-    int b = 0, e = 0, ns = 0, nm = 0, nch = 0;
+    int b = 0, e = 0, ns = 0, nm = 0;
     if (n < N) {
       b = cu ? cu[n] : 0;
       e = cu ? cu[n + 1] : (int)T;
       b = max(0, min(b, (int)T));       // keep every access inside [0, T)
       e = max(b, min(e, (int)T));
-      const int len = e - b;
-      ns = len == 0 ? 1 : (len + seg_len - 1) / seg_len;
+      ns = seg_count(e - b, seg_len);
       nm = ns - 1;
-      nch = (len + kChunk - 1) / kChunk;
     }
     s_nseg[tid] = ns;
     s_nmap[tid] = nm;
@@ -1210,21 +1250,11 @@ __global__ void __launch_bounds__(1024) segment_table_kernel(
     const int firstmap = s_base_map + s_nmap[tid] - nm;
     if (n < N) {
       seq_first[n] = first;
-      // chunks are spread evenly over the segments (the first nch % ns get one
-      // more), so every segment of a split sequence holds >= 4 full chunks
-      const int q = nch / ns, rem = nch % ns;
       for (int s = 0; s < ns; ++s) {
         const int idx = first + s;
         if (idx >= max_segments) break;
-        SegInfo si;
-        si.seq = n;
-        si.begin = b + kChunk * (s * q + min(s, rem));
-        si.len = max(0, min(kChunk * (q + (s < rem ? 1 : 0)), e - si.begin));
-        si.idx = s;
-        si.nseg = ns;
-        si.first = first;
-        si.map = (s < ns - 1 && firstmap + s < max_maps) ? firstmap + s : -1;
-        si.seq_begin = b;
+        SegInfo si = seg_record(n, b, e, s, seg_len, first, firstmap);
+        if (firstmap + s >= max_maps) si.map = -1;
         segs[idx] = si;
         if (si.map >= 0) map_seg[si.map] = idx;
       }
@@ -1306,15 +1336,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
                                                       const int32_t *seq_first, int N,
                                                       const float *init_state, const float *maps,
                                                       const int32_t *map_zero, float *starts,
-                                                      int Hv) {
+                                                      int Hv, int one_seq, int seg_len, int T,
+                                                      const int32_t *cu) {
   __shared__ float sH[kD][17];
   const int slice = blockIdx.x % 8;
   const int h = (blockIdx.x / 8) % Hv;
   const int n = blockIdx.x / (8 * Hv);  // sequence
   if (n >= N) return;
-  const int segi = seq_first[n];  // its first segment
-  if (segi < 0 || segi >= hdr[0]) return;  // (no segments when the table was invalid)
-  const SegInfo s0 = segs[segi];
+  // its first segment (one sequence without a table: segment 0, records formed here)
+  if (one_seq && one_seq_table_bad(cu, T)) return;
+  const int segi = one_seq ? 0 : seq_first[n];
+  if (!one_seq && (segi < 0 || segi >= hdr[0])) return;  // (no segments: invalid table)
+  const SegInfo s0 = one_seq ? seg_record(0, 0, T, 0, seg_len, 0, 0) : segs[segi];
   if (s0.nseg < 2) return;
   const int tid = threadIdx.x;
   const int row = tid >> 1, c0 = (tid & 1) * 8;  // 8 outputs per thread
@@ -1341,7 +1374,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const SegInfo *segs, const
     const int nb = min(256, s0.nseg - 1 - sb);
     __syncthreads();  // previous batch consumed
     if (tid < nb) {
-      const int m = segs[segi + sb + tid].map;
+      const int m = one_seq ? sb + tid : segs[segi + sb + tid].map;
       sMap[tid] = m;
       sZero[tid] = map_zero[(int64_t)m * Hv + h];
     }
@@ -1485,7 +1518,7 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
   // slots: 0 segment table, 1 segment maps (both halves, one launch), 2 combine,
   // 3 full pass, 4 conv-state copy
   if (tm) for (int i = 0; i < kTimedKernels; ++i) tm->ran[i] = false;
-  if (tm) tm->ran[0] = true;  // the segment table was launched by the caller
+  if (tm) tm->ran[0] = !args.one_seq;  // the segment table (launched by the caller)
   mark(1);
   // grids cover ceil(units * Hk / 8) * 8 * r / NH ids (see the id mapping in chunk_kernel)
   auto ids = [&](int64_t units, int nh) {
@@ -1499,7 +1532,8 @@ static hipError_t launch_typed(const PrefillPlan &plan, PrefillArgs args, const 
     dim3 g2((unsigned)((int64_t)N * Hv * 8));
     hipLaunchKernelGGL(combine_kernel, g2, dim3(256), 0, stream, args.segs, args.hdr,
                        args.seq_first, N, args.init_state, (const float *)args.maps,
-                       args.map_zero, args.starts, Hv);
+                       args.map_zero, args.starts, Hv, args.one_seq, args.seg_len, args.T,
+                       args.cu);
     mark(3);
     if (tm) tm->ran[1] = tm->ran[2] = true;
   } else {
@@ -1539,9 +1573,13 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   int32_t *map_seg = (int32_t *)(segs + plan.max_segments);
   int32_t *seq_first = map_seg + plan.max_maps + 1;
   int32_t *order = seq_first + num_seqs;
-  hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, num_seqs,
-                     total_tokens, plan.seg_len, plan.max_segments, plan.max_maps, segs, hdr,
-                     map_seg, seq_first, order);
+  // One sequence needs no table: every kernel forms the records it reads (seg_record),
+  // takes units in order and checks a given cu_seqlens itself.
+  const bool one_seq = num_seqs == 1;
+  if (!one_seq)
+    hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens,
+                       num_seqs, total_tokens, plan.seg_len, plan.max_segments, plan.max_maps,
+                       segs, hdr, map_seg, seq_first, order);
   PrefillArgs A;
   A.q = q; A.k = k; A.v = v; A.z = z; A.a = a; A.b = b;
   A.conv_w = p.conv_weight; A.A_log = p.A_log; A.dt_bias = p.dt_bias; A.norm_w = p.norm_weight;
@@ -1554,6 +1592,10 @@ hipError_t launch_prefill(const PrefillPlan &plan, const void *q, const void *k,
   A.Hk = p.num_qk_heads; A.Hv = p.num_v_heads;
   A.gate = p.output_gate;
   A.Cc = 2LL * p.num_qk_heads * kD + (int64_t)p.num_v_heads * kD;
+  A.one_seq = one_seq ? 1 : 0;
+  A.seg_len = plan.seg_len;
+  A.T = (int)total_tokens;
+  A.cu = cu_seqlens;
   if (p.act_dtype == GDN_BF16)
     return launch_typed<bf16_t>(plan, A, cu_seqlens, num_seqs, total_tokens, conv_state_out,
                                 stream, tm);

@@ -12,7 +12,9 @@
 //                      the fused prologue and epilogue; writes o and, for the
 //                      last segment, the final state.
 // A sequence that fits in one segment runs pass 3 only.  The segment table is
-// built on the device from cu_seqlens, so the host needs only N and T.
+// built on the device from cu_seqlens, so the host needs only N and T; a call with
+// one sequence builds none (each kernel forms the records it reads, and checks a
+// given cu_seqlens itself).
 #pragma once
 
 #include <hip/hip_runtime.h>
