@@ -1026,7 +1026,7 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
     // hb' = gamma_C hb + 32 max|sigma U| (|K^T u| <= 32 max|u| for unit keys, u = U
     // e^{G_C - G}, |u| <= |U|) placed in [2^13, 2^14); hb tracks a bound on |sigma H|.
     // sigma stays within 2^-60 .. 2^60; rho = 1 when the bound is zero or not finite.
-    // Uacc holds X = s sigma U, so every consumer takes it times f = rho / s.
+    // Uacc holds X = s sigma U; f = rho / s brings it to rho sigma U.
     float rho, f;
     {
       float mx = 0.f;
@@ -1047,20 +1047,24 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
       hb = bound * rho;
       sexp = snew;
     }
+    // X -> rho sigma U, which every consumer below takes as it is (f is a power of two)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Uacc[rt][ct][i] *= f;
     if (MODE == kFull) {  // O = gamma Q H + diag(M) U + M_off U, scaled by rho sigma / q_scale
       u16x8 Ub[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct], f);
+      for (int ct = 0; ct < 2; ++ct) Ub[ct] = pack_h(Uacc[0][ct], Uacc[1][ct]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        // rho and f are powers of two: folding them into the row factors changes no rounding
+        // rho is a power of two: folding it into the row factor changes no rounding
         f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
-        f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
+        const f32x4 md = *reinterpret_cast<const f32x4 *>(sMdiag + 16 * rt + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          gm[i] *= rho;
-          md[i] *= f;
-        }
+        for (int i = 0; i < 4; ++i) gm[i] *= rho;
         const u16x8 am = load_a_perm(sM + (16 * rt + ln) * kSqS, 0, 16, lg);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
@@ -1077,13 +1081,10 @@ __global__ void __launch_bounds__(kThreads * NH, 2 / NH) chunk_kernel(PrefillArg
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * rt + 4 * lg);
-        f32x4 dr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dr[i] = dec[i] * f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          uh[ct][2 * rt] = pk_f16(Uacc[rt][ct][0] * dr[0], Uacc[rt][ct][1] * dr[1]);
-          uh[ct][2 * rt + 1] = pk_f16(Uacc[rt][ct][2] * dr[2], Uacc[rt][ct][3] * dr[3]);
+          uh[ct][2 * rt] = pk_f16(Uacc[rt][ct][0] * dec[0], Uacc[rt][ct][1] * dec[1]);
+          uh[ct][2 * rt + 1] = pk_f16(Uacc[rt][ct][2] * dec[2], Uacc[rt][ct][3] * dec[3]);
         }
       }
       u16x8 Uh[2];
