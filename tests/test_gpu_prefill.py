@@ -326,6 +326,21 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+@gpu
+def test_one_sequence_with_or_without_cu_seqlens_is_bitwise():
+    """One sequence builds no segment table: its records come from (segment length, T).
+    Given as cu_seqlens = [0, T] or as NULL, the call runs the same segments (several
+    here, with a ragged tail) and is bitwise equal."""
+    w = S.scaled(S.PREFILL_4K, lengths=(1517,), num_qk_heads=2, num_v_heads=4, seed=19,
+                 init_state_std=0.01, conv_history=True)
+    d = S.prefill_inputs(w, "cuda")
+    o1, f1, c1 = run_gpu(d, cu=True)
+    o2, f2, c2 = run_gpu(d, cu=False)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2) and torch.equal(c1, c2)
+    o_ref, fs_ref, _, _ = run_oracle(d)
+    assert rel_l2(S.to_f64(o1), o_ref) <= O_TOL and rel_l2(S.to_f64(f1), fs_ref) <= STATE_TOL
+
+
 def _split_run(d, t0):
     gdn = _gdn()
     ca = lambda t, a, b: t[a:b].contiguous()
