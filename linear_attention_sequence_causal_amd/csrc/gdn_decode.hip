@@ -433,6 +433,11 @@ __device__ __forceinline__ float rows4_sum(float x) {
                                                   false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Sum over the 64 lanes, left in every lane: a DPP sum inside each 16-lane row, then
+// the four rows (about 8 instructions, against ~30 for a shuffle butterfly).
+__device__ __forceinline__ float wave_sum_dpp(float x) { return rows4_sum(row16_sum(x)); }
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
 
 // One workgroup of four waves per (sequence, v head): wave w holds value columns
 // 32 w + 2 cg, + 1 (cg = lane & 15) and key rows 32 rg .. + 31 (rg = lane >> 4) of the
@@ -549,7 +554,8 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
 #pragma unroll
         for (int t = 0; t < kMaxStepTokens; ++t)
-          xv[t][u] = siluf_(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
+          if (t < n)
+            xv[t][u] = silu_fast(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
         // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
         // (the reads above precede these writes, and only this thread touches ch)
         if (owner && commit > 0) {
@@ -568,8 +574,8 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
 #pragma unroll
       for (int t = 0; t < kMaxStepTokens; ++t) {
         if (t < n) {
-          const float ss = wave_sum(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
-          const float f = (slot == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
+          const float ss = wave_sum_dpp(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
+          const float f = (slot == 0 ? q_scale : 1.0f) * rsq_normal(ss + l2_eps);
           xv[t][0] *= f;
           xv[t][1] *= f;
         }
@@ -589,12 +595,12 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
   if (tid < 8 && gt < n) {
     s_ab[gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
-    s_ab[gt][1] = sigmoidf_(gb);
+    s_ab[gt][1] = sigmoid_fast(gb);
   }
   __syncthreads();
   if (wave == 0) {  // k_t . q_t of each token
     for (int t = 0; t < n; ++t) {
-      const float kq = wave_sum(s_x[t][0][2 * lane] * s_x[t][1][2 * lane] +
+      const float kq = wave_sum_dpp(s_x[t][0][2 * lane] * s_x[t][1][2 * lane] +
                                 s_x[t][0][2 * lane + 1] * s_x[t][1][2 * lane + 1]);
       if (lane == 0) s_kq[t] = kq;
     }
@@ -648,7 +654,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       float be[2];
       float y[2];
       const float vs[2] = {vv.x, vv.y};
-      const float rG = 1.0f / Gt;
+      const float rG = __builtin_amdgcn_rcpf(Gt);  // Gt in [2^-60, 1]
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const float e = vs[c] - Gt * sk[c];   // e = v - S'k
@@ -686,7 +692,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     yown[t] = t < n ? s_y[wave][t][lane] : 0.f;  // this lane's own writes: no barrier
     if (t < n) {
       // each column sits in one of the lanes with rg < 2: sum over those
-      const float ssum = wave_sum(out_lane ? yown[t] * yown[t] : 0.f);
+      const float ssum = wave_sum_dpp(out_lane ? yown[t] * yown[t] : 0.f);
       if (lane == 0) s_ss[wave][t] = ssum;
     }
   }
@@ -696,9 +702,10 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     for (int t = 0; t < kMaxStepTokens; ++t) {
       if (t < n) {
         const float ssh = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
-        const float inv = rsqrtf(ssh * (1.0f / kD) + rms_eps);
+        const float inv = rsq_normal(ssh * (1.0f / kD) + rms_eps);
         const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
-        Act<T>::store(o, oi, yown[t] * inv * nwv * out_gate(gate, zr[t]));
+        const float sz = sigmoid_fast(zr[t]);
+        Act<T>::store(o, oi, yown[t] * inv * nwv * (gate == 1 ? sz : zr[t] * sz));
       }
     }
   }
