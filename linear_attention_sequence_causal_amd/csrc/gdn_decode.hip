@@ -119,6 +119,22 @@ __device__ __forceinline__ int fp8_scale_exp(float m) {
   return min(max(e, -126), 127);
 }
 
+// Sum of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of a
+// wave), left in all four: two row swaps on the gfx950 permlane crossbar.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Sum over the 64 lanes, left in every lane: a DPP sum inside each 16-lane row, then
+// the four rows (about 8 instructions, against ~30 for a shuffle butterfly).
+__device__ __forceinline__ float wave_sum_dpp(float x) { return rows4_sum(row16_sum(x)); }
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
+__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
+
 template <typename T, typename S>
 __global__ void __launch_bounds__(kDecThreads)
 decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -221,7 +237,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         const float h0 = Act<T>::load(cs, ch), h1 = Act<T>::load(cs, Cc + ch),
                     h2 = Act<T>::load(cs, 2 * Cc + ch);
         const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
-        xv[u] = siluf_(w.x * h0 + w.y * h1 + w.z * h2 + w.w * raw);
+        xv[u] = silu_fast(w.x * h0 + w.y * h1 + w.z * h2 + w.w * raw);
         // shift the cache in place (reads above precede these writes)
         Act<T>::store(cs, ch, h1);
         Act<T>::store(cs, Cc + ch, h2);
@@ -229,8 +245,8 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       }
     }
     if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) over 128 channels
-      const float ss = wave_sum(xv[0] * xv[0] + xv[1] * xv[1]);
-      const float f = (slot == 0 ? q_scale : 1.0f) * rsqrtf(ss + l2_eps);
+      const float ss = wave_sum_dpp(xv[0] * xv[0] + xv[1] * xv[1]);
+      const float f = (slot == 0 ? q_scale : 1.0f) * rsq_normal(ss + l2_eps);
       xv[0] *= f;
       xv[1] *= f;
     }
@@ -241,7 +257,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   }
   __syncthreads();
   if (tid < 64) {
-    const float kq = wave_sum(s_x[0][2 * tid] * s_x[1][2 * tid] +
+    const float kq = wave_sum_dpp(s_x[0][2 * tid] * s_x[1][2 * tid] +
                               s_x[0][2 * tid + 1] * s_x[1][2 * tid + 1]);
     if (tid == 0) s_misc[0] = kq;
   }
@@ -258,7 +274,8 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   // ---- 3./4. per v head: state stream and epilogue ---------------------------------
   for (int j = 0; j < r; ++j) {
     const int h = r * g + j;
-    const float zg = out_gate(gate, Act<T>::from_bits(zbits));
+    const float zv = Act<T>::from_bits(zbits), sz = sigmoid_fast(zv);
+    const float zg = gate == 1 ? sz : zv * sz;  // output gate sigmoid(z) or SiLU(z)
     if (j + 1 < r) zbits = Act<T>::bits(z, ((int64_t)bseq * Hv + h + 1) * kD + ztid);
     // the next head's loads go out first (vector-memory waits are in issue order, so
     // waiting for this head's state does not wait for them)
@@ -291,7 +308,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       }
     };
     const float alpha = __expf(log_decay(a[(int64_t)bseq * Hv + h], A_log[h], dt_bias[h]));
-    const float beta = sigmoidf_(b[(int64_t)bseq * Hv + h]);
+    const float beta = sigmoid_fast(b[(int64_t)bseq * Hv + h]);
     float sk[CPT], sq[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) sk[c] = sq[c] = 0.f;
@@ -322,7 +339,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
       const float y = alpha * vq + beta * kq * e;    // S'' q
       s_e[tid] = e;
       s_y[tid] = y;
-      const float ssum = wave_sum(y * y);
+      const float ssum = wave_sum_dpp(y * y);
       if ((tid & 63) == 0) s_misc[1 + (tid >> 6)] = ssum;
     }
     __syncthreads();
@@ -360,7 +377,7 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         *reinterpret_cast<f32x4 *>(scale_ptr(j) + i) = f32x4{snew[i], snew[i + 1], snew[i + 2], snew[i + 3]};
     }
     if (tid < kD) {
-      const float inv = rsqrtf((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
+      const float inv = rsq_normal((s_misc[1] + s_misc[2]) * (1.0f / kD) + rms_eps);
       Act<T>::store(o, ((int64_t)bseq * Hv + h) * kD + tid, s_y[tid] * inv * nwv * zg);
     }
     __syncthreads();  // s_red, s_e, s_y, s_misc are reused by the next head
@@ -423,21 +440,6 @@ template hipError_t launch_decode<bf16_t>(const void *, const void *, const void
 // untouched, and a second pass with the accepted count advances them.
 constexpr int kMaxStepTokens = 8;
 
-// Sum of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of a
-// wave), left in all four: two row swaps on the gfx950 permlane crossbar.
-__device__ __forceinline__ float rows4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-// Sum over the 64 lanes, left in every lane: a DPP sum inside each 16-lane row, then
-// the four rows (about 8 instructions, against ~30 for a shuffle butterfly).
-__device__ __forceinline__ float wave_sum_dpp(float x) { return rows4_sum(row16_sum(x)); }
-// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE divide
-__device__ __forceinline__ float silu_fast(float u) { return u * sigmoid_fast(u); }
 
 // One workgroup of four waves per (sequence, v head): wave w holds value columns
 // 32 w + 2 cg, + 1 (cg = lane & 15) and key rows 32 rg .. + 31 (rg = lane >> 4) of the
