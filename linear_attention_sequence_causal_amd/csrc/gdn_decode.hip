@@ -441,38 +441,62 @@ template hipError_t launch_decode<bf16_t>(const void *, const void *, const void
 constexpr int kMaxStepTokens = 8;
 
 
-// One workgroup of four waves per (sequence, v head): wave w holds value columns
-// 32 w + 2 cg, + 1 (cg = lane & 15) and key rows 32 rg .. + 31 (rg = lane >> 4) of the
-// fp32 state, 64 values per lane, so that four waves fit on a SIMD and the state
-// reads of some workgroups overlap the token loops of others.  The r workgroups of a
-// q/k head each convolve its q and k rows from the cache and only read the cache's
-// q/k channels; a second kernel on the same stream advances those channels after
-// every workgroup has read them (qk_cache_advance_kernel), so no workgroup reads a
-// cache word that another one of the same launch writes.  The v channels of a head
-// are read and advanced by the thread that convolves them, in its head's workgroup.
-// A token's S k and S q sums are finished across the four row lanes with permlane
-// swaps, so the token loop needs no LDS round trip and no barrier; the RMS of each
-// token's y (split over the four waves) is taken once after the loop.
+// One workgroup of four waves per (sequence, v head), in the chunk form of the n
+// tokens: with Gam_t the decay product of tokens 0..t and R_ts = Gam_t / Gam_s (the
+// product of the decays of tokens s+1..t), unrolling the per-token update gives
+//   u_t = beta_t (v_t - Gam_t S_0 k_t - sum_{s<t} R_ts (k_s . k_t) u_s),
+//   y_t = Gam_t S_0 q_t + sum_{s<=t} R_ts (k_s . q_t) u_s,
+//   S_c = Gam_{c-1} S_0 + sum_{s<c} R_{c-1,s} u_s k_s^T     (after c tokens),
+// so every state product is taken against the state the call starts from, S_0:
+// the products S_0 k_t and S_0 q_t of all n tokens, then per value column an n x n
+// triangular recurrence, then one rank-c update.  Both products run on fp32 MFMA
+// (4x4x1 with the A operand broadcast to the 16 blocks, i.e. an outer product of
+// four values with the 64 lanes), with the state in the accumulator layout:
+// wave w holds key rows 64 (w & 1) .. + 63 and value columns 64 (w >> 1) .. + 63,
+// register i of tile m = row 4 m + i of that range, lane = value column.  As the B
+// operand of the first product each register is one key row; as the accumulator of
+// the update, one MFMA per tile adds a token's rank-1 term.  The two key-row halves'
+// partial products meet in LDS.  The r workgroups of a q/k head each convolve its q
+// and k rows from the cache and only read the cache's q/k channels; a second
+// kernel on the same stream advances those channels after every workgroup has read
+// them (qk_cache_advance_kernel), so no workgroup reads a cache word that another
+// one of the same launch writes.  The v channels of a head are read and advanced by
+// the thread that convolves them, in its head's workgroup.
 constexpr int kTokThreads = 256;
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-// One v head's fp32 state as a raw buffer: each lane's 8-byte pieces are addressed by
-// its own offset plus a uniform row offset, so no per-row 64-bit addresses are kept
-// in registers.  Cache policy non-temporal (the state is touched once per call).
+// One v head's fp32 state as a raw buffer: each lane's words are addressed by its
+// own offset plus a uniform row offset, so no per-row 64-bit addresses are kept in
+// registers.  Cache policy non-temporal (the state is touched once per call).
 constexpr int kNtPolicy = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_buf(float *base) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kD * kD * (int)sizeof(float),
                                            0x00020000);
 }
-__device__ __forceinline__ f32x2_t ld_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off) {
-  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, row_off, kNtPolicy));
+__device__ __forceinline__ float ld_row1(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, row_off, kNtPolicy));
 }
-__device__ __forceinline__ void st_row2(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off,
-                                        f32x2_t x) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, x), r, off, row_off,
-                                        kNtPolicy);
+__device__ __forceinline__ void st_row1(__amdgpu_buffer_rsrc_t r, uint32_t off, int row_off,
+                                        float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, row_off, kNtPolicy);
+}
+// C[i][lane] += a[4 abid + i] * b[lane] (i = 0..3): the four values of block abid
+// of a broadcast to all 16 blocks of the 4x4x1 fp32 product.
+template <int ABID>
+__device__ __forceinline__ f32x4 outer4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
 }
 
-template <typename T>
+// The four key rows of one state tile (its registers 0..3) against blocks B0 .. B0 + 3
+// of the k and q operands.
+template <int B0>
+__device__ __forceinline__ void rows4(float ak, float aq, f32x4 hm, f32x4 &yk, f32x4 &yq) {
+  yk = outer4<B0>(ak, hm[0], yk);     yq = outer4<B0>(aq, hm[0], yq);
+  yk = outer4<B0 + 1>(ak, hm[1], yk); yq = outer4<B0 + 1>(aq, hm[1], yq);
+  yk = outer4<B0 + 2>(ak, hm[2], yk); yq = outer4<B0 + 2>(aq, hm[2], yq);
+  yk = outer4<B0 + 3>(ak, hm[3], yk); yq = outer4<B0 + 3>(aq, hm[3], yq);
+}
+
+// NG groups of four token slots (n <= 4 NG).
+template <typename T, int NG>
 __global__ void __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                      const float *__restrict__ a, const float *__restrict__ b,
@@ -482,6 +506,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
                      float rms_eps, float *__restrict__ state, T *__restrict__ conv_state,
                      const int32_t *__restrict__ num_commit, T *__restrict__ o, int Hk, int Hv,
                      int n, int gate) {
+  constexpr int NT = 4 * NG;  // token slots
   const int r = Hv / Hk;
   const int jh = blockIdx.x % r;                  // v head within its q/k group
   const int g = (blockIdx.x / r) % Hk;            // q/k head
@@ -492,30 +517,27 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
 
   // v head (the clamp is a no-op; in this form the kernel fits 128 registers unspilled)
   const int h = r * g + min(jh, r - 1);
-  const int cg = lane & 15, rg = lane >> 4;
-  const int col0 = 32 * (wave & 3) + 2 * cg;      // 2 value columns
-  const int row0 = 32 * rg;                       // 32 key rows
-  const int ocol = col0 + (rg & 1);               // the column this lane outputs
-  const bool out_lane = rg < 2;                   // rows 2, 3 repeat rows 0, 1
+  const int dh = wave & 1, chh = wave >> 1;
+  const int d0 = 64 * dh;                         // key rows d0 .. d0 + 63
+  const int col = 64 * chh + lane;                // this lane's value column
 
   __shared__ float s_x[kMaxStepTokens][3][kD];    // post-prologue q, k, v rows
-  __shared__ float s_kq[kMaxStepTokens];
-  __shared__ float s_ss[4][kMaxStepTokens];       // per-wave partial sums of y^2
+  __shared__ f32x4 s_yp[2][2][2 * NG][64];        // [key half][column half][k|q, group]
   __shared__ float s_ab[kMaxStepTokens][2];       // alpha, beta of each token
-  __shared__ float s_y[4][kMaxStepTokens][64];    // y of each lane's output column
+  __shared__ float s_cq[kMaxStepTokens][kMaxStepTokens];  // R_ts (k_s . q_t), s <= t
+  __shared__ float s_ck[kMaxStepTokens][kMaxStepTokens];  // R_ts (k_s . k_t), s < t
+  __shared__ float s_R[kMaxStepTokens][kMaxStepTokens];   // R_ts
+  __shared__ float s_G[kMaxStepTokens];                   // Gam_t
+  __shared__ float s_ss[2][kMaxStepTokens];       // sum of y^2 per column half
 
-  // the gate inputs first; the state is read after the prologue, whose registers it
-  // would otherwise share (four waves per SIMD need at most 128 registers per lane)
-  float ga = 0.f, gb = 0.f;  // gate inputs of token gt (tid < 8)
+  // gate inputs of token gt (used by tid < 8); every load in the prologue is
+  // unconditional, at a clamped index, so that none of them waits at a branch
   const int gh = r * g + jh, gt = tid & 7;  // gh = h
-  if (tid < 8 && gt < n) {
-    const int64_t gi = ((int64_t)bseq * n + gt) * Hv + gh;
-    ga = a[gi];
-    gb = b[gi];
-  }
+  const int64_t gi = ((int64_t)bseq * n + min(gt, n - 1)) * Hv + gh;
+  const float ga = a[gi], gb = b[gi], gA = A_log[gh], gdt = dt_bias[gh];
   const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
-  const uint32_t hoff = (uint32_t)(row0 * kD + col0) * (uint32_t)sizeof(float);
-  f32x2_t Hs[32];
+  const uint32_t hoff = (uint32_t)(d0 * kD + col) * (uint32_t)sizeof(float);
+  f32x4 H[16];
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
   // section = wave (waves 0-2): q, k, v.  raw[0..2] = cached rows (oldest first),
@@ -524,9 +546,11 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   {
     T *cs = conv_state + (int64_t)bseq * 3 * Cc;
     const int c0 = lane * 2;
-    const int slot = wave;
-    const bool active = slot < 3;
-    const bool owner = slot == 2;  // v channels only
+    // wave 3 repeats the q loads (channels no workgroup of this launch writes) and
+    // stores nothing
+    const int slot = wave == 3 ? 0 : wave;
+    const bool active = wave < 3;
+    const bool owner = wave == 2;   // v channels only
     int64_t cbase, hstride, sidx;
     const T *src;
     if (slot == 0) {
@@ -539,42 +563,58 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
       cbase = 2LL * Hk * kD + (int64_t)h * kD; src = v; hstride = (int64_t)Hv * kD;
       sidx = ((int64_t)bseq * n * Hv + h) * kD;
     }
-    float xv[kMaxStepTokens][2];
+    // the prologue's loads first, then the state's (one key row per register), so
+    // that the state is in flight while the convolution waits for its inputs only
+    // (raw bits; widened after the state loads have gone out)
+    uint32_t rb[2][3 + NT];
+    float4 w[2];
 #pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) xv[t][0] = xv[t][1] = 0.f;
-    if (active) {
+    for (int u = 0; u < 2; ++u) {
+      const int64_t ch = cbase + c0 + u;
+      rb[u][0] = Act<T>::bits(cs, ch);
+      rb[u][1] = Act<T>::bits(cs, Cc + ch);
+      rb[u][2] = Act<T>::bits(cs, 2 * Cc + ch);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t ch = cbase + c0 + u;
-        float raw[3 + kMaxStepTokens];
-        raw[0] = Act<T>::load(cs, ch);
-        raw[1] = Act<T>::load(cs, Cc + ch);
-        raw[2] = Act<T>::load(cs, 2 * Cc + ch);
+      for (int t = 0; t < NT; ++t)  // slots past n hold token n - 1 and are not used
+        rb[u][3 + t] = Act<T>::bits(src, sidx + min(t, n - 1) * hstride + c0 + u);
+      w[u] = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the state loads behind these
 #pragma unroll
-        for (int t = 0; t < kMaxStepTokens; ++t)
-          raw[3 + t] = t < n ? Act<T>::load(src, sidx + t * hstride + c0 + u) : 0.f;
-        const float4 w = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
+    for (int m = 0; m < 16; ++m)
 #pragma unroll
-        for (int t = 0; t < kMaxStepTokens; ++t)
-          if (t < n)
-            xv[t][u] = silu_fast(w.x * raw[t] + w.y * raw[t + 1] + w.z * raw[t + 2] + w.w * raw[t + 3]);
-        // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
-        // (the reads above precede these writes, and only this thread touches ch)
-        if (owner && commit > 0) {
+      for (int i = 0; i < 4; ++i)
+        H[m][i] = ld_row1(hrs, hoff, (4 * m + i) * kD * (int)sizeof(float));
+    __builtin_amdgcn_sched_barrier(0);
+    float raw[2][3 + NT];
 #pragma unroll
-          for (int s2 = 0; s2 < 3; ++s2) {
-            float x = raw[0];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 1; i < 3 + kMaxStepTokens; ++i)
-              if (i == commit + s2) x = raw[i];
-            Act<T>::store(cs, s2 * Cc + ch, x);
-          }
+      for (int i = 0; i < 3 + NT; ++i) raw[u][i] = Act<T>::from_bits(rb[u][i]);
+    float xv[NT][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t ch = cbase + c0 + u;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        xv[t][u] = silu_fast(w[u].x * raw[u][t] + w[u].y * raw[u][t + 1] +
+                             w[u].z * raw[u][t + 2] + w[u].w * raw[u][t + 3]);
+      // the cache advances by `commit` tokens: rows commit .. commit + 2 of raw
+      // (the reads above precede these writes, and only this thread touches ch)
+      if (owner && commit > 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          float x = raw[u][0];
+#pragma unroll
+          for (int i = 1; i < 3 + NT; ++i)
+            if (i == commit + s2) x = raw[u][i];
+          Act<T>::store(cs, s2 * Cc + ch, x);
         }
       }
     }
-    if (slot < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token
+    if (wave < 2) {  // L2-normalise q (wave 0) and k (wave 1) of each token
 #pragma unroll
-      for (int t = 0; t < kMaxStepTokens; ++t) {
+      for (int t = 0; t < NT; ++t) {
         if (t < n) {
           const float ss = wave_sum_dpp(xv[t][0] * xv[t][0] + xv[t][1] * xv[t][1]);
           const float f = (slot == 0 ? q_scale : 1.0f) * rsq_normal(ss + l2_eps);
@@ -583,133 +623,161 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         }
       }
     }
-    if (slot < 3) {
+    if (active) {
 #pragma unroll
-      for (int t = 0; t < kMaxStepTokens; ++t)
+      for (int t = 0; t < NT; ++t)
         if (t < n) {
           s_x[t][slot][c0] = xv[t][0];
           s_x[t][slot][c0 + 1] = xv[t][1];
         }
     }
   }
-  // the state (the barriers below do not wait for these loads)
-#pragma unroll
-  for (int i = 0; i < 32; ++i) Hs[i] = ld_row2(hrs, hoff, i * kD * (int)sizeof(float));
   if (tid < 8 && gt < n) {
-    s_ab[gt][0] = __expf(log_decay(ga, A_log[gh], dt_bias[gh]));
+    s_ab[gt][0] = __expf(log_decay(ga, gA, gdt));
     s_ab[gt][1] = sigmoid_fast(gb);
   }
   __syncthreads();
-  if (wave == 0) {  // k_t . q_t of each token
-    for (int t = 0; t < n; ++t) {
-      const float kq = wave_sum_dpp(s_x[t][0][2 * lane] * s_x[t][1][2 * lane] +
-                                s_x[t][0][2 * lane + 1] * s_x[t][1][2 * lane + 1]);
-      if (lane == 0) s_kq[t] = kq;
+
+  // ---- S_0 k_t and S_0 q_t over this wave's 64 key rows (MFMA) ------------------------
+  // A operand of key rows d0 + 16 gq .. + 15: lane 4 b + i holds token 4 tg + i of row
+  // d0 + 16 gq + b, so block abid = 4 mm + i of it pairs with register i of tile
+  // 4 gq + mm.  Token slots past n read as zero.
+  f32x4 Yk[NG], Yq[NG];
+#pragma unroll
+  for (int tg = 0; tg < NG; ++tg) Yk[tg] = Yq[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int ti = lane & 3, di = lane >> 2;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      float ak[NG], aq[NG];
+#pragma unroll
+      for (int tg = 0; tg < NG; ++tg) {
+        const int t = 4 * tg + ti;
+        const bool live = t < n;
+        ak[tg] = live ? s_x[t][1][d0 + 16 * gq + di] : 0.f;
+        aq[tg] = live ? s_x[t][0][d0 + 16 * gq + di] : 0.f;
+      }
+#pragma unroll
+      for (int tg = 0; tg < NG; ++tg) {
+        rows4<0>(ak[tg], aq[tg], H[4 * gq + 0], Yk[tg], Yq[tg]);
+        rows4<4>(ak[tg], aq[tg], H[4 * gq + 1], Yk[tg], Yq[tg]);
+        rows4<8>(ak[tg], aq[tg], H[4 * gq + 2], Yk[tg], Yq[tg]);
+        rows4<12>(ak[tg], aq[tg], H[4 * gq + 3], Yk[tg], Yq[tg]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tg = 0; tg < NG; ++tg) {
+    s_yp[dh][chh][2 * tg][lane] = Yk[tg];
+    s_yp[dh][chh][2 * tg + 1][lane] = Yq[tg];
+  }
+
+  // ---- the n x n coefficients: token pairs s <= t dealt round-robin to the waves ------
+  {
+    int p = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int s = 0; s <= t; ++s, ++p) {
+        if (t < n && (p & 3) == wave) {
+          const f32x2_t ks = *reinterpret_cast<const f32x2_t *>(&s_x[s][1][2 * lane]);
+          const f32x2_t qt = *reinterpret_cast<const f32x2_t *>(&s_x[t][0][2 * lane]);
+          const float kq = wave_sum_dpp(ks.x * qt.x + ks.y * qt.y);
+          float kk = 0.f;
+          if (s < t) {
+            const f32x2_t kt = *reinterpret_cast<const f32x2_t *>(&s_x[t][1][2 * lane]);
+            kk = wave_sum_dpp(ks.x * kt.x + ks.y * kt.y);
+          }
+          float R = 1.0f;
+#pragma unroll
+          for (int u = s + 1; u <= t; ++u) R *= s_ab[u][0];
+          if (lane == 0) {
+            s_cq[t][s] = R * kq;
+            s_ck[t][s] = R * kk;
+            s_R[t][s] = R;
+            if (s == 0) s_G[t] = R * s_ab[0][0];
+          }
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- token loop: the state stays in registers, no barrier -----------------------------
-  // The registers hold the state divided by the running decay product of this call,
-  // S = Gam * Hs, so a token costs one FMA per state element for the update instead
-  // of a decay multiply and an FMA: with Gam_t = alpha_t Gam_{t-1},
-  //   alpha_t S_{t-1} k = Gam_t (Hs k),  S_t = Gam_t (Hs + (beta e / Gam_t) k^T).
-  // When Gam_t falls below 2^-60 it is folded into Hs (and taken as 1), which also
-  // covers alpha = 0.  Gam is uniform (one head per workgroup).
-  float Gam = 1.0f;
-#pragma unroll 1
-  for (int t = 0; t < n; ++t) {
-    {
-      const float alpha = s_ab[t][0];
-      const float beta = s_ab[t][1];
-      float Gt = Gam * alpha;
-      if (Gt < 0x1p-60f) {
+  // ---- per value column: the n x n recurrence for u_t and y_t -------------------------
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          Hs[i].x *= Gt; Hs[i].y *= Gt;
-        }
-        Gt = 1.0f;
-      }
-      Gam = Gt;
-      // k and q rows 32 rg .. + 31 are read from LDS in blocks of 4 (broadcast
-      // within each 16-lane row); k again for the update, to keep registers low
-      float sk[2] = {0, 0}, sq[2] = {0, 0};
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
-        const f32x4 qq = *reinterpret_cast<const f32x4 *>(&s_x[t][0][row0 + i]);
-        const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x2_t hv = Hs[i + u];
-          sk[0] += hv.x * kv[u]; sk[1] += hv.y * kv[u];
-          sq[0] += hv.x * qv[u]; sq[1] += hv.y * qv[u];
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        sk[c] = rows4_sum(sk[c]);
-        sq[c] = rows4_sum(sq[c]);
-      }
-      const f32x2_t vv = *reinterpret_cast<const f32x2_t *>(&s_x[t][2][col0]);
-      const float kq = s_kq[t];
-      float be[2];
-      float y[2];
-      const float vs[2] = {vv.x, vv.y};
-      const float rG = __builtin_amdgcn_rcpf(Gt);  // Gt in [2^-60, 1]
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float e = vs[c] - Gt * sk[c];   // e = v - S'k
-        y[c] = Gt * sq[c] + beta * kq * e;    // S_t q
-        be[c] = beta * e * rG;
-      }
-      s_y[wave][t][lane] = (rg & 1) ? y[1] : y[0];
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_x[t][1][row0 + i]);
-        const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          Hs[i + u].x = fmaf(kv[u], be[0], Hs[i + u].x);
-          Hs[i + u].y = fmaf(kv[u], be[1], Hs[i + u].y);
-        }
-      }
-      if (t + 1 == commit) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          st_row2(hrs, hoff, i * kD * (int)sizeof(float), f32x2_t{Gam * Hs[i].x, Gam * Hs[i].y});
-      }
-    }
+  for (int tg = 0; tg < NG; ++tg) {
+    Yk[tg] += s_yp[dh ^ 1][chh][2 * tg][lane];
+    Yq[tg] += s_yp[dh ^ 1][chh][2 * tg + 1][lane];
   }
-
-  // ---- epilogue: RMS over the head's 128 columns (four waves), SiLU(z) gate -----------
-  const float nwv = norm_w ? norm_w[ocol] : 1.0f;
-  float zr[kMaxStepTokens];
+  float u[NT], y[NT];
 #pragma unroll
-  for (int t = 0; t < kMaxStepTokens; ++t)
-    zr[t] = Act<T>::load(z, (((int64_t)bseq * n + min(t, n - 1)) * Hv + h) * kD + ocol);
-  float yown[kMaxStepTokens];
-#pragma unroll
-  for (int t = 0; t < kMaxStepTokens; ++t) {
-    yown[t] = t < n ? s_y[wave][t][lane] : 0.f;  // this lane's own writes: no barrier
+  for (int t = 0; t < NT; ++t) {
+    u[t] = y[t] = 0.f;
     if (t < n) {
-      // each column sits in one of the lanes with rg < 2: sum over those
-      const float ssum = wave_sum_dpp(out_lane ? yown[t] * yown[t] : 0.f);
-      if (lane == 0) s_ss[wave][t] = ssum;
+      const float Gt = s_G[t];
+      float e = s_x[t][2][col] - Gt * Yk[t >> 2][t & 3];
+#pragma unroll
+      for (int s = 0; s < t; ++s) e -= s_ck[t][s] * u[s];
+      u[t] = s_ab[t][1] * e;
+      float yy = Gt * Yq[t >> 2][t & 3];
+#pragma unroll
+      for (int s = 0; s <= t; ++s) yy += s_cq[t][s] * u[s];
+      y[t] = yy;
     }
   }
-  __syncthreads();
-  if (out_lane) {
+
+  // ---- epilogue: RMS over the head's 128 columns (two column halves), SiLU(z) gate ----
+  // the two key-half waves of a column half hold the same y; the first one sums it
+  if (dh == 0) {
 #pragma unroll
-    for (int t = 0; t < kMaxStepTokens; ++t) {
+    for (int t = 0; t < NT; ++t)
       if (t < n) {
-        const float ssh = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
-        const float inv = rsq_normal(ssh * (1.0f / kD) + rms_eps);
-        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + ocol;
-        const float sz = sigmoid_fast(zr[t]);
-        Act<T>::store(o, oi, yown[t] * inv * nwv * (gate == 1 ? sz : zr[t] * sz));
+        const float ssum = wave_sum_dpp(y[t] * y[t]);
+        if (lane == 0) s_ss[chh][t] = ssum;
+      }
+  }
+  __syncthreads();
+  {
+    const float nwv = norm_w ? norm_w[col] : 1.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < n && (t & 1) == dh) {  // the key-half waves take alternate tokens
+        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + col;
+        const float zr = Act<T>::load(z, oi);
+        const float inv = rsq_normal((s_ss[0][t] + s_ss[1][t]) * (1.0f / kD) + rms_eps);
+        const float sz = sigmoid_fast(zr);
+        Act<T>::store(o, oi, y[t] * inv * nwv * (gate == 1 ? sz : zr * sz));
       }
     }
+  }
+
+  // ---- state after `commit` tokens: S_c = Gam_{c-1} S_0 + sum_s R_{c-1,s} u_s k_s^T ---
+  // one MFMA per tile and token: A = k_s at key rows d0 + 4 m .. + 3 (block m of the
+  // register holding k_s at row d0 + lane), B = R u_s at this lane's column
+  if (commit > 0) {
+    const float Gc = s_G[commit - 1];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) H[m] *= Gc;
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      if (s < commit) {
+        const float w = s_R[commit - 1][s] * u[s];
+        const float kd = s_x[s][1][d0 + lane];
+        H[0] = outer4<0>(kd, w, H[0]);   H[1] = outer4<1>(kd, w, H[1]);
+        H[2] = outer4<2>(kd, w, H[2]);   H[3] = outer4<3>(kd, w, H[3]);
+        H[4] = outer4<4>(kd, w, H[4]);   H[5] = outer4<5>(kd, w, H[5]);
+        H[6] = outer4<6>(kd, w, H[6]);   H[7] = outer4<7>(kd, w, H[7]);
+        H[8] = outer4<8>(kd, w, H[8]);   H[9] = outer4<9>(kd, w, H[9]);
+        H[10] = outer4<10>(kd, w, H[10]); H[11] = outer4<11>(kd, w, H[11]);
+        H[12] = outer4<12>(kd, w, H[12]); H[13] = outer4<13>(kd, w, H[13]);
+        H[14] = outer4<14>(kd, w, H[14]); H[15] = outer4<15>(kd, w, H[15]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_row1(hrs, hoff, (4 * m + i) * kD * (int)sizeof(float), H[m][i]);
   }
 }
 
@@ -757,10 +825,16 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                                 int n, int Hk, int Hv, int gate, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   dim3 grid((unsigned)batch * (unsigned)Hv);
-  hipLaunchKernelGGL((decode_tokens_kernel<T>), grid, dim3(kTokThreads), 0, stream,
-                     (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w, A_log,
-                     dt_bias, norm_w, q_scale, l2_eps, rms_eps, state, (T *)conv_state,
-                     num_commit, (T *)o, Hk, Hv, n, gate);
+  if (n <= 4)
+    hipLaunchKernelGGL((decode_tokens_kernel<T, 1>), grid, dim3(kTokThreads), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
+                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, state,
+                       (T *)conv_state, num_commit, (T *)o, Hk, Hv, n, gate);
+  else
+    hipLaunchKernelGGL((decode_tokens_kernel<T, 2>), grid, dim3(kTokThreads), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
+                       A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, state,
+                       (T *)conv_state, num_commit, (T *)o, Hk, Hv, n, gate);
   const int64_t nch = (int64_t)batch * 2 * Hk * kD;
   hipLaunchKernelGGL((qk_cache_advance_kernel<T>), dim3((unsigned)((nch + 255) / 256)), dim3(256),
                      0, stream, (const T *)q, (const T *)k, (T *)conv_state, num_commit, batch, Hk,
