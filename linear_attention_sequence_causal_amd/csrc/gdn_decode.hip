@@ -783,37 +783,33 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
 
 // The q/k conv-cache channels advance by commit = num_commit[b] tokens after the
 // n-token step has read them (same stream, so every read of the step precedes these
-// writes): rows commit .. commit + 2 of [cache rows, new tokens].  One thread per
-// (sequence, q/k channel); coalesced over channels.
-template <typename T>
+// writes): new row s = row commit + s of [cache rows, new tokens].  One thread per
+// (sequence, V consecutive q/k channels), coalesced over channels; each thread reads
+// its three source rows before it writes, and no other thread touches its channels.
+template <typename T, int V>
 __global__ void __launch_bounds__(256)
 qk_cache_advance_kernel(const T *__restrict__ q, const T *__restrict__ k, T *__restrict__ conv_state,
                         const int32_t *__restrict__ num_commit, int batch, int Hk, int Hv, int n) {
-  const int64_t Cqk = 2LL * Hk * kD;
+  typedef T vec_t __attribute__((ext_vector_type(V)));
+  const int64_t Cqk = 2LL * Hk * kD, groups = Cqk / V;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)batch * Cqk) return;
-  const int bseq = (int)(i / Cqk);
-  const int64_t ch = i % Cqk;
+  if (i >= (int64_t)batch * groups) return;
+  const int bseq = (int)(i / groups);
+  const int64_t ch = (i % groups) * V;
   const int commit = num_commit ? min(max(num_commit[bseq], 0), n) : n;
   if (commit == 0) return;
   const int64_t Cc = Cqk + (int64_t)Hv * kD;
-  T *cs = conv_state + (int64_t)bseq * 3 * Cc;
+  T *cs = conv_state + (int64_t)bseq * 3 * Cc + ch;
   const int64_t qkD = (int64_t)Hk * kD;
-  const T *src = ch < qkD ? q + (int64_t)bseq * n * qkD + ch : k + (int64_t)bseq * n * qkD + (ch - qkD);
-  T raw[3 + kMaxStepTokens];
-  raw[0] = cs[ch];
-  raw[1] = cs[Cc + ch];
-  raw[2] = cs[2 * Cc + ch];
-#pragma unroll
-  for (int t = 0; t < kMaxStepTokens; ++t) raw[3 + t] = t < n ? src[t * qkD] : raw[2];
+  const T *src = (ch < qkD ? q + ch : k + (ch - qkD)) + (int64_t)bseq * n * qkD;
+  vec_t x[3];
 #pragma unroll
   for (int s2 = 0; s2 < 3; ++s2) {
-    T x = raw[0];
-#pragma unroll
-    for (int j = 1; j < 3 + kMaxStepTokens; ++j)
-      if (j == commit + s2) x = raw[j];
-    cs[s2 * Cc + ch] = x;
+    const int j = commit + s2;  // 1 .. n + 2
+    x[s2] = *reinterpret_cast<const vec_t *>(j < 3 ? cs + j * Cc : src + (j - 3) * qkD);
   }
+#pragma unroll
+  for (int s2 = 0; s2 < 3; ++s2) *reinterpret_cast<vec_t *>(cs + s2 * Cc) = x[s2];
 }
 
 template <typename T>
@@ -835,10 +831,18 @@ hipError_t launch_decode_tokens(const void *q, const void *k, const void *v, con
                        (const T *)q, (const T *)k, (const T *)v, a, b, (const T *)z, conv_w,
                        A_log, dt_bias, norm_w, q_scale, l2_eps, rms_eps, state,
                        (T *)conv_state, num_commit, (T *)o, Hk, Hv, n, gate);
+  // eight channels (one 16-byte access for bf16) per thread when the q, k and cache
+  // pointers allow it, one channel otherwise
   const int64_t nch = (int64_t)batch * 2 * Hk * kD;
-  hipLaunchKernelGGL((qk_cache_advance_kernel<T>), dim3((unsigned)((nch + 255) / 256)), dim3(256),
-                     0, stream, (const T *)q, (const T *)k, (T *)conv_state, num_commit, batch, Hk,
-                     Hv, n);
+  const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)conv_state) % (8 * sizeof(T))) == 0;
+  if (vec)
+    hipLaunchKernelGGL((qk_cache_advance_kernel<T, 8>), dim3((unsigned)((nch / 8 + 255) / 256)),
+                       dim3(256), 0, stream, (const T *)q, (const T *)k, (T *)conv_state,
+                       num_commit, batch, Hk, Hv, n);
+  else
+    hipLaunchKernelGGL((qk_cache_advance_kernel<T, 1>), dim3((unsigned)((nch + 255) / 256)),
+                       dim3(256), 0, stream, (const T *)q, (const T *)k, (T *)conv_state,
+                       num_commit, batch, Hk, Hv, n);
   return hipGetLastError();
 }
 

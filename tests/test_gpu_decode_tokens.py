@@ -88,13 +88,16 @@ def test_tokens_fp32_small_heads():
 
 
 @gpu
-@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 9), (1, 1)])
-def test_tokens_head_layouts(hk, hv):
-    """One, four and three v heads per q/k head: every v head's workgroup convolves the
-    q/k rows from the cache, which a second kernel advances afterwards."""
-    w = S.scaled(S.DECODE_B256, decode_batch=5, num_qk_heads=hk, num_v_heads=hv, seed=71 + hv)
-    setup, t = _case(w, 3)
-    _check(setup, t, 3, label=f"decode_tokens n=3 Hk={hk} Hv={hv}")
+@pytest.mark.parametrize("hk,hv,n", [(4, 4, 3), (2, 8, 3), (3, 9, 3), (1, 1, 3), (4, 4, 6),
+                                     (3, 9, 7), (2, 10, 4), (1, 7, 2), (1, 8, 5)])
+def test_tokens_head_layouts(hk, hv, n):
+    """One to eight v heads per q/k head, with four and with eight token slots: every v
+    head's workgroup convolves the q/k rows from the cache, which a second kernel
+    advances afterwards."""
+    w = S.scaled(S.DECODE_B256, decode_batch=5, num_qk_heads=hk, num_v_heads=hv,
+                 seed=71 + hv + 16 * n)
+    setup, t = _case(w, n)
+    _check(setup, t, n, label=f"decode_tokens n={n} Hk={hk} Hv={hv}")
 
 
 @gpu
