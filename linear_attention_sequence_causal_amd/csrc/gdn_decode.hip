@@ -538,6 +538,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
   const __amdgpu_buffer_rsrc_t hrs = state_buf(state + ((int64_t)bseq * Hv + h) * kD * kD);
   const uint32_t hoff = (uint32_t)(d0 * kD + col) * (uint32_t)sizeof(float);
   f32x4 H[16];
+  uint32_t zb[NT / 2], nwb;  // raw z bits of this lane's output tokens, norm weight bits
 
   // ---- prologue: conv + SiLU of every new token, 2 channels per thread ----------------
   // section = wave (waves 0-2): q, k, v.  raw[0..2] = cached rows (oldest first),
@@ -579,6 +580,11 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         rb[u][3 + t] = Act<T>::bits(src, sidx + min(t, n - 1) * hstride + c0 + u);
       w[u] = *reinterpret_cast<const float4 *>(conv_w + ch * 4);
     }
+    // the epilogue's inputs: z of the tokens this lane outputs (2 i + dh), the norm weight
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i)
+      zb[i] = Act<T>::bits(z, (((int64_t)bseq * n + min(2 * i + dh, n - 1)) * Hv + h) * kD + col);
+    nwb = norm_w ? __float_as_uint(norm_w[col]) : 0x3F800000u;
     __builtin_amdgcn_sched_barrier(0);  // keep the state loads behind these
 #pragma unroll
     for (int m = 0; m < 16; ++m)
@@ -726,8 +732,7 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
     }
   }
 
-  // ---- epilogue: RMS over the head's 128 columns (two column halves), SiLU(z) gate ----
-  // the two key-half waves of a column half hold the same y; the first one sums it
+  // the two key-half waves of a column half hold the same y; the first one sums y^2
   if (dh == 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -736,24 +741,11 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
         if (lane == 0) s_ss[chh][t] = ssum;
       }
   }
-  __syncthreads();
-  {
-    const float nwv = norm_w ? norm_w[col] : 1.0f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < n && (t & 1) == dh) {  // the key-half waves take alternate tokens
-        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + col;
-        const float zr = Act<T>::load(z, oi);
-        const float inv = rsq_normal((s_ss[0][t] + s_ss[1][t]) * (1.0f / kD) + rms_eps);
-        const float sz = sigmoid_fast(zr);
-        Act<T>::store(o, oi, y[t] * inv * nwv * (gate == 1 ? sz : zr * sz));
-      }
-    }
-  }
 
   // ---- state after `commit` tokens: S_c = Gam_{c-1} S_0 + sum_s R_{c-1,s} u_s k_s^T ---
   // one MFMA per tile and token: A = k_s at key rows d0 + 4 m .. + 3 (block m of the
-  // register holding k_s at row d0 + lane), B = R u_s at this lane's column
+  // register holding k_s at row d0 + lane), B = R u_s at this lane's column.  Stored
+  // before the epilogue's barrier, so that the stores are under way while it runs.
   if (commit > 0) {
     const float Gc = s_G[commit - 1];
 #pragma unroll
@@ -778,6 +770,25 @@ decode_tokens_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         st_row1(hrs, hoff, (4 * m + i) * kD * (int)sizeof(float), H[m][i]);
+  }
+
+  // ---- epilogue: RMS over the head's 128 columns (two column halves), output gate -----
+  // (z and the norm weight were loaded with the prologue); the key-half waves take
+  // alternate tokens
+  __syncthreads();
+  {
+    const float nwv = Act<float>::from_bits(nwb);
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      const int t = 2 * i + dh;
+      if (t < n) {
+        const int64_t oi = (((int64_t)bseq * n + t) * Hv + h) * kD + col;
+        const float zr = Act<T>::from_bits(zb[i]);
+        const float inv = rsq_normal((s_ss[0][t] + s_ss[1][t]) * (1.0f / kD) + rms_eps);
+        const float sz = sigmoid_fast(zr);
+        Act<T>::store(o, oi, y[t] * inv * nwv * (gate == 1 ? sz : zr * sz));
+      }
+    }
   }
 }
 
