@@ -161,7 +161,10 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
   static_assert(RPT % 4 == 0 && (!kFp8 || NCG == 8), "state stream layout");
 
   __shared__ float s_x[2 + kDecMaxRatio][kD];  // post-prologue q, k, then v of each v head
-  __shared__ float s_red[NRG][2][kD];          // partial column sums per row group
+  // partial column sums: per row group (fp32, bf16), or per wave once each wave has
+  // summed its own eight row groups on the crossbar (fp8)
+  constexpr int NRED = kFp8 ? kDecThreads / 64 : NRG;
+  __shared__ float s_red[NRED][2][kD];
   __shared__ float s_e[kD];
   __shared__ float s_y[kD];
   __shared__ float s_misc[4];
@@ -322,16 +325,47 @@ decode_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__
         sq[c] += t[c] * qr[i];
       }
     }
+    if constexpr (kFp8) {
+      // The wave's eight row groups are lane bits 3-5 (lane = 8 x row group + column
+      // group).  Reduce-scatter over them: each step pairs two value sets, and the lanes
+      // with the step's bit clear keep the first set summed over the lane pair, those
+      // with it set the second.  After the three steps lane (b5, b4, b3) holds values
+      // 16 b5 + 8 b4 + 4 b3 + 0..3 of the 32 (sk, then sq), summed over the wave.
+      float w16[16], w8[8], w4[4];
 #pragma unroll
-    for (int c = 0; c < CPT; c += 4) {
-      *reinterpret_cast<f32x4 *>(&s_red[rg][0][col + c]) = f32x4{sk[c], sk[c + 1], sk[c + 2], sk[c + 3]};
-      *reinterpret_cast<f32x4 *>(&s_red[rg][1][col + c]) = f32x4{sq[c], sq[c + 1], sq[c + 2], sq[c + 3]};
+      for (int m = 0; m < 16; ++m) {  // bit 5: sk for the lower half, sq for the upper
+        const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(sk[m]),
+                                                        __float_as_uint(sq[m]), false, false);
+        w16[m] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {  // bit 4: the 16-lane rows
+        const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(w16[m]),
+                                                        __float_as_uint(w16[m + 8]), false, false);
+        w8[m] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+      }
+      const bool b3 = (tid & 8) != 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {  // bit 3: lane l and l ^ 8 (rotate by 8 in a row)
+        const float send = b3 ? w8[m] : w8[m + 4];
+        const float keep = b3 ? w8[m + 4] : w8[m];
+        w4[m] = keep + dpp_f<0x128>(send);
+      }
+      const int lane = tid & 63;
+      *reinterpret_cast<f32x4 *>(&s_red[tid >> 6][lane >> 5][col + (lane & 0x18) / 2]) =
+          f32x4{w4[0], w4[1], w4[2], w4[3]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        *reinterpret_cast<f32x4 *>(&s_red[rg][0][col + c]) = f32x4{sk[c], sk[c + 1], sk[c + 2], sk[c + 3]};
+        *reinterpret_cast<f32x4 *>(&s_red[rg][1][col + c]) = f32x4{sq[c], sq[c + 1], sq[c + 2], sq[c + 3]};
+      }
     }
     __syncthreads();
     if (tid < kD) {
       float vk = 0.f, vq = 0.f;
 #pragma unroll
-      for (int p = 0; p < NRG; ++p) {
+      for (int p = 0; p < NRED; ++p) {
         vk += s_red[p][0][tid];
         vq += s_red[p][1][tid];
       }
